@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Throughput of the RankMixer block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
+
+A step is one rm_model_fwd over one batch of the ~1B-class dense workload
+(B=1024, T=32 tokens, D=1536, hidden 6144, L=2 blocks, bf16): token mix +
+residual + LayerNorm, the two grouped per-token FFN products, residual +
+LayerNorm, for both blocks, with inputs and weights resident in HBM.  The
+reported value is samples through one block per second (B * L / step time).
+
+Prints ONE JSON line.  Besides the contract fields it carries
+  roofline      the dominant kernel (by summed time over the timed steps), its
+                algorithmic TFLOP/s from HIP events recorded around each of its
+                launches during the timed region, against the bf16 dense MFMA
+                peak; traffic from the committed rocprofv3 counter summary if it
+                was taken on the current kernel source, else null
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload,
+                timed on this host's cores (rank 0, N=1 only)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "samples/sec RankMixer block fwd (bf16) + % of MI355X MFMA peak"
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def gemm_source_sha() -> str:
+    with open(os.path.join(ROOT, "rankmixer_token_mixing_amd", "csrc", "kernels_gemm.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(config: str, kernel: str):
+    """HBM bytes per launch of `kernel` from profiles/traffic_<config>.json,
+    when that summary was taken on the current GEMM source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("kernels_gemm_sha") != gemm_source_sha():
+        return None
+    k = tr.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inputs, L: int, n_rows: int) -> dict:
+    import numpy as np
+    from oracle import rankmixer_oracle as orc
+    import synthetic_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    cfg = inputs["config"]
+    rows = si.random_rows(cfg.B, n_rows, seed=99)
+    t0 = time.perf_counter()
+    orc.run_config(inputs, rows)
+    dt = time.perf_counter() - t0
+    return {
+        "value": len(rows) * L / dt,
+        "unit": "samples/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {cfg.B} samples through all {L} blocks (fp64 numpy, "
+                  f"{dt:.1f} s); samples are independent, so the rate is per-sample exact",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3", help="workload (c3 is the benchmarked one)")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="samples in the oracle leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-launch HIP events")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "this build has no multi-GPU path; the forward shards data-parallel over samples "
+              "with no exchange, so the one-GPU number is the per-GPU rate.", file=sys.stderr)
+        return 2
+
+    import torch
+    import synthetic_inputs as si
+    from rankmixer_token_mixing_amd import binding as bd
+    from rankmixer_token_mixing_amd import perfmodel as pm
+
+    if not os.path.exists(bd.lib_path()):
+        from rankmixer_token_mixing_amd.build import build
+        build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+
+    cfg = si.CONFIGS[args.config]
+    t0 = time.perf_counter()
+    inputs = si.make_inputs(cfg)
+    log(f"generated {cfg.name} inputs in {time.perf_counter() - t0:.1f}s: {cfg.description}")
+    blocks = bd.upload_blocks(inputs["blocks"])
+    head = {"w": bd.to_device(inputs["head"]["w"]), "c": inputs["head"]["c"]} if "head" in inputs else None
+    dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    model = bd.Model(blocks, cfg.T, cfg.D, dtype, F=cfg.F, head=head)
+    inp = bd.to_device(inputs["emb"] if cfg.F else inputs["x"])
+    out = {}
+
+    def step():
+        bd.rm_model_fwd(model, inp, want_x=True, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    bd.profile_enable(not args.no_profile)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = bd.profile_read() if not args.no_profile else {}
+    bd.profile_enable(False)
+    log(f"timed {args.steps} steps in {elapsed * 1e3:.1f} ms")
+
+    ms_step = elapsed * 1e3 / args.steps
+    L = cfg.L
+    hidden = cfg.hidden
+    value = cfg.B * L / (elapsed / args.steps)
+
+    # algorithmic work of each launch group (one launch group = one block's worth)
+    if cfg.E:
+        gemm_flops = None
+    else:
+        gemm_flops = cfg.T * pm.gemm_flops(cfg.B, hidden, cfg.D)  # either product of one block
+    eb = pm.ELEM_BYTES[cfg.dtype]
+    row_bytes = {  # compulsory HBM bytes per launch
+        "mix_ln1": 2 * cfg.B * cfg.T * cfg.D * eb,
+        "ln2": cfg.B * cfg.T * cfg.D * (4 + eb),
+    }
+    kernels = {}
+    for name, (tot_ms, n) in prof.items():
+        avg = tot_ms / max(n, 1)
+        e = {"avg_ms": round(avg, 5), "launches": n, "total_ms": round(tot_ms, 3)}
+        if gemm_flops and name in ("ffn1", "ffn2_resid"):
+            e["tflops"] = round(gemm_flops / (avg * 1e-3) / 1e12, 1)
+        if name in row_bytes:
+            e["gbs"] = round(row_bytes[name] / (avg * 1e-3) / 1e9, 1)
+        kernels[name] = e
+
+    roofline = None
+    if kernels:
+        dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
+        avg_s = kernels[dom]["avg_ms"] * 1e-3
+        if gemm_flops and dom in ("ffn1", "ffn2_resid"):
+            ach = gemm_flops / avg_s / 1e12
+            roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1),
+                        "peak": pm.PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else pm.PEAK_FP32_MFMA_TFLOPS,
+                        "unit": "TFLOP/s"}
+            roofline["frac"] = round(ach / roofline["peak"], 4)
+            roofline["flop_per_launch"] = gemm_flops
+        elif dom in row_bytes:
+            ach = row_bytes[dom] / avg_s / 1e9
+            roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": pm.PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(ach / pm.PEAK_HBM_GBS, 4)}
+        if roofline is not None:
+            roofline["traffic"] = committed_traffic(cfg.name, dom)
+
+    block_flops = pm.block_flops(cfg.B, cfg.T, cfg.D, hidden) if not cfg.E else None
+    step_tflops = block_flops * L / (ms_step * 1e-3) / 1e12 if block_flops else None
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.description,
+            "B": cfg.B, "T": cfg.T, "D": cfg.D, "hidden": hidden, "L": L,
+            "step": "rm_model_fwd over the batch (all blocks)",
+            "value_is": "B * L / step time (samples through one block per second)",
+        },
+        "roofline": roofline,
+        "step_tflops": round(step_tflops, 1) if step_tflops else None,
+        "step_frac_of_bf16_peak": round(step_tflops / pm.PEAK_BF16_TFLOPS, 4) if step_tflops else None,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a bounded sample ...")
+        rec["cpu_baseline"] = cpu_baseline(inputs, L, args.cpu_rows)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,199 @@
+/*
+ * rankmixer.h - C ABI of librankmixer.so: the RankMixer block forward on
+ * AMD MI355X (gfx950), built from hand-written HIP kernels.
+ *
+ * Pages cited (titles as printed on them):
+ *   [FR] "Rankmixer: 硬件效率优化" (fun-rec textbook chapter)
+ *   [WL] "特征交叉 —— RankMixer 精读笔记" (reading notes on arXiv 2507.15551)
+ *   [TB] "淘宝闪购-爆品团精排 Scaling Up 迭代实践" (BestBlogs.dev report)
+ *   [SX] "重新理解 RankMixer：扩参为什么有效，又为什么划算？" (sxkj888.cn blog)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, contiguous, row-major device buffers.  Activations
+ *    are [B][T][D]: B samples, T tokens, token width D.  Weight matrices are
+ *    stored [out][in], so every product reads both operands along the
+ *    reduction axis.  Biases, LayerNorm gamma/beta, the router bias and the
+ *    logit head are float32.  Activations and weight matrices are float32 or
+ *    bf16 (rm_dtype); products accumulate in float32.
+ *  - Every device pointer must be 16-byte aligned.  Optional pointers may be
+ *    NULL where stated.
+ *  - The caller owns every buffer, including the workspace `ws`, sized with
+ *    the matching rm_*_workspace_bytes call.  The library never allocates,
+ *    frees or synchronises; work is enqueued on `stream` (a hipStream_t, NULL
+ *    for the default stream) and is complete when that stream is.
+ *  - Outputs must not alias inputs.
+ *  - Results are deterministic: two calls with the same inputs give the same
+ *    bits (no floating-point atomics anywhere).
+ *  - Every argument check runs on the host before anything is enqueued.  A
+ *    failing call returns a non-zero rm_status, enqueues nothing and leaves a
+ *    message for rm_last_error() (per thread).  RM_ERR_HIP reports a launch
+ *    failure; a fault inside a kernel surfaces at the caller's next
+ *    synchronisation of the stream.
+ */
+#ifndef RANKMIXER_H
+#define RANKMIXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rm_status {
+  RM_OK = 0,
+  RM_ERR_INVALID = 1,     /* NULL pointer, non-positive size, misaligned pointer */
+  RM_ERR_UNSUPPORTED = 2, /* shape the method or this build does not define (D % T != 0, ...) */
+  RM_ERR_WORKSPACE = 3,   /* ws_bytes smaller than the matching rm_*_workspace_bytes */
+  RM_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} rm_status;
+
+typedef enum rm_dtype { RM_F32 = 0, RM_BF16 = 1 } rm_dtype;
+
+typedef enum rm_block_kind { RM_BLOCK_DENSE = 0, RM_BLOCK_MOE = 1 } rm_block_kind;
+
+/* Per-token FFN of one block ([FR] "Per-Token FFN"; [WL] "Per-Token FFN"):
+ *   v_t = W2_t GELU(W1_t s_t + b1_t) + b2_t,  t = 0..T-1, GELU the exact erf form.
+ * The pages print W1_t as R^{D x kD} but apply it to s_t in R^D; W1_t here maps
+ * R^D -> R^Hd and is stored [Hd][D]. */
+typedef struct rm_pffn_params {
+  const void* w1;  /* [T][Hd][D], dtype */
+  const float* b1; /* [T][Hd] */
+  const void* w2;  /* [T][D][Hd], dtype */
+  const float* b2; /* [T][D] */
+} rm_pffn_params;
+
+/* ReLU-gated per-token MoE ([FR] "Sparse MoE扩展"; [WL] ReLU routing):
+ *   G_{t,j} = ReLU(Wr_t s_t + br_t)_j,   v_t = sum_j G_{t,j} e_{t,j}(s_t),
+ *   e_{t,j}(s) = W2_{t,j} GELU(W1_{t,j} s + b1_{t,j}) + b2_{t,j}.
+ * Only the inference router exists in the forward (dense-train/sparse-infer
+ * keeps h_infer at inference).  A zero gate means the expert is skipped. */
+typedef struct rm_moe_params {
+  const void* wr;  /* [T][E][D], dtype */
+  const float* br; /* [T][E] */
+  const void* w1;  /* [T][E][He][D], dtype */
+  const float* b1; /* [T][E][He] */
+  const void* w2;  /* [T][E][D][He], dtype */
+  const float* b2; /* [T][E][D] */
+} rm_moe_params;
+
+/* One block ([FR] "RankMixer整体架构", block equations):
+ *   S = LN1(TokenMix(X) + X),   X' = LN2(F(S) + S),
+ * F the per-token FFN (kind DENSE) or the ReLU MoE (kind MOE).  LayerNorm:
+ * biased variance over the D entries of one token, epsilon 1e-5. */
+typedef struct rm_block_params {
+  int kind;                   /* rm_block_kind */
+  const float* ln1_g;         /* [D] */
+  const float* ln1_b;         /* [D] */
+  const float* ln2_g;         /* [D] */
+  const float* ln2_b;         /* [D] */
+  rm_pffn_params pffn;        /* used when kind == RM_BLOCK_DENSE */
+  rm_moe_params moe;          /* used when kind == RM_BLOCK_MOE */
+} rm_block_params;
+
+/* A stack of L blocks ([FR] "RankMixer整体架构": X_L = block_L(...block_1(X_0))),
+ * with an optional pad-split tokenizer in front and optional mean pooling
+ * plus a D -> 1 logit behind ([WL]: the last block's tokens are averaged). */
+typedef struct rm_model_desc {
+  int T, D;
+  int hidden;                 /* Hd = kD for dense blocks, He for MoE blocks */
+  int E;                      /* experts per token (MoE blocks), else 0 */
+  int dtype;                  /* rm_dtype of activations and weight matrices */
+  int L;                      /* number of blocks */
+  const rm_block_params* blocks; /* host array of L block descriptors */
+  int64_t F;                  /* > 0: the input is an fp32 embedding [B][F], pad-split tokenized */
+  const float* head_w;        /* [D] device, or NULL: no pooling / logit */
+  float head_c;               /* logit bias */
+} rm_model_desc;
+
+/* Pad-split tokenizer ([TB] section 3.4: concatenate -> pad -> split, no
+ * projection).  x0[b][t][j] = emb[b][t*D + j] cast to out_dtype (round to
+ * nearest even) when t*D + j < F, else 0.
+ *   emb: [B][F] fp32 device; x0: [B][T][D] out_dtype device.
+ * Errors: F > T*D -> RM_ERR_UNSUPPORTED. */
+rm_status rm_tokenize_padsplit(const float* emb, int64_t B, int64_t F, int T, int D,
+                               int out_dtype, void* x0, void* stream);
+
+/* Multi-head token mixing with H = T ([FR] "Token Mixing机制"; [WL] "Multi-Head
+ * Token Mixer"): SplitHead cuts token t into T heads of width d = D/T, Concat
+ * joins head h of all tokens in token order:
+ *   y[b][h][t*d + j] = x[b][t][h*d + j].
+ * Pure data movement, bit-exact; applying it twice gives x back.
+ *   x, y: [B][T][D] dtype device.  Errors: D % T != 0 -> RM_ERR_UNSUPPORTED. */
+rm_status rm_token_mix(const void* x, void* y, int64_t B, int T, int D, int dtype, void* stream);
+
+/* Per-token FFN without residual or LayerNorm: v = PFFN(s).
+ *   s, v: [B][T][D] dtype device; params as rm_pffn_params (device pointers).
+ * Workspace: rm_pffn_workspace_bytes(B, T, D, Hd, dtype). */
+rm_status rm_pffn_fwd(const void* s, const rm_pffn_params* p, void* v, int64_t B, int T, int D,
+                      int Hd, int dtype, void* ws, size_t ws_bytes, void* stream);
+size_t rm_pffn_workspace_bytes(int64_t B, int T, int D, int Hd, int dtype);
+
+/* ReLU-gated per-token MoE without residual or LayerNorm: v = MoE(s).
+ *   s, v: [B][T][D] dtype device; gates: optional [B][T][E] fp32 device output
+ *   of G (NULL to skip).  E <= 32.  Experts run only on compacted lists of the
+ *   (sample, token) rows whose gate is positive.
+ * Workspace: rm_moe_workspace_bytes(B, T, D, E, He, dtype). */
+rm_status rm_moe_relu_fwd(const void* s, const rm_moe_params* p, void* v, float* gates, int64_t B,
+                          int T, int D, int E, int He, int dtype, void* ws, size_t ws_bytes,
+                          void* stream);
+size_t rm_moe_workspace_bytes(int64_t B, int T, int D, int E, int He, int dtype);
+
+/* Routing step of the MoE alone: gates and the compacted active lists.
+ *   gates:   [B][T][E] fp32 device output, G = ReLU(Wr_t s + br_t).
+ *   offsets: [T*E + 1] int32 device output; list g = t*E + j holds entries
+ *            offsets[g] .. offsets[g+1]-1.
+ *   rows:    [B*T*E] int32 device output; rows[i] = sample b of entry i, in
+ *            increasing b within each list (only offsets[T*E] entries are set).
+ * Workspace: rm_moe_workspace_bytes(...) (the same buffer as rm_moe_relu_fwd). */
+rm_status rm_moe_route(const void* s, const void* wr, const float* br, float* gates, int* offsets,
+                       int* rows, int64_t B, int T, int D, int E, int dtype, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* One block: x_out = LN2(F(S) + S), S = LN1(TokenMix(x) + x).
+ *   x, x_out: [B][T][D] dtype device.  hidden = Hd (dense) or He (MoE);
+ *   E = experts per token (MoE) or 0.
+ * Workspace: rm_block_workspace_bytes(kind, B, T, D, hidden, E, dtype). */
+rm_status rm_block_fwd(const void* x, const rm_block_params* p, void* x_out, int64_t B, int T,
+                       int D, int hidden, int E, int dtype, void* ws, size_t ws_bytes,
+                       void* stream);
+size_t rm_block_workspace_bytes(int kind, int64_t B, int T, int D, int hidden, int E, int dtype);
+
+/* The whole stack.
+ *   in:     m->F > 0: emb [B][F] fp32 device; else x0 [B][T][D] dtype device.
+ *   x_out:  [B][T][D] dtype device output of the last block, or NULL.
+ *   pooled: [B][D] fp32 device output of the token mean, or NULL (needs head_w).
+ *   logits: [B] fp32 device output, or NULL (needs head_w).
+ * Workspace: rm_model_workspace_bytes(m, B). */
+rm_status rm_model_fwd(const rm_model_desc* m, const void* in, void* x_out, float* pooled,
+                       float* logits, int64_t B, void* ws, size_t ws_bytes, void* stream);
+size_t rm_model_workspace_bytes(const rm_model_desc* m, int64_t B);
+
+/* Launch timing for benchmarks.  While enabled, every group of kernel
+ * launches an entry point makes (the W1 product, the W2 product, a LayerNorm,
+ * ...) is bracketed by two HIP events recorded on the caller's stream, under
+ * a fixed name ("mix_ln1", "ffn1", "ffn2_resid", "ln2", "moe_ffn1", ...).
+ * rm_profile_enable(on) clears what was recorded and switches recording on or
+ * off (creating events is a host-side cost; leave it off outside timing).
+ * rm_profile_count() is the number of names recorded; rm_profile_read(i, ...)
+ * waits for entry i's events and returns its name, the summed event-to-event
+ * time in ms and the number of launch groups.  Not thread-safe against
+ * concurrent launches on other threads. */
+int rm_profile_enable(int on);
+int rm_profile_count(void);
+int rm_profile_read(int idx, char* name, size_t name_len, double* total_ms, int* launches);
+
+/* Text of a status code; never NULL. */
+const char* rm_status_string(int status);
+/* Message of the last failing call on this thread ("" if none); valid until
+ * the next call on this thread. */
+const char* rm_last_error(void);
+/* Library version string. */
+const char* rm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RANKMIXER_H */

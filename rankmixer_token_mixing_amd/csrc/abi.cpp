@@ -1,0 +1,582 @@
+// C ABI of librankmixer.so (declared in include/rankmixer.h): argument
+// checks, workspace carving and kernel dispatch.  Nothing here allocates,
+// frees or synchronises; every check runs before the first launch.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/rankmixer.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rm_status fail(rm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+rm_status ok() {
+  g_last_error.clear();
+  return RM_OK;
+}
+
+rm_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(RM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return RM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// optional launch timing (rm_profile_*): a pair of HIP events around every
+// launch group, recorded on the stream the kernels go to
+
+struct ProfEntry {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<std::string> g_prof_names;
+std::map<std::string, ProfEntry> g_prof;
+
+struct ProfScope {
+  hipEvent_t a = nullptr, b = nullptr;
+  hipStream_t st;
+  const char* name;
+  ProfScope(const char* n, hipStream_t s) : st(s), name(n) {
+    if (!g_prof_on) return;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+      a = b = nullptr;
+      return;
+    }
+    (void)hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (!a) return;
+    (void)hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    auto it = g_prof.find(name);
+    if (it == g_prof.end()) {
+      g_prof_names.push_back(name);
+      it = g_prof.emplace(name, ProfEntry()).first;
+    }
+    it->second.ev.emplace_back(a, b);
+  }
+};
+
+void prof_clear() {
+  for (auto& kv : g_prof)
+    for (auto& e : kv.second.ev) {
+      (void)hipEventDestroy(e.first);
+      (void)hipEventDestroy(e.second);
+    }
+  g_prof.clear();
+  g_prof_names.clear();
+}
+
+#define RM_TRY(expr)                     \
+  do {                                   \
+    const rm_status _st = (expr);        \
+    if (_st != RM_OK) return _st;        \
+  } while (0)
+
+#define RM_HIP(expr, what) RM_TRY(hip_status((expr), (what)))
+#define RM_PROF_CAT2(a, b) a##b
+#define RM_PROF_CAT(a, b) RM_PROF_CAT2(a, b)
+// time the launches of the enclosing statement under `name`
+#define RM_TIMED(name, st, expr)                         \
+  do {                                                   \
+    ProfScope RM_PROF_CAT(_ps, __LINE__)((name), (st));  \
+    expr;                                                \
+  } while (0)
+
+int elem_bytes(int dt) { return dt == RM_BF16 ? 2 : 4; }
+
+rm_status check_ptr(const void* p, const char* name, bool required = true) {
+  if (!p) return required ? fail(RM_ERR_INVALID, "%s is NULL", name) : RM_OK;
+  if (reinterpret_cast<uintptr_t>(p) % 16) return fail(RM_ERR_INVALID, "%s is not 16-byte aligned", name);
+  return RM_OK;
+}
+
+rm_status check_dtype(int dt) {
+  if (dt != RM_F32 && dt != RM_BF16) return fail(RM_ERR_UNSUPPORTED, "unsupported dtype %d", dt);
+  return RM_OK;
+}
+
+rm_status check_shape(int64_t B, int T, int D, int dt) {
+  RM_TRY(check_dtype(dt));
+  if (B <= 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B, T and D must be positive (B=%lld T=%d D=%d)", (long long)B, T, D);
+  if (D % T) return fail(RM_ERR_UNSUPPORTED, "D=%d is not divisible by H=T=%d", D, T);
+  if (D % 8) return fail(RM_ERR_UNSUPPORTED, "D=%d must be a multiple of 8", D);
+  if (!rm::row_width_supported(T, D, dt)) return fail(RM_ERR_UNSUPPORTED, "D=%d with T=%d is wider than the row kernels support", D, T);
+  if (B * T > (int64_t)1 << 31) return fail(RM_ERR_UNSUPPORTED, "B*T too large");
+  return RM_OK;
+}
+
+rm_status check_hidden(int hidden) {
+  if (hidden <= 0) return fail(RM_ERR_INVALID, "hidden width must be positive (%d)", hidden);
+  if (hidden % 8) return fail(RM_ERR_UNSUPPORTED, "hidden width %d must be a multiple of 8", hidden);
+  return RM_OK;
+}
+
+rm_status check_moe_shape(int64_t B, int T, int E) {
+  if (E < 1 || E > 32) return fail(RM_ERR_UNSUPPORTED, "E=%d experts per token (supported: 1..32)", E);
+  if ((int64_t)T * E > 4096) return fail(RM_ERR_UNSUPPORTED, "T*E=%lld lists (supported: <= 4096)", (long long)T * E);
+  if (B * T * E >= ((int64_t)1 << 31)) return fail(RM_ERR_UNSUPPORTED, "B*T*E too large");
+  return RM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace carving: sub-buffers aligned to 256 bytes
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+constexpr int kMoeTileM = 128;  // M tile of the ragged expert products (see kernels_gemm.hip)
+
+struct PffnWs {
+  void* H;
+};
+size_t pffn_ws(Carver& c, int64_t B, int T, int Hd, int dt, PffnWs* w) {
+  PffnWs x;
+  x.H = c.take((size_t)B * T * Hd * elem_bytes(dt));
+  if (w) *w = x;
+  return c.off;
+}
+
+struct MoeWs {
+  rm::MoeWork mw;
+  void* Hc;
+  float* Yc;
+  int max_mtiles;
+};
+size_t moe_ws(Carver& c, int64_t B, int T, int D, int E, int He, int dt, MoeWs* w) {
+  MoeWs x;
+  const int64_t G = (int64_t)T * E;
+  const int64_t nmax = B * G;
+  x.max_mtiles = (int)(G * ((B + kMoeTileM - 1) / kMoeTileM));
+  x.mw.gates = (float*)c.take(nmax * 4);
+  x.mw.counts = (int*)c.take(G * 4);
+  x.mw.offsets = (int*)c.take((G + 1) * 4);
+  x.mw.ntiles = (int*)c.take(4);
+  x.mw.tiles = (int*)c.take((size_t)x.max_mtiles * 2 * 4);
+  x.mw.rows = (int*)c.take(nmax * 4);
+  x.mw.gatec = (float*)c.take(nmax * 4);
+  x.mw.pos = (int*)c.take(nmax * 4);
+  x.Hc = c.take((size_t)nmax * He * elem_bytes(dt));
+  x.Yc = (float*)c.take((size_t)nmax * D * 4);
+  if (w) *w = x;
+  return c.off;
+}
+
+struct BlockWs {
+  void* S;
+  float* Z;
+  PffnWs pffn;
+  MoeWs moe;
+};
+size_t block_ws(Carver& c, int kind, int64_t B, int T, int D, int hidden, int E, int dt, BlockWs* w) {
+  BlockWs x;
+  x.S = c.take((size_t)B * T * D * elem_bytes(dt));
+  if (kind == RM_BLOCK_DENSE) {
+    x.Z = (float*)c.take((size_t)B * T * D * 4);
+    pffn_ws(c, B, T, hidden, dt, &x.pffn);
+  } else {
+    x.Z = nullptr;
+    moe_ws(c, B, T, D, E, hidden, dt, &x.moe);
+  }
+  if (w) *w = x;
+  return c.off;
+}
+
+// ---------------------------------------------------------------------------
+// launch sequences
+
+rm::GemmArgs ffn1_args(const void* s, const rm_pffn_params* p, void* H, int64_t B, int T, int D, int Hd, int dt) {
+  rm::GemmArgs a;
+  a.dt = dt;
+  a.epi = rm::kEpiBiasGelu;
+  a.M = (int)B; a.N = Hd; a.K = D; a.G = T;
+  a.A = s; a.a_gs = D; a.a_rs = (int64_t)T * D;
+  a.W = p->w1; a.b_gs = (int64_t)Hd * D;
+  a.C = H; a.c_gs = B * Hd; a.c_rs = Hd;
+  a.bias = p->b1; a.bias_gs = Hd;
+  return a;
+}
+
+rm::GemmArgs ffn2_args(const void* H, const rm_pffn_params* p, int64_t B, int T, int D, int Hd, int dt) {
+  rm::GemmArgs a;
+  a.dt = dt;
+  a.M = (int)B; a.N = D; a.K = Hd; a.G = T;
+  a.A = H; a.a_gs = B * Hd; a.a_rs = Hd;
+  a.W = p->w2; a.b_gs = (int64_t)D * Hd;
+  a.c_gs = D; a.c_rs = (int64_t)T * D;
+  a.bias = p->b2; a.bias_gs = D;
+  return a;
+}
+
+rm_status run_pffn(const void* s, const rm_pffn_params* p, void* v, int64_t B, int T, int D, int Hd, int dt,
+                   const PffnWs& w, hipStream_t st) {
+  RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(s, p, w.H, B, T, D, Hd, dt), st), "pffn W1 product"));
+  rm::GemmArgs a2 = ffn2_args(w.H, p, B, T, D, Hd, dt);
+  a2.epi = rm::kEpiBias;
+  a2.C = v;
+  RM_TIMED("ffn2", st, RM_HIP(rm::launch_gemm(a2, st), "pffn W2 product"));
+  return RM_OK;
+}
+
+// v = MoE(s); if ln_g: out = LN(v + s) instead
+rm_status run_moe(const void* s, const rm_moe_params* p, void* out, float* gates_out, const float* ln_g,
+                  const float* ln_b, int64_t B, int T, int D, int E, int He, int dt, MoeWs w, hipStream_t st) {
+  if (gates_out) w.mw.gates = gates_out;
+  RM_TIMED("moe_router", st, RM_HIP(rm::launch_moe_router(s, p->wr, p->br, w.mw.gates, B, T, D, E, dt, st), "moe router"));
+  RM_TIMED("moe_compact", st, RM_HIP(rm::launch_moe_compact(w.mw, B, T, E, kMoeTileM, st), "moe compaction"));
+  const int G = T * E;
+  rm::GemmArgs a;
+  a.dt = dt;
+  a.epi = rm::kEpiBiasGelu;
+  a.M = (int)B; a.N = He; a.K = D; a.G = G;
+  a.A = s; a.a_gdiv = E; a.a_gs = D; a.a_rs = (int64_t)T * D; a.a_rowidx = w.mw.rows;
+  a.W = p->w1; a.b_gs = (int64_t)He * D;
+  a.C = w.Hc; a.c_gs = 0; a.c_rs = He;
+  a.bias = p->b1; a.bias_gs = He;
+  a.row_off = w.mw.offsets; a.tiles = w.mw.tiles; a.ntiles = w.mw.ntiles; a.max_mtiles = w.max_mtiles;
+  if (rm::gemm_tile_m(a) != kMoeTileM) return fail(RM_ERR_HIP, "internal: MoE tile size mismatch");
+  RM_TIMED("moe_ffn1", st, RM_HIP(rm::launch_gemm(a, st), "moe W1 product"));
+  rm::GemmArgs b;
+  b.dt = dt;
+  b.epi = rm::kEpiBiasScaleF32;
+  b.M = (int)B; b.N = D; b.K = He; b.G = G;
+  b.A = w.Hc; b.a_gs = 0; b.a_rs = He;
+  b.W = p->w2; b.b_gs = (int64_t)D * He;
+  b.C = w.Yc; b.c_gs = 0; b.c_rs = D;
+  b.bias = p->b2; b.bias_gs = D;
+  b.rowscale = w.mw.gatec;
+  b.row_off = w.mw.offsets; b.tiles = w.mw.tiles; b.ntiles = w.mw.ntiles; b.max_mtiles = w.max_mtiles;
+  if (rm::gemm_tile_m(b) != kMoeTileM) return fail(RM_ERR_HIP, "internal: MoE tile size mismatch");
+  RM_TIMED("moe_ffn2", st, RM_HIP(rm::launch_gemm(b, st), "moe W2 product"));
+  RM_TIMED("moe_combine", st,
+           RM_HIP(rm::launch_moe_combine(w.Yc, w.mw.pos, s, ln_g, ln_b, out, B, T, D, E, ln_g != nullptr, dt, st),
+                  "moe combine"));
+  return RM_OK;
+}
+
+rm_status check_block_params(const rm_block_params* p, int dt) {
+  if (!p) return fail(RM_ERR_INVALID, "block params is NULL");
+  RM_TRY(check_ptr(p->ln1_g, "ln1_g")); RM_TRY(check_ptr(p->ln1_b, "ln1_b"));
+  RM_TRY(check_ptr(p->ln2_g, "ln2_g")); RM_TRY(check_ptr(p->ln2_b, "ln2_b"));
+  if (p->kind == RM_BLOCK_DENSE) {
+    RM_TRY(check_ptr(p->pffn.w1, "pffn.w1")); RM_TRY(check_ptr(p->pffn.b1, "pffn.b1"));
+    RM_TRY(check_ptr(p->pffn.w2, "pffn.w2")); RM_TRY(check_ptr(p->pffn.b2, "pffn.b2"));
+  } else if (p->kind == RM_BLOCK_MOE) {
+    RM_TRY(check_ptr(p->moe.wr, "moe.wr")); RM_TRY(check_ptr(p->moe.br, "moe.br"));
+    RM_TRY(check_ptr(p->moe.w1, "moe.w1")); RM_TRY(check_ptr(p->moe.b1, "moe.b1"));
+    RM_TRY(check_ptr(p->moe.w2, "moe.w2")); RM_TRY(check_ptr(p->moe.b2, "moe.b2"));
+  } else {
+    return fail(RM_ERR_UNSUPPORTED, "unknown block kind %d", p->kind);
+  }
+  (void)dt;
+  return RM_OK;
+}
+
+rm_status check_block_shape(int kind, int64_t B, int T, int D, int hidden, int E, int dt) {
+  RM_TRY(check_shape(B, T, D, dt));
+  RM_TRY(check_hidden(hidden));
+  if (kind == RM_BLOCK_MOE) RM_TRY(check_moe_shape(B, T, E));
+  return RM_OK;
+}
+
+rm_status run_block(const void* x, const rm_block_params* p, void* xo, int64_t B, int T, int D, int hidden,
+                    int E, int dt, const BlockWs& w, hipStream_t st) {
+  RM_TIMED("mix_ln1", st, RM_HIP(rm::launch_mix_ln(x, w.S, p->ln1_g, p->ln1_b, B, T, D, dt, st), "token mix + LayerNorm"));
+  if (p->kind == RM_BLOCK_DENSE) {
+    RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(w.S, &p->pffn, w.pffn.H, B, T, D, hidden, dt), st), "block W1 product"));
+    rm::GemmArgs a2 = ffn2_args(w.pffn.H, &p->pffn, B, T, D, hidden, dt);
+    a2.epi = rm::kEpiBiasResidF32;
+    a2.C = w.Z;
+    a2.R = w.S; a2.r_gs = D; a2.r_rs = (int64_t)T * D;
+    RM_TIMED("ffn2_resid", st, RM_HIP(rm::launch_gemm(a2, st), "block W2 product"));
+    RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows_f32(w.Z, xo, p->ln2_g, p->ln2_b, B * T, D, dt, st), "LayerNorm 2"));
+    return RM_OK;
+  }
+  return run_moe(w.S, &p->moe, xo, nullptr, p->ln2_g, p->ln2_b, B, T, D, E, hidden, dt, w.moe, st);
+}
+
+size_t model_ws(Carver& c, const rm_model_desc* m, int64_t B, void** x0, void** x1, BlockWs* bw) {
+  const size_t xb = (size_t)B * m->T * m->D * elem_bytes(m->dtype);
+  void* a = c.take(xb);
+  void* b = c.take(xb);
+  if (x0) *x0 = a;
+  if (x1) *x1 = b;
+  // one block workspace, sized for the largest block kind present
+  size_t start = c.off, best = 0;
+  int best_kind = RM_BLOCK_DENSE;
+  for (int l = 0; l < m->L; ++l) {
+    Carver probe(nullptr);
+    probe.off = start;
+    const size_t end = block_ws(probe, m->blocks[l].kind, B, m->T, m->D, m->hidden, m->E, m->dtype, nullptr);
+    if (end - start > best) {
+      best = end - start;
+      best_kind = m->blocks[l].kind;
+    }
+  }
+  if (m->L > 0) {
+    Carver real = c;
+    block_ws(real, best_kind, B, m->T, m->D, m->hidden, m->E, m->dtype, bw);
+    // a block workspace of the other kind is carved from the same region
+    c.off = start + best;
+  }
+  return c.off;
+}
+
+}  // namespace
+
+// ===========================================================================
+extern "C" {
+
+const char* rm_status_string(int st) {
+  switch (st) {
+    case RM_OK: return "ok";
+    case RM_ERR_INVALID: return "invalid argument";
+    case RM_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case RM_ERR_WORKSPACE: return "workspace too small";
+    case RM_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* rm_last_error(void) { return g_last_error.c_str(); }
+
+const char* rm_version(void) { return "rankmixer-mi355x 0.1 (gfx950)"; }
+
+int rm_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_clear();
+  g_prof_on = on != 0;
+  return RM_OK;
+}
+
+int rm_profile_count(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  return (int)g_prof_names.size();
+}
+
+int rm_profile_read(int idx, char* name, size_t name_len, double* total_ms, int* launches) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (idx < 0 || idx >= (int)g_prof_names.size() || !name || !total_ms || !launches)
+    return fail(RM_ERR_INVALID, "profile entry %d does not exist", idx);
+  const std::string& n = g_prof_names[idx];
+  snprintf(name, name_len, "%s", n.c_str());
+  double tot = 0.0;
+  for (auto& e : g_prof[n].ev) {
+    RM_HIP(hipEventSynchronize(e.second), "profile event");
+    float ms = 0.f;
+    RM_HIP(hipEventElapsedTime(&ms, e.first, e.second), "profile event");
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = (int)g_prof[n].ev.size();
+  return RM_OK;
+}
+
+rm_status rm_tokenize_padsplit(const float* emb, int64_t B, int64_t F, int T, int D, int out_dtype, void* x0,
+                               void* stream) {
+  RM_TRY(check_dtype(out_dtype));
+  if (B <= 0 || F <= 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B, F, T, D must be positive");
+  if (F > (int64_t)T * D) return fail(RM_ERR_UNSUPPORTED, "F=%lld floats do not fit in T*D=%lld", (long long)F, (long long)T * D);
+  RM_TRY(check_ptr(emb, "emb"));
+  RM_TRY(check_ptr(x0, "x0"));
+  RM_TIMED("tokenize", (hipStream_t)stream, RM_HIP(rm::launch_tokenize_padsplit(emb, B, F, T, D, out_dtype, x0, (hipStream_t)stream), "tokenize"));
+  return ok();
+}
+
+rm_status rm_token_mix(const void* x, void* y, int64_t B, int T, int D, int dtype, void* stream) {
+  RM_TRY(check_dtype(dtype));
+  if (B <= 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B, T, D must be positive");
+  if (D % T) return fail(RM_ERR_UNSUPPORTED, "D=%d is not divisible by H=T=%d", D, T);
+  RM_TRY(check_ptr(x, "x"));
+  RM_TRY(check_ptr(y, "y"));
+  if (x == y) return fail(RM_ERR_INVALID, "y must not alias x");
+  RM_TIMED("token_mix", (hipStream_t)stream, RM_HIP(rm::launch_token_mix(x, y, B, T, D, dtype, (hipStream_t)stream), "token mix"));
+  return ok();
+}
+
+size_t rm_pffn_workspace_bytes(int64_t B, int T, int D, int Hd, int dtype) {
+  (void)D;
+  Carver c(nullptr);
+  return pffn_ws(c, B, T, Hd, dtype, nullptr);
+}
+
+rm_status rm_pffn_fwd(const void* s, const rm_pffn_params* p, void* v, int64_t B, int T, int D, int Hd, int dtype,
+                      void* ws, size_t ws_bytes, void* stream) {
+  RM_TRY(check_shape(B, T, D, dtype));
+  RM_TRY(check_hidden(Hd));
+  if (!p) return fail(RM_ERR_INVALID, "params is NULL");
+  RM_TRY(check_ptr(s, "s")); RM_TRY(check_ptr(v, "v"));
+  RM_TRY(check_ptr(p->w1, "w1")); RM_TRY(check_ptr(p->b1, "b1"));
+  RM_TRY(check_ptr(p->w2, "w2")); RM_TRY(check_ptr(p->b2, "b2"));
+  if (s == v) return fail(RM_ERR_INVALID, "v must not alias s");
+  RM_TRY(check_ptr(ws, "ws"));
+  const size_t need = rm_pffn_workspace_bytes(B, T, D, Hd, dtype);
+  if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  Carver c(ws);
+  PffnWs w;
+  pffn_ws(c, B, T, Hd, dtype, &w);
+  RM_TRY(run_pffn(s, p, v, B, T, D, Hd, dtype, w, (hipStream_t)stream));
+  return ok();
+}
+
+size_t rm_moe_workspace_bytes(int64_t B, int T, int D, int E, int He, int dtype) {
+  Carver c(nullptr);
+  return moe_ws(c, B, T, D, E, He, dtype, nullptr);
+}
+
+static rm_status check_moe_params(const rm_moe_params* p) {
+  if (!p) return fail(RM_ERR_INVALID, "params is NULL");
+  RM_TRY(check_ptr(p->wr, "wr")); RM_TRY(check_ptr(p->br, "br"));
+  RM_TRY(check_ptr(p->w1, "w1")); RM_TRY(check_ptr(p->b1, "b1"));
+  RM_TRY(check_ptr(p->w2, "w2")); RM_TRY(check_ptr(p->b2, "b2"));
+  return RM_OK;
+}
+
+rm_status rm_moe_relu_fwd(const void* s, const rm_moe_params* p, void* v, float* gates, int64_t B, int T, int D,
+                          int E, int He, int dtype, void* ws, size_t ws_bytes, void* stream) {
+  RM_TRY(check_shape(B, T, D, dtype));
+  RM_TRY(check_hidden(He));
+  RM_TRY(check_moe_shape(B, T, E));
+  RM_TRY(check_moe_params(p));
+  RM_TRY(check_ptr(s, "s")); RM_TRY(check_ptr(v, "v")); RM_TRY(check_ptr(gates, "gates", false));
+  if (s == v) return fail(RM_ERR_INVALID, "v must not alias s");
+  RM_TRY(check_ptr(ws, "ws"));
+  const size_t need = rm_moe_workspace_bytes(B, T, D, E, He, dtype);
+  if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  Carver c(ws);
+  MoeWs w;
+  moe_ws(c, B, T, D, E, He, dtype, &w);
+  RM_TRY(run_moe(s, p, v, gates, nullptr, nullptr, B, T, D, E, He, dtype, w, (hipStream_t)stream));
+  return ok();
+}
+
+rm_status rm_moe_route(const void* s, const void* wr, const float* br, float* gates, int* offsets, int* rows,
+                       int64_t B, int T, int D, int E, int dtype, void* ws, size_t ws_bytes, void* stream) {
+  RM_TRY(check_shape(B, T, D, dtype));
+  RM_TRY(check_moe_shape(B, T, E));
+  RM_TRY(check_ptr(s, "s")); RM_TRY(check_ptr(wr, "wr")); RM_TRY(check_ptr(br, "br"));
+  RM_TRY(check_ptr(gates, "gates")); RM_TRY(check_ptr(offsets, "offsets")); RM_TRY(check_ptr(rows, "rows"));
+  RM_TRY(check_ptr(ws, "ws"));
+  const size_t need = rm_moe_workspace_bytes(B, T, D, E, 8, dtype);
+  if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  Carver c(ws);
+  MoeWs w;
+  moe_ws(c, B, T, D, E, 8, dtype, &w);
+  w.mw.gates = gates;
+  w.mw.offsets = offsets;
+  w.mw.rows = rows;
+  hipStream_t st = (hipStream_t)stream;
+  RM_HIP(rm::launch_moe_router(s, wr, br, gates, B, T, D, E, dtype, st), "moe router");
+  RM_HIP(rm::launch_moe_compact(w.mw, B, T, E, kMoeTileM, st), "moe compaction");
+  return ok();
+}
+
+size_t rm_block_workspace_bytes(int kind, int64_t B, int T, int D, int hidden, int E, int dtype) {
+  Carver c(nullptr);
+  return block_ws(c, kind, B, T, D, hidden, E, dtype, nullptr);
+}
+
+rm_status rm_block_fwd(const void* x, const rm_block_params* p, void* x_out, int64_t B, int T, int D, int hidden,
+                       int E, int dtype, void* ws, size_t ws_bytes, void* stream) {
+  RM_TRY(check_block_params(p, dtype));
+  RM_TRY(check_block_shape(p->kind, B, T, D, hidden, E, dtype));
+  RM_TRY(check_ptr(x, "x")); RM_TRY(check_ptr(x_out, "x_out"));
+  if (x == x_out) return fail(RM_ERR_INVALID, "x_out must not alias x");
+  RM_TRY(check_ptr(ws, "ws"));
+  const size_t need = rm_block_workspace_bytes(p->kind, B, T, D, hidden, E, dtype);
+  if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  Carver c(ws);
+  BlockWs w;
+  block_ws(c, p->kind, B, T, D, hidden, E, dtype, &w);
+  RM_TRY(run_block(x, p, x_out, B, T, D, hidden, E, dtype, w, (hipStream_t)stream));
+  return ok();
+}
+
+size_t rm_model_workspace_bytes(const rm_model_desc* m, int64_t B) {
+  if (!m || (m->L > 0 && !m->blocks)) return 0;
+  Carver c(nullptr);
+  return model_ws(c, m, B, nullptr, nullptr, nullptr);
+}
+
+rm_status rm_model_fwd(const rm_model_desc* m, const void* in, void* x_out, float* pooled, float* logits, int64_t B,
+                       void* ws, size_t ws_bytes, void* stream) {
+  if (!m) return fail(RM_ERR_INVALID, "model descriptor is NULL");
+  if (m->L < 0) return fail(RM_ERR_INVALID, "L=%d must not be negative", m->L);
+  if (m->L > 0 && !m->blocks) return fail(RM_ERR_INVALID, "blocks is NULL");
+  RM_TRY(check_shape(B, m->T, m->D, m->dtype));
+  bool any_moe = false;
+  for (int l = 0; l < m->L; ++l) {
+    RM_TRY(check_block_params(&m->blocks[l], m->dtype));
+    any_moe |= m->blocks[l].kind == RM_BLOCK_MOE;
+  }
+  if (m->L > 0) RM_TRY(check_hidden(m->hidden));
+  if (any_moe) RM_TRY(check_moe_shape(B, m->T, m->E));
+  if (m->F < 0) return fail(RM_ERR_INVALID, "F must not be negative");
+  if (m->F > (int64_t)m->T * m->D) return fail(RM_ERR_UNSUPPORTED, "F=%lld floats do not fit in T*D", (long long)m->F);
+  RM_TRY(check_ptr(in, "in"));
+  RM_TRY(check_ptr(x_out, "x_out", false));
+  RM_TRY(check_ptr(pooled, "pooled", false));
+  RM_TRY(check_ptr(logits, "logits", false));
+  RM_TRY(check_ptr(m->head_w, "head_w", false));
+  if ((pooled || logits) && !m->head_w) return fail(RM_ERR_INVALID, "pooled/logits requested without head_w");
+  if (x_out && x_out == in) return fail(RM_ERR_INVALID, "x_out must not alias in");
+  RM_TRY(check_ptr(ws, "ws"));
+  const size_t need = rm_model_workspace_bytes(m, B);
+  if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+
+  hipStream_t st = (hipStream_t)stream;
+  Carver c(ws);
+  void* buf[2];
+  BlockWs bw;
+  model_ws(c, m, B, &buf[0], &buf[1], &bw);
+  const int T = m->T, D = m->D, dt = m->dtype;
+  const void* cur = in;
+  int next = 0;
+  if (m->F > 0) {
+    RM_TIMED("tokenize", st, RM_HIP(rm::launch_tokenize_padsplit((const float*)in, B, m->F, T, D, dt, buf[0], st), "tokenize"));
+    cur = buf[0];
+    next = 1;
+  }
+  for (int l = 0; l < m->L; ++l) {
+    void* dst = (l == m->L - 1 && x_out) ? x_out : buf[next];
+    // a block workspace sized for the largest kind; re-carve for this kind
+    Carver bc(bw.S);
+    BlockWs w;
+    block_ws(bc, m->blocks[l].kind, B, T, D, m->hidden, m->E, dt, &w);
+    RM_TRY(run_block(cur, &m->blocks[l], dst, B, T, D, m->hidden, m->E, dt, w, st));
+    cur = dst;
+    next ^= 1;
+  }
+  if (x_out && cur != x_out) RM_HIP(hipMemcpyAsync(x_out, cur, (size_t)B * T * D * elem_bytes(dt), hipMemcpyDeviceToDevice, st), "copy x_out");
+  if (m->head_w) RM_TIMED("pool_logit", st, RM_HIP(rm::launch_pool_logit(cur, m->head_w, m->head_c, pooled, logits, B, T, D, dt, st), "pool + logit"));
+  return ok();
+}
+
+}  // extern "C"

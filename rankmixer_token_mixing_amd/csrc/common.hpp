@@ -1,0 +1,94 @@
+// Device helpers shared by the RankMixer HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rm {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// float -> bf16, round to nearest even (gfx950 converts in hardware)
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
+
+// ---------------------------------------------------------------------------
+// vector loads / stores of N consecutive elements, converted to / from float.
+// N * sizeof(T) is 2, 4, 8, 16 or 32 bytes; the address is aligned to
+// min(16, N * sizeof(T)) bytes.
+
+template <int BYTES> struct RawVec;
+template <> struct RawVec<2> { typedef uint16_t type; };
+template <> struct RawVec<4> { typedef uint32_t type; };
+template <> struct RawVec<8> { typedef uint2 type; };
+template <> struct RawVec<16> { typedef uint4 type; };
+struct Raw32 { uint4 lo, hi; };
+template <> struct RawVec<32> { typedef Raw32 type; };
+
+template <typename T, int N>
+struct Vec {
+  static constexpr int kBytes = N * (int)sizeof(T);
+  typedef typename RawVec<kBytes>::type raw_t;
+  union {
+    raw_t raw;
+    T e[N];
+  };
+};
+
+template <typename T, int N>
+__device__ __forceinline__ void load_f32(const T* p, float (&out)[N]) {
+  Vec<T, N> v;
+  v.raw = *reinterpret_cast<const typename Vec<T, N>::raw_t*>(p);
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = to_f32(v.e[i]);
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void store_from_f32(T* p, const float (&in)[N]) {
+  Vec<T, N> v;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v.e[i] = from_f32<T>(in[i]);
+  *reinterpret_cast<typename Vec<T, N>::raw_t*>(p) = v.raw;
+}
+
+// ---------------------------------------------------------------------------
+// wave-level reductions (all 64 lanes get the result)
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// ---------------------------------------------------------------------------
+// GELU, exact form x * Phi(x) = x/2 * (1 + erf(x / sqrt 2))
+
+__device__ __forceinline__ float gelu_erf(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup ids are handed to the 8 XCDs round-robin (id % 8).  Map the ids
+// of one XCD to a contiguous range of logical tiles so that tiles sharing
+// operand panels run under the same L2.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  constexpr int kXcd = 8;
+  const int q = n / kXcd, r = n % kXcd;
+  const int x = id % kXcd, local = id / kXcd;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
+}  // namespace rm

@@ -1,0 +1,303 @@
+// ReLU-gated per-token MoE around the grouped GEMMs: the router, the
+// compaction of active (sample, token, expert) rows into per-(token, expert)
+// lists, and the deterministic combine (+ residual + LayerNorm).
+//
+// Routing follows the ReLU router of "Rankmixer: 硬件效率优化", section
+// "Sparse MoE扩展": G = ReLU(h(s)), expert j of token t runs only where its
+// gate is positive.  Lists are built without any host round trip: counts,
+// an exclusive scan and a stable scatter, all on the device.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rm {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;
+constexpr int kMaxGroups = 4096;  // T * E
+
+int pick_slots(int chunks) {
+  const int need = (chunks + kWave - 1) / kWave;
+  if (need <= 1) return 1;
+  if (need <= 2) return 2;
+  if (need <= 4) return 4;
+  if (need <= 8) return 8;
+  if (need <= 16) return 16;
+  return 0;
+}
+
+// gates[b,t,j] = max(0, Wr[t,j,:] . s[b,t,:] + br[t,j]); one wave per (b, t)
+template <typename T, int VEC, int MAXI>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_router(const T* __restrict__ s, const T* __restrict__ wr,
+                                                                  const float* __restrict__ br,
+                                                                  float* __restrict__ gates, int64_t B, int T_,
+                                                                  int D, int E) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  if (row >= B * T_) return;
+  const int lane = lane_id();
+  const int t = (int)(row % T_);
+  const int nch = D / VEC;
+  const T* sr = s + row * (int64_t)D;
+  float v[MAXI][VEC];
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) load_f32<T, VEC>(sr + c * VEC, v[i]);
+  }
+  for (int j = 0; j < E; ++j) {
+    const T* w = wr + ((int64_t)t * E + j) * D;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nch) {
+        float q[VEC];
+        load_f32<T, VEC>(w + c * VEC, q);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc += v[i][e] * q[e];
+      }
+    }
+    const float z = wave_sum(acc) + br[t * E + j];
+    if (lane == j % kWave) gates[row * E + j] = z > 0.f ? z : 0.f;
+  }
+}
+
+// counts[g] = #{b : gates[b, g] > 0}, g = t*E + j; one workgroup per group
+__global__ __launch_bounds__(256) void k_moe_count(const float* __restrict__ gates, int* __restrict__ counts,
+                                                   int64_t B, int G) {
+  const int g = blockIdx.x;
+  int c = 0;
+  for (int64_t b = threadIdx.x; b < B; b += blockDim.x) c += gates[b * G + g] > 0.f ? 1 : 0;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, kWave);
+  __shared__ int part[4];
+  if (lane_id() == 0) part[threadIdx.x / kWave] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) counts[g] = part[0] + part[1] + part[2] + part[3];
+}
+
+// offsets = exclusive scan of counts; tile list of (g, m0) pairs with bm rows
+// per tile; ntiles = its length.  One workgroup of 256 threads; thread i
+// owns groups [i*per, (i+1)*per).
+__global__ __launch_bounds__(256) void k_moe_scan(const int* __restrict__ counts, int* __restrict__ offsets,
+                                                  int* __restrict__ tiles, int* __restrict__ ntiles, int G,
+                                                  int bm) {
+  __shared__ int s_rows[256], s_tiles[256];
+  const int per = (G + 255) / 256;
+  const int g0 = threadIdx.x * per;
+  int my_rows = 0, my_tiles = 0;
+  for (int g = g0; g < g0 + per && g < G; ++g) {
+    my_rows += counts[g];
+    my_tiles += (counts[g] + bm - 1) / bm;
+  }
+  s_rows[threadIdx.x] = my_rows;
+  s_tiles[threadIdx.x] = my_tiles;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the 256 partial sums
+  for (int off = 1; off < 256; off <<= 1) {
+    const int r = threadIdx.x >= off ? s_rows[threadIdx.x - off] : 0;
+    const int q = threadIdx.x >= off ? s_tiles[threadIdx.x - off] : 0;
+    __syncthreads();
+    s_rows[threadIdx.x] += r;
+    s_tiles[threadIdx.x] += q;
+    __syncthreads();
+  }
+  int o = s_rows[threadIdx.x] - my_rows;
+  int to = s_tiles[threadIdx.x] - my_tiles;
+  for (int g = g0; g < g0 + per && g < G; ++g) {
+    const int c = counts[g];
+    offsets[g] = o;
+    const int nt = (c + bm - 1) / bm;
+    for (int i = 0; i < nt; ++i) {
+      tiles[2 * (to + i)] = g;
+      tiles[2 * (to + i) + 1] = i * bm;
+    }
+    o += c;
+    to += nt;
+  }
+  if (threadIdx.x == 255) {
+    offsets[G] = s_rows[255];
+    *ntiles = s_tiles[255];
+  }
+}
+
+// stable scatter: entry offsets[g] + rank of each active b (in increasing b)
+__global__ __launch_bounds__(256) void k_moe_scatter(const float* __restrict__ gates,
+                                                     const int* __restrict__ offsets, int* __restrict__ rows,
+                                                     float* __restrict__ gatec, int* __restrict__ pos,
+                                                     int64_t B, int G) {
+  const int g = blockIdx.x;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  __shared__ int wtot[4];
+  int running = offsets[g];
+  for (int64_t base = 0; base < B; base += blockDim.x) {
+    const int64_t b = base + threadIdx.x;
+    const float gv = b < B ? gates[b * G + g] : 0.f;
+    const bool on = gv > 0.f;
+    const unsigned long long mask = __ballot(on);
+    const int before = __popcll(mask & ((1ull << lane) - 1ull));
+    if (lane == 0) wtot[wave] = __popcll(mask);
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += wtot[w];
+    const int total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    if (b < B) {
+      if (on) {
+        const int idx = running + wbase + before;
+        rows[idx] = (int)b;
+        gatec[idx] = gv;
+        pos[b * G + g] = idx;
+      } else {
+        pos[b * G + g] = -1;
+      }
+    }
+    running += total;
+    __syncthreads();
+  }
+}
+
+// v = sum_j y[pos[b,t,j]] (fixed j order); out = ln ? LN(v + s) : v
+template <typename T, int MAXI>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_moe_combine(const float* __restrict__ y,
+                                                                       const int* __restrict__ pos,
+                                                                       const T* __restrict__ s,
+                                                                       const float* __restrict__ g,
+                                                                       const float* __restrict__ beta,
+                                                                       T* __restrict__ out, int64_t rows_n,
+                                                                       int D, int E, int ln) {
+  constexpr int VEC = 4;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  if (row >= rows_n) return;
+  const int lane = lane_id();
+  const int nch = D / VEC;
+  float v[MAXI][VEC];
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) v[i][e] = 0.f;
+  for (int j = 0; j < E; ++j) {
+    const int p = pos[row * E + j];
+    if (p < 0) continue;
+    const float* yr = y + (int64_t)p * D;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nch) {
+        float q[VEC];
+        load_f32<float, VEC>(yr + c * VEC, q);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[i][e] += q[e];
+      }
+    }
+  }
+  T* orow = out + row * (int64_t)D;
+  if (!ln) {
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nch) store_from_f32<T, VEC>(orow + c * VEC, v[i]);
+    }
+    return;
+  }
+  const T* sr = s + row * (int64_t)D;
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+      float q[VEC];
+      load_f32<T, VEC>(sr + c * VEC, q);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        v[i][e] += q[e];
+        sum += v[i][e];
+      }
+    }
+  }
+  const float mean = wave_sum(sum) / (float)D;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float q = v[i][e] - mean;
+        sq += q * q;
+      }
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D + 1e-5f);
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+      const int k = c * VEC;
+      float o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = (v[i][e] - mean) * rstd * g[k + e] + beta[k + e];
+      store_from_f32<T, VEC>(orow + k, o);
+    }
+  }
+}
+
+template <typename T, int VEC>
+hipError_t router_t(const void* s, const void* wr, const float* br, float* gates, int64_t B, int T_, int D,
+                    int E, hipStream_t st) {
+  const dim3 grid((unsigned)((B * T_ + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
+  const T* ss = (const T*)s;
+  const T* ww = (const T*)wr;
+  switch (pick_slots(D / VEC)) {
+    case 0: return hipErrorInvalidValue;
+    case 1: hipLaunchKernelGGL((k_router<T, VEC, 1>), grid, block, 0, st, ss, ww, br, gates, B, T_, D, E); break;
+    case 2: hipLaunchKernelGGL((k_router<T, VEC, 2>), grid, block, 0, st, ss, ww, br, gates, B, T_, D, E); break;
+    case 4: hipLaunchKernelGGL((k_router<T, VEC, 4>), grid, block, 0, st, ss, ww, br, gates, B, T_, D, E); break;
+    case 8: hipLaunchKernelGGL((k_router<T, VEC, 8>), grid, block, 0, st, ss, ww, br, gates, B, T_, D, E); break;
+    default: hipLaunchKernelGGL((k_router<T, VEC, 16>), grid, block, 0, st, ss, ww, br, gates, B, T_, D, E); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t combine_t(const float* y, const int* pos, const void* s, const float* g, const float* b, void* out,
+                     int64_t B, int T_, int D, int E, bool ln, hipStream_t st) {
+  const int64_t rows = B * T_;
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
+  const T* ss = (const T*)s;
+  T* oo = (T*)out;
+  const int l = ln ? 1 : 0;
+  switch (pick_slots(D / 4)) {
+    case 0: return hipErrorInvalidValue;
+    case 1: hipLaunchKernelGGL((k_moe_combine<T, 1>), grid, block, 0, st, y, pos, ss, g, b, oo, rows, D, E, l); break;
+    case 2: hipLaunchKernelGGL((k_moe_combine<T, 2>), grid, block, 0, st, y, pos, ss, g, b, oo, rows, D, E, l); break;
+    case 4: hipLaunchKernelGGL((k_moe_combine<T, 4>), grid, block, 0, st, y, pos, ss, g, b, oo, rows, D, E, l); break;
+    case 8: hipLaunchKernelGGL((k_moe_combine<T, 8>), grid, block, 0, st, y, pos, ss, g, b, oo, rows, D, E, l); break;
+    default: hipLaunchKernelGGL((k_moe_combine<T, 16>), grid, block, 0, st, y, pos, ss, g, b, oo, rows, D, E, l); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_moe_router(const void* s, const void* wr, const float* br, float* gates, int64_t B, int T,
+                             int D, int E, int dt, hipStream_t st) {
+  if (dt == kBF16) return router_t<bf16, 8>(s, wr, br, gates, B, T, D, E, st);
+  return router_t<float, 4>(s, wr, br, gates, B, T, D, E, st);
+}
+
+hipError_t launch_moe_compact(const MoeWork& w, int64_t B, int T, int E, int bm, hipStream_t st) {
+  const int G = T * E;
+  if (G > kMaxGroups) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_moe_count, dim3(G), dim3(256), 0, st, w.gates, w.counts, B, G);
+  hipLaunchKernelGGL(k_moe_scan, dim3(1), dim3(256), 0, st, w.counts, w.offsets, w.tiles, w.ntiles, G, bm);
+  hipLaunchKernelGGL(k_moe_scatter, dim3(G), dim3(256), 0, st, w.gates, w.offsets, w.rows, w.gatec, w.pos, B, G);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_combine(const float* y, const int* pos, const void* s, const float* g, const float* b,
+                              void* out, int64_t B, int T, int D, int E, bool ln, int dt, hipStream_t st) {
+  if (dt == kBF16) return combine_t<bf16>(y, pos, s, g, b, out, B, T, D, E, ln, st);
+  return combine_t<float>(y, pos, s, g, b, out, B, T, D, E, ln, st);
+}
+
+}  // namespace rm

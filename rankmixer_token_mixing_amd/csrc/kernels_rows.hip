@@ -1,0 +1,372 @@
+// Row kernels of the RankMixer forward: pad-split tokenizer, token mixing,
+// the fused token-mix + residual + LayerNorm that produces S, a LayerNorm
+// over fp32 rows, and mean pooling with the logit head.  All are bound by
+// HBM bandwidth; each wave owns one [D] row and keeps it in registers.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rm {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // waves (rows) per workgroup
+__device__ __forceinline__ float ln_eps() { return 1e-5f; }
+
+// largest chunk (elements) that divides `d`, is at most 16 bytes and keeps the
+// address aligned
+int chunk_elems(int d, int elem_bytes) {
+  const int max_e = 16 / elem_bytes;
+  for (int v = max_e; v > 1; v >>= 1)
+    if (d % v == 0) return v;
+  return 1;
+}
+
+// register slots per lane for a row of `chunks` chunks (0: row too wide)
+int pick_maxi(int chunks) {
+  const int need = (chunks + kWave - 1) / kWave;
+  if (need <= 1) return 1;
+  if (need <= 2) return 2;
+  if (need <= 4) return 4;
+  if (need <= 8) return 8;
+  if (need <= 16) return 16;
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// pad-split tokenizer: x0[b][i] = i < F ? cast(emb[b][i]) : 0, i < T*D.
+// Each thread writes 4 consecutive outputs of one sample.
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_tokenize(const float* __restrict__ emb, T* __restrict__ x0,
+                                                  int64_t B, int64_t F, int64_t TD) {
+  const int64_t per_row = TD / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * per_row) return;
+  const int64_t b = idx / per_row;
+  const int64_t i = (idx - b * per_row) * 4;
+  const float* src = emb + b * F;
+  float v[4];
+  if (i + 4 <= F && (F & 3) == 0) {
+    const float4 q = *reinterpret_cast<const float4*>(src + i);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (i + e < F) ? src[i + e] : 0.0f;
+  }
+  store_from_f32<T, 4>(x0 + b * TD + i, v);
+}
+
+// odd T*D: one element per thread
+template <typename T>
+__global__ __launch_bounds__(256) void k_tokenize1(const float* __restrict__ emb, T* __restrict__ x0,
+                                                   int64_t B, int64_t F, int64_t TD) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * TD) return;
+  const int64_t b = idx / TD, i = idx - b * TD;
+  x0[idx] = from_f32<T>(i < F ? emb[b * F + i] : 0.0f);
+}
+
+// ---------------------------------------------------------------------------
+// token mixing, H = T: y[b][h][t*d + j] = x[b][t][h*d + j].  One wave per
+// output row (b, h); VEC-element chunks never straddle a head.
+
+template <int EB, int VEC>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_token_mix(const void* __restrict__ xv,
+                                                                     void* __restrict__ yv,
+                                                                     int64_t B, int T, int D) {
+  typedef typename RawVec<EB * VEC>::type raw_t;
+  typedef typename RawVec<EB>::type elem_t;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  if (row >= B * T) return;
+  const int lane = lane_id();
+  const int64_t b = row / T;
+  const int h = (int)(row - b * T);
+  const int d = D / T;
+  const elem_t* xb = reinterpret_cast<const elem_t*>(xv) + b * (int64_t)T * D;
+  elem_t* yr = reinterpret_cast<elem_t*>(yv) + row * (int64_t)D;
+  const int nch = D / VEC;
+  for (int c = lane; c < nch; c += kWave) {
+    const int k = c * VEC;
+    const int t = k / d, j = k - t * d;
+    *reinterpret_cast<raw_t*>(yr + k) = *reinterpret_cast<const raw_t*>(xb + (int64_t)t * D + h * d + j);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// S[b,t,:] = LN(TokenMix(X)[b,t,:] + X[b,t,:]) * g + beta.  One wave per row.
+// Element k of mixed token t is element t*d + (k mod d) of token k / d.
+
+template <typename T, int VEC, int MAXI>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __restrict__ x, T* __restrict__ s,
+                                                                  const float* __restrict__ g,
+                                                                  const float* __restrict__ beta,
+                                                                  int64_t B, int T_, int D) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  if (row >= B * T_) return;
+  const int lane = lane_id();
+  const int64_t b = row / T_;
+  const int t = (int)(row - b * T_);
+  const int d = D / T_;
+  const T* xb = x + b * (int64_t)T_ * D;
+  const int nch = D / VEC;
+  float v[MAXI][VEC];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+      const int k = c * VEC;
+      const int tp = k / d, j = k - tp * d;
+      float m[VEC], r[VEC];
+      load_f32<T, VEC>(xb + (int64_t)tp * D + t * d + j, m);
+      load_f32<T, VEC>(xb + (int64_t)t * D + k, r);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        v[i][e] = m[e] + r[e];
+        sum += v[i][e];
+      }
+    }
+  }
+  const float mean = wave_sum(sum) / (float)D;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float q = v[i][e] - mean;
+        sq += q * q;
+      }
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D + ln_eps());
+  T* sr = s + row * (int64_t)D;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+      const int k = c * VEC;
+      float o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = (v[i][e] - mean) * rstd * g[k + e] + beta[k + e];
+      store_from_f32<T, VEC>(sr + k, o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// out[r,:] = LN(z[r,:]) * g + beta for fp32 rows (D % 4 == 0).
+
+template <typename T, int MAXI>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const float* __restrict__ z, T* __restrict__ out,
+                                                                   const float* __restrict__ g,
+                                                                   const float* __restrict__ beta,
+                                                                   int64_t rows, int D) {
+  constexpr int VEC = 4;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  if (row >= rows) return;
+  const int lane = lane_id();
+  const int nch = D / VEC;
+  const float* zr = z + row * (int64_t)D;
+  float v[MAXI][VEC];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+      load_f32<float, VEC>(zr + c * VEC, v[i]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sum += v[i][e];
+    }
+  }
+  const float mean = wave_sum(sum) / (float)D;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float q = v[i][e] - mean;
+        sq += q * q;
+      }
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D + ln_eps());
+  T* orow = out + row * (int64_t)D;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+      const int k = c * VEC;
+      float o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = (v[i][e] - mean) * rstd * g[k + e] + beta[k + e];
+      store_from_f32<T, VEC>(orow + k, o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pooled[b,k] = (1/T) sum_t x[b,t,k];  logit[b] = sum_k w[k] pooled[b,k] + c
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_pool_logit(const T* __restrict__ x,
+                                                                      const float* __restrict__ w, float c0,
+                                                                      float* __restrict__ pooled,
+                                                                      float* __restrict__ logits,
+                                                                      int64_t B, int T_, int D) {
+  const int64_t b = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  if (b >= B) return;
+  const int lane = lane_id();
+  const T* xb = x + b * (int64_t)T_ * D;
+  const float inv_t = 1.0f / (float)T_;
+  float dot = 0.f;
+  for (int c = lane; c < D / VEC; c += kWave) {
+    const int k = c * VEC;
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    for (int t = 0; t < T_; ++t) {
+      float q[VEC];
+      load_f32<T, VEC>(xb + (int64_t)t * D + k, q);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += q[e];
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      acc[e] *= inv_t;
+      if (w) dot += acc[e] * w[k + e];
+    }
+    if (pooled) store_from_f32<float, VEC>(pooled + b * D + k, acc);
+  }
+  dot = wave_sum(dot);
+  if (logits && lane == 0) logits[b] = dot + c0;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+
+hipError_t launch_tokenize_padsplit(const float* emb, int64_t B, int64_t F, int T, int D, int dt,
+                                    void* x0, hipStream_t s) {
+  const int64_t TD = (int64_t)T * D;
+  if (TD % 4 == 0) {
+    const int64_t n = B * (TD / 4);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (dt == kBF16)
+      hipLaunchKernelGGL(k_tokenize<bf16>, grid, dim3(256), 0, s, emb, (bf16*)x0, B, F, TD);
+    else
+      hipLaunchKernelGGL(k_tokenize<float>, grid, dim3(256), 0, s, emb, (float*)x0, B, F, TD);
+  } else {
+    const int64_t n = B * TD;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (dt == kBF16)
+      hipLaunchKernelGGL(k_tokenize1<bf16>, grid, dim3(256), 0, s, emb, (bf16*)x0, B, F, TD);
+    else
+      hipLaunchKernelGGL(k_tokenize1<float>, grid, dim3(256), 0, s, emb, (float*)x0, B, F, TD);
+  }
+  return hipGetLastError();
+}
+
+namespace {
+template <int EB>
+hipError_t token_mix_eb(const void* x, void* y, int64_t B, int T, int D, int vec, hipStream_t s) {
+  const dim3 grid((unsigned)((B * T + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
+  switch (vec) {
+    case 1: hipLaunchKernelGGL((k_token_mix<EB, 1>), grid, block, 0, s, x, y, B, T, D); break;
+    case 2: hipLaunchKernelGGL((k_token_mix<EB, 2>), grid, block, 0, s, x, y, B, T, D); break;
+    case 4: hipLaunchKernelGGL((k_token_mix<EB, 4>), grid, block, 0, s, x, y, B, T, D); break;
+    default:
+      if constexpr (EB == 2) hipLaunchKernelGGL((k_token_mix<EB, 8>), grid, block, 0, s, x, y, B, T, D);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int VEC>
+hipError_t mix_ln_vec(const void* x, void* so, const float* g, const float* b, int64_t B, int T_, int D,
+                      hipStream_t s) {
+  const dim3 grid((unsigned)((B * T_ + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
+  const T* xx = (const T*)x;
+  T* ss = (T*)so;
+  switch (pick_maxi(D / VEC)) {
+    case 0: return hipErrorInvalidValue;
+    case 1: hipLaunchKernelGGL((k_mix_ln<T, VEC, 1>), grid, block, 0, s, xx, ss, g, b, B, T_, D); break;
+    case 2: hipLaunchKernelGGL((k_mix_ln<T, VEC, 2>), grid, block, 0, s, xx, ss, g, b, B, T_, D); break;
+    case 4: hipLaunchKernelGGL((k_mix_ln<T, VEC, 4>), grid, block, 0, s, xx, ss, g, b, B, T_, D); break;
+    case 8: hipLaunchKernelGGL((k_mix_ln<T, VEC, 8>), grid, block, 0, s, xx, ss, g, b, B, T_, D); break;
+    default: hipLaunchKernelGGL((k_mix_ln<T, VEC, 16>), grid, block, 0, s, xx, ss, g, b, B, T_, D); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t ln_rows_t(const float* z, void* out, const float* g, const float* b, int64_t rows, int D,
+                     hipStream_t s) {
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
+  T* o = (T*)out;
+  switch (pick_maxi(D / 4)) {
+    case 0: return hipErrorInvalidValue;
+    case 1: hipLaunchKernelGGL((k_ln_rows<T, 1>), grid, block, 0, s, z, o, g, b, rows, D); break;
+    case 2: hipLaunchKernelGGL((k_ln_rows<T, 2>), grid, block, 0, s, z, o, g, b, rows, D); break;
+    case 4: hipLaunchKernelGGL((k_ln_rows<T, 4>), grid, block, 0, s, z, o, g, b, rows, D); break;
+    case 8: hipLaunchKernelGGL((k_ln_rows<T, 8>), grid, block, 0, s, z, o, g, b, rows, D); break;
+    default: hipLaunchKernelGGL((k_ln_rows<T, 16>), grid, block, 0, s, z, o, g, b, rows, D); break;
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+bool row_width_supported(int T, int D, int dt) {
+  const int eb = dt == kBF16 ? 2 : 4;
+  if (T <= 0 || D <= 0 || D % T || D % 8) return false;
+  return pick_maxi(D / chunk_elems(D / T, eb)) != 0 && pick_maxi(D / 4) != 0;
+}
+
+hipError_t launch_token_mix(const void* x, void* y, int64_t B, int T, int D, int dt, hipStream_t s) {
+  const int eb = dt == kBF16 ? 2 : 4;
+  const int vec = chunk_elems(D / T, eb);
+  return eb == 2 ? token_mix_eb<2>(x, y, B, T, D, vec, s) : token_mix_eb<4>(x, y, B, T, D, vec, s);
+}
+
+hipError_t launch_mix_ln(const void* x, void* so, const float* g, const float* b, int64_t B, int T,
+                         int D, int dt, hipStream_t s) {
+  const int d = D / T;
+  if (dt == kBF16) {
+    switch (chunk_elems(d, 2)) {
+      case 8: return mix_ln_vec<bf16, 8>(x, so, g, b, B, T, D, s);
+      case 4: return mix_ln_vec<bf16, 4>(x, so, g, b, B, T, D, s);
+      case 2: return mix_ln_vec<bf16, 2>(x, so, g, b, B, T, D, s);
+      default: return mix_ln_vec<bf16, 1>(x, so, g, b, B, T, D, s);
+    }
+  }
+  switch (chunk_elems(d, 4)) {
+    case 4: return mix_ln_vec<float, 4>(x, so, g, b, B, T, D, s);
+    case 2: return mix_ln_vec<float, 2>(x, so, g, b, B, T, D, s);
+    default: return mix_ln_vec<float, 1>(x, so, g, b, B, T, D, s);
+  }
+}
+
+hipError_t launch_ln_rows_f32(const float* z, void* out, const float* g, const float* b, int64_t rows,
+                              int D, int dt, hipStream_t s) {
+  return dt == kBF16 ? ln_rows_t<bf16>(z, out, g, b, rows, D, s) : ln_rows_t<float>(z, out, g, b, rows, D, s);
+}
+
+hipError_t launch_pool_logit(const void* x, const float* w, float c, float* pooled, float* logits,
+                             int64_t B, int T, int D, int dt, hipStream_t s) {
+  const dim3 grid((unsigned)((B + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
+  if (dt == kBF16) {
+    if (D % 8 == 0)
+      hipLaunchKernelGGL((k_pool_logit<bf16, 8>), grid, block, 0, s, (const bf16*)x, w, c, pooled, logits, B, T, D);
+    else
+      hipLaunchKernelGGL((k_pool_logit<bf16, 4>), grid, block, 0, s, (const bf16*)x, w, c, pooled, logits, B, T, D);
+  } else {
+    hipLaunchKernelGGL((k_pool_logit<float, 4>), grid, block, 0, s, (const float*)x, w, c, pooled, logits, B, T, D);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rm

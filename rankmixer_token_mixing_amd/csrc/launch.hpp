@@ -1,0 +1,93 @@
+// Host-side launchers of the RankMixer kernels.  Each returns the
+// hipError_t of its launch(es); argument checking is done by the caller
+// (abi.cpp) before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rm {
+
+enum ElemType { kF32 = 0, kBF16 = 1 };
+
+// ---- elementwise / row kernels (kernels_rows.hip) ---------------------------
+
+// The row kernels keep one [D] row per wave in registers: D must be a
+// multiple of 8 and of T, and at most 1024 chunks wide (D <= 8192 when the
+// head width d = D/T is a multiple of 8).
+bool row_width_supported(int T, int D, int dt);
+
+hipError_t launch_tokenize_padsplit(const float* emb, int64_t B, int64_t F, int T, int D, int dt,
+                                    void* x0, hipStream_t s);
+hipError_t launch_token_mix(const void* x, void* y, int64_t B, int T, int D, int dt, hipStream_t s);
+// S = LN(TokenMix(X) + X) row by row
+hipError_t launch_mix_ln(const void* x, void* s_out, const float* g, const float* b, int64_t B,
+                         int T, int D, int dt, hipStream_t s);
+// out = LN(z) for fp32 rows z [rows][D]
+hipError_t launch_ln_rows_f32(const float* z, void* out, const float* g, const float* b,
+                              int64_t rows, int D, int dt, hipStream_t s);
+// pooled[b] = mean_t x[b,t,:]; logit[b] = w . pooled[b] + c
+hipError_t launch_pool_logit(const void* x, const float* w, float c, float* pooled, float* logits,
+                             int64_t B, int T, int D, int dt, hipStream_t s);
+
+// ---- MoE routing and combine (kernels_moe.hip) -------------------------------
+
+struct MoeWork {
+  float* gates;     // [B][T][E]
+  int* counts;      // [G]   G = T*E
+  int* offsets;     // [G+1]
+  int* rows;        // [B*T*E]  sample index per compacted entry
+  float* gatec;     // [B*T*E]  gate per compacted entry
+  int* pos;         // [B][T][E] compacted index or -1
+  int* tiles;       // [2 * max_tiles] (group, m0) pairs
+  int* ntiles;      // [1]
+};
+hipError_t launch_moe_router(const void* s, const void* wr, const float* br, float* gates,
+                             int64_t B, int T, int D, int E, int dt, hipStream_t st);
+hipError_t launch_moe_compact(const MoeWork& w, int64_t B, int T, int E, int bm, hipStream_t st);
+// v[b,t,:] = sum_j y[pos[b,t,j], :]; if ln: out = LN(v + s) else out = v
+hipError_t launch_moe_combine(const float* y, const int* pos, const void* s, const float* g,
+                              const float* b, void* out, int64_t B, int T, int D, int E, bool ln,
+                              int dt, hipStream_t st);
+
+// ---- grouped MFMA GEMM (kernels_gemm.hip) ------------------------------------
+
+enum Epilogue {
+  kEpiBiasGelu = 0,       // C(dt)  = GELU(acc + bias[n])
+  kEpiBias = 1,           // C(dt)  = acc + bias[n]
+  kEpiBiasResidF32 = 2,   // C(f32) = acc + bias[n] + R[m][n]
+  kEpiBiasScaleF32 = 3,   // C(f32) = rowscale[m] * (acc + bias[n])
+};
+
+// C_g[m][n] = sum_k A_g[m][k] * W_g[n][k], g = 0..G-1, followed by an epilogue.
+// Element offsets (not bytes).  Row m of A in group g sits at
+//   (g / a_gdiv) * a_gs + rowid(m) * a_rs,   rowid(m) = a_rowidx ? a_rowidx[base+m] : base+m
+// with base = row_off ? row_off[g] : 0; W_g row n at g * b_gs + n * K; output
+// row m of group g at (base + m) * c_rs + g * c_gs (the residual the same way
+// with r_rs / r_gs); bias of group g at g * bias_gs.
+struct GemmArgs {
+  int dt = kBF16;
+  int epi = kEpiBias;
+  int M = 0, N = 0, K = 0, G = 0;
+  const void* A = nullptr; int64_t a_gs = 0, a_rs = 0; int a_gdiv = 1;
+  const int* a_rowidx = nullptr;
+  const void* W = nullptr; int64_t b_gs = 0;
+  void* C = nullptr; int64_t c_gs = 0, c_rs = 0;
+  const float* bias = nullptr; int64_t bias_gs = 0;
+  const void* R = nullptr; int64_t r_gs = 0, r_rs = 0;
+  const float* rowscale = nullptr;
+  // ragged mode (MoE): group g has row_off[g+1]-row_off[g] rows; the tiles
+  // to run are the (g, m0) pairs tiles[0..2*ntiles) with *ntiles on the device;
+  // max_mtiles bounds *ntiles (the grid is sized for it).
+  const int* row_off = nullptr;
+  const int* tiles = nullptr;
+  const int* ntiles = nullptr;
+  int max_mtiles = 0;
+  int tile_cfg = -1;  // -1: choose automatically
+};
+// Row count of the M tile a launch of `a` will use (ragged tile lists are
+// built for this).
+int gemm_tile_m(const GemmArgs& a);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace rm

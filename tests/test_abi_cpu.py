@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/rankmixer.h declares, and rejects bad arguments on the host before
+anything is launched.  No call here reaches a kernel launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from rankmixer_token_mixing_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rankmixer.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.lib_path()):
+        from rankmixer_token_mixing_amd.build import build
+        build()
+    return bd.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_six_calls():
+    names = declared_functions()
+    for n in ("rm_tokenize_padsplit", "rm_token_mix", "rm_pffn_fwd", "rm_block_fwd", "rm_moe_relu_fwd",
+              "rm_model_fwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # and the binding wraps the same set
+    for name in declared_functions():
+        assert name in bd._SIGNATURES, name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.rm_status_string(0) == b"ok"
+    assert lib.rm_status_string(3) == b"workspace too small"
+    assert lib.rm_status_string(99) == b"unknown status"
+    assert b"gfx950" in lib.rm_version()
+
+
+A16 = 0x10000  # a 16-byte aligned stand-in address; never dereferenced
+
+
+def err(lib):
+    return lib.rm_last_error().decode()
+
+
+def test_token_mix_argument_errors(lib):
+    assert lib.rm_token_mix(None, A16, 4, 2, 8, bd.RM_BF16, None) == bd.RM_ERR_INVALID
+    assert "NULL" in err(lib)
+    assert lib.rm_token_mix(A16, A16 + 4096, 4, 3, 8, bd.RM_BF16, None) == bd.RM_ERR_UNSUPPORTED
+    assert "divisible" in err(lib)
+    assert lib.rm_token_mix(A16 + 2, A16 + 4096, 4, 2, 8, bd.RM_BF16, None) == bd.RM_ERR_INVALID
+    assert "aligned" in err(lib)
+    assert lib.rm_token_mix(A16, A16, 4, 2, 8, bd.RM_BF16, None) == bd.RM_ERR_INVALID
+    assert "alias" in err(lib)
+    assert lib.rm_token_mix(A16, A16 + 4096, 0, 2, 8, bd.RM_BF16, None) == bd.RM_ERR_INVALID
+    assert lib.rm_token_mix(A16, A16 + 4096, 4, 2, 8, 7, None) == bd.RM_ERR_UNSUPPORTED
+
+
+def test_tokenizer_argument_errors(lib):
+    assert lib.rm_tokenize_padsplit(A16, 4, 5121, 16, 320, bd.RM_BF16, A16 * 2, None) == bd.RM_ERR_UNSUPPORTED
+    assert "fit" in err(lib)
+    assert lib.rm_tokenize_padsplit(None, 4, 5000, 16, 320, bd.RM_BF16, A16, None) == bd.RM_ERR_INVALID
+
+
+def _pffn():
+    return bd.PffnParams(A16, A16, A16, A16)
+
+
+def test_pffn_workspace_and_shape_errors(lib):
+    need = lib.rm_pffn_workspace_bytes(64, 4, 64, 128, bd.RM_F32)
+    assert need >= 64 * 4 * 128 * 4
+    p = _pffn()
+    s, v, ws = A16 * 2, A16 * 3, A16 * 4
+    assert lib.rm_pffn_fwd(s, C.byref(p), v, 64, 4, 64, 128, bd.RM_F32, ws, need - 1, None) == bd.RM_ERR_WORKSPACE
+    assert "workspace" in err(lib)
+    assert lib.rm_pffn_fwd(s, C.byref(p), v, 64, 4, 68, 128, bd.RM_F32, ws, need, None) == bd.RM_ERR_UNSUPPORTED
+    assert lib.rm_pffn_fwd(s, C.byref(p), v, 64, 4, 64, 100, bd.RM_F32, ws, need, None) == bd.RM_ERR_UNSUPPORTED
+    assert lib.rm_pffn_fwd(s, None, v, 64, 4, 64, 128, bd.RM_F32, ws, need, None) == bd.RM_ERR_INVALID
+    p.b2 = None
+    assert lib.rm_pffn_fwd(s, C.byref(p), v, 64, 4, 64, 128, bd.RM_F32, ws, need, None) == bd.RM_ERR_INVALID
+    assert "b2" in err(lib)
+    assert lib.rm_pffn_fwd(s, C.byref(_pffn()), s, 64, 4, 64, 128, bd.RM_F32, ws, need, None) == bd.RM_ERR_INVALID
+
+
+def test_moe_shape_errors(lib):
+    p = bd.MoeParams(A16, A16, A16, A16, A16, A16)
+    need = lib.rm_moe_workspace_bytes(64, 4, 64, 8, 128, bd.RM_BF16)
+    assert need > 0
+    args = (A16 * 2, C.byref(p), A16 * 3, None, 64, 4, 64)
+    assert lib.rm_moe_relu_fwd(*args, 0, 128, bd.RM_BF16, A16 * 4, need, None) == bd.RM_ERR_UNSUPPORTED
+    assert lib.rm_moe_relu_fwd(*args, 33, 128, bd.RM_BF16, A16 * 4, need, None) == bd.RM_ERR_UNSUPPORTED
+    assert lib.rm_moe_relu_fwd(*args, 8, 128, bd.RM_BF16, A16 * 4, 16, None) == bd.RM_ERR_WORKSPACE
+    assert lib.rm_moe_relu_fwd(A16 * 2, C.byref(p), A16 * 3, A16 + 4, 64, 4, 64, 8, 128, bd.RM_BF16, A16 * 4, need,
+                               None) == bd.RM_ERR_INVALID  # misaligned gates
+
+
+def test_block_and_model_errors(lib):
+    bp = bd.BlockParams()
+    bp.kind = 5
+    bp.ln1_g = bp.ln1_b = bp.ln2_g = bp.ln2_b = A16
+    assert lib.rm_block_fwd(A16, C.byref(bp), A16 * 2, 8, 4, 64, 128, 0, bd.RM_BF16, A16 * 3, 1 << 30,
+                            None) == bd.RM_ERR_UNSUPPORTED
+    bp.kind = bd.RM_BLOCK_DENSE
+    bp.pffn = _pffn()
+    need = lib.rm_block_workspace_bytes(0, 8, 4, 64, 128, 0, bd.RM_BF16)
+    assert lib.rm_block_fwd(A16, C.byref(bp), A16 * 2, 8, 4, 64, 128, 0, bd.RM_BF16, A16 * 3, need - 1,
+                            None) == bd.RM_ERR_WORKSPACE
+    arr = (bd.BlockParams * 1)(bp)
+    m = bd.ModelDesc(4, 64, 128, 0, bd.RM_BF16, 1, arr, 0, None, 0.0)
+    need = lib.rm_model_workspace_bytes(C.byref(m), 8)
+    assert need >= lib.rm_block_workspace_bytes(0, 8, 4, 64, 128, 0, bd.RM_BF16)
+    assert lib.rm_model_fwd(C.byref(m), A16, None, None, A16 * 2, 8, A16 * 3, need, None) == bd.RM_ERR_INVALID
+    assert "head_w" in err(lib)
+    m.F = 300
+    assert lib.rm_model_fwd(C.byref(m), A16, None, None, None, 8, A16 * 3, need, None) == bd.RM_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_scale_with_the_problem(lib):
+    small = lib.rm_block_workspace_bytes(0, 1024, 32, 1536, 6144, 0, bd.RM_BF16)
+    # S (bf16) + H (bf16) + the fp32 pre-LayerNorm rows
+    assert small >= 1024 * 32 * (1536 * 2 + 6144 * 2 + 1536 * 4)
+    assert lib.rm_block_workspace_bytes(1, 2048, 16, 768, 1536, 8, bd.RM_BF16) > \
+        lib.rm_block_workspace_bytes(1, 1024, 16, 768, 1536, 8, bd.RM_BF16)

@@ -1,0 +1,115 @@
+"""GPU parity of the block and the whole stack on the five workload
+configurations, through the C ABI, in the launch configuration the
+benchmark times (rm_model_fwd over the full batch).  The oracle evaluates a
+seeded subset of samples (always the first and the last): samples never
+interact, so the subset is exact."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic_inputs as si
+from oracle import rankmixer_oracle as orc
+from tests.gpu_util import TOL, config_inputs, ensure_lib, host, note, rel_l2, rel_l2_rows
+
+pytestmark = pytest.mark.gpu
+
+ORACLE_ROWS = {"c0": 64, "c1": 48, "c2": 64, "c3": 24, "c4": 32}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    note(f"[gpu] {request.node.nodeid}")
+
+
+def _model(inputs):
+    from rankmixer_token_mixing_amd import binding as bd
+    cfg = inputs["config"]
+    blocks = bd.upload_blocks(inputs["blocks"])
+    head = None
+    if "head" in inputs:
+        head = {"w": bd.to_device(inputs["head"]["w"]), "c": inputs["head"]["c"]}
+    model = bd.Model(blocks, cfg.T, cfg.D, DT[cfg.dtype], F=cfg.F, head=head)
+    inp = bd.to_device(inputs["emb"] if cfg.F else inputs["x"])
+    return model, inp
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4"])
+def test_config_matches_oracle(name):
+    from rankmixer_token_mixing_amd import binding as bd
+    inputs = config_inputs(name)
+    cfg = inputs["config"]
+    model, inp = _model(inputs)
+    note(f"[gpu] rm_model_fwd {cfg.description}")
+    out = bd.rm_model_fwd(model, inp, want_x=True, want_pooled=cfg.head)
+    torch.cuda.synchronize()
+    rows = si.random_rows(cfg.B, ORACLE_ROWS[name])
+    ref = orc.run_config(inputs, rows)
+    err = rel_l2_rows(host(out["x"])[rows], ref["x"])
+    assert err <= TOL[cfg.dtype], f"{name}: max relative L2 {err:.3e}"
+    if cfg.head:
+        err_l = rel_l2(host(out["logit"])[rows], ref["logit"])
+        assert err_l <= TOL[cfg.dtype], f"{name}: logit relative L2 {err_l:.3e}"
+        err_p = rel_l2_rows(host(out["pooled"])[rows], ref["pooled"])
+        assert err_p <= TOL[cfg.dtype]
+    # LayerNorm output statistics (gamma = 1, beta = 0): every token row has
+    # mean ~0 and variance ~1 over the whole batch, not just the sample
+    x = out["x"].float()
+    assert x.mean(dim=-1).abs().max().item() < 0.02
+    assert (x.var(dim=-1, unbiased=False) - 1).abs().max().item() < 0.03
+    assert torch.isfinite(x).all()
+
+
+@pytest.mark.parametrize("name", ["c1", "c4"])
+def test_model_is_deterministic(name):
+    from rankmixer_token_mixing_amd import binding as bd
+    inputs = config_inputs(name)
+    model, inp = _model(inputs)
+    a = bd.rm_model_fwd(model, inp)["x"].clone()
+    b = bd.rm_model_fwd(model, inp)["x"]
+    assert torch.equal(a, b)
+
+
+def test_block_fwd_equals_first_block_of_the_model():
+    from rankmixer_token_mixing_amd import binding as bd
+    inputs = config_inputs("c1")
+    cfg = inputs["config"]
+    blocks = bd.upload_blocks(inputs["blocks"][:1])
+    x = bd.to_device(inputs["x"])
+    y1 = bd.rm_block_fwd(x, blocks[0])
+    y2 = bd.rm_model_fwd(bd.Model(blocks, cfg.T, cfg.D, torch.bfloat16), x)["x"]
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("dtype,B,T,D,k", [
+    ("bf16", 1, 4, 64, 2),       # one sample
+    ("f32", 33, 1, 64, 2),       # T = 1: the mix is the identity
+    ("bf16", 20, 32, 64, 2),     # heads of width 2
+    ("bf16", 300, 16, 320, 4),   # heads of width 20, ragged batch
+    ("f32", 17, 8, 40, 3),       # odd hidden multiple, heads of width 5
+])
+def test_block_edge_shapes(dtype, B, T, D, k):
+    from rankmixer_token_mixing_amd import binding as bd
+    cfg = si.Config("edge", B=B, T=T, D=D, L=1, dtype=dtype, k=k, bias_var=0.01)
+    inputs = si.make_inputs(cfg, seed=B + T)
+    blocks = bd.upload_blocks(inputs["blocks"])
+    y = bd.rm_block_fwd(bd.to_device(inputs["x"]), blocks[0])
+    ref = orc.block_fwd(inputs["x"], inputs["blocks"][0])
+    assert rel_l2_rows(host(y), ref) <= TOL[dtype]
+
+
+def test_moe_block_edge_all_gates_off():
+    # router bias far below zero: every gate is 0, so X' = LN2(S)
+    from rankmixer_token_mixing_amd import binding as bd
+    cfg = si.Config("moe-off", B=40, T=4, D=64, L=1, dtype="bf16", E=4, He=64)
+    inputs = si.make_inputs(cfg, seed=3)
+    inputs["blocks"][0]["br"][:] = -1e4
+    blocks = bd.upload_blocks(inputs["blocks"])
+    y = bd.rm_block_fwd(bd.to_device(inputs["x"]), blocks[0])
+    ref = orc.block_fwd(inputs["x"], inputs["blocks"][0])
+    assert rel_l2_rows(host(y), ref) <= TOL["bf16"]
