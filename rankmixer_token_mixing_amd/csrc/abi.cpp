@@ -124,6 +124,17 @@ rm_status check_shape(int64_t B, int T, int D, int dt) {
   return RM_OK;
 }
 
+// shapes of the per-token FFN / MoE alone (no token mixing, so D need not
+// divide by T)
+rm_status check_ffn_shape(int64_t B, int T, int D, int dt) {
+  RM_TRY(check_dtype(dt));
+  if (B <= 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B, T and D must be positive (B=%lld T=%d D=%d)", (long long)B, T, D);
+  if (D % 8) return fail(RM_ERR_UNSUPPORTED, "D=%d must be a multiple of 8", D);
+  if (D > 4096) return fail(RM_ERR_UNSUPPORTED, "D=%d is wider than the row kernels support (4096)", D);
+  if (B * T > (int64_t)1 << 31) return fail(RM_ERR_UNSUPPORTED, "B*T too large");
+  return RM_OK;
+}
+
 rm_status check_hidden(int hidden) {
   if (hidden <= 0) return fail(RM_ERR_INVALID, "hidden width must be positive (%d)", hidden);
   if (hidden % 8) return fail(RM_ERR_UNSUPPORTED, "hidden width %d must be a multiple of 8", hidden);
@@ -429,7 +440,7 @@ size_t rm_pffn_workspace_bytes(int64_t B, int T, int D, int Hd, int dtype) {
 
 rm_status rm_pffn_fwd(const void* s, const rm_pffn_params* p, void* v, int64_t B, int T, int D, int Hd, int dtype,
                       void* ws, size_t ws_bytes, void* stream) {
-  RM_TRY(check_shape(B, T, D, dtype));
+  RM_TRY(check_ffn_shape(B, T, D, dtype));
   RM_TRY(check_hidden(Hd));
   if (!p) return fail(RM_ERR_INVALID, "params is NULL");
   RM_TRY(check_ptr(s, "s")); RM_TRY(check_ptr(v, "v"));
@@ -461,7 +472,7 @@ static rm_status check_moe_params(const rm_moe_params* p) {
 
 rm_status rm_moe_relu_fwd(const void* s, const rm_moe_params* p, void* v, float* gates, int64_t B, int T, int D,
                           int E, int He, int dtype, void* ws, size_t ws_bytes, void* stream) {
-  RM_TRY(check_shape(B, T, D, dtype));
+  RM_TRY(check_ffn_shape(B, T, D, dtype));
   RM_TRY(check_hidden(He));
   RM_TRY(check_moe_shape(B, T, E));
   RM_TRY(check_moe_params(p));
@@ -479,7 +490,7 @@ rm_status rm_moe_relu_fwd(const void* s, const rm_moe_params* p, void* v, float*
 
 rm_status rm_moe_route(const void* s, const void* wr, const float* br, float* gates, int* offsets, int* rows,
                        int64_t B, int T, int D, int E, int dtype, void* ws, size_t ws_bytes, void* stream) {
-  RM_TRY(check_shape(B, T, D, dtype));
+  RM_TRY(check_ffn_shape(B, T, D, dtype));
   RM_TRY(check_moe_shape(B, T, E));
   RM_TRY(check_ptr(s, "s")); RM_TRY(check_ptr(wr, "wr")); RM_TRY(check_ptr(br, "br"));
   RM_TRY(check_ptr(gates, "gates")); RM_TRY(check_ptr(offsets, "offsets")); RM_TRY(check_ptr(rows, "rows"));
