@@ -223,12 +223,16 @@ size_t block_ws(Carver& c, int kind, int64_t B, int T, int D, int hidden, int E,
 // ---------------------------------------------------------------------------
 // launch sequences
 
-rm::GemmArgs ffn1_args(const void* s, const rm_pffn_params* p, void* H, int64_t B, int T, int D, int Hd, int dt) {
+// S row (b, t) at b * sb + t * st elements: [B][T][D] is sb = T*D, st = D; the
+// block path keeps S token-major ([T][B][D]: sb = D, st = B*D) so the rows the
+// W1 product reads for one token are contiguous.
+rm::GemmArgs ffn1_args(const void* s, int64_t sb, int64_t st, const rm_pffn_params* p, void* H, int64_t B, int T,
+                       int D, int Hd, int dt) {
   rm::GemmArgs a;
   a.dt = dt;
   a.epi = rm::kEpiBiasGelu;
   a.M = (int)B; a.N = Hd; a.K = D; a.G = T;
-  a.A = s; a.a_gs = D; a.a_rs = (int64_t)T * D;
+  a.A = s; a.a_gs = st; a.a_rs = sb;
   a.W = p->w1; a.b_gs = (int64_t)Hd * D;
   a.C = H; a.c_gs = B * Hd; a.c_rs = Hd;
   a.bias = p->b1; a.bias_gs = Hd;
@@ -248,7 +252,7 @@ rm::GemmArgs ffn2_args(const void* H, const rm_pffn_params* p, int64_t B, int T,
 
 rm_status run_pffn(const void* s, const rm_pffn_params* p, void* v, int64_t B, int T, int D, int Hd, int dt,
                    const PffnWs& w, hipStream_t st) {
-  RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(s, p, w.H, B, T, D, Hd, dt), st), "pffn W1 product"));
+  RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(s, (int64_t)T * D, D, p, w.H, B, T, D, Hd, dt), st), "pffn W1 product"));
   rm::GemmArgs a2 = ffn2_args(w.H, p, B, T, D, Hd, dt);
   a2.epi = rm::kEpiBias;
   a2.C = v;
@@ -256,18 +260,19 @@ rm_status run_pffn(const void* s, const rm_pffn_params* p, void* v, int64_t B, i
   return RM_OK;
 }
 
-// v = MoE(s); if ln_g: out = LN(v + s) instead
-rm_status run_moe(const void* s, const rm_moe_params* p, void* out, float* gates_out, const float* ln_g,
-                  const float* ln_b, int64_t B, int T, int D, int E, int He, int dt, MoeWs w, hipStream_t st) {
+// v = MoE(s); if ln_g: out = LN(v + s) instead.  S row (b, t) at b * sb + t * sT.
+rm_status run_moe(const void* s, int64_t sb, int64_t sT, const rm_moe_params* p, void* out, float* gates_out,
+                  const float* ln_g, const float* ln_b, int64_t B, int T, int D, int E, int He, int dt, MoeWs w,
+                  hipStream_t st) {
   if (gates_out) w.mw.gates = gates_out;
-  RM_TIMED("moe_router", st, RM_HIP(rm::launch_moe_router(s, p->wr, p->br, w.mw.gates, B, T, D, E, dt, st), "moe router"));
+  RM_TIMED("moe_router", st, RM_HIP(rm::launch_moe_router(s, sb, sT, p->wr, p->br, w.mw.gates, B, T, D, E, dt, st), "moe router"));
   RM_TIMED("moe_compact", st, RM_HIP(rm::launch_moe_compact(w.mw, B, T, E, kMoeTileM, st), "moe compaction"));
   const int G = T * E;
   rm::GemmArgs a;
   a.dt = dt;
   a.epi = rm::kEpiBiasGelu;
   a.M = (int)B; a.N = He; a.K = D; a.G = G;
-  a.A = s; a.a_gdiv = E; a.a_gs = D; a.a_rs = (int64_t)T * D; a.a_rowidx = w.mw.rows;
+  a.A = s; a.a_gdiv = E; a.a_gs = sT; a.a_rs = sb; a.a_rowidx = w.mw.rows;
   a.W = p->w1; a.b_gs = (int64_t)He * D;
   a.C = w.Hc; a.c_gs = 0; a.c_rs = He;
   a.bias = p->b1; a.bias_gs = He;
@@ -287,7 +292,7 @@ rm_status run_moe(const void* s, const rm_moe_params* p, void* out, float* gates
   if (rm::gemm_tile_m(b) != kMoeTileM) return fail(RM_ERR_HIP, "internal: MoE tile size mismatch");
   RM_TIMED("moe_ffn2", st, RM_HIP(rm::launch_gemm(b, st), "moe W2 product"));
   RM_TIMED("moe_combine", st,
-           RM_HIP(rm::launch_moe_combine(w.Yc, w.mw.pos, s, ln_g, ln_b, out, B, T, D, E, ln_g != nullptr, dt, st),
+           RM_HIP(rm::launch_moe_combine(w.Yc, w.mw.pos, s, sb, sT, ln_g, ln_b, out, B, T, D, E, ln_g != nullptr, dt, st),
                   "moe combine"));
   return RM_OK;
 }
@@ -319,18 +324,19 @@ rm_status check_block_shape(int kind, int64_t B, int T, int D, int hidden, int E
 
 rm_status run_block(const void* x, const rm_block_params* p, void* xo, int64_t B, int T, int D, int hidden,
                     int E, int dt, const BlockWs& w, hipStream_t st) {
-  RM_TIMED("mix_ln1", st, RM_HIP(rm::launch_mix_ln(x, w.S, p->ln1_g, p->ln1_b, B, T, D, dt, st), "token mix + LayerNorm"));
+  RM_TIMED("mix_ln1", st, RM_HIP(rm::launch_mix_ln(x, w.S, p->ln1_g, p->ln1_b, B, T, D, dt, true, st), "token mix + LayerNorm"));
+  const int64_t sb = D, sT = B * D;  // S is token-major
   if (p->kind == RM_BLOCK_DENSE) {
-    RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(w.S, &p->pffn, w.pffn.H, B, T, D, hidden, dt), st), "block W1 product"));
+    RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(w.S, sb, sT, &p->pffn, w.pffn.H, B, T, D, hidden, dt), st), "block W1 product"));
     rm::GemmArgs a2 = ffn2_args(w.pffn.H, &p->pffn, B, T, D, hidden, dt);
     a2.epi = rm::kEpiBiasResidF32;
     a2.C = w.Z;
-    a2.R = w.S; a2.r_gs = D; a2.r_rs = (int64_t)T * D;
+    a2.R = w.S; a2.r_gs = sT; a2.r_rs = sb;
     RM_TIMED("ffn2_resid", st, RM_HIP(rm::launch_gemm(a2, st), "block W2 product"));
     RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows_f32(w.Z, xo, p->ln2_g, p->ln2_b, B * T, D, dt, st), "LayerNorm 2"));
     return RM_OK;
   }
-  return run_moe(w.S, &p->moe, xo, nullptr, p->ln2_g, p->ln2_b, B, T, D, E, hidden, dt, w.moe, st);
+  return run_moe(w.S, sb, sT, &p->moe, xo, nullptr, p->ln2_g, p->ln2_b, B, T, D, E, hidden, dt, w.moe, st);
 }
 
 size_t model_ws(Carver& c, const rm_model_desc* m, int64_t B, void** x0, void** x1, BlockWs* bw) {
@@ -484,7 +490,7 @@ rm_status rm_moe_relu_fwd(const void* s, const rm_moe_params* p, void* v, float*
   Carver c(ws);
   MoeWs w;
   moe_ws(c, B, T, D, E, He, dtype, &w);
-  RM_TRY(run_moe(s, p, v, gates, nullptr, nullptr, B, T, D, E, He, dtype, w, (hipStream_t)stream));
+  RM_TRY(run_moe(s, (int64_t)T * D, D, p, v, gates, nullptr, nullptr, B, T, D, E, He, dtype, w, (hipStream_t)stream));
   return ok();
 }
 
@@ -504,7 +510,7 @@ rm_status rm_moe_route(const void* s, const void* wr, const float* br, float* ga
   w.mw.offsets = offsets;
   w.mw.rows = rows;
   hipStream_t st = (hipStream_t)stream;
-  RM_HIP(rm::launch_moe_router(s, wr, br, gates, B, T, D, E, dtype, st), "moe router");
+  RM_HIP(rm::launch_moe_router(s, (int64_t)T * D, D, wr, br, gates, B, T, D, E, dtype, st), "moe router");
   RM_HIP(rm::launch_moe_compact(w.mw, B, T, E, kMoeTileM, st), "moe compaction");
   return ok();
 }

@@ -74,10 +74,27 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 // ---------------------------------------------------------------------------
-// GELU, exact form x * Phi(x) = x/2 * (1 + erf(x / sqrt 2))
+// GELU, exact form x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), with erf from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+//   erf(a) = 1 - (c1 t + c2 t^2 + c3 t^3 + c4 t^4 + c5 t^5) exp(-a^2),
+//   t = 1 / (1 + p a),  a >= 0,  |error| <= 1.5e-7,
+// odd in a.  Two transcendental ops (rcp, exp2) and a 5-term Horner sum.
+
+__device__ __forceinline__ float erf_as7126(float x) {
+  const float a = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * a);
+  float y = 1.061405429f;
+  y = y * t - 1.453152027f;
+  y = y * t + 1.421413741f;
+  y = y * t - 0.284496736f;
+  y = y * t + 0.254829592f;
+  y = y * t;
+  const float e = __builtin_amdgcn_exp2f(-a * a * 1.4426950408889634f);
+  return copysignf(1.0f - y * e, x);
+}
 
 __device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+  return 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752f));
 }
 
 // ---------------------------------------------------------------------------

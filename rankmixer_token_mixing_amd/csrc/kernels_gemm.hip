@@ -6,18 +6,37 @@
 //
 // C_g[m][n] = sum_k A_g[m][k] W_g[n][k]: both operands are read along k
 // (weights stored [out][in]).  One workgroup computes a BM x BN tile of one
-// group; 16-byte chunks of A and W stream global -> registers -> LDS (double
-// buffered, XOR-swizzled rows of 8 chunks), and each wave multiplies its
-// FM x FN grid of 16x16 fragments with MFMA (bf16: 16x16x32 bf16, fp32:
-// 16x16x4 f32), accumulating in fp32.  The MFMA is issued with the weight
-// fragment as its first operand, so each lane ends up holding 4 consecutive
-// output columns of one row: the epilogue writes 8- or 16-byte vectors.
+// group.  Operand k-slices stream straight from global memory into LDS with
+// global_load_lds_dwordx4 (no VGPR staging); LDS rows are 8 chunks of 16
+// bytes, XOR-swizzled (chunk ^ (row/2 mod 8)) so the 32-row fragment reads of
+// a wave hit distinct banks, and the DMA writes 1 KB contiguous per
+// instruction with each lane fetching the global chunk that belongs at its
+// swizzled slot.  Each wave multiplies an FM x FN grid of 32x32 blocks with
+// v_mfma_f32_32x32x16_bf16 (fp32 data: 4 x v_mfma_f32_32x32x2f32), fp32
+// accumulators in registers, the weight fragment as first MFMA operand so a
+// lane ends up holding 4 consecutive output columns of one row.
+//
+// Two main loops:
+//  * ring (bf16, K a multiple of 64): k-slices of 64 (one full 128-byte cache
+//    line per row), five LDS slots of max(BM,BN) rows each; stage k reads
+//    slots 2k%5 (A) and (2k+1)%5 (W) and, once every wave has passed the
+//    stage barrier, refills the two slots stage k-1 used with W_{k+1} and
+//    A_{k+2}.  Three k-slices (96 KB for 256x256) are always in flight, which
+//    is what the L2 -> LDS path needs to stream full lines at rate; the slots
+//    are separate LDS objects and the loop is unrolled by 5 so the compiler's
+//    DMA wait tracking sees which slot each read touches.
+//  * generic (fp32, or K not a multiple of 64): two LDS stages, chunks past K
+//    fetched from a 16-byte zero block.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace rm {
 
 namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
 
 struct KParams {
   const void* A;
@@ -39,141 +58,223 @@ struct KParams {
   int M, N, K, G, tiles_m, tiles_n;
 };
 
+// 16 zero bytes: the source of every chunk that lies past K
+__device__ __align__(16) uint4 g_zero_chunk = {0, 0, 0, 0};
+
 template <typename T> struct Mma;
 
 template <> struct Mma<bf16> {
-  // one chunk = 8 bf16 along k; one 16x16x32 MFMA per chunk
-  static __device__ __forceinline__ void run(floatx4& c, const uint4& a, const uint4& b) {
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+  // 2 chunks (lane halves) x 8 bf16 = 16 k per MFMA
+  static __device__ __forceinline__ void run(floatx16& c, const uint4& a, const uint4& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                 0, 0, 0);
   }
 };
 
 template <> struct Mma<float> {
-  // one chunk = 4 fp32 along k; four 16x16x4 MFMAs (element e of every lane's
-  // chunk forms the k-slice of MFMA e, the same slice in both operands)
-  static __device__ __forceinline__ void run(floatx4& c, const uint4& a, const uint4& b) {
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  // 2 chunks x 4 fp32 = 8 k: element e of every lane's chunk is the k-slice of
+  // MFMA e, the same slice in both operands
+  static __device__ __forceinline__ void run(floatx16& c, const uint4& a, const uint4& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
   }
 };
 
-constexpr int kCpr = 8;  // 16-byte chunks per LDS tile row (128 bytes of k)
+constexpr int kCpr = 8;  // 16-byte chunks per LDS operand row
 
-// physical chunk slot of (row, chunk): XOR swizzle so that the 16 rows read by
-// one quarter-wave and the 2 rows written by 16 lanes hit distinct banks
 __device__ __forceinline__ int swz(int row, int c) { return row * kCpr + (c ^ ((row >> 1) & 7)); }
 
-template <typename T, int NWM, int NWN, int FM, int FN, int EPI, bool RAGGED, bool AIDX>
-__global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm(KParams p) {
-  constexpr int NT = NWM * NWN * kWave;
-  constexpr int BM = NWM * FM * 16, BN = NWN * FN * 16;
-  constexpr int EPC = 16 / (int)sizeof(T);  // elements per chunk
-  constexpr int BK = kCpr * EPC;
-  constexpr int RPP = NT / kCpr;  // tile rows covered by one pass of the loader
-  constexpr int ACH = BM / RPP, BCH = BN / RPP;
-  static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of the loader pass");
-  typedef typename std::conditional<EPI == kEpiBiasGelu || EPI == kEpiBias, T, float>::type TO;
+// s_waitcnt vmcnt(n) only (expcnt / lgkmcnt untouched); n < 16
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
+}
 
-  __shared__ uint4 lds[2][(BM + BN) * kCpr];
+template <int EPI, typename T>
+struct OutType {
+  typedef typename std::conditional<EPI == kEpiBiasGelu || EPI == kEpiBias, T, float>::type type;
+};
 
-  const int tid = threadIdx.x;
-
-  // ---- which tile
+// which tile this workgroup owns
+struct TileId {
   int g, m0, n0, Mg;
   long long row_base;
+};
+
+template <bool RAGGED, int BM, int BN>
+__device__ __forceinline__ bool tile_id(const KParams& p, TileId& t) {
   if constexpr (RAGGED) {
     const int nv = (*p.ntiles) * p.tiles_n;
-    if ((int)blockIdx.x >= nv) return;
+    if ((int)blockIdx.x >= nv) return false;
     const int lid = xcd_remap(blockIdx.x, nv);
     const int slot = lid / p.tiles_n;
-    n0 = (lid - slot * p.tiles_n) * BN;
-    g = p.tiles[2 * slot];
-    m0 = p.tiles[2 * slot + 1];
-    row_base = p.row_off[g];
-    Mg = p.row_off[g + 1] - (int)row_base;
+    t.n0 = (lid - slot * p.tiles_n) * BN;
+    t.g = p.tiles[2 * slot];
+    t.m0 = p.tiles[2 * slot + 1];
+    t.row_base = p.row_off[t.g];
+    t.Mg = p.row_off[t.g + 1] - (int)t.row_base;
   } else {
+    // consecutive ids (one XCD after xcd_remap) walk the M tiles of one N
+    // column first, so concurrently running tiles share W panels and A panels
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int per = p.tiles_m * p.tiles_n;
-    g = lid / per;
-    const int r = lid - g * per;
+    t.g = lid / per;
+    const int r = lid - t.g * per;
     const int tn = r / p.tiles_m;
-    m0 = (r - tn * p.tiles_m) * BM;
-    n0 = tn * BN;
-    row_base = 0;
-    Mg = p.M;
+    t.m0 = (r - tn * p.tiles_m) * BM;
+    t.n0 = tn * BN;
+    t.row_base = 0;
+    t.Mg = p.M;
   }
+  return true;
+}
 
-  // ---- loader: thread owns chunk column kc of rows lrow + i*RPP
-  const int kc = tid % kCpr;
-  const int lrow = tid / kCpr;
-  const T* aptr[ACH];
-  const T* bptr[BCH];
-  {
-    const T* Ab = (const T*)p.A + (long long)(g / p.a_gdiv) * p.a_gs + kc * EPC;
+// epilogue math on 4 consecutive columns of one row
+template <int EPI, typename T>
+__device__ __forceinline__ void epi4(const KParams& p, const TileId& t, int m, int n, float scale, float (&v)[4]) {
+  if constexpr (EPI == kEpiBiasGelu) {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int m = min(m0 + lrow + i * RPP, Mg - 1);  // rows past the end re-read the last row
-      const long long r = AIDX ? (long long)p.a_rowidx[row_base + m] : row_base + m;
-      aptr[i] = Ab + r * p.a_rs;
-    }
-    const T* Bb = (const T*)p.W + (long long)g * p.b_gs + kc * EPC;
+    for (int e = 0; e < 4; ++e) v[e] = gelu_erf(v[e]);
+  }
+  if constexpr (EPI == kEpiBiasResidF32) {
+    float r[4];
+    load_f32<T, 4>((const T*)p.R + (t.row_base + m) * p.r_rs + (long long)t.g * p.r_gs + n, r);
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int n = min(n0 + lrow + i * RPP, p.N - 1);
-      bptr[i] = Bb + (long long)n * p.K;
+    for (int e = 0; e < 4; ++e) v[e] += r[e];
+  }
+  if constexpr (EPI == kEpiBiasScaleF32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= scale;
+  }
+}
+
+// direct epilogue: block (i, j), register 4q+e holds row m0 + wm*FM*32 + i*32 + lr,
+// column n0 + wn*FN*32 + j*32 + 8q + 4lh + e
+template <typename T, int FM, int FN, int EPI>
+__device__ __forceinline__ void store_direct(const KParams& p, const TileId& t, const floatx16 (&acc)[FM][FN], int wm,
+                                             int wn, int lr, int lh) {
+  typedef typename OutType<EPI, T>::type TO;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = t.m0 + wm * FM * 32 + i * 32 + lr;
+    if (m >= t.Mg) continue;
+    const long long orow = (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs;
+    float scale = 1.f;
+    if constexpr (EPI == kEpiBiasScaleF32) scale = p.rowscale[t.row_base + m];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = t.n0 + wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
+        if (n >= p.N) continue;
+        float4 bias = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.bias) bias = *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + n);
+        float v[4] = {acc[i][j][4 * q + 0] + bias.x, acc[i][j][4 * q + 1] + bias.y, acc[i][j][4 * q + 2] + bias.z,
+                      acc[i][j][4 * q + 3] + bias.w};
+        epi4<EPI, T>(p, t, m, n, scale, v);
+        store_from_f32<TO, 4>((TO*)p.C + orow + n, v);
+      }
     }
   }
+}
 
-  uint4 ra[ACH], rb[BCH];
+// ===========================================================================
+// generic main loop: two LDS stages, any K (multiple of the chunk), bf16/fp32
+
+template <typename T, int NWM, int NWN, int FM, int FN>
+struct Tile {
+  static constexpr int NW = NWM * NWN;
+  static constexpr int NT = NW * kWave;
+  static constexpr int BM = NWM * FM * 32, BN = NWN * FN * 32;
+  static constexpr int EPC = 16 / (int)sizeof(T);  // elements per chunk
+  static constexpr int BK = kCpr * EPC;             // k per stage
+  static constexpr int A_DMA = BM / 8 / NW;         // 1 KB DMA blocks per wave
+  static constexpr int B_DMA = BN / 8 / NW;
+  static constexpr int STAGE = (BM + BN) * kCpr;    // uint4 per stage
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split into 1 KB blocks per wave");
+};
+
+template <typename T, int NWM, int NWN, int FM, int FN, int EPI, bool RAGGED, bool AIDX>
+__global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_generic(KParams p) {
+  typedef Tile<T, NWM, NWN, FM, FN> TL;
+  constexpr int BM = TL::BM, BN = TL::BN, EPC = TL::EPC, BK = TL::BK;
+  constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
+
+  __shared__ uint4 lds0[TL::STAGE];
+  __shared__ uint4 lds1[TL::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  TileId t;
+  if (!tile_id<RAGGED, BM, BN>(p, t)) return;
+
+  // DMA sources: wave w fills 1 KB blocks w, w+NW, ... of each operand tile;
+  // block b holds tile rows 8b..8b+7, lane L its slot L (row 8b + L/8,
+  // physical chunk L%8, logical chunk (L%8) ^ (row/2 mod 8)).
   const int K = p.K;
-  auto gload = [&](int kt) {
+  const T* asrc[A_DMA];
+  const T* bsrc[B_DMA];
+  int a_chunk[A_DMA], b_chunk[B_DMA];
+  {
+    const T* Ab = (const T*)p.A + (long long)(t.g / p.a_gdiv) * p.a_gs;
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+      const int row = 8 * (wave + i * TL::NW) + (lane >> 3);
+      const int m = min(t.m0 + row, t.Mg - 1);  // rows past the end re-read the last row
+      const long long r = AIDX ? (long long)p.a_rowidx[t.row_base + m] : t.row_base + m;
+      a_chunk[i] = ((lane & 7) ^ ((row >> 1) & 7)) * EPC;
+      asrc[i] = Ab + r * p.a_rs + a_chunk[i];
+    }
+    const T* Bb = (const T*)p.W + (long long)t.g * p.b_gs;
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+      const int row = 8 * (wave + i * TL::NW) + (lane >> 3);
+      const int n = min(t.n0 + row, p.N - 1);
+      b_chunk[i] = ((lane & 7) ^ ((row >> 1) & 7)) * EPC;
+      bsrc[i] = Bb + (long long)n * K + b_chunk[i];
+    }
+  }
+
+  auto issue = [&](uint4* st, int kt) {
     const int koff = kt * BK;
-    if (koff + BK <= K) {
+    const bool full = koff + BK <= K;
 #pragma unroll
-      for (int i = 0; i < ACH; ++i) ra[i] = *reinterpret_cast<const uint4*>(aptr[i] + koff);
+    for (int i = 0; i < A_DMA; ++i) {
+      const void* src = (full || koff + a_chunk[i] < K) ? (const void*)(asrc[i] + koff) : (const void*)&g_zero_chunk;
+      __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)(st + (wave + i * TL::NW) * 64), 16, 0, 0);
+    }
 #pragma unroll
-      for (int i = 0; i < BCH; ++i) rb[i] = *reinterpret_cast<const uint4*>(bptr[i] + koff);
-    } else {  // k tail: chunks past K are zero (K is a multiple of the chunk)
-      const bool ok = koff + kc * EPC < K;
-      const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < ACH; ++i) ra[i] = ok ? *reinterpret_cast<const uint4*>(aptr[i] + koff) : z;
-#pragma unroll
-      for (int i = 0; i < BCH; ++i) rb[i] = ok ? *reinterpret_cast<const uint4*>(bptr[i] + koff) : z;
+    for (int i = 0; i < B_DMA; ++i) {
+      const void* src = (full || koff + b_chunk[i] < K) ? (const void*)(bsrc[i] + koff) : (const void*)&g_zero_chunk;
+      __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)(st + BM * kCpr + (wave + i * TL::NW) * 64),
+                                       16, 0, 0);
     }
   };
-  auto sstore = [&](int st) {
-    uint4* As = lds[st];
-    uint4* Bs = lds[st] + BM * kCpr;
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) As[swz(lrow + i * RPP, kc)] = ra[i];
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) Bs[swz(lrow + i * RPP, kc)] = rb[i];
-  };
 
-  // ---- MFMA
-  const int wave = tid / kWave, lane = tid % kWave;
   const int wm = wave / NWN, wn = wave % NWN;
-  const int lr = lane & 15, lk = lane >> 4;
-  floatx4 acc[FM][FN];
+  const int lr = lane & 31, lh = lane >> 5;
+  floatx16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int st) {
-    const uint4* As = lds[st];
-    const uint4* Bs = lds[st] + BM * kCpr;
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-    for (int sub = 0; sub < kCpr / 4; ++sub) {
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  auto compute = [&](const uint4* st) {
+    const uint4* As = st;
+    const uint4* Bs = st + BM * kCpr;
+#pragma unroll
+    for (int kk = 0; kk < kCpr / 2; ++kk) {
       uint4 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = As[swz(wm * FM * 16 + i * 16 + lr, sub * 4 + lk)];
+      for (int i = 0; i < FM; ++i) af[i] = As[swz(wm * FM * 32 + i * 32 + lr, kk * 2 + lh)];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = Bs[swz(wn * FN * 16 + j * 16 + lr, sub * 4 + lk)];
+      for (int j = 0; j < FN; ++j) bfr[j] = Bs[swz(wn * FN * 32 + j * 32 + lr, kk * 2 + lh)];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -181,71 +282,224 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm(KParams p) {
     }
   };
 
+  // two stages, the k loop unrolled by 2 so each half names its stage
   const int nk = (K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
-    compute(kt & 1);
-    if (more) sstore((kt + 1) & 1);
+  issue(lds0, 0);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    __syncthreads();  // stage 0 landed (each wave waits for its DMA before the barrier); stage 1 free
+    issue(lds1, kt + 1);
+    compute(lds0);
+    __syncthreads();  // stage 1 landed; stage 0 free
+    if (kt + 2 < nk) issue(lds0, kt + 2);
+    compute(lds1);
+  }
+  if (kt < nk) {
     __syncthreads();
+    compute(lds0);
   }
+  store_direct<T, FM, FN, EPI>(p, t, acc, wm, wn, lr, lh);
+}
 
-  // ---- epilogue: lane holds C[m0 + wm*FM*16 + i*16 + lr][n .. n+3] of fragment (i, j)
-  float4 bias[FN];
-  bool nvalid[FN];
+// ===========================================================================
+// ring main loop (bf16, K % 64 == 0)
+
+template <int NWM, int NWN, int FM, int FN>
+struct Ring {
+  static constexpr int NW = NWM * NWN;
+  static constexpr int NT = NW * kWave;
+  static constexpr int BM = NWM * FM * 32, BN = NWN * FN * 32;
+  static constexpr int BK = 64;
+  static constexpr int SR = BM > BN ? BM : BN;  // rows per LDS slot
+  static constexpr int SLOT = SR * kCpr;        // uint4 per slot
+  static constexpr int A_DMA = BM / 8 / NW;     // 1 KB DMA blocks per wave per operand slice
+  static constexpr int B_DMA = BN / 8 / NW;
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split into 1 KB blocks per wave");
+  static_assert(A_DMA < 16, "vmcnt field");
+};
+
+template <int NWM, int NWN, int FM, int FN, int EPI, bool RAGGED, bool AIDX>
+__global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
+  typedef Ring<NWM, NWN, FM, FN> RG;
+  constexpr int BM = RG::BM, BN = RG::BN, BK = RG::BK, NW = RG::NW;
+  constexpr int A_DMA = RG::A_DMA, B_DMA = RG::B_DMA;
+  typedef typename OutType<EPI, bf16>::type TO;
+
+  __shared__ uint4 r0[RG::SLOT];
+  __shared__ uint4 r1[RG::SLOT];
+  __shared__ uint4 r2[RG::SLOT];
+  __shared__ uint4 r3[RG::SLOT];
+  __shared__ uint4 r4[RG::SLOT];
+  auto slot = [&](auto ic) -> uint4* {
+    constexpr int i = decltype(ic)::value % 5;
+    if constexpr (i == 0) return r0;
+    else if constexpr (i == 1) return r1;
+    else if constexpr (i == 2) return r2;
+    else if constexpr (i == 3) return r3;
+    else return r4;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  TileId t;
+  if (!tile_id<RAGGED, BM, BN>(p, t)) return;
+
+  const int K = p.K;
+  const bf16* Ab = (const bf16*)p.A + (long long)(t.g / p.a_gdiv) * p.a_gs;
+  const bf16* Bb = (const bf16*)p.W + (long long)t.g * p.b_gs;
+  const bf16* asrc[A_DMA];
+  const bf16* bsrc[B_DMA];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int n = n0 + wn * FN * 16 + j * 16 + lk * 4;
-    nvalid[j] = n < p.N;
-    bias[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (p.bias && nvalid[j]) bias[j] = *reinterpret_cast<const float4*>(p.bias + (long long)g * p.bias_gs + n);
+  for (int i = 0; i < A_DMA; ++i) {
+    const int row = 8 * (wave + i * NW) + (lane >> 3);
+    const int m = min(t.m0 + row, t.Mg - 1);  // rows past the end re-read the last row
+    const long long r = AIDX ? (long long)p.a_rowidx[t.row_base + m] : t.row_base + m;
+    asrc[i] = Ab + r * p.a_rs + ((lane & 7) ^ ((row >> 1) & 7)) * 8;
   }
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * FM * 16 + i * 16 + lr;
-    if (m >= Mg) continue;
-    const long long orow = (row_base + m) * p.c_rs + (long long)g * p.c_gs;
-    float scale = 1.f;
-    if constexpr (EPI == kEpiBiasScaleF32) scale = p.rowscale[row_base + m];
+  for (int i = 0; i < B_DMA; ++i) {
+    const int row = 8 * (wave + i * NW) + (lane >> 3);
+    const int n = min(t.n0 + row, p.N - 1);
+    bsrc[i] = Bb + (long long)n * K + ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+  }
+  const int nk_real = K / BK;
+  // k-slices past the end re-read the last slice; they land in slots no
+  // compute reads again
+  auto issueA = [&](uint4* dst, int kt) {
+    const int koff = min(kt, nk_real - 1) * BK;
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i)
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(asrc[i] + koff), (lds_void*)(dst + (wave + i * NW) * 64), 16,
+                                       0, 0);
+  };
+  auto issueB = [&](uint4* dst, int kt) {
+    const int koff = min(kt, nk_real - 1) * BK;
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i)
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(bsrc[i] + koff), (lds_void*)(dst + (wave + i * NW) * 64), 16,
+                                       0, 0);
+  };
+
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int lr = lane & 31, lh = lane >> 5;
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // fragments of k-step kk (16 k) double-buffered in registers
+  auto compute = [&](const uint4* As, const uint4* Bs) {
+    uint4 af[2][FM], bfr[2][FN];
+    auto ld = [&](int kk, int b) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[b][i] = As[swz(wm * FM * 32 + i * 32 + lr, kk * 2 + lh)];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[b][j] = Bs[swz(wn * FN * 32 + j * 32 + lr, kk * 2 + lh)];
+    };
+    auto mm = [&](int b) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mma<bf16>::run(acc[i][j], bfr[b][j], af[b][i]);
+    };
+    ld(0, 0);
+    ld(1, 1);
+    mm(0);
+    ld(2, 0);
+    mm(1);
+    ld(3, 1);
+    mm(0);
+    mm(1);
+  };
+
+  // prologue: A_0 -> slot 0, W_0 -> slot 1, A_1 -> slot 2
+  issueA(slot(std::integral_constant<int, 0>()), 0);
+  issueB(slot(std::integral_constant<int, 1>()), 0);
+  issueA(slot(std::integral_constant<int, 2>()), 1);
+  auto step = [&](auto ic, int k) {
+    constexpr int s5 = decltype(ic)::value;  // k mod 5
+    // A_k and W_k landed: the only newer DMA of this wave is A_{k+1}
+    wait_vmcnt<A_DMA>();
+    __builtin_amdgcn_s_barrier();
+    // every wave is past stage k-1: refill its slots with W_{k+1}, A_{k+2}
+    issueB(slot(std::integral_constant<int, 2 * s5 + 3>()), k + 1);
+    issueA(slot(std::integral_constant<int, 2 * s5 + 4>()), k + 2);
+    if (k < nk_real) compute(slot(std::integral_constant<int, 2 * s5>()), slot(std::integral_constant<int, 2 * s5 + 1>()));
+  };
+  const int nk = (nk_real + 4) / 5 * 5;
+  for (int kt = 0; kt < nk; kt += 5) {
+    step(std::integral_constant<int, 0>(), kt);
+    step(std::integral_constant<int, 1>(), kt + 1);
+    step(std::integral_constant<int, 2>(), kt + 2);
+    step(std::integral_constant<int, 3>(), kt + 3);
+    step(std::integral_constant<int, 4>(), kt + 4);
+  }
+  wait_vmcnt<0>();  // no DMA may land in LDS after this point
+
+  if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias) {
+    // bf16 output staged through LDS so every global store writes whole
+    // row segments: rows of BN*2 bytes, 16-byte chunks XOR-swizzled by row
+    constexpr int OCH = BN / 8;                 // 16-byte chunks per output row
+    constexpr int RPS = RG::SLOT * 16 / (BN * 2);  // output rows per slot
+    static_assert(BM <= 4 * RPS, "output tile must fit in four slots");
+    auto orow = [&](int ml) -> char* {
+      const int s = ml / RPS;
+      char* base = s == 0 ? (char*)r0 : s == 1 ? (char*)r1 : s == 2 ? (char*)r2 : (char*)r3;
+      return base + (ml - s * RPS) * (BN * 2);
+    };
+    __syncthreads();  // every wave is done reading operand slots
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      if (!nvalid[j]) continue;
-      const int n = n0 + wn * FN * 16 + j * 16 + lk * 4;
-      float v[4] = {acc[i][j][0] + bias[j].x, acc[i][j][1] + bias[j].y, acc[i][j][2] + bias[j].z,
-                    acc[i][j][3] + bias[j].w};
-      if constexpr (EPI == kEpiBiasGelu) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = gelu_erf(v[e]);
-      }
-      if constexpr (EPI == kEpiBiasResidF32) {
-        float r[4];
-        load_f32<T, 4>((const T*)p.R + (row_base + m) * p.r_rs + (long long)g * p.r_gs + n, r);
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
+        float4 bias = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.bias && t.n0 + nl < p.N)
+          bias = *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + t.n0 + nl);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += r[e];
+        for (int i = 0; i < FM; ++i) {
+          const int ml = wm * FM * 32 + i * 32 + lr;
+          float v[4] = {acc[i][j][4 * q + 0] + bias.x, acc[i][j][4 * q + 1] + bias.y, acc[i][j][4 * q + 2] + bias.z,
+                        acc[i][j][4 * q + 3] + bias.w};
+          epi4<EPI, bf16>(p, t, 0, 0, 1.f, v);
+          const int phys = (nl >> 3) ^ (ml & (OCH - 1));
+          store_from_f32<bf16, 4>(reinterpret_cast<bf16*>(orow(ml) + phys * 16 + (nl & 7) * 2), v);
+        }
       }
-      if constexpr (EPI == kEpiBiasScaleF32) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] *= scale;
-      }
-      store_from_f32<TO, 4>((TO*)p.C + orow + n, v);
     }
+    __syncthreads();
+    constexpr int RPP = RG::NT / OCH;  // output rows per pass
+#pragma unroll 4
+    for (int pass = 0; pass < BM / RPP; ++pass) {
+      const int ml = pass * RPP + tid / OCH;
+      const int c = tid % OCH;
+      const uint4 val = *reinterpret_cast<const uint4*>(orow(ml) + ((c ^ (ml & (OCH - 1))) * 16));
+      const int m = t.m0 + ml;
+      if (m < t.Mg && t.n0 + c * 8 < p.N)
+        *reinterpret_cast<uint4*>((TO*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + t.n0 + c * 8) = val;
+    }
+  } else {
+    store_direct<bf16, FM, FN, EPI>(p, t, acc, wm, wn, lr, lh);
   }
 }
 
+// ===========================================================================
+// host side
+
 struct TileCfg {
   int nwm, nwn, fm, fn;
-  int bm() const { return nwm * fm * 16; }
-  int bn() const { return nwn * fn * 16; }
-  int threads() const { return nwm * nwn * kWave; }
+  int bm() const { return nwm * fm * 32; }
+  int bn() const { return nwn * fn * 32; }
 };
 constexpr TileCfg kCfgs[] = {
-    {2, 4, 8, 4},  // 0: 256 x 256, 8 waves
-    {2, 2, 8, 4},  // 1: 256 x 128, 4 waves
-    {2, 2, 4, 4},  // 2: 128 x 128, 4 waves
-    {2, 2, 2, 2},  // 3:  64 x  64, 4 waves
+    {2, 4, 4, 2},  // 0: 256 x 256, 8 waves of 128 x 64
+    {2, 2, 4, 2},  // 1: 256 x 128, 4 waves of 128 x 64
+    {2, 2, 2, 2},  // 2: 128 x 128, 4 waves of 64 x 64
+    {2, 2, 1, 1},  // 3:  64 x  64, 4 waves of 32 x 32
 };
 constexpr int kNumCfgs = 4;
 constexpr int kMoeCfg = 2;
@@ -265,9 +519,7 @@ int choose_cfg(const GemmArgs& a) {
   return kNumCfgs - 1;
 }
 
-template <typename T, int NWM, int NWN, int FM, int FN>
-hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int BM = NWM * FM * 16, BN = NWN * FN * 16;
+KParams make_params(const GemmArgs& a, int bm, int bn) {
   KParams p;
   p.A = a.A; p.a_gs = a.a_gs; p.a_rs = a.a_rs; p.a_gdiv = a.a_gdiv; p.a_rowidx = a.a_rowidx;
   p.W = a.W; p.b_gs = a.b_gs;
@@ -277,46 +529,47 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   p.rowscale = a.rowscale;
   p.row_off = a.row_off; p.tiles = a.tiles; p.ntiles = a.ntiles;
   p.M = a.M; p.N = a.N; p.K = a.K; p.G = a.G;
-  p.tiles_m = ceil_div(a.M, BM);
-  p.tiles_n = ceil_div(a.N, BN);
+  p.tiles_m = ceil_div(a.M, bm);
+  p.tiles_n = ceil_div(a.N, bn);
+  return p;
+}
+
+template <int NWM, int NWN, int FM, int FN, int EPI, bool RAGGED, bool AIDX>
+void launch_one(const GemmArgs& a, const KParams& p, dim3 grid, hipStream_t s, bool ring) {
   const dim3 block(NWM * NWN * kWave);
+  if (ring)
+    hipLaunchKernelGGL((k_gemm_ring<NWM, NWN, FM, FN, EPI, RAGGED, AIDX>), grid, block, 0, s, p);
+  else if (a.dt == kBF16)
+    hipLaunchKernelGGL((k_gemm_generic<bf16, NWM, NWN, FM, FN, EPI, RAGGED, AIDX>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((k_gemm_generic<float, NWM, NWN, FM, FN, EPI, RAGGED, AIDX>), grid, block, 0, s, p);
+}
+
+template <int NWM, int NWN, int FM, int FN>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+  constexpr int BM = NWM * FM * 32, BN = NWN * FN * 32;
+  const KParams p = make_params(a, BM, BN);
+  const bool ring = a.dt == kBF16 && a.K % 64 == 0;
   if (a.row_off) {
     const dim3 grid((unsigned)((long long)a.max_mtiles * p.tiles_n));
     if (grid.x == 0) return hipSuccess;
     if (a.epi == kEpiBiasGelu && a.a_rowidx)
-      hipLaunchKernelGGL((k_gemm<T, NWM, NWN, FM, FN, kEpiBiasGelu, true, true>), grid, block, 0, s, p);
+      launch_one<NWM, NWN, FM, FN, kEpiBiasGelu, true, true>(a, p, grid, s, ring);
     else if (a.epi == kEpiBiasScaleF32 && !a.a_rowidx)
-      hipLaunchKernelGGL((k_gemm<T, NWM, NWN, FM, FN, kEpiBiasScaleF32, true, false>), grid, block, 0, s, p);
+      launch_one<NWM, NWN, FM, FN, kEpiBiasScaleF32, true, false>(a, p, grid, s, ring);
     else
       return hipErrorInvalidValue;
   } else {
     const dim3 grid((unsigned)((long long)a.G * p.tiles_m * p.tiles_n));
     if (grid.x == 0) return hipSuccess;
     switch (a.epi) {
-      case kEpiBiasGelu:
-        hipLaunchKernelGGL((k_gemm<T, NWM, NWN, FM, FN, kEpiBiasGelu, false, false>), grid, block, 0, s, p);
-        break;
-      case kEpiBias:
-        hipLaunchKernelGGL((k_gemm<T, NWM, NWN, FM, FN, kEpiBias, false, false>), grid, block, 0, s, p);
-        break;
-      case kEpiBiasResidF32:
-        hipLaunchKernelGGL((k_gemm<T, NWM, NWN, FM, FN, kEpiBiasResidF32, false, false>), grid, block, 0, s, p);
-        break;
-      default:
-        return hipErrorInvalidValue;
+      case kEpiBiasGelu: launch_one<NWM, NWN, FM, FN, kEpiBiasGelu, false, false>(a, p, grid, s, ring); break;
+      case kEpiBias: launch_one<NWM, NWN, FM, FN, kEpiBias, false, false>(a, p, grid, s, ring); break;
+      case kEpiBiasResidF32: launch_one<NWM, NWN, FM, FN, kEpiBiasResidF32, false, false>(a, p, grid, s, ring); break;
+      default: return hipErrorInvalidValue;
     }
   }
   return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
-  switch (choose_cfg(a)) {
-    case 0: return launch_cfg<T, 2, 4, 8, 4>(a, s);
-    case 1: return launch_cfg<T, 2, 2, 8, 4>(a, s);
-    case 2: return launch_cfg<T, 2, 2, 4, 4>(a, s);
-    default: return launch_cfg<T, 2, 2, 2, 2>(a, s);
-  }
 }
 
 }  // namespace
@@ -324,7 +577,12 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
 int gemm_tile_m(const GemmArgs& a) { return kCfgs[choose_cfg(a)].bm(); }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
-  return a.dt == kBF16 ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
+  switch (choose_cfg(a)) {
+    case 0: return launch_cfg<2, 4, 4, 2>(a, s);
+    case 1: return launch_cfg<2, 2, 4, 2>(a, s);
+    case 2: return launch_cfg<2, 2, 2, 2>(a, s);
+    default: return launch_cfg<2, 2, 1, 1>(a, s);
+  }
 }
 
 }  // namespace rm

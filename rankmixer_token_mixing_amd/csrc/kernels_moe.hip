@@ -28,7 +28,8 @@ int pick_slots(int chunks) {
 
 // gates[b,t,j] = max(0, Wr[t,j,:] . s[b,t,:] + br[t,j]); one wave per (b, t)
 template <typename T, int VEC, int MAXI>
-__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_router(const T* __restrict__ s, const T* __restrict__ wr,
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_router(const T* __restrict__ s, int64_t sb, int64_t st,
+                                                                  const T* __restrict__ wr,
                                                                   const float* __restrict__ br,
                                                                   float* __restrict__ gates, int64_t B, int T_,
                                                                   int D, int E) {
@@ -36,8 +37,9 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_router(const T* __res
   if (row >= B * T_) return;
   const int lane = lane_id();
   const int t = (int)(row % T_);
+  const int64_t b = row / T_;
   const int nch = D / VEC;
-  const T* sr = s + row * (int64_t)D;
+  const T* sr = s + b * sb + t * st;
   float v[MAXI][VEC];
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
@@ -160,7 +162,8 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const float* __restrict__ g
 template <typename T, int MAXI>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_moe_combine(const float* __restrict__ y,
                                                                        const int* __restrict__ pos,
-                                                                       const T* __restrict__ s,
+                                                                       const T* __restrict__ s, int64_t sb,
+                                                                       int64_t st, int T_,
                                                                        const float* __restrict__ g,
                                                                        const float* __restrict__ beta,
                                                                        T* __restrict__ out, int64_t rows_n,
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_moe_combine(const flo
     }
     return;
   }
-  const T* sr = s + row * (int64_t)D;
+  const T* sr = s + (row / T_) * sb + (row % T_) * st;
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
@@ -242,25 +245,25 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_moe_combine(const flo
 }
 
 template <typename T, int VEC>
-hipError_t router_t(const void* s, const void* wr, const float* br, float* gates, int64_t B, int T_, int D,
-                    int E, hipStream_t st) {
+hipError_t router_t(const void* s, int64_t sb, int64_t sT, const void* wr, const float* br, float* gates,
+                    int64_t B, int T_, int D, int E, hipStream_t st) {
   const dim3 grid((unsigned)((B * T_ + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
   const T* ss = (const T*)s;
   const T* ww = (const T*)wr;
   switch (pick_slots(D / VEC)) {
     case 0: return hipErrorInvalidValue;
-    case 1: hipLaunchKernelGGL((k_router<T, VEC, 1>), grid, block, 0, st, ss, ww, br, gates, B, T_, D, E); break;
-    case 2: hipLaunchKernelGGL((k_router<T, VEC, 2>), grid, block, 0, st, ss, ww, br, gates, B, T_, D, E); break;
-    case 4: hipLaunchKernelGGL((k_router<T, VEC, 4>), grid, block, 0, st, ss, ww, br, gates, B, T_, D, E); break;
-    case 8: hipLaunchKernelGGL((k_router<T, VEC, 8>), grid, block, 0, st, ss, ww, br, gates, B, T_, D, E); break;
-    default: hipLaunchKernelGGL((k_router<T, VEC, 16>), grid, block, 0, st, ss, ww, br, gates, B, T_, D, E); break;
+    case 1: hipLaunchKernelGGL((k_router<T, VEC, 1>), grid, block, 0, st, ss, sb, sT, ww, br, gates, B, T_, D, E); break;
+    case 2: hipLaunchKernelGGL((k_router<T, VEC, 2>), grid, block, 0, st, ss, sb, sT, ww, br, gates, B, T_, D, E); break;
+    case 4: hipLaunchKernelGGL((k_router<T, VEC, 4>), grid, block, 0, st, ss, sb, sT, ww, br, gates, B, T_, D, E); break;
+    case 8: hipLaunchKernelGGL((k_router<T, VEC, 8>), grid, block, 0, st, ss, sb, sT, ww, br, gates, B, T_, D, E); break;
+    default: hipLaunchKernelGGL((k_router<T, VEC, 16>), grid, block, 0, st, ss, sb, sT, ww, br, gates, B, T_, D, E); break;
   }
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t combine_t(const float* y, const int* pos, const void* s, const float* g, const float* b, void* out,
-                     int64_t B, int T_, int D, int E, bool ln, hipStream_t st) {
+hipError_t combine_t(const float* y, const int* pos, const void* s, int64_t sb, int64_t sT, const float* g,
+                     const float* b, void* out, int64_t B, int T_, int D, int E, bool ln, hipStream_t st) {
   const int64_t rows = B * T_;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
   const T* ss = (const T*)s;
@@ -268,21 +271,21 @@ hipError_t combine_t(const float* y, const int* pos, const void* s, const float*
   const int l = ln ? 1 : 0;
   switch (pick_slots(D / 4)) {
     case 0: return hipErrorInvalidValue;
-    case 1: hipLaunchKernelGGL((k_moe_combine<T, 1>), grid, block, 0, st, y, pos, ss, g, b, oo, rows, D, E, l); break;
-    case 2: hipLaunchKernelGGL((k_moe_combine<T, 2>), grid, block, 0, st, y, pos, ss, g, b, oo, rows, D, E, l); break;
-    case 4: hipLaunchKernelGGL((k_moe_combine<T, 4>), grid, block, 0, st, y, pos, ss, g, b, oo, rows, D, E, l); break;
-    case 8: hipLaunchKernelGGL((k_moe_combine<T, 8>), grid, block, 0, st, y, pos, ss, g, b, oo, rows, D, E, l); break;
-    default: hipLaunchKernelGGL((k_moe_combine<T, 16>), grid, block, 0, st, y, pos, ss, g, b, oo, rows, D, E, l); break;
+    case 1: hipLaunchKernelGGL((k_moe_combine<T, 1>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
+    case 2: hipLaunchKernelGGL((k_moe_combine<T, 2>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
+    case 4: hipLaunchKernelGGL((k_moe_combine<T, 4>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
+    case 8: hipLaunchKernelGGL((k_moe_combine<T, 8>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
+    default: hipLaunchKernelGGL((k_moe_combine<T, 16>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_moe_router(const void* s, const void* wr, const float* br, float* gates, int64_t B, int T,
-                             int D, int E, int dt, hipStream_t st) {
-  if (dt == kBF16) return router_t<bf16, 8>(s, wr, br, gates, B, T, D, E, st);
-  return router_t<float, 4>(s, wr, br, gates, B, T, D, E, st);
+hipError_t launch_moe_router(const void* s, int64_t sb, int64_t sT, const void* wr, const float* br, float* gates,
+                             int64_t B, int T, int D, int E, int dt, hipStream_t st) {
+  if (dt == kBF16) return router_t<bf16, 8>(s, sb, sT, wr, br, gates, B, T, D, E, st);
+  return router_t<float, 4>(s, sb, sT, wr, br, gates, B, T, D, E, st);
 }
 
 hipError_t launch_moe_compact(const MoeWork& w, int64_t B, int T, int E, int bm, hipStream_t st) {
@@ -294,10 +297,11 @@ hipError_t launch_moe_compact(const MoeWork& w, int64_t B, int T, int E, int bm,
   return hipGetLastError();
 }
 
-hipError_t launch_moe_combine(const float* y, const int* pos, const void* s, const float* g, const float* b,
-                              void* out, int64_t B, int T, int D, int E, bool ln, int dt, hipStream_t st) {
-  if (dt == kBF16) return combine_t<bf16>(y, pos, s, g, b, out, B, T, D, E, ln, st);
-  return combine_t<float>(y, pos, s, g, b, out, B, T, D, E, ln, st);
+hipError_t launch_moe_combine(const float* y, const int* pos, const void* s, int64_t sb, int64_t sT, const float* g,
+                              const float* b, void* out, int64_t B, int T, int D, int E, bool ln, int dt,
+                              hipStream_t st) {
+  if (dt == kBF16) return combine_t<bf16>(y, pos, s, sb, sT, g, b, out, B, T, D, E, ln, st);
+  return combine_t<float>(y, pos, s, sb, sT, g, b, out, B, T, D, E, ln, st);
 }
 
 }  // namespace rm

@@ -100,7 +100,7 @@ template <typename T, int VEC, int MAXI>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __restrict__ x, T* __restrict__ s,
                                                                   const float* __restrict__ g,
                                                                   const float* __restrict__ beta,
-                                                                  int64_t B, int T_, int D) {
+                                                                  int64_t B, int T_, int D, int token_major) {
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
   if (row >= B * T_) return;
   const int lane = lane_id();
@@ -141,7 +141,8 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __res
     }
   }
   const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D + ln_eps());
-  T* sr = s + row * (int64_t)D;
+  // S row (b, t) at [b][t] or, token-major, at [t][b]
+  T* sr = s + (token_major ? ((int64_t)t * B + b) : row) * (int64_t)D;
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     const int c = lane + i * kWave;
@@ -287,18 +288,18 @@ hipError_t token_mix_eb(const void* x, void* y, int64_t B, int T, int D, int vec
 }
 
 template <typename T, int VEC>
-hipError_t mix_ln_vec(const void* x, void* so, const float* g, const float* b, int64_t B, int T_, int D,
+hipError_t mix_ln_vec(const void* x, void* so, const float* g, const float* b, int64_t B, int T_, int D, int tm,
                       hipStream_t s) {
   const dim3 grid((unsigned)((B * T_ + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
   const T* xx = (const T*)x;
   T* ss = (T*)so;
   switch (pick_maxi(D / VEC)) {
     case 0: return hipErrorInvalidValue;
-    case 1: hipLaunchKernelGGL((k_mix_ln<T, VEC, 1>), grid, block, 0, s, xx, ss, g, b, B, T_, D); break;
-    case 2: hipLaunchKernelGGL((k_mix_ln<T, VEC, 2>), grid, block, 0, s, xx, ss, g, b, B, T_, D); break;
-    case 4: hipLaunchKernelGGL((k_mix_ln<T, VEC, 4>), grid, block, 0, s, xx, ss, g, b, B, T_, D); break;
-    case 8: hipLaunchKernelGGL((k_mix_ln<T, VEC, 8>), grid, block, 0, s, xx, ss, g, b, B, T_, D); break;
-    default: hipLaunchKernelGGL((k_mix_ln<T, VEC, 16>), grid, block, 0, s, xx, ss, g, b, B, T_, D); break;
+    case 1: hipLaunchKernelGGL((k_mix_ln<T, VEC, 1>), grid, block, 0, s, xx, ss, g, b, B, T_, D, tm); break;
+    case 2: hipLaunchKernelGGL((k_mix_ln<T, VEC, 2>), grid, block, 0, s, xx, ss, g, b, B, T_, D, tm); break;
+    case 4: hipLaunchKernelGGL((k_mix_ln<T, VEC, 4>), grid, block, 0, s, xx, ss, g, b, B, T_, D, tm); break;
+    case 8: hipLaunchKernelGGL((k_mix_ln<T, VEC, 8>), grid, block, 0, s, xx, ss, g, b, B, T_, D, tm); break;
+    default: hipLaunchKernelGGL((k_mix_ln<T, VEC, 16>), grid, block, 0, s, xx, ss, g, b, B, T_, D, tm); break;
   }
   return hipGetLastError();
 }
@@ -333,20 +334,21 @@ hipError_t launch_token_mix(const void* x, void* y, int64_t B, int T, int D, int
 }
 
 hipError_t launch_mix_ln(const void* x, void* so, const float* g, const float* b, int64_t B, int T,
-                         int D, int dt, hipStream_t s) {
+                         int D, int dt, bool token_major, hipStream_t s) {
+  const int tm = token_major ? 1 : 0;
   const int d = D / T;
   if (dt == kBF16) {
     switch (chunk_elems(d, 2)) {
-      case 8: return mix_ln_vec<bf16, 8>(x, so, g, b, B, T, D, s);
-      case 4: return mix_ln_vec<bf16, 4>(x, so, g, b, B, T, D, s);
-      case 2: return mix_ln_vec<bf16, 2>(x, so, g, b, B, T, D, s);
-      default: return mix_ln_vec<bf16, 1>(x, so, g, b, B, T, D, s);
+      case 8: return mix_ln_vec<bf16, 8>(x, so, g, b, B, T, D, tm, s);
+      case 4: return mix_ln_vec<bf16, 4>(x, so, g, b, B, T, D, tm, s);
+      case 2: return mix_ln_vec<bf16, 2>(x, so, g, b, B, T, D, tm, s);
+      default: return mix_ln_vec<bf16, 1>(x, so, g, b, B, T, D, tm, s);
     }
   }
   switch (chunk_elems(d, 4)) {
-    case 4: return mix_ln_vec<float, 4>(x, so, g, b, B, T, D, s);
-    case 2: return mix_ln_vec<float, 2>(x, so, g, b, B, T, D, s);
-    default: return mix_ln_vec<float, 1>(x, so, g, b, B, T, D, s);
+    case 4: return mix_ln_vec<float, 4>(x, so, g, b, B, T, D, tm, s);
+    case 2: return mix_ln_vec<float, 2>(x, so, g, b, B, T, D, tm, s);
+    default: return mix_ln_vec<float, 1>(x, so, g, b, B, T, D, tm, s);
   }
 }
 

@@ -20,9 +20,10 @@ bool row_width_supported(int T, int D, int dt);
 hipError_t launch_tokenize_padsplit(const float* emb, int64_t B, int64_t F, int T, int D, int dt,
                                     void* x0, hipStream_t s);
 hipError_t launch_token_mix(const void* x, void* y, int64_t B, int T, int D, int dt, hipStream_t s);
-// S = LN(TokenMix(X) + X) row by row
+// S = LN(TokenMix(X) + X) row by row; S row (b, t) is written at [b][t] or,
+// token_major, at [t][b] (so the rows of one token are contiguous)
 hipError_t launch_mix_ln(const void* x, void* s_out, const float* g, const float* b, int64_t B,
-                         int T, int D, int dt, hipStream_t s);
+                         int T, int D, int dt, bool token_major, hipStream_t s);
 // out = LN(z) for fp32 rows z [rows][D]
 hipError_t launch_ln_rows_f32(const float* z, void* out, const float* g, const float* b,
                               int64_t rows, int D, int dt, hipStream_t s);
@@ -42,13 +43,14 @@ struct MoeWork {
   int* tiles;       // [2 * max_tiles] (group, m0) pairs
   int* ntiles;      // [1]
 };
-hipError_t launch_moe_router(const void* s, const void* wr, const float* br, float* gates,
-                             int64_t B, int T, int D, int E, int dt, hipStream_t st);
+// S row (b, t) of the MoE kernels sits at b * sb + t * st (elements)
+hipError_t launch_moe_router(const void* s, int64_t sb, int64_t st_, const void* wr, const float* br,
+                             float* gates, int64_t B, int T, int D, int E, int dt, hipStream_t st);
 hipError_t launch_moe_compact(const MoeWork& w, int64_t B, int T, int E, int bm, hipStream_t st);
 // v[b,t,:] = sum_j y[pos[b,t,j], :]; if ln: out = LN(v + s) else out = v
-hipError_t launch_moe_combine(const float* y, const int* pos, const void* s, const float* g,
-                              const float* b, void* out, int64_t B, int T, int D, int E, bool ln,
-                              int dt, hipStream_t st);
+hipError_t launch_moe_combine(const float* y, const int* pos, const void* s, int64_t sb, int64_t st_,
+                              const float* g, const float* b, void* out, int64_t B, int T, int D,
+                              int E, bool ln, int dt, hipStream_t st);
 
 // ---- grouped MFMA GEMM (kernels_gemm.hip) ------------------------------------
 
