@@ -90,9 +90,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", help="workload (c3 is the benchmarked one)")
-    ap.add_argument("--cpu-rows", type=int, default=64, help="samples in the oracle leg")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="samples in the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-launch HIP events")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before warmup, one device-to-device copy of this many MiB (a known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -128,6 +131,16 @@ def main() -> int:
 
     def step():
         bd.rm_model_fwd(model, inp, want_x=True, out=out)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read, {n} bytes written")
+        del src, dst
 
     for _ in range(args.warmup):
         step()
