@@ -116,7 +116,7 @@ rm_status check_dtype(int dt) {
 
 rm_status check_shape(int64_t B, int T, int D, int dt) {
   RM_TRY(check_dtype(dt));
-  if (B <= 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B, T and D must be positive (B=%lld T=%d D=%d)", (long long)B, T, D);
+  if (B < 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B must be >= 0, T and D positive (B=%lld T=%d D=%d)", (long long)B, T, D);
   if (D % T) return fail(RM_ERR_UNSUPPORTED, "D=%d is not divisible by H=T=%d", D, T);
   if (D % 8) return fail(RM_ERR_UNSUPPORTED, "D=%d must be a multiple of 8", D);
   if (!rm::row_width_supported(T, D, dt)) return fail(RM_ERR_UNSUPPORTED, "D=%d with T=%d is wider than the row kernels support", D, T);
@@ -128,7 +128,7 @@ rm_status check_shape(int64_t B, int T, int D, int dt) {
 // divide by T)
 rm_status check_ffn_shape(int64_t B, int T, int D, int dt) {
   RM_TRY(check_dtype(dt));
-  if (B <= 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B, T and D must be positive (B=%lld T=%d D=%d)", (long long)B, T, D);
+  if (B < 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B must be >= 0, T and D positive (B=%lld T=%d D=%d)", (long long)B, T, D);
   if (D % 8) return fail(RM_ERR_UNSUPPORTED, "D=%d must be a multiple of 8", D);
   if (D > 4096) return fail(RM_ERR_UNSUPPORTED, "D=%d is wider than the row kernels support (4096)", D);
   if (B * T > (int64_t)1 << 31) return fail(RM_ERR_UNSUPPORTED, "B*T too large");
@@ -419,8 +419,9 @@ int rm_profile_read(int idx, char* name, size_t name_len, double* total_ms, int*
 rm_status rm_tokenize_padsplit(const float* emb, int64_t B, int64_t F, int T, int D, int out_dtype, void* x0,
                                void* stream) {
   RM_TRY(check_dtype(out_dtype));
-  if (B <= 0 || F <= 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B, F, T, D must be positive");
+  if (B < 0 || F <= 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B must be >= 0, F, T, D positive");
   if (F > (int64_t)T * D) return fail(RM_ERR_UNSUPPORTED, "F=%lld floats do not fit in T*D=%lld", (long long)F, (long long)T * D);
+  if (B == 0) return ok();  // empty batch: nothing to do
   RM_TRY(check_ptr(emb, "emb"));
   RM_TRY(check_ptr(x0, "x0"));
   RM_TIMED("tokenize", (hipStream_t)stream, RM_HIP(rm::launch_tokenize_padsplit(emb, B, F, T, D, out_dtype, x0, (hipStream_t)stream), "tokenize"));
@@ -429,8 +430,9 @@ rm_status rm_tokenize_padsplit(const float* emb, int64_t B, int64_t F, int T, in
 
 rm_status rm_token_mix(const void* x, void* y, int64_t B, int T, int D, int dtype, void* stream) {
   RM_TRY(check_dtype(dtype));
-  if (B <= 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B, T, D must be positive");
+  if (B < 0 || T <= 0 || D <= 0) return fail(RM_ERR_INVALID, "B must be >= 0, T and D positive");
   if (D % T) return fail(RM_ERR_UNSUPPORTED, "D=%d is not divisible by H=T=%d", D, T);
+  if (B == 0) return ok();
   RM_TRY(check_ptr(x, "x"));
   RM_TRY(check_ptr(y, "y"));
   if (x == y) return fail(RM_ERR_INVALID, "y must not alias x");
@@ -448,6 +450,7 @@ rm_status rm_pffn_fwd(const void* s, const rm_pffn_params* p, void* v, int64_t B
                       void* ws, size_t ws_bytes, void* stream) {
   RM_TRY(check_ffn_shape(B, T, D, dtype));
   RM_TRY(check_hidden(Hd));
+  if (B == 0) return ok();
   if (!p) return fail(RM_ERR_INVALID, "params is NULL");
   RM_TRY(check_ptr(s, "s")); RM_TRY(check_ptr(v, "v"));
   RM_TRY(check_ptr(p->w1, "w1")); RM_TRY(check_ptr(p->b1, "b1"));
@@ -481,6 +484,7 @@ rm_status rm_moe_relu_fwd(const void* s, const rm_moe_params* p, void* v, float*
   RM_TRY(check_ffn_shape(B, T, D, dtype));
   RM_TRY(check_hidden(He));
   RM_TRY(check_moe_shape(B, T, E));
+  if (B == 0) return ok();
   RM_TRY(check_moe_params(p));
   RM_TRY(check_ptr(s, "s")); RM_TRY(check_ptr(v, "v")); RM_TRY(check_ptr(gates, "gates", false));
   if (s == v) return fail(RM_ERR_INVALID, "v must not alias s");
@@ -498,6 +502,7 @@ rm_status rm_moe_route(const void* s, const void* wr, const float* br, float* ga
                        int64_t B, int T, int D, int E, int dtype, void* ws, size_t ws_bytes, void* stream) {
   RM_TRY(check_ffn_shape(B, T, D, dtype));
   RM_TRY(check_moe_shape(B, T, E));
+  if (B == 0) return ok();
   RM_TRY(check_ptr(s, "s")); RM_TRY(check_ptr(wr, "wr")); RM_TRY(check_ptr(br, "br"));
   RM_TRY(check_ptr(gates, "gates")); RM_TRY(check_ptr(offsets, "offsets")); RM_TRY(check_ptr(rows, "rows"));
   RM_TRY(check_ptr(ws, "ws"));
@@ -524,6 +529,7 @@ rm_status rm_block_fwd(const void* x, const rm_block_params* p, void* x_out, int
                        int E, int dtype, void* ws, size_t ws_bytes, void* stream) {
   RM_TRY(check_block_params(p, dtype));
   RM_TRY(check_block_shape(p->kind, B, T, D, hidden, E, dtype));
+  if (B == 0) return ok();
   RM_TRY(check_ptr(x, "x")); RM_TRY(check_ptr(x_out, "x_out"));
   if (x == x_out) return fail(RM_ERR_INVALID, "x_out must not alias x");
   RM_TRY(check_ptr(ws, "ws"));
@@ -557,6 +563,8 @@ rm_status rm_model_fwd(const rm_model_desc* m, const void* in, void* x_out, floa
   if (any_moe) RM_TRY(check_moe_shape(B, m->T, m->E));
   if (m->F < 0) return fail(RM_ERR_INVALID, "F must not be negative");
   if (m->F > (int64_t)m->T * m->D) return fail(RM_ERR_UNSUPPORTED, "F=%lld floats do not fit in T*D", (long long)m->F);
+  if ((pooled || logits) && !m->head_w) return fail(RM_ERR_INVALID, "pooled/logits requested without head_w");
+  if (B == 0) return ok();
   RM_TRY(check_ptr(in, "in"));
   RM_TRY(check_ptr(x_out, "x_out", false));
   RM_TRY(check_ptr(pooled, "pooled", false));

@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_token_mix(const void*
                                                                      int64_t B, int T, int D) {
   typedef typename RawVec<EB * VEC>::type raw_t;
   typedef typename RawVec<EB>::type elem_t;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  // the T rows of one sample read the same [T][D] block: keep them on one XCD
+  const int64_t row = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * kRowsPerBlock + (threadIdx.x / kWave);
   if (row >= B * T) return;
   const int lane = lane_id();
   const int64_t b = row / T;
@@ -101,7 +102,9 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __res
                                                                   const float* __restrict__ g,
                                                                   const float* __restrict__ beta,
                                                                   int64_t B, int T_, int D, int token_major) {
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  // the T rows of one sample gather from the same [T][D] block: keep them on
+  // one XCD so the second read of each element hits its L2
+  const int64_t row = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * kRowsPerBlock + (threadIdx.x / kWave);
   if (row >= B * T_) return;
   const int lane = lane_id();
   const int64_t b = row / T_;

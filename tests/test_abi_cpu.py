@@ -65,7 +65,7 @@ def test_token_mix_argument_errors(lib):
     assert "aligned" in err(lib)
     assert lib.rm_token_mix(A16, A16, 4, 2, 8, bd.RM_BF16, None) == bd.RM_ERR_INVALID
     assert "alias" in err(lib)
-    assert lib.rm_token_mix(A16, A16 + 4096, 0, 2, 8, bd.RM_BF16, None) == bd.RM_ERR_INVALID
+    assert lib.rm_token_mix(A16, A16 + 4096, -3, 2, 8, bd.RM_BF16, None) == bd.RM_ERR_INVALID
     assert lib.rm_token_mix(A16, A16 + 4096, 4, 2, 8, 7, None) == bd.RM_ERR_UNSUPPORTED
 
 
@@ -134,3 +134,39 @@ def test_workspace_sizes_scale_with_the_problem(lib):
     assert small >= 1024 * 32 * (1536 * 2 + 6144 * 2 + 1536 * 4)
     assert lib.rm_block_workspace_bytes(1, 2048, 16, 768, 1536, 8, bd.RM_BF16) > \
         lib.rm_block_workspace_bytes(1, 1024, 16, 768, 1536, 8, bd.RM_BF16)
+
+
+def test_empty_batch_is_a_no_op(lib):
+    # B = 0: arguments other than the data pointers are still checked
+    assert lib.rm_token_mix(None, None, 0, 4, 64, bd.RM_BF16, None) == bd.RM_OK
+    assert lib.rm_token_mix(None, None, 0, 3, 64, bd.RM_BF16, None) == bd.RM_ERR_UNSUPPORTED
+    assert lib.rm_token_mix(None, None, -1, 4, 64, bd.RM_BF16, None) == bd.RM_ERR_INVALID
+    assert lib.rm_tokenize_padsplit(None, 0, 5000, 16, 320, bd.RM_BF16, None, None) == bd.RM_OK
+    assert lib.rm_pffn_fwd(None, None, None, 0, 4, 64, 128, bd.RM_BF16, None, 0, None) == bd.RM_OK
+    assert lib.rm_moe_relu_fwd(None, None, None, None, 0, 4, 64, 8, 128, bd.RM_BF16, None, 0, None) == bd.RM_OK
+    bp = bd.BlockParams()
+    bp.kind = bd.RM_BLOCK_DENSE
+    bp.ln1_g = bp.ln1_b = bp.ln2_g = bp.ln2_b = A16
+    bp.pffn = _pffn()
+    assert lib.rm_block_fwd(None, C.byref(bp), None, 0, 4, 64, 128, 0, bd.RM_BF16, None, 0, None) == bd.RM_OK
+    arr = (bd.BlockParams * 1)(bp)
+    m = bd.ModelDesc(4, 64, 128, 0, bd.RM_BF16, 1, arr, 0, None, 0.0)
+    assert lib.rm_model_fwd(C.byref(m), None, None, None, None, 0, None, 0, None) == bd.RM_OK
+
+
+def test_width_limits(lib):
+    # one [D] row per wavefront: 8192 wide with heads of 8*k is the limit
+    need = lib.rm_block_workspace_bytes(0, 1, 16, 8192, 64, 0, bd.RM_BF16)
+    bp = bd.BlockParams()
+    bp.kind = bd.RM_BLOCK_DENSE
+    bp.ln1_g = bp.ln1_b = bp.ln2_g = bp.ln2_b = A16
+    bp.pffn = _pffn()
+    assert lib.rm_block_fwd(A16, C.byref(bp), A16 * 2, 1, 16, 8200, 64, 0, bd.RM_BF16, A16 * 3, 1 << 40,
+                            None) == bd.RM_ERR_UNSUPPORTED  # 8200 % 16 != 0
+    assert lib.rm_block_fwd(A16, C.byref(bp), A16 * 2, 1, 16, 8192 * 2, 64, 0, bd.RM_BF16, A16 * 3, 1 << 40,
+                            None) == bd.RM_ERR_UNSUPPORTED  # too wide
+    assert "wider" in err(lib)
+    p = bd.MoeParams(A16, A16, A16, A16, A16, A16)
+    assert lib.rm_moe_relu_fwd(A16, C.byref(p), A16 * 2, None, 4, 256, 64, 32, 64, bd.RM_BF16, A16 * 3, 1 << 40,
+                               None) == bd.RM_ERR_UNSUPPORTED  # T*E = 8192 lists
+    assert need > 0
