@@ -24,8 +24,8 @@
  *  - Width limits of this build: D a multiple of 8 (and of T wherever tokens
  *    are mixed), hidden widths a multiple of 8, one [D] row per wavefront in
  *    registers (D <= 8192 when D/T is a multiple of 8; the FFN and MoE calls
- *    alone: D <= 4096); MoE: 1 <= E <= 32, T*E <= 4096.  Larger shapes are
- *    RM_ERR_UNSUPPORTED.
+ *    and blocks with an MoE: D <= 4096); MoE: 1 <= E <= 32, T*E <= 4096.
+ *    Larger shapes are RM_ERR_UNSUPPORTED.
  *  - The caller owns every buffer, including the workspace `ws`, sized with
  *    the matching rm_*_workspace_bytes call.  The library never allocates,
  *    frees or synchronises; work is enqueued on `stream` (a hipStream_t, NULL

@@ -318,7 +318,10 @@ rm_status check_block_params(const rm_block_params* p, int dt) {
 rm_status check_block_shape(int kind, int64_t B, int T, int D, int hidden, int E, int dt) {
   RM_TRY(check_shape(B, T, D, dt));
   RM_TRY(check_hidden(hidden));
-  if (kind == RM_BLOCK_MOE) RM_TRY(check_moe_shape(B, T, E));
+  if (kind == RM_BLOCK_MOE) {
+    RM_TRY(check_moe_shape(B, T, E));
+    if (D > 4096) return fail(RM_ERR_UNSUPPORTED, "D=%d is wider than the MoE row kernels support (4096)", D);
+  }
   return RM_OK;
 }
 
@@ -560,7 +563,10 @@ rm_status rm_model_fwd(const rm_model_desc* m, const void* in, void* x_out, floa
     any_moe |= m->blocks[l].kind == RM_BLOCK_MOE;
   }
   if (m->L > 0) RM_TRY(check_hidden(m->hidden));
-  if (any_moe) RM_TRY(check_moe_shape(B, m->T, m->E));
+  if (any_moe) {
+    RM_TRY(check_moe_shape(B, m->T, m->E));
+    if (m->D > 4096) return fail(RM_ERR_UNSUPPORTED, "D=%d is wider than the MoE row kernels support (4096)", m->D);
+  }
   if (m->F < 0) return fail(RM_ERR_INVALID, "F must not be negative");
   if (m->F > (int64_t)m->T * m->D) return fail(RM_ERR_UNSUPPORTED, "F=%lld floats do not fit in T*D", (long long)m->F);
   if ((pooled || logits) && !m->head_w) return fail(RM_ERR_INVALID, "pooled/logits requested without head_w");

@@ -160,14 +160,15 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __res
 }
 
 // ---------------------------------------------------------------------------
-// out[r,:] = LN(z[r,:]) * g + beta for fp32 rows (D % 4 == 0).
+// out[r,:] = LN(z[r,:]) * g + beta for fp32 rows (D % 8 == 0), 8 floats per
+// lane-chunk.
 
 template <typename T, int MAXI>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const float* __restrict__ z, T* __restrict__ out,
                                                                    const float* __restrict__ g,
                                                                    const float* __restrict__ beta,
                                                                    int64_t rows, int D) {
-  constexpr int VEC = 4;
+  constexpr int VEC = 8;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
   if (row >= rows) return;
   const int lane = lane_id();
@@ -312,7 +313,7 @@ hipError_t ln_rows_t(const float* z, void* out, const float* g, const float* b, 
                      hipStream_t s) {
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
   T* o = (T*)out;
-  switch (pick_maxi(D / 4)) {
+  switch (pick_maxi(D / 8)) {
     case 0: return hipErrorInvalidValue;
     case 1: hipLaunchKernelGGL((k_ln_rows<T, 1>), grid, block, 0, s, z, o, g, b, rows, D); break;
     case 2: hipLaunchKernelGGL((k_ln_rows<T, 2>), grid, block, 0, s, z, o, g, b, rows, D); break;
@@ -327,7 +328,7 @@ hipError_t ln_rows_t(const float* z, void* out, const float* g, const float* b, 
 bool row_width_supported(int T, int D, int dt) {
   const int eb = dt == kBF16 ? 2 : 4;
   if (T <= 0 || D <= 0 || D % T || D % 8) return false;
-  return pick_maxi(D / chunk_elems(D / T, eb)) != 0 && pick_maxi(D / 4) != 0;
+  return pick_maxi(D / chunk_elems(D / T, eb)) != 0 && pick_maxi(D / 8) != 0;
 }
 
 hipError_t launch_token_mix(const void* x, void* y, int64_t B, int T, int D, int dt, hipStream_t s) {

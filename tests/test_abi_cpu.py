@@ -169,4 +169,10 @@ def test_width_limits(lib):
     p = bd.MoeParams(A16, A16, A16, A16, A16, A16)
     assert lib.rm_moe_relu_fwd(A16, C.byref(p), A16 * 2, None, 4, 256, 64, 32, 64, bd.RM_BF16, A16 * 3, 1 << 40,
                                None) == bd.RM_ERR_UNSUPPORTED  # T*E = 8192 lists
+    # blocks with an MoE keep the 4096 limit of the MoE row kernels
+    bp.kind = bd.RM_BLOCK_MOE
+    bp.moe = p
+    assert lib.rm_block_fwd(A16, C.byref(bp), A16 * 2, 1, 16, 8192, 64, 4, bd.RM_BF16, A16 * 3, 1 << 40,
+                            None) == bd.RM_ERR_UNSUPPORTED
+    assert "MoE" in err(lib)
     assert need > 0
