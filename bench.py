@@ -39,23 +39,36 @@ def log(msg: str) -> None:
     sys.stderr.flush()
 
 
-def gemm_source_sha() -> str:
-    with open(os.path.join(ROOT, "rankmixer_token_mixing_amd", "csrc", "kernels_gemm.hip"), "rb") as f:
+CSRC = os.path.join(ROOT, "rankmixer_token_mixing_amd", "csrc")
+# the sources that define each launch group's kernel
+KERNEL_SOURCES = {
+    "ffn1": ("kernels_gemm.hip", "common.hpp"),
+    "ffn2_resid": ("kernels_gemm.hip", "common.hpp"),
+    "mix_ln1": ("kernels_rows.hip", "common.hpp"),
+    "ln2": ("kernels_rows.hip", "common.hpp"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_fwd_{config}_traffic.json")
+
+
+def source_sha(name: str) -> str:
+    with open(os.path.join(CSRC, name), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def committed_traffic(config: str, kernel: str):
-    """HBM bytes per launch of `kernel` from profiles/traffic_<config>.json,
-    when that summary was taken on the current GEMM source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
-    if not os.path.exists(path):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary of this workload, or None when there is
+    none or the kernel's sources changed since the counters were taken."""
+    path = TRAFFIC_FILE.format(config=config)
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
         return None
     with open(path) as f:
         tr = json.load(f)
-    if tr.get("kernels_gemm_sha") != gemm_source_sha():
-        return None
     k = tr.get("kernels", {}).get(kernel)
     if not k:
+        return None
+    taken = k.get("source_sha", {})
+    if any(taken.get(src) != source_sha(src) for src in KERNEL_SOURCES[kernel]):
         return None
     return k.get("hbm_bytes_per_launch")
 
