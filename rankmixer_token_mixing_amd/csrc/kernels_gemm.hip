@@ -301,6 +301,57 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_generic(KParams p) {
   store_direct<T, FM, FN, EPI>(p, t, acc, wm, wn, lr, lh);
 }
 
+// Epilogue of the ring kernels.  bf16 output is staged through LDS (orow(ml)
+// = the LDS row that holds output row ml, BN*2 bytes, 16-byte chunks
+// XOR-swizzled by row) so every global store writes whole row segments; fp32
+// output goes straight from the accumulators.  Every DMA has landed and every
+// wave is past its last operand read when this runs.
+template <int NWM, int NWN, int FM, int FN, int EPI, typename ORow>
+__device__ __forceinline__ void ring_epilogue(const KParams& p, const TileId& t, const floatx16 (&acc)[FM][FN],
+                                              int wave, int lane, ORow orow) {
+  constexpr int BM = NWM * FM * 32, BN = NWN * FN * 32, NT = NWM * NWN * kWave;
+  typedef typename OutType<EPI, bf16>::type TO;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int tid = threadIdx.x;
+  if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias) {
+    constexpr int OCH = BN / 8;  // 16-byte chunks per output row
+    __syncthreads();             // every wave is done reading operand slots
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
+        float4 bias = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.bias && t.n0 + nl < p.N)
+          bias = *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + t.n0 + nl);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int ml = wm * FM * 32 + i * 32 + lr;
+          float v[4] = {acc[i][j][4 * q + 0] + bias.x, acc[i][j][4 * q + 1] + bias.y, acc[i][j][4 * q + 2] + bias.z,
+                        acc[i][j][4 * q + 3] + bias.w};
+          epi4<EPI, bf16>(p, t, 0, 0, 1.f, v);
+          const int phys = (nl >> 3) ^ (ml & (OCH - 1));
+          store_from_f32<bf16, 4>(reinterpret_cast<bf16*>(orow(ml) + phys * 16 + (nl & 7) * 2), v);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int RPP = NT / OCH;  // output rows per pass
+#pragma unroll 4
+    for (int pass = 0; pass < BM / RPP; ++pass) {
+      const int ml = pass * RPP + tid / OCH;
+      const int c = tid % OCH;
+      const uint4 val = *reinterpret_cast<const uint4*>(orow(ml) + ((c ^ (ml & (OCH - 1))) * 16));
+      const int m = t.m0 + ml;
+      if (m < t.Mg && t.n0 + c * 8 < p.N)
+        *reinterpret_cast<uint4*>((TO*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + t.n0 + c * 8) = val;
+    }
+  } else {
+    store_direct<bf16, FM, FN, EPI>(p, t, acc, wm, wn, lr, lh);
+  }
+}
+
 // ===========================================================================
 // ring main loop (bf16, K % 64 == 0)
 
@@ -323,7 +374,6 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
   typedef Ring<NWM, NWN, FM, FN> RG;
   constexpr int BM = RG::BM, BN = RG::BN, BK = RG::BK, NW = RG::NW;
   constexpr int A_DMA = RG::A_DMA, B_DMA = RG::B_DMA;
-  typedef typename OutType<EPI, bf16>::type TO;
 
   __shared__ uint4 r0[RG::SLOT];
   __shared__ uint4 r1[RG::SLOT];
@@ -440,51 +490,199 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
   }
   wait_vmcnt<0>();  // no DMA may land in LDS after this point
 
-  if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias) {
-    // bf16 output staged through LDS so every global store writes whole
-    // row segments: rows of BN*2 bytes, 16-byte chunks XOR-swizzled by row
-    constexpr int OCH = BN / 8;                 // 16-byte chunks per output row
+  ring_epilogue<NWM, NWN, FM, FN, EPI>(p, t, acc, wave, lane, [&](int ml) -> char* {
     constexpr int RPS = RG::SLOT * 16 / (BN * 2);  // output rows per slot
-    static_assert(BM <= 4 * RPS, "output tile must fit in four slots");
-    auto orow = [&](int ml) -> char* {
-      const int s = ml / RPS;
-      char* base = s == 0 ? (char*)r0 : s == 1 ? (char*)r1 : s == 2 ? (char*)r2 : (char*)r3;
-      return base + (ml - s * RPS) * (BN * 2);
-    };
-    __syncthreads();  // every wave is done reading operand slots
+    const int s = ml / RPS;
+    char* base = s == 0 ? (char*)r0 : s == 1 ? (char*)r1 : s == 2 ? (char*)r2 : (char*)r3;
+    return base + (ml - s * RPS) * (BN * 2);
+  });
+}
+
+
+// ===========================================================================
+// pipelined ring (bf16, K % 64 == 0, dense, 128 x 64 per wave: the 256 x 256
+// and 256 x 128 tiles).  Same five slots and slot assignment as k_gemm_ring
+// (A_j in slot 2j mod 5, W_j in slot 2j+1 mod 5), scheduled by hand:
+//  * a stage is four k-steps of 16.  Each k-step is one asm block: its eight
+//    MFMAs, the six fragment reads of the next k-step in the order the next
+//    block consumes them (A_0, W_0, W_1, A_1, A_2, A_3) behind the first six
+//    MFMAs, and up to four DMA ops; the block waits for its own reads at its
+//    end, so no LDS load result outlives the statement that issued it.
+//  * the stage barrier sits before the last k-step.  By then every wave has
+//    read all of stage k's fragments (the last k-step's were read by the
+//    third block), so after it stage k's slots take W_{k+2} (first block
+//    after the barrier) and the last k-step already reads stage k+1's first
+//    fragments.  A_{k+2} goes into the slot of W_{k-1} in the first block(s)
+//    of stage k.
+//  * DMA and fragment reads are plain asm, invisible to the compiler's wait
+//    tracking; the waits are explicit: before barrier k, everything but the
+//    A_{k+2} ops (the newest A_DMA) has landed, i.e. A_{k+1} and W_{k+1}.
+// Spread this way, the eight waves' DMA ops no longer arrive in one burst
+// that stalls each wave's MFMA issue behind the vector-memory queue, and no
+// fragment read latency is exposed at a stage boundary.
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // one fragment (register operand)
+struct Frags {
+  u32x4 a0, a1, a2, a3, b0, b1;
+};
+
+#define RM_MF(c, b, a) "v_mfma_f32_32x32x16_bf16 %[" #c "], %[" #b "], %[" #a "], %[" #c "]\n\t"
+#define RM_RD(dst, addr, off) "ds_read_b128 %[" #dst "], %[" #addr "] offset:" #off "\n\t"
+#define RM_DMA(v) "global_load_lds_dwordx4 %[" #v "], %[sb]\n\t"
+#define RM_M0NEXT "s_add_u32 m0, m0, %[ms]\n\t"
+
+// one k-step with four DMA ops: voff v0..v3 against the 64-bit base sb, LDS
+// destinations mb, mb + ms, mb + 2ms, mb + 3ms (M0 is set at least one
+// instruction before each DMA that reads it)
+#define RM_KSTEP_DMA                                                                                     \
+  "s_mov_b32 m0, %[mb]\n\t" RM_MF(c00, b0, a0) RM_RD(na0, la, 0) RM_DMA(v0) RM_M0NEXT RM_MF(c01, b1, a0) \
+      RM_RD(nb0, lb, 0) RM_MF(c10, b0, a1) RM_RD(nb1, lb, 4096) RM_DMA(v1) RM_M0NEXT RM_MF(c11, b1, a1)  \
+          RM_RD(na1, la, 4096) RM_MF(c20, b0, a2) RM_RD(na2, la, 8192) RM_DMA(v2) RM_M0NEXT               \
+              RM_MF(c21, b1, a2) RM_RD(na3, la, 12288) RM_MF(c30, b0, a3) RM_DMA(v3) RM_MF(c31, b1, a3)  \
+                  "s_waitcnt lgkmcnt(0)\n\t"
+#define RM_KSTEP                                                                                               \
+  RM_MF(c00, b0, a0) RM_RD(na0, la, 0) RM_MF(c01, b1, a0) RM_RD(nb0, lb, 0) RM_MF(c10, b0, a1) RM_RD(nb1, lb, 4096) \
+      RM_MF(c11, b1, a1) RM_RD(na1, la, 4096) RM_MF(c20, b0, a2) RM_RD(na2, la, 8192) RM_MF(c21, b1, a2)           \
+          RM_RD(na3, la, 12288) RM_MF(c30, b0, a3) RM_MF(c31, b1, a3) "s_waitcnt lgkmcnt(0)\n\t"
+
+#define RM_KSTEP_ACC                                                                                   \
+  [c00] "+v"(acc[0][0]), [c01] "+v"(acc[0][1]), [c10] "+v"(acc[1][0]), [c11] "+v"(acc[1][1]),         \
+      [c20] "+v"(acc[2][0]), [c21] "+v"(acc[2][1]), [c30] "+v"(acc[3][0]), [c31] "+v"(acc[3][1]),     \
+      [na0] "=&v"(nx.a0), [na1] "=&v"(nx.a1), [na2] "=&v"(nx.a2), [na3] "=&v"(nx.a3), [nb0] "=&v"(nx.b0), \
+      [nb1] "=&v"(nx.b1)
+#define RM_KSTEP_IN \
+  [a0] "v"(cu.a0), [a1] "v"(cu.a1), [a2] "v"(cu.a2), [a3] "v"(cu.a3), [b0] "v"(cu.b0), [b1] "v"(cu.b1), \
+      [la] "v"(la), [lb] "v"(lb)
+
+__device__ __forceinline__ void kstep(floatx16 (&acc)[4][2], const Frags& cu, Frags& nx, uint32_t la, uint32_t lb) {
+  asm volatile(RM_KSTEP : RM_KSTEP_ACC : RM_KSTEP_IN);
+}
+
+template <int MS>
+__device__ __forceinline__ void kstep_dma(floatx16 (&acc)[4][2], const Frags& cu, Frags& nx, uint32_t la,
+                                          uint32_t lb, uint32_t mb, const void* sb, const uint32_t* v) {
+  asm volatile(RM_KSTEP_DMA
+               : RM_KSTEP_ACC
+               : RM_KSTEP_IN, [mb] "s"(mb), [sb] "s"(sb), [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]),
+                 [v3] "v"(v[3]), [ms] "n"(MS)
+               : "m0", "scc");
+}
+
+// the six fragment reads of one k-step on their own (first k-step of a tile)
+__device__ __forceinline__ void read_frags(Frags& nx, uint32_t la, uint32_t lb) {
+  asm volatile(RM_RD(na0, la, 0) RM_RD(nb0, lb, 0) RM_RD(nb1, lb, 4096) RM_RD(na1, la, 4096) RM_RD(na2, la, 8192)
+                   RM_RD(na3, la, 12288) "s_waitcnt lgkmcnt(0)\n\t"
+               : [na0] "=&v"(nx.a0), [na1] "=&v"(nx.a1), [na2] "=&v"(nx.a2), [na3] "=&v"(nx.a3), [nb0] "=&v"(nx.b0),
+                 [nb1] "=&v"(nx.b1)
+               : [la] "v"(la), [lb] "v"(lb));
+}
+
+// one DMA op on its own (prologue)
+__device__ __forceinline__ void dma1(uint32_t m0v, const void* sb, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v], %[sb]\n\t"
+               :
+               : [m] "s"(m0v), [sb] "s"(sb), [v] "v"(voff)
+               : "m0");
+}
+
+template <int NWM, int NWN, int EPI>
+__global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
+  constexpr int FM = 4, FN = 2;
+  typedef Ring<NWM, NWN, FM, FN> RG;
+  constexpr int BM = RG::BM, BN = RG::BN, NW = RG::NW;
+  constexpr int A_DMA = RG::A_DMA, B_DMA = RG::B_DMA;
+  constexpr uint32_t SLOTB = RG::SLOT * 16;  // bytes per slot
+  static_assert(B_DMA == 4 && (A_DMA == 4 || A_DMA == 8), "DMA ops come in blocks of four");
+  static_assert(BM * BN * 2 <= 5 * (int)SLOTB, "staged output tile must fit in the ring");
+
+  __shared__ uint4 lds[5 * RG::SLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  TileId t;
+  tile_id<false, BM, BN>(p, t);
+
+  const int K = p.K;
+  const int nk = K / 64;
+  const char* Ab = (const char*)p.A + (long long)(t.g / p.a_gdiv) * p.a_gs * 2;
+  const char* Bb = (const char*)p.W + (long long)t.g * p.b_gs * 2;
+  // per DMA op: 32-bit byte offset of this lane's 16-byte chunk from the
+  // operand base (the host checks that every offset fits)
+  uint32_t va[A_DMA], vw[B_DMA];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nl = wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
-        float4 bias = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (p.bias && t.n0 + nl < p.N)
-          bias = *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + t.n0 + nl);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int ml = wm * FM * 32 + i * 32 + lr;
-          float v[4] = {acc[i][j][4 * q + 0] + bias.x, acc[i][j][4 * q + 1] + bias.y, acc[i][j][4 * q + 2] + bias.z,
-                        acc[i][j][4 * q + 3] + bias.w};
-          epi4<EPI, bf16>(p, t, 0, 0, 1.f, v);
-          const int phys = (nl >> 3) ^ (ml & (OCH - 1));
-          store_from_f32<bf16, 4>(reinterpret_cast<bf16*>(orow(ml) + phys * 16 + (nl & 7) * 2), v);
-        }
-      }
-    }
-    __syncthreads();
-    constexpr int RPP = RG::NT / OCH;  // output rows per pass
-#pragma unroll 4
-    for (int pass = 0; pass < BM / RPP; ++pass) {
-      const int ml = pass * RPP + tid / OCH;
-      const int c = tid % OCH;
-      const uint4 val = *reinterpret_cast<const uint4*>(orow(ml) + ((c ^ (ml & (OCH - 1))) * 16));
-      const int m = t.m0 + ml;
-      if (m < t.Mg && t.n0 + c * 8 < p.N)
-        *reinterpret_cast<uint4*>((TO*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + t.n0 + c * 8) = val;
-    }
-  } else {
-    store_direct<bf16, FM, FN, EPI>(p, t, acc, wm, wn, lr, lh);
+  for (int i = 0; i < A_DMA; ++i) {
+    const int row = 8 * (wave + i * NW) + (lane >> 3);
+    const int m = min(t.m0 + row, t.Mg - 1);  // rows past the end re-read the last row
+    va[i] = (uint32_t)(((long long)m * p.a_rs + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
   }
+#pragma unroll
+  for (int i = 0; i < B_DMA; ++i) {
+    const int row = 8 * (wave + i * NW) + (lane >> 3);
+    const int n = min(t.n0 + row, p.N - 1);
+    vw[i] = (uint32_t)(((long long)n * K + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  auto slot = [&](int j) -> uint32_t { return lds0 + (uint32_t)(j % 5) * SLOTB; };
+  auto kbase = [&](const char* base, int kt) -> const void* { return base + (long long)min(kt, nk - 1) * 128; };
+  const uint32_t wof = (uint32_t)wave * 1024;
+
+  // fragment address of lane for k-step kk: row * 128 + swizzled chunk
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int lr = lane & 31, lh = lane >> 5;
+  uint32_t oa[4], ob[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const uint32_t ch = (uint32_t)(((kk * 2 + lh) ^ ((lr >> 1) & 7)) * 16);
+    oa[kk] = (uint32_t)(wm * FM * 32 + lr) * 128 + ch;
+    ob[kk] = (uint32_t)(wn * FN * 32 + lr) * 128 + ch;
+  }
+
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // prologue: A_0 -> 0, W_0 -> 1, A_1 -> 2, W_1 -> 3
+#pragma unroll
+  for (int i = 0; i < A_DMA; ++i) dma1(slot(0) + wof + i * NW * 1024, kbase(Ab, 0), va[i]);
+#pragma unroll
+  for (int i = 0; i < B_DMA; ++i) dma1(slot(1) + wof + i * NW * 1024, kbase(Bb, 0), vw[i]);
+#pragma unroll
+  for (int i = 0; i < A_DMA; ++i) dma1(slot(2) + wof + i * NW * 1024, kbase(Ab, 1), va[i]);
+#pragma unroll
+  for (int i = 0; i < B_DMA; ++i) dma1(slot(3) + wof + i * NW * 1024, kbase(Bb, 1), vw[i]);
+  wait_vmcnt<A_DMA + B_DMA>();  // A_0 and W_0 landed
+  __builtin_amdgcn_s_barrier();
+  Frags f0, f1;
+  read_frags(f0, slot(0) + oa[0], slot(1) + ob[0]);
+
+  for (int k = 0; k < nk; ++k) {
+    const uint32_t sA = slot(2 * k), sW = slot(2 * k + 1);
+    // A_{k+2} into the slot of W_{k-1}
+    const uint32_t dA = slot(2 * k + 4) + wof;
+    kstep_dma<NW * 1024>(acc, f0, f1, sA + oa[1], sW + ob[1], dA, kbase(Ab, k + 2), va);
+    if constexpr (A_DMA == 8)
+      kstep_dma<NW * 1024>(acc, f1, f0, sA + oa[2], sW + ob[2], dA + 4 * NW * 1024, kbase(Ab, k + 2), va + 4);
+    else
+      kstep(acc, f1, f0, sA + oa[2], sW + ob[2]);
+    kstep(acc, f0, f1, sA + oa[3], sW + ob[3]);
+    // everything but A_{k+2} has landed: A_{k+1} and W_{k+1}
+    wait_vmcnt<A_DMA>();
+    __builtin_amdgcn_s_barrier();
+    // stage k's slots are free: W_{k+2} into A_k's; read stage k+1's first fragments
+    kstep_dma<NW * 1024>(acc, f1, f0, slot(2 * k + 2) + oa[0], slot(2 * k + 3) + ob[0], sA + wof, kbase(Bb, k + 2),
+                         vw);
+  }
+  wait_vmcnt<0>();  // no DMA may land in LDS after this point
+  // the last MFMAs' results are read by ordinary code from here on
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t" ::);
+
+  ring_epilogue<NWM, NWN, FM, FN, EPI>(p, t, acc, wave, lane,
+                                       [&](int ml) -> char* { return (char*)lds + ml * (BN * 2); });
 }
 
 // ===========================================================================
@@ -562,6 +760,23 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   } else {
     const dim3 grid((unsigned)((long long)a.G * p.tiles_m * p.tiles_n));
     if (grid.x == 0) return hipSuccess;
+    if constexpr (FM == 4 && FN == 2) {
+      // the pipelined ring addresses operands by 32-bit byte offsets
+      const bool fits = ((long long)(a.M - 1) * a.a_rs + a.K) * 2 < (1LL << 32) &&
+                        ((long long)(a.N - 1) * a.K + a.K) * 2 < (1LL << 32) && a.a_gdiv == 1 && !a.a_rowidx;
+      if (ring && fits && a.pipe != 0) {
+        const dim3 block(NWM * NWN * kWave);
+        switch (a.epi) {
+          case kEpiBiasGelu: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasGelu>), grid, block, 0, s, p); break;
+          case kEpiBias: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBias>), grid, block, 0, s, p); break;
+          case kEpiBiasResidF32:
+            hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasResidF32>), grid, block, 0, s, p);
+            break;
+          default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+      }
+    }
     switch (a.epi) {
       case kEpiBiasGelu: launch_one<NWM, NWN, FM, FN, kEpiBiasGelu, false, false>(a, p, grid, s, ring); break;
       case kEpiBias: launch_one<NWM, NWN, FM, FN, kEpiBias, false, false>(a, p, grid, s, ring); break;

@@ -86,6 +86,7 @@ struct GemmArgs {
   const int* ntiles = nullptr;
   int max_mtiles = 0;
   int tile_cfg = -1;  // -1: choose automatically
+  int pipe = -1;      // 0: never use the hand-scheduled ring (for comparisons)
 };
 // Row count of the M tile a launch of `a` will use (ragged tile lists are
 // built for this).
