@@ -43,7 +43,7 @@ CSRC = os.path.join(ROOT, "rankmixer_token_mixing_amd", "csrc")
 # the sources that define each launch group's kernel
 KERNEL_SOURCES = {
     "ffn1": ("kernels_gemm.hip", "common.hpp"),
-    "ffn2_resid": ("kernels_gemm.hip", "common.hpp"),
+    "ffn2": ("kernels_gemm.hip", "common.hpp"),
     "mix_ln1": ("kernels_rows.hip", "common.hpp"),
     "ln2": ("kernels_rows.hip", "common.hpp"),
 }
@@ -184,13 +184,13 @@ def main() -> int:
     eb = pm.ELEM_BYTES[cfg.dtype]
     row_bytes = {  # compulsory HBM bytes per launch
         "mix_ln1": 2 * cfg.B * cfg.T * cfg.D * eb,
-        "ln2": cfg.B * cfg.T * cfg.D * (4 + eb),
+        "ln2": cfg.B * cfg.T * cfg.D * (4 + 2 * eb),  # Z (fp32) and the residual S in, X' out
     }
     kernels = {}
     for name, (tot_ms, n) in prof.items():
         avg = tot_ms / max(n, 1)
         e = {"avg_ms": round(avg, 5), "launches": n, "total_ms": round(tot_ms, 3)}
-        if gemm_flops and name in ("ffn1", "ffn2_resid"):
+        if gemm_flops and name in ("ffn1", "ffn2"):
             e["tflops"] = round(gemm_flops / (avg * 1e-3) / 1e12, 1)
         if name in row_bytes:
             e["gbs"] = round(row_bytes[name] / (avg * 1e-3) / 1e9, 1)
@@ -200,7 +200,7 @@ def main() -> int:
     if kernels:
         dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
         avg_s = kernels[dom]["avg_ms"] * 1e-3
-        if gemm_flops and dom in ("ffn1", "ffn2_resid"):
+        if gemm_flops and dom in ("ffn1", "ffn2"):
             ach = gemm_flops / avg_s / 1e12
             roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1),
                         "peak": pm.PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else pm.PEAK_FP32_MFMA_TFLOPS,

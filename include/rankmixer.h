@@ -181,7 +181,7 @@ size_t rm_model_workspace_bytes(const rm_model_desc* m, int64_t B);
 /* Launch timing for benchmarks.  While enabled, every group of kernel
  * launches an entry point makes (the W1 product, the W2 product, a LayerNorm,
  * ...) is bracketed by two HIP events recorded on the caller's stream, under
- * a fixed name ("mix_ln1", "ffn1", "ffn2_resid", "ln2", "moe_ffn1", ...).
+ * a fixed name ("mix_ln1", "ffn1", "ffn2", "ln2", "moe_ffn1", ...).
  * rm_profile_enable(on) clears what was recorded and switches recording on or
  * off (creating events is a host-side cost; leave it off outside timing).
  * rm_profile_count() is the number of names recorded; rm_profile_read(i, ...)

@@ -332,11 +332,13 @@ rm_status run_block(const void* x, const rm_block_params* p, void* xo, int64_t B
   if (p->kind == RM_BLOCK_DENSE) {
     RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(w.S, sb, sT, &p->pffn, w.pffn.H, B, T, D, hidden, dt), st), "block W1 product"));
     rm::GemmArgs a2 = ffn2_args(w.pffn.H, &p->pffn, B, T, D, hidden, dt);
-    a2.epi = rm::kEpiBiasResidF32;
+    // Z = W2 product + bias (fp32); the residual S is added inside LayerNorm 2,
+    // which streams Z anyway, instead of by loads in the product's epilogue
+    a2.epi = rm::kEpiBiasF32;
     a2.C = w.Z;
-    a2.R = w.S; a2.r_gs = sT; a2.r_rs = sb;
-    RM_TIMED("ffn2_resid", st, RM_HIP(rm::launch_gemm(a2, st), "block W2 product"));
-    RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows_f32(w.Z, xo, p->ln2_g, p->ln2_b, B * T, D, dt, st), "LayerNorm 2"));
+    RM_TIMED("ffn2", st, RM_HIP(rm::launch_gemm(a2, st), "block W2 product"));
+    RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows_f32(w.Z, w.S, sb, sT, T, xo, p->ln2_g, p->ln2_b, B * T, D, dt, st),
+                               "residual + LayerNorm 2"));
     return RM_OK;
   }
   return run_moe(w.S, sb, sT, &p->moe, xo, nullptr, p->ln2_g, p->ln2_b, B, T, D, E, hidden, dt, w.moe, st);

@@ -49,8 +49,6 @@ struct KParams {
   long long c_gs, c_rs;
   const float* bias;
   long long bias_gs;
-  const void* R;
-  long long r_gs, r_rs;
   const float* rowscale;
   const int* row_off;
   const int* tiles;
@@ -138,12 +136,6 @@ __device__ __forceinline__ void epi4(const KParams& p, const TileId& t, int m, i
   if constexpr (EPI == kEpiBiasGelu) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = gelu_erf(v[e]);
-  }
-  if constexpr (EPI == kEpiBiasResidF32) {
-    float r[4];
-    load_f32<T, 4>((const T*)p.R + (t.row_base + m) * p.r_rs + (long long)t.g * p.r_gs + n, r);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] += r[e];
   }
   if constexpr (EPI == kEpiBiasScaleF32) {
 #pragma unroll
@@ -723,7 +715,6 @@ KParams make_params(const GemmArgs& a, int bm, int bn) {
   p.W = a.W; p.b_gs = a.b_gs;
   p.C = a.C; p.c_gs = a.c_gs; p.c_rs = a.c_rs;
   p.bias = a.bias; p.bias_gs = a.bias_gs;
-  p.R = a.R; p.r_gs = a.r_gs; p.r_rs = a.r_rs;
   p.rowscale = a.rowscale;
   p.row_off = a.row_off; p.tiles = a.tiles; p.ntiles = a.ntiles;
   p.M = a.M; p.N = a.N; p.K = a.K; p.G = a.G;
@@ -769,9 +760,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
         switch (a.epi) {
           case kEpiBiasGelu: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasGelu>), grid, block, 0, s, p); break;
           case kEpiBias: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBias>), grid, block, 0, s, p); break;
-          case kEpiBiasResidF32:
-            hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasResidF32>), grid, block, 0, s, p);
-            break;
+          case kEpiBiasF32: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasF32>), grid, block, 0, s, p); break;
           default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
@@ -780,7 +769,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
     switch (a.epi) {
       case kEpiBiasGelu: launch_one<NWM, NWN, FM, FN, kEpiBiasGelu, false, false>(a, p, grid, s, ring); break;
       case kEpiBias: launch_one<NWM, NWN, FM, FN, kEpiBias, false, false>(a, p, grid, s, ring); break;
-      case kEpiBiasResidF32: launch_one<NWM, NWN, FM, FN, kEpiBiasResidF32, false, false>(a, p, grid, s, ring); break;
+      case kEpiBiasF32: launch_one<NWM, NWN, FM, FN, kEpiBiasF32, false, false>(a, p, grid, s, ring); break;
       default: return hipErrorInvalidValue;
     }
   }

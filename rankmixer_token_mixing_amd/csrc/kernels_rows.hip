@@ -160,11 +160,15 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __res
 }
 
 // ---------------------------------------------------------------------------
-// out[r,:] = LN(z[r,:]) * g + beta for fp32 rows (D % 8 == 0), 8 floats per
-// lane-chunk.
+// out[r,:] = LN(z[r,:] + res[r,:]) * g + beta for fp32 rows (D % 8 == 0), 8
+// floats per lane-chunk.  Row r = b * Tn + t; the residual (optional, element
+// type T) of row r starts at res + b * res_bs + t * res_ts, so a token-major
+// residual is read in place.
 
 template <typename T, int MAXI>
-__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const float* __restrict__ z, T* __restrict__ out,
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const float* __restrict__ z,
+                                                                   const T* __restrict__ res, int64_t res_bs,
+                                                                   int64_t res_ts, int Tn, T* __restrict__ out,
                                                                    const float* __restrict__ g,
                                                                    const float* __restrict__ beta,
                                                                    int64_t rows, int D) {
@@ -174,6 +178,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const float* 
   const int lane = lane_id();
   const int nch = D / VEC;
   const float* zr = z + row * (int64_t)D;
+  const T* rr = res ? res + (row / Tn) * res_bs + (row % Tn) * res_ts : nullptr;
   float v[MAXI][VEC];
   float sum = 0.f;
 #pragma unroll
@@ -181,6 +186,12 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const float* 
     const int c = lane + i * kWave;
     if (c < nch) {
       load_f32<float, VEC>(zr + c * VEC, v[i]);
+      if (rr) {
+        float r[VEC];
+        load_f32<T, VEC>(rr + c * VEC, r);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[i][e] += r[e];
+      }
 #pragma unroll
       for (int e = 0; e < VEC; ++e) sum += v[i][e];
     }
@@ -309,17 +320,19 @@ hipError_t mix_ln_vec(const void* x, void* so, const float* g, const float* b, i
 }
 
 template <typename T>
-hipError_t ln_rows_t(const float* z, void* out, const float* g, const float* b, int64_t rows, int D,
-                     hipStream_t s) {
+hipError_t ln_rows_t(const float* z, const void* res, int64_t rbs, int64_t rts, int Tn, void* out, const float* g,
+                     const float* b, int64_t rows, int D, hipStream_t s) {
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
   T* o = (T*)out;
+  const T* r = (const T*)res;
+  if (Tn <= 0) Tn = 1;
   switch (pick_maxi(D / 8)) {
     case 0: return hipErrorInvalidValue;
-    case 1: hipLaunchKernelGGL((k_ln_rows<T, 1>), grid, block, 0, s, z, o, g, b, rows, D); break;
-    case 2: hipLaunchKernelGGL((k_ln_rows<T, 2>), grid, block, 0, s, z, o, g, b, rows, D); break;
-    case 4: hipLaunchKernelGGL((k_ln_rows<T, 4>), grid, block, 0, s, z, o, g, b, rows, D); break;
-    case 8: hipLaunchKernelGGL((k_ln_rows<T, 8>), grid, block, 0, s, z, o, g, b, rows, D); break;
-    default: hipLaunchKernelGGL((k_ln_rows<T, 16>), grid, block, 0, s, z, o, g, b, rows, D); break;
+    case 1: hipLaunchKernelGGL((k_ln_rows<T, 1>), grid, block, 0, s, z, r, rbs, rts, Tn, o, g, b, rows, D); break;
+    case 2: hipLaunchKernelGGL((k_ln_rows<T, 2>), grid, block, 0, s, z, r, rbs, rts, Tn, o, g, b, rows, D); break;
+    case 4: hipLaunchKernelGGL((k_ln_rows<T, 4>), grid, block, 0, s, z, r, rbs, rts, Tn, o, g, b, rows, D); break;
+    case 8: hipLaunchKernelGGL((k_ln_rows<T, 8>), grid, block, 0, s, z, r, rbs, rts, Tn, o, g, b, rows, D); break;
+    default: hipLaunchKernelGGL((k_ln_rows<T, 16>), grid, block, 0, s, z, r, rbs, rts, Tn, o, g, b, rows, D); break;
   }
   return hipGetLastError();
 }
@@ -356,9 +369,10 @@ hipError_t launch_mix_ln(const void* x, void* so, const float* g, const float* b
   }
 }
 
-hipError_t launch_ln_rows_f32(const float* z, void* out, const float* g, const float* b, int64_t rows,
-                              int D, int dt, hipStream_t s) {
-  return dt == kBF16 ? ln_rows_t<bf16>(z, out, g, b, rows, D, s) : ln_rows_t<float>(z, out, g, b, rows, D, s);
+hipError_t launch_ln_rows_f32(const float* z, const void* res, int64_t res_bs, int64_t res_ts, int Tn, void* out,
+                              const float* g, const float* b, int64_t rows, int D, int dt, hipStream_t s) {
+  return dt == kBF16 ? ln_rows_t<bf16>(z, res, res_bs, res_ts, Tn, out, g, b, rows, D, s)
+                     : ln_rows_t<float>(z, res, res_bs, res_ts, Tn, out, g, b, rows, D, s);
 }
 
 hipError_t launch_pool_logit(const void* x, const float* w, float c, float* pooled, float* logits,

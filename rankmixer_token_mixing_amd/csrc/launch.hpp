@@ -25,8 +25,10 @@ hipError_t launch_token_mix(const void* x, void* y, int64_t B, int T, int D, int
 hipError_t launch_mix_ln(const void* x, void* s_out, const float* g, const float* b, int64_t B,
                          int T, int D, int dt, bool token_major, hipStream_t s);
 // out = LN(z) for fp32 rows z [rows][D]
-hipError_t launch_ln_rows_f32(const float* z, void* out, const float* g, const float* b,
-                              int64_t rows, int D, int dt, hipStream_t s);
+// out[r] = LN(z[r] + res[r]) * g + b over fp32 rows r = b*Tn + t; res (dt,
+// optional) row r at res + b * res_bs + t * res_ts elements
+hipError_t launch_ln_rows_f32(const float* z, const void* res, int64_t res_bs, int64_t res_ts, int Tn, void* out,
+                              const float* g, const float* b, int64_t rows, int D, int dt, hipStream_t s);
 // pooled[b] = mean_t x[b,t,:]; logit[b] = w . pooled[b] + c
 hipError_t launch_pool_logit(const void* x, const float* w, float c, float* pooled, float* logits,
                              int64_t B, int T, int D, int dt, hipStream_t s);
@@ -57,7 +59,7 @@ hipError_t launch_moe_combine(const float* y, const int* pos, const void* s, int
 enum Epilogue {
   kEpiBiasGelu = 0,       // C(dt)  = GELU(acc + bias[n])
   kEpiBias = 1,           // C(dt)  = acc + bias[n]
-  kEpiBiasResidF32 = 2,   // C(f32) = acc + bias[n] + R[m][n]
+  kEpiBiasF32 = 2,        // C(f32) = acc + bias[n]
   kEpiBiasScaleF32 = 3,   // C(f32) = rowscale[m] * (acc + bias[n])
 };
 
@@ -76,7 +78,6 @@ struct GemmArgs {
   const void* W = nullptr; int64_t b_gs = 0;
   void* C = nullptr; int64_t c_gs = 0, c_rs = 0;
   const float* bias = nullptr; int64_t bias_gs = 0;
-  const void* R = nullptr; int64_t r_gs = 0, r_rs = 0;
   const float* rowscale = nullptr;
   // ragged mode (MoE): group g has row_off[g+1]-row_off[g] rows; the tiles
   // to run are the (g, m0) pairs tiles[0..2*ntiles) with *ntiles on the device;
