@@ -27,6 +27,8 @@
 //    DMA wait tracking sees which slot each read touches.
 //  * generic (fp32, or K not a multiple of 64): two LDS stages, chunks past K
 //    fetched from a 16-byte zero block.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -577,6 +579,67 @@ __device__ __forceinline__ void dma1(uint32_t m0v, const void* sb, uint32_t voff
                : "m0");
 }
 
+// bf16 epilogue of the persistent pipelined ring, in two halves through
+// slots 3 and 4 (the next tile's first slices are already landing in slots
+// 0-2): half h holds accumulator rows i = 2h, 2h+1 of every wave, i.e. tile
+// rows wm*128 + 64h .. +63, at staging row wm*64 + (i-2h)*32 + lr.
+template <int NWM, int NWN, int EPI>
+__device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileId& t, const floatx16 (&acc)[4][2],
+                                                   int wave, int lane, char* stage) {
+  constexpr int FM = 4, FN = 2, BN = NWN * FN * 32, NT = NWM * NWN * kWave;
+  constexpr int OCH = BN / 8;       // 16-byte chunks per output row
+  constexpr int RPP = NT / OCH;     // staging rows per store pass
+  constexpr int SROWS = NWM * 64;   // staging rows per half
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int tid = threadIdx.x;
+  float4 bias[FN][4];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = t.n0 + wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
+      bias[j][q] = (p.bias && n < p.N) ? *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + n)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * h + ii;
+      const int sr = wm * 64 + ii * 32 + lr;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
+          float v[4] = {acc[i][j][4 * q + 0] + bias[j][q].x, acc[i][j][4 * q + 1] + bias[j][q].y,
+                        acc[i][j][4 * q + 2] + bias[j][q].z, acc[i][j][4 * q + 3] + bias[j][q].w};
+          epi4<EPI, bf16>(p, t, 0, 0, 1.f, v);
+          const int phys = (nl >> 3) ^ (sr & (OCH - 1));
+          store_from_f32<bf16, 4>(reinterpret_cast<bf16*>(stage + sr * (BN * 2) + phys * 16 + (nl & 7) * 2), v);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < SROWS / RPP; ++pass) {
+      const int sr = pass * RPP + tid / OCH;
+      const int c = tid % OCH;
+      const uint4 val = *reinterpret_cast<const uint4*>(stage + sr * (BN * 2) + ((c ^ (sr & (OCH - 1))) * 16));
+      const int m = t.m0 + (sr / 64) * 128 + h * 64 + (sr % 64);
+      if (m < t.Mg && t.n0 + c * 8 < p.N)
+        *reinterpret_cast<uint4*>((bf16*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + t.n0 + c * 8) =
+            val;
+    }
+    __syncthreads();  // staging is free again
+  }
+}
+
+// Persistent: each workgroup walks tiles v = blockIdx.x, + gridDim.x, ...
+// (gridDim.x a multiple of 8, so every tile of a workgroup runs on its XCD,
+// and at any time the workgroups of one XCD hold consecutive logical tiles).
+// The next tile's A_0, W_0, A_1 are issued before this tile's epilogue, so
+// they land while it runs; its W_1 follows once the staging slot is free.
 template <int NWM, int NWN, int EPI>
 __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
   constexpr int FM = 4, FN = 2;
@@ -585,39 +648,67 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
   constexpr int A_DMA = RG::A_DMA, B_DMA = RG::B_DMA;
   constexpr uint32_t SLOTB = RG::SLOT * 16;  // bytes per slot
   static_assert(B_DMA == 4 && (A_DMA == 4 || A_DMA == 8), "DMA ops come in blocks of four");
-  static_assert(BM * BN * 2 <= 5 * (int)SLOTB, "staged output tile must fit in the ring");
+  static_assert(BM / 2 * BN * 2 <= 2 * (int)SLOTB, "half the staged output tile must fit in two slots");
 
   __shared__ uint4 lds[5 * RG::SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  TileId t;
-  tile_id<false, BM, BN>(p, t);
+  const int ntile = p.G * p.tiles_m * p.tiles_n;
+  int v = blockIdx.x;
+  if (v >= ntile) return;
+
+  // logical tile of virtual id v: consecutive ids of one XCD walk the M tiles
+  // of one N column first, so concurrently running tiles share panels
+  auto tile_of = [&](int vv, TileId& t) {
+    const int lid = xcd_remap(vv, ntile);
+    const int per = p.tiles_m * p.tiles_n;
+    t.g = lid / per;
+    const int r = lid - t.g * per;
+    const int tn = r / p.tiles_m;
+    t.m0 = (r - tn * p.tiles_m) * BM;
+    t.n0 = tn * BN;
+    t.row_base = 0;
+    t.Mg = p.M;
+  };
 
   const int K = p.K;
   const int nk = K / 64;
-  const char* Ab = (const char*)p.A + (long long)(t.g / p.a_gdiv) * p.a_gs * 2;
-  const char* Bb = (const char*)p.W + (long long)t.g * p.b_gs * 2;
-  // per DMA op: 32-bit byte offset of this lane's 16-byte chunk from the
-  // operand base (the host checks that every offset fits)
-  uint32_t va[A_DMA], vw[B_DMA];
-#pragma unroll
-  for (int i = 0; i < A_DMA; ++i) {
-    const int row = 8 * (wave + i * NW) + (lane >> 3);
-    const int m = min(t.m0 + row, t.Mg - 1);  // rows past the end re-read the last row
-    va[i] = (uint32_t)(((long long)m * p.a_rs + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
-  }
-#pragma unroll
-  for (int i = 0; i < B_DMA; ++i) {
-    const int row = 8 * (wave + i * NW) + (lane >> 3);
-    const int n = min(t.n0 + row, p.N - 1);
-    vw[i] = (uint32_t)(((long long)n * K + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
-  }
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   auto slot = [&](int j) -> uint32_t { return lds0 + (uint32_t)(j % 5) * SLOTB; };
-  auto kbase = [&](const char* base, int kt) -> const void* { return base + (long long)min(kt, nk - 1) * 128; };
   const uint32_t wof = (uint32_t)wave * 1024;
+
+  // per tile: operand bases and, per DMA op, the 32-bit byte offset of this
+  // lane's 16-byte chunk (the host checks that every offset fits)
+  const char* Ab;
+  const char* Bb;
+  uint32_t va[A_DMA], vw[B_DMA];
+  auto setup = [&](const TileId& t) {
+    Ab = (const char*)p.A + (long long)(t.g / p.a_gdiv) * p.a_gs * 2;
+    Bb = (const char*)p.W + (long long)t.g * p.b_gs * 2;
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+      const int row = 8 * (wave + i * NW) + (lane >> 3);
+      const int m = min(t.m0 + row, t.Mg - 1);  // rows past the end re-read the last row
+      va[i] = (uint32_t)(((long long)m * p.a_rs + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+      const int row = 8 * (wave + i * NW) + (lane >> 3);
+      const int n = min(t.n0 + row, p.N - 1);
+      vw[i] = (uint32_t)(((long long)n * K + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
+    }
+  };
+  auto kbase = [&](const char* base, int kt) -> const void* { return base + (long long)min(kt, nk - 1) * 128; };
+  auto issue_a = [&](int s, int kt) {
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) dma1(slot(s) + wof + i * NW * 1024, kbase(Ab, kt), va[i]);
+  };
+  auto issue_w = [&](int s, int kt) {
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) dma1(slot(s) + wof + i * NW * 1024, kbase(Bb, kt), vw[i]);
+  };
 
   // fragment address of lane for k-step kk: row * 128 + swizzled chunk
   const int wm = wave / NWN, wn = wave % NWN;
@@ -630,51 +721,67 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
     ob[kk] = (uint32_t)(wn * FN * 32 + lr) * 128 + ch;
   }
 
+  TileId t;
+  tile_of(v, t);
+  setup(t);
+  // first tile's A_0 -> 0, W_0 -> 1, A_1 -> 2
+  issue_a(0, 0);
+  issue_w(1, 0);
+  issue_a(2, 1);
+
   floatx16 acc[FM][FN];
+  for (;;) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  // prologue: A_0 -> 0, W_0 -> 1, A_1 -> 2, W_1 -> 3
-#pragma unroll
-  for (int i = 0; i < A_DMA; ++i) dma1(slot(0) + wof + i * NW * 1024, kbase(Ab, 0), va[i]);
-#pragma unroll
-  for (int i = 0; i < B_DMA; ++i) dma1(slot(1) + wof + i * NW * 1024, kbase(Bb, 0), vw[i]);
-#pragma unroll
-  for (int i = 0; i < A_DMA; ++i) dma1(slot(2) + wof + i * NW * 1024, kbase(Ab, 1), va[i]);
-#pragma unroll
-  for (int i = 0; i < B_DMA; ++i) dma1(slot(3) + wof + i * NW * 1024, kbase(Bb, 1), vw[i]);
-  wait_vmcnt<A_DMA + B_DMA>();  // A_0 and W_0 landed
-  __builtin_amdgcn_s_barrier();
-  Frags f0, f1;
-  read_frags(f0, slot(0) + oa[0], slot(1) + ob[0]);
-
-  for (int k = 0; k < nk; ++k) {
-    const uint32_t sA = slot(2 * k), sW = slot(2 * k + 1);
-    // A_{k+2} into the slot of W_{k-1}
-    const uint32_t dA = slot(2 * k + 4) + wof;
-    kstep_dma<NW * 1024>(acc, f0, f1, sA + oa[1], sW + ob[1], dA, kbase(Ab, k + 2), va);
-    if constexpr (A_DMA == 8)
-      kstep_dma<NW * 1024>(acc, f1, f0, sA + oa[2], sW + ob[2], dA + 4 * NW * 1024, kbase(Ab, k + 2), va + 4);
-    else
-      kstep(acc, f1, f0, sA + oa[2], sW + ob[2]);
-    kstep(acc, f0, f1, sA + oa[3], sW + ob[3]);
-    // everything but A_{k+2} has landed: A_{k+1} and W_{k+1}
-    wait_vmcnt<A_DMA>();
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    // W_1 -> 3; then all but W_1 has landed (A_0, W_0, A_1 and any stores)
+    issue_w(3, 1);
+    wait_vmcnt<B_DMA>();
     __builtin_amdgcn_s_barrier();
-    // stage k's slots are free: W_{k+2} into A_k's; read stage k+1's first fragments
-    kstep_dma<NW * 1024>(acc, f1, f0, slot(2 * k + 2) + oa[0], slot(2 * k + 3) + ob[0], sA + wof, kbase(Bb, k + 2),
-                         vw);
-  }
-  wait_vmcnt<0>();  // no DMA may land in LDS after this point
-  // the last MFMAs' results are read by ordinary code from here on
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t" ::);
+    Frags f0, f1;
+    read_frags(f0, slot(0) + oa[0], slot(1) + ob[0]);
 
-  ring_epilogue<NWM, NWN, FM, FN, EPI>(p, t, acc, wave, lane,
-                                       [&](int ml) -> char* { return (char*)lds + ml * (BN * 2); });
+    for (int k = 0; k < nk; ++k) {
+      const uint32_t sA = slot(2 * k), sW = slot(2 * k + 1);
+      // A_{k+2} into the slot of W_{k-1}
+      const uint32_t dA = slot(2 * k + 4) + wof;
+      kstep_dma<NW * 1024>(acc, f0, f1, sA + oa[1], sW + ob[1], dA, kbase(Ab, k + 2), va);
+      if constexpr (A_DMA == 8)
+        kstep_dma<NW * 1024>(acc, f1, f0, sA + oa[2], sW + ob[2], dA + 4 * NW * 1024, kbase(Ab, k + 2), va + 4);
+      else
+        kstep(acc, f1, f0, sA + oa[2], sW + ob[2]);
+      kstep(acc, f0, f1, sA + oa[3], sW + ob[3]);
+      // everything but A_{k+2} has landed: A_{k+1} and W_{k+1}
+      wait_vmcnt<A_DMA>();
+      __builtin_amdgcn_s_barrier();
+      // stage k's slots are free: W_{k+2} into A_k's; read stage k+1's first fragments
+      kstep_dma<NW * 1024>(acc, f1, f0, slot(2 * k + 2) + oa[0], slot(2 * k + 3) + ob[0], sA + wof,
+                           kbase(Bb, k + 2), vw);
+    }
+    wait_vmcnt<0>();  // no DMA may land in LDS after this point
+    // the last MFMAs' results are read by ordinary code from here on
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t" ::);
+    __syncthreads();  // every wave is past its last operand read
+
+    const TileId cur = t;
+    v += gridDim.x;
+    const bool more = v < ntile;
+    if (more) {
+      tile_of(v, t);
+      setup(t);
+      issue_a(0, 0);
+      issue_w(1, 0);
+      issue_a(2, 1);
+    }
+    if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias)
+      pipe_epilogue_bf16<NWM, NWN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
+    else
+      store_direct<bf16, FM, FN, EPI>(p, cur, acc, wm, wn, lr, lh);
+    if (!more) break;
+  }
 }
 
 // ===========================================================================
@@ -695,6 +802,19 @@ constexpr int kNumCfgs = 4;
 constexpr int kMoeCfg = 2;
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// compute units of the current device (cached per device)
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 int choose_cfg(const GemmArgs& a) {
   if (a.tile_cfg >= 0 && a.tile_cfg < kNumCfgs) return a.tile_cfg;
@@ -756,11 +876,15 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
       const bool fits = ((long long)(a.M - 1) * a.a_rs + a.K) * 2 < (1LL << 32) &&
                         ((long long)(a.N - 1) * a.K + a.K) * 2 < (1LL << 32) && a.a_gdiv == 1 && !a.a_rowidx;
       if (ring && fits && a.pipe != 0) {
+        // persistent: one workgroup per CU (the ring takes all of LDS), a
+        // multiple of 8 of them so each stays on its XCD
+        const int cus = device_cus();
+        const dim3 grid2(grid.x <= (unsigned)cus ? grid.x : (unsigned)(cus / 8 * 8 > 0 ? cus / 8 * 8 : cus));
         const dim3 block(NWM * NWN * kWave);
         switch (a.epi) {
-          case kEpiBiasGelu: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasGelu>), grid, block, 0, s, p); break;
-          case kEpiBias: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBias>), grid, block, 0, s, p); break;
-          case kEpiBiasF32: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasF32>), grid, block, 0, s, p); break;
+          case kEpiBiasGelu: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasGelu>), grid2, block, 0, s, p); break;
+          case kEpiBias: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBias>), grid2, block, 0, s, p); break;
+          case kEpiBiasF32: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasF32>), grid2, block, 0, s, p); break;
           default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
