@@ -74,27 +74,25 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 // ---------------------------------------------------------------------------
-// GELU, exact form x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), with erf from
-// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
-//   erf(a) = 1 - (c1 t + c2 t^2 + c3 t^3 + c4 t^4 + c5 t^5) exp(-a^2),
-//   t = 1 / (1 + p a),  a >= 0,  |error| <= 1.5e-7,
-// odd in a.  Two transcendental ops (rcp, exp2) and a 5-term Horner sum.
-
-__device__ __forceinline__ float erf_as7126(float x) {
-  const float a = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * a);
-  float y = 1.061405429f;
-  y = y * t - 1.453152027f;
-  y = y * t + 1.421413741f;
-  y = y * t - 0.284496736f;
-  y = y * t + 0.254829592f;
-  y = y * t;
-  const float e = __builtin_amdgcn_exp2f(-a * a * 1.4426950408889634f);
-  return copysignf(1.0f - y * e, x);
-}
+// GELU, exact form x * Phi(x) with Phi the standard normal CDF.  Written as
+//   GELU(x) = max(x, 0) - |x| Phi(-|x|)
+// (for x >= 0, x Phi(x) = x - x Phi(-x); for x < 0 it is x Phi(-|x|)), with the
+// tail Phi(-a) = erfc(a / sqrt 2) / 2 from Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26:
+//   erfc(z) = (c1 t + c2 t^2 + c3 t^3 + c4 t^4 + c5 t^5) exp(-z^2),
+//   t = 1 / (1 + p z),  z >= 0,  |error| <= 1.5e-7.
+// The coefficients below are c_i / 2 and p / sqrt 2; exp(-a^2 / 2) is
+// exp2(-a^2 log2(e) / 2).  Eleven ALU ops and two transcendental ones.
 
 __device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752f));
+  const float a = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(a, 0.23164188826636f, 1.0f));  // p / sqrt 2, p = 0.3275911
+  float y = fmaf(0.5307027145f, t, -0.7265760135f);
+  y = fmaf(y, t, 0.7107068705f);
+  y = fmaf(y, t, -0.142248368f);
+  y = fmaf(y, t, 0.127414796f);  // Phi(-a) = t y e
+  const float e = __builtin_amdgcn_exp2f((x * x) * -0.7213475204444817f);
+  return fmaf(-(a * t) * y, e, fmaxf(x, 0.0f));
 }
 
 // ---------------------------------------------------------------------------
