@@ -103,7 +103,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", help="workload (c3 is the benchmarked one)")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="samples in the oracle leg")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="samples in the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-launch HIP events")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
