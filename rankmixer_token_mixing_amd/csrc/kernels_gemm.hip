@@ -635,6 +635,57 @@ __device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileI
   }
 }
 
+// fp32 epilogue of the persistent pipelined ring, in four quarters through
+// slots 3 and 4: quarter i holds accumulator row block i of every wave, tile
+// rows wm*128 + 32i + lr at staging row wm*32 + lr, BN*4 bytes per row in
+// 16-byte chunks XOR-swizzled by (row mod 16); each store writes a whole row.
+template <int NWM, int NWN, int EPI>
+__device__ __forceinline__ void pipe_epilogue_f32(const KParams& p, const TileId& t, const floatx16 (&acc)[4][2],
+                                                  int wave, int lane, char* stage) {
+  constexpr int FM = 4, FN = 2, BN = NWN * FN * 32, NT = NWM * NWN * kWave;
+  constexpr int OCH = BN / 4;      // 16-byte chunks per output row
+  constexpr int RPP = NT / OCH;    // staging rows per store pass
+  constexpr int SROWS = NWM * 32;  // staging rows per quarter
+  static_assert(SROWS % RPP == 0, "store passes");
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int tid = threadIdx.x;
+  float4 bias[FN][4];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = t.n0 + wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
+      bias[j][q] = (p.bias && n < p.N) ? *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + n)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int sr = wm * 32 + lr;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cix = (wn * FN * 32 + j * 32 + 8 * q + 4 * lh) >> 2;
+        const float4 v = make_float4(acc[i][j][4 * q + 0] + bias[j][q].x, acc[i][j][4 * q + 1] + bias[j][q].y,
+                                     acc[i][j][4 * q + 2] + bias[j][q].z, acc[i][j][4 * q + 3] + bias[j][q].w);
+        *reinterpret_cast<float4*>(stage + sr * (BN * 4) + ((cix ^ (sr & 15)) * 16)) = v;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < SROWS / RPP; ++pass) {
+      const int r = pass * RPP + tid / OCH;
+      const int c = tid % OCH;
+      const uint4 val = *reinterpret_cast<const uint4*>(stage + r * (BN * 4) + ((c ^ (r & 15)) * 16));
+      const int m = t.m0 + (r / 32) * 128 + i * 32 + (r % 32);
+      if (m < t.Mg && t.n0 + c * 4 < p.N)
+        *reinterpret_cast<uint4*>((float*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + t.n0 + c * 4) =
+            val;
+    }
+    __syncthreads();  // staging is free again
+  }
+}
+
 // Persistent: each workgroup walks tiles v = blockIdx.x, + gridDim.x, ...
 // (gridDim.x a multiple of 8, so every tile of a workgroup runs on its XCD,
 // and at any time the workgroups of one XCD hold consecutive logical tiles).
@@ -648,7 +699,8 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
   constexpr int A_DMA = RG::A_DMA, B_DMA = RG::B_DMA;
   constexpr uint32_t SLOTB = RG::SLOT * 16;  // bytes per slot
   static_assert(B_DMA == 4 && (A_DMA == 4 || A_DMA == 8), "DMA ops come in blocks of four");
-  static_assert(BM / 2 * BN * 2 <= 2 * (int)SLOTB, "half the staged output tile must fit in two slots");
+  static_assert(BM / 2 * BN * 2 <= 2 * (int)SLOTB && BM / 4 * BN * 4 <= 2 * (int)SLOTB,
+                "a staged part of the output tile must fit in two slots");
 
   __shared__ uint4 lds[5 * RG::SLOT];
 
@@ -779,7 +831,7 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
     if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias)
       pipe_epilogue_bf16<NWM, NWN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
     else
-      store_direct<bf16, FM, FN, EPI>(p, cur, acc, wm, wn, lr, lh);
+      pipe_epilogue_f32<NWM, NWN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
     if (!more) break;
   }
 }
