@@ -73,6 +73,36 @@ def committed_traffic(config: str, kernel: str):
     return k.get("hbm_bytes_per_launch")
 
 
+def block0_protocol(bd, blocks, x0, B: int, flop_block, peak: float) -> dict:
+    """One rm_block_fwd on block 0 of the workload: 10 warm-up calls, then 3
+    groups of 30 timed calls (events on the launching stream), the median of
+    the three group means."""
+    import statistics
+    import torch
+    y = torch.empty_like(x0)
+    for _ in range(10):
+        bd.rm_block_fwd(x0, blocks[0], out=y)
+    means = []
+    for _ in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(30):
+            bd.rm_block_fwd(x0, blocks[0], out=y)
+        e1.record()
+        e1.synchronize()
+        means.append(e0.elapsed_time(e1) / 30)
+    ms = statistics.median(means)
+    rec = {"ms": round(ms, 4), "samples_per_s": round(B / (ms * 1e-3), 1),
+           "group_means_ms": [round(m, 4) for m in means],
+           "protocol": "rm_block_fwd on block 0: 10 warm-up calls, 3 groups of 30 timed calls, median of group means"}
+    if flop_block:
+        tf = flop_block / (ms * 1e-3) / 1e12
+        rec["tflops"] = round(tf, 1)
+        rec["frac_of_bf16_peak"] = round(tf / peak, 4)
+    return rec
+
+
 def cpu_baseline(inputs, L: int, n_rows: int) -> dict:
     import numpy as np
     from oracle import rankmixer_oracle as orc
@@ -216,6 +246,9 @@ def main() -> int:
 
     block_flops = pm.block_flops(cfg.B, cfg.T, cfg.D, hidden) if not cfg.E else None
     step_tflops = block_flops * L / (ms_step * 1e-3) / 1e12 if block_flops else None
+    x0 = bd.rm_tokenize_padsplit(inp, cfg.T, cfg.D, out_dtype=dtype) if cfg.F else inp
+    block0 = block0_protocol(bd, blocks, x0, cfg.B, block_flops, pm.PEAK_BF16_TFLOPS)
+    log(f"block 0 alone: {block0['ms']} ms")
 
     rec = {
         "metric": METRIC,
@@ -240,6 +273,7 @@ def main() -> int:
         "step_tflops": round(step_tflops, 1) if step_tflops else None,
         "step_frac_of_bf16_peak": round(step_tflops / pm.PEAK_BF16_TFLOPS, 4) if step_tflops else None,
         "kernels": kernels,
+        "block0_fwd": block0,
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample ...")

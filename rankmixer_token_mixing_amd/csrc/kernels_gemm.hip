@@ -583,10 +583,10 @@ __device__ __forceinline__ void dma1(uint32_t m0v, const void* sb, uint32_t voff
 // slots 3 and 4 (the next tile's first slices are already landing in slots
 // 0-2): half h holds accumulator rows i = 2h, 2h+1 of every wave, i.e. tile
 // rows wm*128 + 64h .. +63, at staging row wm*64 + (i-2h)*32 + lr.
-template <int NWM, int NWN, int EPI>
-__device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileId& t, const floatx16 (&acc)[4][2],
+template <int NWM, int NWN, int FN, int EPI>
+__device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileId& t, const floatx16 (&acc)[4][FN],
                                                    int wave, int lane, char* stage) {
-  constexpr int FM = 4, FN = 2, BN = NWN * FN * 32, NT = NWM * NWN * kWave;
+  constexpr int BN = NWN * FN * 32, NT = NWM * NWN * kWave;
   constexpr int OCH = BN / 8;       // 16-byte chunks per output row
   constexpr int RPP = NT / OCH;     // staging rows per store pass
   constexpr int SROWS = NWM * 64;   // staging rows per half
@@ -639,10 +639,10 @@ __device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileI
 // slots 3 and 4: quarter i holds accumulator row block i of every wave, tile
 // rows wm*128 + 32i + lr at staging row wm*32 + lr, BN*4 bytes per row in
 // 16-byte chunks XOR-swizzled by (row mod 16); each store writes a whole row.
-template <int NWM, int NWN, int EPI>
-__device__ __forceinline__ void pipe_epilogue_f32(const KParams& p, const TileId& t, const floatx16 (&acc)[4][2],
+template <int NWM, int NWN, int FN, int EPI>
+__device__ __forceinline__ void pipe_epilogue_f32(const KParams& p, const TileId& t, const floatx16 (&acc)[4][FN],
                                                   int wave, int lane, char* stage) {
-  constexpr int FM = 4, FN = 2, BN = NWN * FN * 32, NT = NWM * NWN * kWave;
+  constexpr int FM = 4, BN = NWN * FN * 32, NT = NWM * NWN * kWave;
   constexpr int OCH = BN / 4;      // 16-byte chunks per output row
   constexpr int RPP = NT / OCH;    // staging rows per store pass
   constexpr int SROWS = NWM * 32;  // staging rows per quarter
@@ -829,9 +829,9 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
       issue_a(2, 1);
     }
     if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias)
-      pipe_epilogue_bf16<NWM, NWN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
+      pipe_epilogue_bf16<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
     else
-      pipe_epilogue_f32<NWM, NWN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
+      pipe_epilogue_f32<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
     if (!more) break;
   }
 }
