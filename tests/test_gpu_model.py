@@ -146,3 +146,22 @@ def test_widest_supported_rows():
     assert rel_l2_rows(host(y), ref) <= TOL["bf16"]
     m = bd.rm_token_mix(bd.to_device(x))
     np.testing.assert_array_equal(host(m), orc.token_mix(x))
+
+
+def test_ragged_tiles_of_the_pipelined_products():
+    # B = 1100 rows (last M tile holds 76), hidden 1472 (last N tile of the W1
+    # product holds 192 columns): the W1 product takes 256x256 tiles and the
+    # W2 product 256x128 tiles of the hand-scheduled persistent kernel, each
+    # with 960 tiles (3.75 rounds of one workgroup per CU)
+    from rankmixer_token_mixing_amd import binding as bd
+    cfg = si.Config("ragged-pipe", B=1100, T=32, D=768, L=1, dtype="bf16", k=2, bias_var=0.01)
+    inputs = si.make_inputs(cfg, seed=11)
+    blk = dict(inputs["blocks"][0])
+    blk["w1"] = blk["w1"][:, :1472, :].copy()
+    blk["b1"] = blk["b1"][:, :1472].copy()
+    blk["w2"] = np.ascontiguousarray(blk["w2"][:, :, :1472])
+    blocks = bd.upload_blocks([blk])
+    y = host(bd.rm_block_fwd(bd.to_device(inputs["x"]), blocks[0]))
+    rows = np.unique(np.concatenate([si.random_rows(cfg.B, 24, seed=3), np.arange(1024, 1100, 7), [1099]]))
+    ref = orc.block_fwd(inputs["x"][rows], blk)
+    assert rel_l2_rows(y[rows], ref) <= TOL["bf16"]
