@@ -163,7 +163,7 @@ struct Carver {
   }
 };
 
-constexpr int kMoeTileM = 128;  // M tile of the ragged expert products (see kernels_gemm.hip)
+constexpr int kMoeTileM = 256;  // M tile of the ragged expert products (see kernels_gemm.hip)
 
 struct PffnWs {
   void* H;

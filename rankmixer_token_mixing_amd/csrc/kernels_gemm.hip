@@ -662,13 +662,20 @@ __device__ __forceinline__ void pipe_epilogue_f32(const KParams& p, const TileId
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int sr = wm * 32 + lr;
+    float scale = 1.f;  // kEpiBiasScaleF32: the row's gate
+    if constexpr (EPI == kEpiBiasScaleF32) {
+      const int m = t.m0 + wm * 128 + i * 32 + lr;
+      scale = m < t.Mg ? p.rowscale[t.row_base + m] : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cix = (wn * FN * 32 + j * 32 + 8 * q + 4 * lh) >> 2;
-        const float4 v = make_float4(acc[i][j][4 * q + 0] + bias[j][q].x, acc[i][j][4 * q + 1] + bias[j][q].y,
-                                     acc[i][j][4 * q + 2] + bias[j][q].z, acc[i][j][4 * q + 3] + bias[j][q].w);
+        const float4 v = make_float4((acc[i][j][4 * q + 0] + bias[j][q].x) * scale,
+                                     (acc[i][j][4 * q + 1] + bias[j][q].y) * scale,
+                                     (acc[i][j][4 * q + 2] + bias[j][q].z) * scale,
+                                     (acc[i][j][4 * q + 3] + bias[j][q].w) * scale);
         *reinterpret_cast<float4*>(stage + sr * (BN * 4) + ((cix ^ (sr & 15)) * 16)) = v;
       }
     __syncthreads();
@@ -691,7 +698,10 @@ __device__ __forceinline__ void pipe_epilogue_f32(const KParams& p, const TileId
 // and at any time the workgroups of one XCD hold consecutive logical tiles).
 // The next tile's A_0, W_0, A_1 are issued before this tile's epilogue, so
 // they land while it runs; its W_1 follows once the staging slot is free.
-template <int NWM, int NWN, int EPI>
+// RAGGED: the tiles are the device-side (group, m0) list times the N tiles,
+// group g's rows start at row_off[g]; AIDX: A row m of group g is row
+// a_rowidx[row_off[g] + m] of that group's A.
+template <int NWM, int NWN, int EPI, bool RAGGED, bool AIDX>
 __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
   constexpr int FM = 4, FN = 2;
   typedef Ring<NWM, NWN, FM, FN> RG;
@@ -707,22 +717,32 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int ntile = p.G * p.tiles_m * p.tiles_n;
+  const int ntile = RAGGED ? (*p.ntiles) * p.tiles_n : p.G * p.tiles_m * p.tiles_n;
   int v = blockIdx.x;
   if (v >= ntile) return;
 
   // logical tile of virtual id v: consecutive ids of one XCD walk the M tiles
-  // of one N column first, so concurrently running tiles share panels
+  // of one N column first (dense) or the N tiles of one (group, m0) (ragged),
+  // so concurrently running tiles share operand panels
   auto tile_of = [&](int vv, TileId& t) {
     const int lid = xcd_remap(vv, ntile);
-    const int per = p.tiles_m * p.tiles_n;
-    t.g = lid / per;
-    const int r = lid - t.g * per;
-    const int tn = r / p.tiles_m;
-    t.m0 = (r - tn * p.tiles_m) * BM;
-    t.n0 = tn * BN;
-    t.row_base = 0;
-    t.Mg = p.M;
+    if constexpr (RAGGED) {
+      const int slot_ = lid / p.tiles_n;
+      t.n0 = (lid - slot_ * p.tiles_n) * BN;
+      t.g = p.tiles[2 * slot_];
+      t.m0 = p.tiles[2 * slot_ + 1];
+      t.row_base = p.row_off[t.g];
+      t.Mg = p.row_off[t.g + 1] - (int)t.row_base;
+    } else {
+      const int per = p.tiles_m * p.tiles_n;
+      t.g = lid / per;
+      const int r = lid - t.g * per;
+      const int tn = r / p.tiles_m;
+      t.m0 = (r - tn * p.tiles_m) * BM;
+      t.n0 = tn * BN;
+      t.row_base = 0;
+      t.Mg = p.M;
+    }
   };
 
   const int K = p.K;
@@ -743,7 +763,8 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
     for (int i = 0; i < A_DMA; ++i) {
       const int row = 8 * (wave + i * NW) + (lane >> 3);
       const int m = min(t.m0 + row, t.Mg - 1);  // rows past the end re-read the last row
-      va[i] = (uint32_t)(((long long)m * p.a_rs + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
+      const long long r = AIDX ? (long long)p.a_rowidx[t.row_base + m] : t.row_base + m;
+      va[i] = (uint32_t)((r * p.a_rs + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
     }
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i) {
@@ -851,7 +872,7 @@ constexpr TileCfg kCfgs[] = {
     {2, 2, 1, 1},  // 3:  64 x  64, 4 waves of 32 x 32
 };
 constexpr int kNumCfgs = 4;
-constexpr int kMoeCfg = 2;
+constexpr int kMoeCfg = 0;  // ragged expert products: 256 x 256 tiles
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
@@ -911,42 +932,54 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   constexpr int BM = NWM * FM * 32, BN = NWN * FN * 32;
   const KParams p = make_params(a, BM, BN);
   const bool ring = a.dt == kBF16 && a.K % 64 == 0;
-  if (a.row_off) {
-    const dim3 grid((unsigned)((long long)a.max_mtiles * p.tiles_n));
-    if (grid.x == 0) return hipSuccess;
-    if (a.epi == kEpiBiasGelu && a.a_rowidx)
-      launch_one<NWM, NWN, FM, FN, kEpiBiasGelu, true, true>(a, p, grid, s, ring);
-    else if (a.epi == kEpiBiasScaleF32 && !a.a_rowidx)
-      launch_one<NWM, NWN, FM, FN, kEpiBiasScaleF32, true, false>(a, p, grid, s, ring);
-    else
-      return hipErrorInvalidValue;
-  } else {
-    const dim3 grid((unsigned)((long long)a.G * p.tiles_m * p.tiles_n));
-    if (grid.x == 0) return hipSuccess;
-    if constexpr (FM == 4 && FN == 2) {
-      // the pipelined ring addresses operands by 32-bit byte offsets
-      const bool fits = ((long long)(a.M - 1) * a.a_rs + a.K) * 2 < (1LL << 32) &&
-                        ((long long)(a.N - 1) * a.K + a.K) * 2 < (1LL << 32) && a.a_gdiv == 1 && !a.a_rowidx;
-      if (ring && fits && a.pipe != 0) {
-        // persistent: one workgroup per CU (the ring takes all of LDS), a
-        // multiple of 8 of them so each stays on its XCD
-        const int cus = device_cus();
-        const dim3 grid2(grid.x <= (unsigned)cus ? grid.x : (unsigned)(cus / 8 * 8 > 0 ? cus / 8 * 8 : cus));
-        const dim3 block(NWM * NWN * kWave);
+  const bool ragged = a.row_off != nullptr;
+  const dim3 grid(ragged ? (unsigned)((long long)a.max_mtiles * p.tiles_n)
+                         : (unsigned)((long long)a.G * p.tiles_m * p.tiles_n));
+  if (grid.x == 0) return hipSuccess;
+  if (ragged && !((a.epi == kEpiBiasGelu && a.a_rowidx) || (a.epi == kEpiBiasScaleF32 && !a.a_rowidx)))
+    return hipErrorInvalidValue;
+  if (!ragged && !(a.epi == kEpiBiasGelu || a.epi == kEpiBias || a.epi == kEpiBiasF32)) return hipErrorInvalidValue;
+
+  if constexpr (FM == 4 && FN == 2) {
+    // the pipelined ring addresses operands by 32-bit byte offsets from the
+    // group's base: the largest A row index is below M (dense, gathered) or
+    // below M * G (ragged compacted rows)
+    const long long arows = ragged && !a.a_rowidx ? (long long)a.M * a.G : a.M;
+    const bool fits = ((arows - 1) * a.a_rs + a.K) * 2 < (1LL << 32) &&
+                      ((long long)(a.N - 1) * a.K + a.K) * 2 < (1LL << 32);
+    if (ring && fits && a.pipe != 0) {
+      // persistent: one workgroup per CU (the ring takes all of LDS), a
+      // multiple of 8 of them so each stays on its XCD
+      const int cus = device_cus();
+      const dim3 grid2(grid.x <= (unsigned)cus ? grid.x : (unsigned)(cus / 8 * 8 > 0 ? cus / 8 * 8 : cus));
+      const dim3 block(NWM * NWN * kWave);
+      if (ragged) {
+        if (a.a_rowidx)
+          hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasGelu, true, true>), grid2, block, 0, s, p);
+        else
+          hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasScaleF32, true, false>), grid2, block, 0, s, p);
+      } else {
         switch (a.epi) {
-          case kEpiBiasGelu: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasGelu>), grid2, block, 0, s, p); break;
-          case kEpiBias: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBias>), grid2, block, 0, s, p); break;
-          case kEpiBiasF32: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasF32>), grid2, block, 0, s, p); break;
-          default: return hipErrorInvalidValue;
+          case kEpiBiasGelu:
+            hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasGelu, false, false>), grid2, block, 0, s, p);
+            break;
+          case kEpiBias: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBias, false, false>), grid2, block, 0, s, p); break;
+          default: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasF32, false, false>), grid2, block, 0, s, p); break;
         }
-        return hipGetLastError();
       }
+      return hipGetLastError();
     }
+  }
+  if (ragged) {
+    if (a.a_rowidx)
+      launch_one<NWM, NWN, FM, FN, kEpiBiasGelu, true, true>(a, p, grid, s, ring);
+    else
+      launch_one<NWM, NWN, FM, FN, kEpiBiasScaleF32, true, false>(a, p, grid, s, ring);
+  } else {
     switch (a.epi) {
       case kEpiBiasGelu: launch_one<NWM, NWN, FM, FN, kEpiBiasGelu, false, false>(a, p, grid, s, ring); break;
       case kEpiBias: launch_one<NWM, NWN, FM, FN, kEpiBias, false, false>(a, p, grid, s, ring); break;
-      case kEpiBiasF32: launch_one<NWM, NWN, FM, FN, kEpiBiasF32, false, false>(a, p, grid, s, ring); break;
-      default: return hipErrorInvalidValue;
+      default: launch_one<NWM, NWN, FM, FN, kEpiBiasF32, false, false>(a, p, grid, s, ring); break;
     }
   }
   return hipGetLastError();
