@@ -214,7 +214,7 @@ def main() -> int:
     eb = pm.ELEM_BYTES[cfg.dtype]
     row_bytes = {  # compulsory HBM bytes per launch
         "mix_ln1": 2 * cfg.B * cfg.T * cfg.D * eb,
-        "ln2": cfg.B * cfg.T * cfg.D * (4 + 2 * eb),  # Z (fp32) and the residual S in, X' out
+        "ln2": cfg.B * cfg.T * cfg.D * 3 * eb,  # Z and the residual S in, X' out
     }
     kernels = {}
     for name, (tot_ms, n) in prof.items():

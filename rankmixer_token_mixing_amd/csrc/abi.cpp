@@ -202,7 +202,7 @@ size_t moe_ws(Carver& c, int64_t B, int T, int D, int E, int He, int dt, MoeWs* 
 
 struct BlockWs {
   void* S;
-  float* Z;
+  void* Z;  // W2 product + bias, activation dtype
   PffnWs pffn;
   MoeWs moe;
 };
@@ -210,7 +210,7 @@ size_t block_ws(Carver& c, int kind, int64_t B, int T, int D, int hidden, int E,
   BlockWs x;
   x.S = c.take((size_t)B * T * D * elem_bytes(dt));
   if (kind == RM_BLOCK_DENSE) {
-    x.Z = (float*)c.take((size_t)B * T * D * 4);
+    x.Z = c.take((size_t)B * T * D * elem_bytes(dt));
     pffn_ws(c, B, T, hidden, dt, &x.pffn);
   } else {
     x.Z = nullptr;
@@ -332,12 +332,13 @@ rm_status run_block(const void* x, const rm_block_params* p, void* xo, int64_t B
   if (p->kind == RM_BLOCK_DENSE) {
     RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(w.S, sb, sT, &p->pffn, w.pffn.H, B, T, D, hidden, dt), st), "block W1 product"));
     rm::GemmArgs a2 = ffn2_args(w.pffn.H, &p->pffn, B, T, D, hidden, dt);
-    // Z = W2 product + bias (fp32); the residual S is added inside LayerNorm 2,
-    // which streams Z anyway, instead of by loads in the product's epilogue
-    a2.epi = rm::kEpiBiasF32;
+    // Z = W2 product + bias in the activation dtype; the residual S is added
+    // inside LayerNorm 2 (fp32 arithmetic), which streams Z anyway, instead of
+    // by loads in the product's epilogue
+    a2.epi = rm::kEpiBias;
     a2.C = w.Z;
     RM_TIMED("ffn2", st, RM_HIP(rm::launch_gemm(a2, st), "block W2 product"));
-    RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows_f32(w.Z, w.S, sb, sT, T, xo, p->ln2_g, p->ln2_b, B * T, D, dt, st),
+    RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows(w.Z, w.S, sb, sT, T, xo, p->ln2_g, p->ln2_b, B * T, D, dt, st),
                                "residual + LayerNorm 2"));
     return RM_OK;
   }

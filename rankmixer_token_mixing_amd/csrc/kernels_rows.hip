@@ -160,13 +160,13 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __res
 }
 
 // ---------------------------------------------------------------------------
-// out[r,:] = LN(z[r,:] + res[r,:]) * g + beta for fp32 rows (D % 8 == 0), 8
-// floats per lane-chunk.  Row r = b * Tn + t; the residual (optional, element
-// type T) of row r starts at res + b * res_bs + t * res_ts, so a token-major
-// residual is read in place.
+// out[r,:] = LN(z[r,:] + res[r,:]) * g + beta over rows of D (D % 8 == 0), 8
+// elements per lane-chunk, fp32 arithmetic.  Row r = b * Tn + t; the residual
+// (optional) of row r starts at res + b * res_bs + t * res_ts, so a
+// token-major residual is read in place.
 
 template <typename T, int MAXI>
-__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const float* __restrict__ z,
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const T* __restrict__ z,
                                                                    const T* __restrict__ res, int64_t res_bs,
                                                                    int64_t res_ts, int Tn, T* __restrict__ out,
                                                                    const float* __restrict__ g,
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const float* 
   if (row >= rows) return;
   const int lane = lane_id();
   const int nch = D / VEC;
-  const float* zr = z + row * (int64_t)D;
+  const T* zr = z + row * (int64_t)D;
   const T* rr = res ? res + (row / Tn) * res_bs + (row % Tn) * res_ts : nullptr;
   float v[MAXI][VEC];
   float sum = 0.f;
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const float* 
   for (int i = 0; i < MAXI; ++i) {
     const int c = lane + i * kWave;
     if (c < nch) {
-      load_f32<float, VEC>(zr + c * VEC, v[i]);
+      load_f32<T, VEC>(zr + c * VEC, v[i]);
       if (rr) {
         float r[VEC];
         load_f32<T, VEC>(rr + c * VEC, r);
@@ -320,9 +320,10 @@ hipError_t mix_ln_vec(const void* x, void* so, const float* g, const float* b, i
 }
 
 template <typename T>
-hipError_t ln_rows_t(const float* z, const void* res, int64_t rbs, int64_t rts, int Tn, void* out, const float* g,
+hipError_t ln_rows_t(const void* zv, const void* res, int64_t rbs, int64_t rts, int Tn, void* out, const float* g,
                      const float* b, int64_t rows, int D, hipStream_t s) {
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
+  const T* z = (const T*)zv;
   T* o = (T*)out;
   const T* r = (const T*)res;
   if (Tn <= 0) Tn = 1;
@@ -369,8 +370,8 @@ hipError_t launch_mix_ln(const void* x, void* so, const float* g, const float* b
   }
 }
 
-hipError_t launch_ln_rows_f32(const float* z, const void* res, int64_t res_bs, int64_t res_ts, int Tn, void* out,
-                              const float* g, const float* b, int64_t rows, int D, int dt, hipStream_t s) {
+hipError_t launch_ln_rows(const void* z, const void* res, int64_t res_bs, int64_t res_ts, int Tn, void* out,
+                          const float* g, const float* b, int64_t rows, int D, int dt, hipStream_t s) {
   return dt == kBF16 ? ln_rows_t<bf16>(z, res, res_bs, res_ts, Tn, out, g, b, rows, D, s)
                      : ln_rows_t<float>(z, res, res_bs, res_ts, Tn, out, g, b, rows, D, s);
 }

@@ -25,10 +25,11 @@ hipError_t launch_token_mix(const void* x, void* y, int64_t B, int T, int D, int
 hipError_t launch_mix_ln(const void* x, void* s_out, const float* g, const float* b, int64_t B,
                          int T, int D, int dt, bool token_major, hipStream_t s);
 // out = LN(z) for fp32 rows z [rows][D]
-// out[r] = LN(z[r] + res[r]) * g + b over fp32 rows r = b*Tn + t; res (dt,
-// optional) row r at res + b * res_bs + t * res_ts elements
-hipError_t launch_ln_rows_f32(const float* z, const void* res, int64_t res_bs, int64_t res_ts, int Tn, void* out,
-                              const float* g, const float* b, int64_t rows, int D, int dt, hipStream_t s);
+// out[r] = LN(z[r] + res[r]) * g + b over rows r = b*Tn + t (fp32 math); z,
+// res (optional) and out in dtype dt, res row r at res + b * res_bs + t * res_ts
+// elements
+hipError_t launch_ln_rows(const void* z, const void* res, int64_t res_bs, int64_t res_ts, int Tn, void* out,
+                          const float* g, const float* b, int64_t rows, int D, int dt, hipStream_t s);
 // pooled[b] = mean_t x[b,t,:]; logit[b] = w . pooled[b] + c
 hipError_t launch_pool_logit(const void* x, const float* w, float c, float* pooled, float* logits,
                              int64_t B, int T, int D, int dt, hipStream_t s);
