@@ -115,6 +115,24 @@ def test_moe_block_edge_all_gates_off():
     assert rel_l2_rows(host(y), ref) <= TOL["bf16"]
 
 
+def test_moe_block_one_expert_takes_all_rows():
+    # per token one expert whose gate is on for (almost) every sample, the
+    # others off: full 256-row expert tiles, a partial last tile, and empty
+    # groups in the device-side tile list of the ragged products
+    from rankmixer_token_mixing_amd import binding as bd
+    cfg = si.Config("moe-one", B=600, T=4, D=256, L=1, dtype="bf16", E=4, He=512)
+    inputs = si.make_inputs(cfg, seed=5)
+    br = inputs["blocks"][0]["br"]
+    br[:] = -1e4
+    for t in range(cfg.T):
+        br[t, t % cfg.E] = 3.0
+    blocks = bd.upload_blocks(inputs["blocks"])
+    y = bd.rm_block_fwd(bd.to_device(inputs["x"]), blocks[0])
+    rows = si.random_rows(cfg.B, 48, seed=2)
+    ref = orc.block_fwd(inputs["x"][rows], inputs["blocks"][0])
+    assert rel_l2_rows(host(y)[rows], ref) <= TOL["bf16"]
+
+
 def test_empty_batch_returns_empty():
     from rankmixer_token_mixing_amd import binding as bd
     cfg = si.Config("empty", B=4, T=4, D=64, L=1, dtype="bf16", k=2)
