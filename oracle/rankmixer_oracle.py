@@ -91,6 +91,30 @@ def tokenize_padsplit(emb, T: int, D: int, dtype: str) -> np.ndarray:
     return round_to_bf16(X0) if dtype == "bf16" else X0.astype(np.float32).astype(np.float64)
 
 
+def tokenize_project(emb, w, b, T: int, seg: int, dtype: str) -> np.ndarray:
+    """Projection tokenizer ([WL] section "特征的Tokenization"): the
+    concatenated embedding e_input of a sample is cut evenly into T segments
+    and each segment is mapped to R^D by its own linear layer,
+    x_t = W_t seg_t + b_t.  Readings: the segments have length seg (at least
+    ceil(F / T)) and e_input is zero-padded to T*seg, as the pad-split
+    tokenizer pads; the embedding is cast to the model dtype first, as the
+    pad-split tokenizer casts; "linear layer" includes a bias.  w is
+    [T][D][seg] (W_t maps R^seg -> R^D), b is [T][D]."""
+    e = as_f64(emb)
+    B, F = e.shape
+    if F > T * seg:
+        raise ValueError("embedding longer than T*seg")
+    padded = np.zeros((B, T * seg))
+    padded[:, :F] = e
+    if dtype == "bf16":
+        padded = round_to_bf16(padded)
+    else:
+        padded = padded.astype(np.float32).astype(np.float64)
+    segs = padded.reshape(B, T, seg)
+    W = as_f64(w)
+    return np.einsum("bts,tds->btd", segs, W) + np.asarray(b, np.float64)[None, :, :]
+
+
 def token_mix(X) -> np.ndarray:
     """Multi-head token mixing with H = T ([FR] section "Token Mixing机制";
     [WL] "Multi-Head Token Mixer").  SplitHead cuts every token x_t into H

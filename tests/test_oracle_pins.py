@@ -451,3 +451,62 @@ def test_subset_rows_give_the_same_outputs():
     full = orc.model_fwd(x, [p], T, D, "f32")["x"]
     part = orc.model_fwd(x[[0, 3, 9]], [p], T, D, "f32")["x"]
     np.testing.assert_array_equal(full[[0, 3, 9]], part)
+
+
+# ---------------------------------------------------------------------------
+# projection tokenizer ([WL] "特征的Tokenization")
+
+def test_tokenize_project_hand_worked_example():
+    g = _golden("tokenize_project_T2_seg2.json")
+    x0 = orc.tokenize_project(np.array(g["emb"], np.float32), np.array(g["w"]), np.array(g["b"]), g["T"], g["seg"],
+                              "f32")
+    np.testing.assert_allclose(x0, np.array(g["x0"]), rtol=0, atol=1e-12)
+
+
+def test_tokenize_project_with_identity_weights_is_padsplit():
+    # seg = D and W_t = I, b = 0: each token is its own segment, i.e. the
+    # pad-split tokenizer (pinned above against its own layout table)
+    rng = np.random.default_rng(4)
+    B, F, T, D = 3, 37, 5, 8
+    emb = rng.standard_normal((B, F)).astype(np.float32)
+    w = np.broadcast_to(np.eye(D), (T, D, D)).copy()
+    for dt in ("f32", "bf16"):
+        x0 = orc.tokenize_project(emb, w, np.zeros((T, D)), T, D, dt)
+        np.testing.assert_array_equal(x0, orc.tokenize_padsplit(emb, T, D, dt))
+
+
+def test_tokenize_project_brute_force_loops():
+    rng = np.random.default_rng(5)
+    B, F, T, seg, D = 2, 7, 3, 3, 2
+    emb = rng.standard_normal((B, F)).astype(np.float32)
+    w = rng.standard_normal((T, D, seg))
+    b = rng.standard_normal((T, D))
+    x0 = orc.tokenize_project(emb, w, b, T, seg, "f32")
+    for bb in range(B):
+        for t in range(T):
+            for d in range(D):
+                acc = b[t, d]
+                for s in range(seg):
+                    pos = t * seg + s  # position in the concatenated embedding
+                    if pos < F:
+                        acc += w[t, d, s] * float(emb[bb, pos])
+                assert abs(x0[bb, t, d] - acc) < 1e-12
+
+
+def test_tokenize_project_tokens_see_only_their_segment():
+    rng = np.random.default_rng(6)
+    B, F, T, seg, D = 2, 40, 4, 10, 6
+    emb = rng.standard_normal((B, F)).astype(np.float32)
+    w = rng.standard_normal((T, D, seg))
+    b = rng.standard_normal((T, D))
+    x0 = orc.tokenize_project(emb, w, b, T, seg, "f32")
+    emb2 = emb.copy()
+    emb2[:, 2 * seg:3 * seg] += 1.0  # segment 2 only
+    x1 = orc.tokenize_project(emb2, w, b, T, seg, "f32")
+    changed = np.abs(x1 - x0).max(axis=(0, 2)) > 0
+    assert changed.tolist() == [False, False, True, False]
+
+
+def test_tokenize_project_rejects_overlong():
+    with pytest.raises(ValueError):
+        orc.tokenize_project(np.zeros((1, 9), np.float32), np.zeros((2, 1, 4)), np.zeros((2, 1)), 2, 4, "f32")
