@@ -123,6 +123,28 @@ typedef struct rm_model_desc {
 rm_status rm_tokenize_padsplit(const float* emb, int64_t B, int64_t F, int T, int D,
                                int out_dtype, void* x0, void* stream);
 
+/* Weights of the projection tokenizer: one linear layer per token. */
+typedef struct rm_proj_params {
+  const void* w;   /* [T][D][seg], dtype: W_t maps a segment R^seg -> R^D */
+  const float* b;  /* [T][D] */
+} rm_proj_params;
+
+/* Projection tokenizer ([WL] "特征的Tokenization": the concatenated embedding
+ * is cut evenly into T segments and each segment goes through its own linear
+ * layer into R^D).  Segments have length seg >= ceil(F/T); emb is zero-padded
+ * to T*seg and cast to dtype (round to nearest even), then
+ *   x0[b][t][:] = W_t pad(emb[b])[t*seg : (t+1)*seg] + b_t,
+ * accumulated in fp32 and rounded once to dtype.
+ *   emb: [B][F] fp32 device; x0: [B][T][D] dtype device; params as
+ *   rm_proj_params (device pointers).
+ * Workspace: rm_tokenize_project_workspace_bytes(B, T, seg, dtype) (holds the
+ * padded, cast segments).
+ * Errors: F > T*seg, seg or D not a multiple of 8 -> RM_ERR_UNSUPPORTED. */
+rm_status rm_tokenize_project(const float* emb, const rm_proj_params* p, int64_t B, int64_t F,
+                              int T, int seg, int D, int dtype, void* x0, void* ws,
+                              size_t ws_bytes, void* stream);
+size_t rm_tokenize_project_workspace_bytes(int64_t B, int T, int seg, int dtype);
+
 /* Multi-head token mixing with H = T ([FR] "Token Mixing机制"; [WL] "Multi-Head
  * Token Mixer"): SplitHead cuts token t into T heads of width d = D/T, Concat
  * joins head h of all tokens in token order:

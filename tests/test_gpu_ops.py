@@ -72,6 +72,70 @@ def test_tokenizer_bit_exact(dtype, B, F, T, D):
 
 
 # --------------------------------------------------------------------------
+# projection tokenizer
+
+
+def _proj_params(T, D, seg, dtype, seed, bias=0.1):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((T, D, seg)) / math.sqrt(seg)).astype(np.float32)
+    p = {"w": si.to_bf16_bits(w) if dtype == "bf16" else w,
+         "b": (bias * rng.standard_normal((T, D))).astype(np.float32)}
+    return p
+
+
+def _proj_dev(p):
+    from rankmixer_token_mixing_amd.binding import to_device
+    return {k: to_device(v) for k, v in p.items()}
+
+
+@pytest.mark.parametrize("dtype,B,F,T,seg,D", [
+    ("bf16", 4096, 5000, 16, 320, 320),  # the pad-split model's embedding, seg = 320 (313 rounded up to 8)
+    ("bf16", 600, 4000, 32, 128, 256),   # full k tiles, N = one tile, ragged M
+    ("bf16", 300, 1000, 8, 128, 136),    # N = 136: a partial N tile
+    ("bf16", 1, 37, 4, 16, 8),           # one sample, F not a multiple of seg
+    ("f32", 70, 300, 4, 80, 64),         # fp32, K = 80: a partial k tile
+    ("f32", 5, 5, 2, 8, 16),             # F < seg: the second segment is all padding
+])
+def test_projection_tokenizer_matches_oracle(dtype, B, F, T, seg, D):
+    from rankmixer_token_mixing_amd import binding as bd
+    rng = np.random.default_rng(F + seg)
+    emb = (rng.standard_normal((B, F)) * math.sqrt(0.1)).astype(np.float32)
+    p = _proj_params(T, D, seg, dtype, seed=B + D)
+    note(f"[gpu] rm_tokenize_project {dtype} B={B} F={F} T={T} seg={seg} D={D}")
+    x0 = host(bd.rm_tokenize_project(torch.from_numpy(emb).cuda(), _proj_dev(p), T, seg, DT[dtype]))
+    rows = si.random_rows(B, 64, seed=7)
+    ref = orc.tokenize_project(emb[rows], p["w"], p["b"], T, seg, dtype)
+    assert rel_l2_rows(x0[rows], ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_projection_tokenizer_identity_is_padsplit(dtype):
+    # W_t = I (seg = D), b = 0: every output is one exact product, so the
+    # result equals the pad-split tokenizer bit for bit
+    from rankmixer_token_mixing_amd import binding as bd
+    B, F, T, D = 260, 1000, 8, 128
+    emb = torch.from_numpy((np.random.default_rng(9).standard_normal((B, F)) * 0.3).astype(np.float32)).cuda()
+    eye = np.broadcast_to(np.eye(D, dtype=np.float32), (T, D, D)).copy()
+    p = {"w": si.to_bf16_bits(eye) if dtype == "bf16" else eye, "b": np.zeros((T, D), np.float32)}
+    x0 = bd.rm_tokenize_project(emb, _proj_dev(p), T, D, DT[dtype])
+    assert torch.equal(x0, bd.rm_tokenize_padsplit(emb, T, D, DT[dtype]))
+
+
+def test_projection_tokenizer_locality():
+    # changing the floats of segment 2 changes token 2 only
+    from rankmixer_token_mixing_amd import binding as bd
+    B, F, T, seg, D = 64, 500, 4, 128, 64
+    emb = torch.from_numpy((np.random.default_rng(2).standard_normal((B, F)) * 0.3).astype(np.float32)).cuda()
+    p = _proj_dev(_proj_params(T, D, seg, "bf16", seed=4))
+    x = bd.rm_tokenize_project(emb, p, T, seg)
+    emb2 = emb.clone()
+    emb2[:, 2 * seg:2 * seg + 40] += 1.0
+    x2 = bd.rm_tokenize_project(emb2, p, T, seg)
+    diff = (x2.float() - x.float()).abs().amax(dim=(0, 2)).cpu()
+    assert diff[2] > 0 and torch.all(diff[[0, 1, 3]] == 0)
+
+
+# --------------------------------------------------------------------------
 # per-token FFN
 
 
