@@ -46,8 +46,10 @@ KERNEL_SOURCES = {
     "ffn2": ("kernels_gemm.hip", "common.hpp"),
     "mix_ln1": ("kernels_rows.hip", "common.hpp"),
     "ln2": ("kernels_rows.hip", "common.hpp"),
+    "tokenize_proj": ("kernels_gemm.hip", "common.hpp"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_fwd_{config}_traffic.json")
+PROJ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tokenize_project_traffic.json")
 
 
 def source_sha(name: str) -> str:
@@ -55,11 +57,11 @@ def source_sha(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def committed_traffic(config: str, kernel: str):
+def committed_traffic(config: str, kernel: str, path: str = ""):
     """HBM bytes per launch of `kernel` from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary of this workload, or None when there is
     none or the kernel's sources changed since the counters were taken."""
-    path = TRAFFIC_FILE.format(config=config)
+    path = path or TRAFFIC_FILE.format(config=config)
     if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
         return None
     with open(path) as f:
@@ -127,12 +129,101 @@ def cpu_baseline(inputs, L: int, n_rows: int) -> dict:
     }
 
 
+def bench_project(args) -> int:
+    """The projection tokenizer alone: one rm_tokenize_project per step over
+    the pad-split model's embedding batch (B=4096 x 5000 fp32 -> 16 segments
+    of 320 -> [4096, 16, 320] bf16).  HBM-bound: the roofline is the
+    compulsory bytes (embedding, weights, output) over the launch time."""
+    import numpy as np
+    import torch
+    import synthetic_inputs as si
+    from rankmixer_token_mixing_amd import binding as bd
+    from rankmixer_token_mixing_amd import perfmodel as pm
+
+    w = si.PROJ_WORKLOAD
+    B, F, T, seg, D = w["B"], w["F"], w["T"], w["seg"], w["D"]
+    t0 = time.perf_counter()
+    inp = si.make_proj_inputs(B, F, T, seg, D, w["dtype"])
+    log(f"generated projection-tokenizer inputs in {time.perf_counter() - t0:.1f}s")
+    emb = bd.to_device(inp["emb"])
+    p = {"w": bd.to_device(inp["w"]), "b": bd.to_device(inp["b"])}
+    out = torch.empty((B, T, D), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        bd.rm_tokenize_project(emb, p, T, seg, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # one launch per step on torch's current stream: a HIP event pair around
+    # the timed launches on that stream gives the mean launch duration (a pair
+    # around every launch would add its own overhead to a ~30 us kernel)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    nbytes = pm.project_bytes(B, F, T, seg, D, "bf16")
+    ev_ms = e0.elapsed_time(e1)
+    kernels = {"tokenize_proj": {"avg_ms": round(ev_ms / args.steps, 5), "launches": args.steps,
+                                 "total_ms": round(ev_ms, 3)}}
+    roofline = None
+    if not args.no_profile:
+        avg_s = kernels["tokenize_proj"]["avg_ms"] * 1e-3
+        ach = nbytes / avg_s / 1e9
+        roofline = {"bound": "hbm", "kernel": "tokenize_proj", "achieved": round(ach, 1),
+                    "peak": pm.PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / pm.PEAK_HBM_GBS, 4),
+                    "bytes_per_launch": nbytes,
+                    "traffic": committed_traffic("", "tokenize_proj", PROJ_TRAFFIC_FILE)}
+        kernels["tokenize_proj"]["tflops"] = round(pm.project_flops(B, T, seg, D) / avg_s / 1e12, 1)
+    rec = {
+        "metric": "samples/sec projection tokenizer (bf16) + % of MI355X HBM roofline",
+        "value": round(B / (ms_step * 1e-3), 1),
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"projection tokenizer: B={B} embeddings of F={F} fp32 floats -> "
+                               f"T={T} segments of {seg} -> D={D} each, bf16",
+                   "B": B, "F": F, "T": T, "seg": seg, "D": D,
+                   "step": "rm_tokenize_project over the batch"},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import rankmixer_oracle as orc
+        # the oracle does the whole batch in about a second: no sampling needed
+        t0 = time.perf_counter()
+        orc.tokenize_project(inp["emb"], inp["w"], inp["b"], T, seg, "bf16")
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": B / dt, "unit": "samples/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the whole batch of {B} samples (fp64 numpy einsum, one thread, {dt:.1f} s)"}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", help="workload (c3 is the benchmarked one)")
+    ap.add_argument("--op", default="model", choices=["model", "tokenize_project"],
+                    help="model: the block stack (default); tokenize_project: the projection "
+                         "tokenizer alone on the pad-split model's embedding")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="samples in the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-launch HIP events")
@@ -160,6 +251,18 @@ def main() -> int:
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read, {n} bytes written")
+        del src, dst
+
+    if args.op == "tokenize_project":
+        return bench_project(args)
 
     cfg = si.CONFIGS[args.config]
     t0 = time.perf_counter()
@@ -174,16 +277,6 @@ def main() -> int:
 
     def step():
         bd.rm_model_fwd(model, inp, want_x=True, out=out)
-
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy probe: {n} bytes read, {n} bytes written")
-        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -137,13 +137,15 @@ typedef struct rm_proj_params {
  * accumulated in fp32 and rounded once to dtype.
  *   emb: [B][F] fp32 device; x0: [B][T][D] dtype device; params as
  *   rm_proj_params (device pointers).
- * Workspace: rm_tokenize_project_workspace_bytes(B, T, seg, dtype) (holds the
- * padded, cast segments).
+ * Workspace: rm_tokenize_project_workspace_bytes(B, F, T, seg, dtype): 0 for
+ * bf16 with F a multiple of 4 (one launch reads emb in place and rounds it to
+ * bf16 on the way into the product; ws may then be NULL), else room for the
+ * padded, cast segments.
  * Errors: F > T*seg, seg or D not a multiple of 8 -> RM_ERR_UNSUPPORTED. */
 rm_status rm_tokenize_project(const float* emb, const rm_proj_params* p, int64_t B, int64_t F,
                               int T, int seg, int D, int dtype, void* x0, void* ws,
                               size_t ws_bytes, void* stream);
-size_t rm_tokenize_project_workspace_bytes(int64_t B, int T, int seg, int dtype);
+size_t rm_tokenize_project_workspace_bytes(int64_t B, int64_t F, int T, int seg, int dtype);
 
 /* Multi-head token mixing with H = T ([FR] "Token Mixing机制"; [WL] "Multi-Head
  * Token Mixer"): SplitHead cuts token t into T heads of width d = D/T, Concat

@@ -63,7 +63,7 @@ _SIGNATURES = {
     "rm_tokenize_padsplit": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp]),
     "rm_tokenize_project": (_int, [_vp, C.POINTER(ProjParams), _i64, _i64, _int, _int, _int, _int, _vp, _vp, _sz,
                                    _vp]),
-    "rm_tokenize_project_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
+    "rm_tokenize_project_workspace_bytes": (_sz, [_i64, _i64, _int, _int, _int]),
     "rm_token_mix": (_int, [_vp, _vp, _i64, _int, _int, _int, _vp]),
     "rm_pffn_fwd": (_int, [_vp, C.POINTER(PffnParams), _vp, _i64, _int, _int, _int, _int, _vp, _sz, _vp]),
     "rm_pffn_workspace_bytes": (_sz, [_i64, _int, _int, _int, _int]),
@@ -201,16 +201,16 @@ def rm_tokenize_padsplit(emb: torch.Tensor, T: int, D: int, out_dtype=torch.bflo
     return x0
 
 
-def rm_tokenize_project(emb: torch.Tensor, p: dict, T: int, seg: int,
-                        out_dtype=torch.bfloat16) -> torch.Tensor:
+def rm_tokenize_project(emb: torch.Tensor, p: dict, T: int, seg: int, out_dtype=torch.bfloat16,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """p: {"w": [T][D][seg] out_dtype, "b": [T][D] fp32} device tensors."""
     lib = load()
     B, F = emb.shape
     D = p["w"].shape[1]
     if p["w"].dtype != out_dtype or tuple(p["w"].shape) != (T, D, seg):
         raise ValueError("w must be [T][D][seg] in the output dtype")
-    x0 = torch.empty((B, T, D), dtype=out_dtype, device=emb.device)
-    n = lib.rm_tokenize_project_workspace_bytes(B, T, seg, _DT[out_dtype])
+    x0 = torch.empty((B, T, D), dtype=out_dtype, device=emb.device) if out is None else out
+    n = lib.rm_tokenize_project_workspace_bytes(B, F, T, seg, _DT[out_dtype])
     ws = _workspace(emb.device, n)
     st = ProjParams(_p(p["w"]), _p(p["b"]))
     _check(lib.rm_tokenize_project(_p(emb), C.byref(st), B, F, T, seg, D, _DT[out_dtype], _p(x0), _p(ws),

@@ -434,16 +434,21 @@ rm_status rm_tokenize_padsplit(const float* emb, int64_t B, int64_t F, int T, in
   return ok();
 }
 
-size_t rm_tokenize_project_workspace_bytes(int64_t B, int T, int seg, int dtype) {
+// bf16 with whole float4 segments of the embedding: one fused launch that
+// reads the fp32 embedding in place; otherwise pad-split into the workspace
+// (token width seg) and one grouped product over the padded copy
+static bool project_fused(int64_t F, int dtype) { return dtype == RM_BF16 && F % 4 == 0; }
+
+size_t rm_tokenize_project_workspace_bytes(int64_t B, int64_t F, int T, int seg, int dtype) {
+  if (project_fused(F, dtype) || B <= 0) return 0;
   Carver c(nullptr);
   c.take((size_t)B * T * seg * elem_bytes(dtype));
   return c.off;
 }
 
-// Pad-split into the workspace with token width seg (zero tail, cast to the
-// activation dtype), then one grouped product over the T tokens: group t maps
-// segment rows (stride T*seg) through W_t [D][seg] into x0's token-t rows
-// (stride T*D), with b_t added in the epilogue.
+// Group t maps segment rows (stride F in place, or T*seg in the padded copy)
+// through W_t [D][seg] into x0's token-t rows (stride T*D), b_t added in the
+// epilogue.
 rm_status rm_tokenize_project(const float* emb, const rm_proj_params* p, int64_t B, int64_t F, int T, int seg,
                               int D, int dtype, void* x0, void* ws, size_t ws_bytes, void* stream) {
   RM_TRY(check_dtype(dtype));
@@ -453,25 +458,30 @@ rm_status rm_tokenize_project(const float* emb, const rm_proj_params* p, int64_t
     return fail(RM_ERR_UNSUPPORTED, "F=%lld floats do not fit in T*seg=%lld", (long long)F, (long long)T * seg);
   if (seg % 8) return fail(RM_ERR_UNSUPPORTED, "seg=%d must be a multiple of 8", seg);
   if (D % 8) return fail(RM_ERR_UNSUPPORTED, "D=%d must be a multiple of 8", D);
-  if (B * T > (int64_t)1 << 31) return fail(RM_ERR_UNSUPPORTED, "B*T too large");
+  if (B * T > (int64_t)1 << 31 || B > INT32_MAX) return fail(RM_ERR_UNSUPPORTED, "B*T too large");
   if (B == 0) return ok();
   if (!p) return fail(RM_ERR_INVALID, "params is NULL");
   RM_TRY(check_ptr(emb, "emb"));
   RM_TRY(check_ptr(p->w, "w")); RM_TRY(check_ptr(p->b, "b"));
   RM_TRY(check_ptr(x0, "x0"));
-  RM_TRY(check_ptr(ws, "ws"));
-  const size_t need = rm_tokenize_project_workspace_bytes(B, T, seg, dtype);
+  const bool fused = project_fused(F, dtype);
+  const size_t need = rm_tokenize_project_workspace_bytes(B, F, T, seg, dtype);
+  if (need) RM_TRY(check_ptr(ws, "ws"));
   if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
-  RM_TIMED("tokenize", st, RM_HIP(rm::launch_tokenize_padsplit(emb, B, F, T, seg, dtype, ws, st), "tokenize pad-split"));
   rm::GemmArgs a;
   a.dt = dtype;
   a.epi = rm::kEpiBias;
   a.M = (int)B; a.N = D; a.K = seg; a.G = T;
-  a.A = ws; a.a_gs = seg; a.a_rs = (int64_t)T * seg;
   a.W = p->w; a.b_gs = (int64_t)D * seg;
   a.C = x0; a.c_gs = D; a.c_rs = (int64_t)T * D;
   a.bias = p->b; a.bias_gs = D;
+  if (fused) {
+    a.A = emb; a.a_gs = seg; a.a_rs = F; a.a_klim = F;
+  } else {
+    RM_TIMED("tokenize", st, RM_HIP(rm::launch_tokenize_padsplit(emb, B, F, T, seg, dtype, ws, st), "tokenize pad-split"));
+    a.A = ws; a.a_gs = seg; a.a_rs = (int64_t)T * seg;
+  }
   RM_TIMED("tokenize_proj", st, RM_HIP(rm::launch_gemm(a, st), "tokenize projection"));
   return ok();
 }

@@ -80,6 +80,9 @@ struct GemmArgs {
   void* C = nullptr; int64_t c_gs = 0, c_rs = 0;
   const float* bias = nullptr; int64_t bias_gs = 0;
   const float* rowscale = nullptr;
+  // > 0: A is fp32, rounded to bf16 as it is loaded; A columns (counted from
+  // the row start of group 0) at or past a_klim read as zero
+  int64_t a_klim = 0;
   // ragged mode (MoE): group g has row_off[g+1]-row_off[g] rows; the tiles
   // to run are the (g, m0) pairs tiles[0..2*ntiles) with *ntiles on the device;
   // max_mtiles bounds *ntiles (the grid is sized for it).

@@ -74,3 +74,15 @@ def dcnv2_full_flops(batch: int, width: int, layers: int) -> int:
 
 def dcnv2_lowrank_flops(batch: int, width: int, rank: int, layers: int) -> int:
     return layers * (gemm_flops(batch, rank, width) + gemm_flops(batch, width, rank))
+
+
+def project_bytes(B: int, F: int, T: int, seg: int, D: int, dtype: str) -> int:
+    """Compulsory HBM traffic of the projection tokenizer: the fp32 embedding
+    read once, the T weight matrices and biases read once, x0 written once."""
+    e = ELEM_BYTES[dtype]
+    return B * F * 4 + T * D * seg * e + T * D * 4 + B * T * D * e
+
+
+def project_flops(B: int, T: int, seg: int, D: int) -> int:
+    """T products [B, seg] x [seg, D] (the padded segment length counts)."""
+    return T * gemm_flops(B, D, seg)

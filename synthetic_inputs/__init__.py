@@ -218,6 +218,25 @@ def make_inputs(cfg: Config, seed: Optional[int] = None) -> dict:
     return out
 
 
+# the projection tokenizer's workload: the pad-split model's embedding
+# (B = 4096 samples of F = 5000 floats ~ N(0, 0.1)) cut into T = 16 segments
+# of seg = 320 floats (ceil(5000 / 16) = 313, rounded up to a multiple of 8),
+# each mapped to D = 320
+PROJ_WORKLOAD = dict(B=4096, F=5000, T=16, seg=320, D=320, dtype="bf16")
+
+
+def make_proj_inputs(B: int, F: int, T: int, seg: int, D: int, dtype: str, seed: int = 2,
+                     emb_var: float = 0.1, bias_var: float = 0.0) -> dict:
+    """Draw the projection tokenizer's tensors: ``emb`` float32 [B,F] ~ N(0,
+    emb_var); ``w`` [T,D,seg] ~ N(0, 1/seg) (uint16 bf16 bits for bf16);
+    ``b`` float32 [T,D] ~ N(0, bias_var) (zeros when bias_var is 0)."""
+    dr = _Drawer(seed)
+    emb = dr.normal((B, F), emb_var)
+    w = dr.normal((T, D, seg), 1.0 / seg)
+    b = dr.normal((T, D), bias_var) if bias_var else np.zeros((T, D), np.float32)
+    return {"emb": emb, "w": to_bf16_bits(w) if dtype == "bf16" else w, "b": b}
+
+
 def random_rows(B: int, n: int, seed: int = 12345) -> np.ndarray:
     """A seeded, sorted subset of n sample indices that always holds 0 and B-1."""
     if n >= B:

@@ -180,22 +180,23 @@ def test_width_limits(lib):
 
 def test_projection_tokenizer_errors(lib):
     p = bd.ProjParams(A16, A16)
-    need = lib.rm_tokenize_project_workspace_bytes(64, 16, 320, bd.RM_BF16)
-    assert need >= 64 * 16 * 320 * 2
+    # bf16 with F % 4 == 0 reads the embedding in place: no workspace
+    assert lib.rm_tokenize_project_workspace_bytes(64, 5000, 16, 320, bd.RM_BF16) == 0
+    assert lib.rm_tokenize_project_workspace_bytes(64, 4999, 16, 320, bd.RM_BF16) >= 64 * 16 * 320 * 2
+    need = lib.rm_tokenize_project_workspace_bytes(64, 5000, 16, 320, bd.RM_F32)
+    assert need >= 64 * 16 * 320 * 4
     args = (A16 * 2, C.byref(p), 64)
-    assert lib.rm_tokenize_project(*args, 5121, 16, 320, 320, bd.RM_BF16, A16 * 3, A16 * 4, need, None) \
-        == bd.RM_ERR_UNSUPPORTED
+    f32 = (A16 * 3, A16 * 4, need, None)
+    assert lib.rm_tokenize_project(*args, 5121, 16, 320, 320, bd.RM_F32, *f32) == bd.RM_ERR_UNSUPPORTED
     assert "fit" in err(lib)
-    assert lib.rm_tokenize_project(*args, 5000, 16, 316, 320, bd.RM_BF16, A16 * 3, A16 * 4, need, None) \
-        == bd.RM_ERR_UNSUPPORTED
-    assert lib.rm_tokenize_project(*args, 5000, 16, 320, 324, bd.RM_BF16, A16 * 3, A16 * 4, need, None) \
-        == bd.RM_ERR_UNSUPPORTED
-    assert lib.rm_tokenize_project(*args, 5000, 16, 320, 320, bd.RM_BF16, A16 * 3, A16 * 4, need - 1, None) \
+    assert lib.rm_tokenize_project(*args, 5000, 16, 316, 320, bd.RM_F32, *f32) == bd.RM_ERR_UNSUPPORTED
+    assert lib.rm_tokenize_project(*args, 5000, 16, 320, 324, bd.RM_F32, *f32) == bd.RM_ERR_UNSUPPORTED
+    assert lib.rm_tokenize_project(*args, 5000, 16, 320, 320, bd.RM_F32, A16 * 3, A16 * 4, need - 1, None) \
         == bd.RM_ERR_WORKSPACE
-    assert lib.rm_tokenize_project(A16 * 2, None, 64, 5000, 16, 320, 320, bd.RM_BF16, A16 * 3, A16 * 4, need,
-                                   None) == bd.RM_ERR_INVALID
-    p.b = None
-    assert lib.rm_tokenize_project(*args, 5000, 16, 320, 320, bd.RM_BF16, A16 * 3, A16 * 4, need, None) \
+    assert lib.rm_tokenize_project(*args, 5000, 16, 320, 320, bd.RM_F32, A16 * 3, None, need, None) \
         == bd.RM_ERR_INVALID
+    assert lib.rm_tokenize_project(A16 * 2, None, 64, 5000, 16, 320, 320, bd.RM_F32, *f32) == bd.RM_ERR_INVALID
+    p.b = None
+    assert lib.rm_tokenize_project(*args, 5000, 16, 320, 320, bd.RM_F32, *f32) == bd.RM_ERR_INVALID
     assert "b is NULL" in err(lib)
     assert lib.rm_tokenize_project(None, None, 0, 5000, 16, 320, 320, bd.RM_BF16, None, None, 0, None) == bd.RM_OK

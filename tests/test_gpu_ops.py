@@ -92,7 +92,9 @@ def _proj_dev(p):
     ("bf16", 4096, 5000, 16, 320, 320),  # the pad-split model's embedding, seg = 320 (313 rounded up to 8)
     ("bf16", 600, 4000, 32, 128, 256),   # full k tiles, N = one tile, ragged M
     ("bf16", 300, 1000, 8, 128, 136),    # N = 136: a partial N tile
-    ("bf16", 1, 37, 4, 16, 8),           # one sample, F not a multiple of seg
+    ("bf16", 1, 37, 4, 16, 8),           # one sample, F % 4 != 0: pad-split copy + product
+    ("bf16", 257, 4998, 16, 320, 320),   # F % 4 != 0 at the workload's width
+    ("bf16", 130, 20, 4, 8, 64),         # segments 3 and 4 entirely padding, K = 8
     ("f32", 70, 300, 4, 80, 64),         # fp32, K = 80: a partial k tile
     ("f32", 5, 5, 2, 8, 16),             # F < seg: the second segment is all padding
 ])
