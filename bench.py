@@ -42,11 +42,11 @@ def log(msg: str) -> None:
 CSRC = os.path.join(ROOT, "rankmixer_token_mixing_amd", "csrc")
 # the sources that define each launch group's kernel
 KERNEL_SOURCES = {
-    "ffn1": ("kernels_gemm.hip", "common.hpp"),
-    "ffn2": ("kernels_gemm.hip", "common.hpp"),
+    "ffn1": ("kernels_gemm.hip", "frag.hpp", "common.hpp"),
+    "ffn2": ("kernels_gemm.hip", "frag.hpp", "common.hpp"),
     "mix_ln1": ("kernels_rows.hip", "common.hpp"),
     "ln2": ("kernels_rows.hip", "common.hpp"),
-    "tokenize_proj": ("kernels_gemm.hip", "common.hpp"),
+    "tokenize_proj": ("kernels_tokproj.hip", "frag.hpp", "common.hpp"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_fwd_{config}_traffic.json")
 PROJ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tokenize_project_traffic.json")

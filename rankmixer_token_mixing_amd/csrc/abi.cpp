@@ -437,10 +437,12 @@ rm_status rm_tokenize_padsplit(const float* emb, int64_t B, int64_t F, int T, in
 // bf16 with whole float4 segments of the embedding: one fused launch that
 // reads the fp32 embedding in place; otherwise pad-split into the workspace
 // (token width seg) and one grouped product over the padded copy
-static bool project_fused(int64_t F, int dtype) { return dtype == RM_BF16 && F % 4 == 0; }
+static bool project_fused(int64_t F, int seg, int dtype) {
+  return dtype == RM_BF16 && F % 4 == 0 && seg <= rm::tokenize_project_max_seg();
+}
 
 size_t rm_tokenize_project_workspace_bytes(int64_t B, int64_t F, int T, int seg, int dtype) {
-  if (project_fused(F, dtype) || B <= 0) return 0;
+  if (project_fused(F, seg, dtype) || B <= 0) return 0;
   Carver c(nullptr);
   c.take((size_t)B * T * seg * elem_bytes(dtype));
   return c.off;
@@ -464,24 +466,25 @@ rm_status rm_tokenize_project(const float* emb, const rm_proj_params* p, int64_t
   RM_TRY(check_ptr(emb, "emb"));
   RM_TRY(check_ptr(p->w, "w")); RM_TRY(check_ptr(p->b, "b"));
   RM_TRY(check_ptr(x0, "x0"));
-  const bool fused = project_fused(F, dtype);
+  const bool fused = project_fused(F, seg, dtype);
   const size_t need = rm_tokenize_project_workspace_bytes(B, F, T, seg, dtype);
   if (need) RM_TRY(check_ptr(ws, "ws"));
   if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
+  if (fused) {
+    RM_TIMED("tokenize_proj", st,
+             RM_HIP(rm::launch_tokenize_project(emb, p->w, p->b, x0, B, F, T, seg, D, st), "tokenize projection"));
+    return ok();
+  }
+  RM_TIMED("tokenize", st, RM_HIP(rm::launch_tokenize_padsplit(emb, B, F, T, seg, dtype, ws, st), "tokenize pad-split"));
   rm::GemmArgs a;
   a.dt = dtype;
   a.epi = rm::kEpiBias;
   a.M = (int)B; a.N = D; a.K = seg; a.G = T;
+  a.A = ws; a.a_gs = seg; a.a_rs = (int64_t)T * seg;
   a.W = p->w; a.b_gs = (int64_t)D * seg;
   a.C = x0; a.c_gs = D; a.c_rs = (int64_t)T * D;
   a.bias = p->b; a.bias_gs = D;
-  if (fused) {
-    a.A = emb; a.a_gs = seg; a.a_rs = F; a.a_klim = F;
-  } else {
-    RM_TIMED("tokenize", st, RM_HIP(rm::launch_tokenize_padsplit(emb, B, F, T, seg, dtype, ws, st), "tokenize pad-split"));
-    a.A = ws; a.a_gs = seg; a.a_rs = (int64_t)T * seg;
-  }
   RM_TIMED("tokenize_proj", st, RM_HIP(rm::launch_gemm(a, st), "tokenize projection"));
   return ok();
 }

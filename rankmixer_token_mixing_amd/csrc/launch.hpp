@@ -57,6 +57,9 @@ hipError_t launch_moe_combine(const float* y, const int* pos, const void* s, int
 
 // ---- grouped MFMA GEMM (kernels_gemm.hip) ------------------------------------
 
+// compute units of the current device (cached per device)
+int device_cus();
+
 enum Epilogue {
   kEpiBiasGelu = 0,       // C(dt)  = GELU(acc + bias[n])
   kEpiBias = 1,           // C(dt)  = acc + bias[n]
@@ -80,9 +83,6 @@ struct GemmArgs {
   void* C = nullptr; int64_t c_gs = 0, c_rs = 0;
   const float* bias = nullptr; int64_t bias_gs = 0;
   const float* rowscale = nullptr;
-  // > 0: A is fp32, rounded to bf16 as it is loaded; A columns (counted from
-  // the row start of group 0) at or past a_klim read as zero
-  int64_t a_klim = 0;
   // ragged mode (MoE): group g has row_off[g+1]-row_off[g] rows; the tiles
   // to run are the (g, m0) pairs tiles[0..2*ntiles) with *ntiles on the device;
   // max_mtiles bounds *ntiles (the grid is sized for it).
@@ -97,5 +97,15 @@ struct GemmArgs {
 // built for this).
 int gemm_tile_m(const GemmArgs& a);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+// ---- projection tokenizer (kernels_tokproj.hip) -------------------------------
+
+// x0[b][t][:] = W_t . bf16(pad(emb[b])[t*seg : (t+1)*seg]) + bias_t in one
+// kernel that reads the fp32 embedding in place: bf16 weights [T][D][seg]
+// and output [B][T][D], F % 4 == 0, seg % 8 == 0, seg <= the returned
+// maximum, D % 8 == 0
+hipError_t launch_tokenize_project(const float* emb, const void* w, const float* bias, void* x0, int64_t B, int64_t F,
+                                   int T, int seg, int D, hipStream_t s);
+int tokenize_project_max_seg();
 
 }  // namespace rm
