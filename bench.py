@@ -215,15 +215,113 @@ def bench_project(args) -> int:
     return 0
 
 
+def bench_block_bwd(args) -> int:
+    """The dense block backward alone: one rm_block_bwd per step on block 0 of
+    the workload (default c3: B=1024, T=32, D=1536, hidden 6144, bf16), given
+    the saved tensors of one rm_block_fwd_train and a seeded N(0, 1) upstream
+    gradient.  Four grouped products of 2*B*D*Hd*T flops each (dH, dW2, dW1,
+    dS); the roofline is the dominant one against the bf16 MFMA peak."""
+    import numpy as np
+    import torch
+    import synthetic_inputs as si
+    from rankmixer_token_mixing_amd import binding as bd
+    from rankmixer_token_mixing_amd import perfmodel as pm
+
+    cfg = si.CONFIGS[args.config]
+    if cfg.E:
+        print("block_bwd: dense workloads only", file=sys.stderr)
+        return 2
+    t0 = time.perf_counter()
+    inputs = si.make_inputs(si.scaled(cfg, L=1))
+    d_out_np = si.make_inputs(si.scaled(cfg, L=0), seed=100 + si.SEEDS[cfg.name])["x"]
+    log(f"generated {cfg.name} inputs in {time.perf_counter() - t0:.1f}s: {cfg.description}")
+    blk = bd.upload_blocks(inputs["blocks"][:1])[0]
+    x = bd.to_device(inputs["x"])
+    d_out = bd.to_device(d_out_np)
+    B, T, D, Hd = cfg.B, cfg.T, cfg.D, cfg.hidden
+    _, saved = bd.rm_block_fwd_train(x, blk)
+
+    for _ in range(args.warmup):
+        bd.rm_block_bwd(x, blk, saved, d_out)
+    torch.cuda.synchronize()
+    bd.profile_enable(not args.no_profile)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        bd.rm_block_bwd(x, blk, saved, d_out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = bd.profile_read() if not args.no_profile else {}
+    bd.profile_enable(False)
+    ms_step = elapsed * 1e3 / args.steps
+    gemm = T * pm.gemm_flops(B, Hd, D)  # each of the four products
+    kernels = {}
+    for name, (tot_ms, n) in prof.items():
+        avg = tot_ms / max(n, 1)
+        e = {"avg_ms": round(avg, 5), "launches": n, "total_ms": round(tot_ms, 3)}
+        if name.startswith("bwd_d"):
+            e["tflops"] = round(gemm / (avg * 1e-3) / 1e12, 1)
+        kernels[name] = e
+    roofline = None
+    gk = {k: v for k, v in kernels.items() if k.startswith("bwd_d")}
+    if gk:
+        dom = max(gk, key=lambda k: gk[k]["total_ms"])
+        ach = gemm / (gk[dom]["avg_ms"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": pm.PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / pm.PEAK_BF16_TFLOPS, 4), "flop_per_launch": gemm,
+                    "traffic": None}
+    bwd_tf = 4 * gemm / (ms_step * 1e-3) / 1e12
+    rec = {
+        "metric": "samples/sec RankMixer block backward (bf16) + % of MI355X MFMA peak",
+        "value": round(B / (ms_step * 1e-3), 1),
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.description}: backward of block 0", "B": B, "T": T, "D": D, "hidden": Hd,
+                   "step": "rm_block_bwd over the batch (dX and every parameter gradient)"},
+        "roofline": roofline,
+        "step_tflops": round(bwd_tf, 1),
+        "step_frac_of_bf16_peak": round(bwd_tf / pm.PEAK_BF16_TFLOPS, 4),
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import block_backward as obw
+        n = min(B, 128)
+        rows = si.random_rows(B, n, seed=99)
+        t0 = time.perf_counter()
+        obw.block_bwd(inputs["x"][rows], inputs["blocks"][0], d_out_np[rows])
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([q.get("num_threads", 1) for q in threadpool_info() if q.get("user_api") == "blas"] or [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        rec["cpu_baseline"] = {"value": n / dt, "unit": "samples/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"{n} of {B} samples (fp64 numpy forward + backward of block 0, {dt:.1f} s); "
+                                         f"the work is linear in the samples, so the rate is per-sample exact"}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", help="workload (c3 is the benchmarked one)")
-    ap.add_argument("--op", default="model", choices=["model", "tokenize_project"],
+    ap.add_argument("--op", default="model", choices=["model", "tokenize_project", "block_bwd"],
                     help="model: the block stack (default); tokenize_project: the projection "
-                         "tokenizer alone on the pad-split model's embedding")
+                         "tokenizer alone on the pad-split model's embedding; block_bwd: the dense "
+                         "block backward on block 0 of the workload")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="samples in the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-launch HIP events")
@@ -263,6 +361,8 @@ def main() -> int:
 
     if args.op == "tokenize_project":
         return bench_project(args)
+    if args.op == "block_bwd":
+        return bench_block_bwd(args)
 
     cfg = si.CONFIGS[args.config]
     t0 = time.perf_counter()

@@ -20,7 +20,8 @@
  *    NULL where stated.
  *  - B is the batch size; B = 0 is an empty batch: the call checks its other
  *    arguments, returns RM_OK and enqueues nothing (data pointers may then be
- *    NULL).  B < 0 is RM_ERR_INVALID.
+ *    NULL), except rm_block_bwd, which writes zero gradients.  B < 0 is
+ *    RM_ERR_INVALID.
  *  - Width limits of this build: D a multiple of 8 (and of T wherever tokens
  *    are mixed), hidden widths a multiple of 8, one [D] row per wavefront in
  *    registers (D <= 8192 when D/T is a multiple of 8; the FFN and MoE calls
@@ -100,6 +101,19 @@ typedef struct rm_block_params {
   rm_moe_params moe;          /* used when kind == RM_BLOCK_MOE */
 } rm_block_params;
 
+/* Gradients of one dense block: float32 device buffers, overwritten (not
+ * accumulated) by rm_block_bwd. */
+typedef struct rm_block_grads {
+  float* w1;     /* [T][Hd][D] */
+  float* b1;     /* [T][Hd] */
+  float* w2;     /* [T][D][Hd] */
+  float* b2;     /* [T][D] */
+  float* ln1_g;  /* [D] */
+  float* ln1_b;  /* [D] */
+  float* ln2_g;  /* [D] */
+  float* ln2_b;  /* [D] */
+} rm_block_grads;
+
 /* A stack of L blocks ([FR] "RankMixer整体架构": X_L = block_L(...block_1(X_0))),
  * with an optional pad-split tokenizer in front and optional mean pooling
  * plus a D -> 1 logit behind ([WL]: the last block's tokens are averaged). */
@@ -138,9 +152,9 @@ typedef struct rm_proj_params {
  *   emb: [B][F] fp32 device; x0: [B][T][D] dtype device; params as
  *   rm_proj_params (device pointers).
  * Workspace: rm_tokenize_project_workspace_bytes(B, F, T, seg, dtype): 0 for
- * bf16 with F a multiple of 4 (one launch reads emb in place and rounds it to
- * bf16 on the way into the product; ws may then be NULL), else room for the
- * padded, cast segments.
+ * bf16 with F a multiple of 4 and seg <= 384 (one launch reads emb in place
+ * and rounds it to bf16 on the way into the product; ws may then be NULL),
+ * else room for the padded, cast segments.
  * Errors: F > T*seg, seg or D not a multiple of 8 -> RM_ERR_UNSUPPORTED. */
 rm_status rm_tokenize_project(const float* emb, const rm_proj_params* p, int64_t B, int64_t F,
                               int T, int seg, int D, int dtype, void* x0, void* ws,
@@ -201,6 +215,38 @@ size_t rm_block_workspace_bytes(int kind, int64_t B, int T, int D, int hidden, i
 rm_status rm_model_fwd(const rm_model_desc* m, const void* in, void* x_out, float* pooled,
                        float* logits, int64_t B, void* ws, size_t ws_bytes, void* stream);
 size_t rm_model_workspace_bytes(const rm_model_desc* m, int64_t B);
+
+/* Dense block training forward: the forward of rm_block_fwd, which also keeps
+ * what rm_block_bwd needs in the caller's `saved` buffer (S, the W1 product +
+ * b1 before GELU, the W2 product + b2; size rm_block_saved_bytes).  The output
+ * equals rm_block_fwd's up to the rounding of the GELU input to dtype.
+ *   Workspace: rm_block_workspace_bytes(RM_BLOCK_DENSE, B, T, D, hidden, 0, dtype).
+ * Errors: an MoE block, D > 4096 -> RM_ERR_UNSUPPORTED (besides rm_block_fwd's). */
+size_t rm_block_saved_bytes(int64_t B, int T, int D, int hidden, int dtype);
+rm_status rm_block_fwd_train(const void* x, const rm_block_params* p, void* x_out, void* saved,
+                             size_t saved_bytes, int64_t B, int T, int D, int hidden, int dtype,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Dense block backward: the chain rule through the block equations of
+ * [FR] "RankMixer整体架构" (the pages train the block but print no backward).
+ * Given d_out = dL/dX' it writes dx = dL/dX and every parameter gradient:
+ *   LN2:  dY2 = LNbwd(d_out);  dV = dY2;  dgamma2 = sum d_out*xhat2, dbeta2 = sum d_out
+ *   W2:   db2_t = sum_b dV_t;  dW2_t = dV_t^T H_t;  dH_t = dV_t W2_t
+ *   GELU: dU = dH * GELU'(U)
+ *   W1:   db1_t = sum_b dU_t;  dW1_t = dU_t^T S_t;  dS = dY2 + dU_t W1_t
+ *   LN1:  dY1 = LNbwd(dS);  dX = dY1 + TM(dY1)   (TM is its own transpose)
+ * with LNbwd(g) = (g*gamma - mean(g*gamma) - xhat * mean(g*gamma*xhat)) / sigma.
+ *   x: the block input [B][T][D] dtype; saved: from rm_block_fwd_train on the
+ *   same x and params; d_out, dx: [B][T][D] dtype; g: gradients (fp32).
+ * Products run in dtype with fp32 accumulation (bf16: dV, dH, dU rounded to
+ * bf16); sums over the batch and over rows run in a fixed order, so results
+ * are deterministic.  B = 0 writes zero gradients.
+ *   Workspace: rm_block_bwd_workspace_bytes(B, T, D, hidden, dtype).
+ * Errors: as rm_block_fwd_train; dx aliasing x or d_out -> RM_ERR_INVALID. */
+size_t rm_block_bwd_workspace_bytes(int64_t B, int T, int D, int hidden, int dtype);
+rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* saved, size_t saved_bytes,
+                       const void* d_out, void* dx, const rm_block_grads* g, int64_t B, int T,
+                       int D, int hidden, int dtype, void* ws, size_t ws_bytes, void* stream);
 
 /* Launch timing for benchmarks.  While enabled, every group of kernel
  * launches an entry point makes (the W1 product, the W2 product, a LayerNorm,

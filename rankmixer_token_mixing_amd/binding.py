@@ -51,6 +51,11 @@ class BlockParams(C.Structure):
                 ("ln2_b", C.c_void_p), ("pffn", PffnParams), ("moe", MoeParams)]
 
 
+class BlockGrads(C.Structure):
+    _fields_ = [("w1", C.c_void_p), ("b1", C.c_void_p), ("w2", C.c_void_p), ("b2", C.c_void_p),
+                ("ln1_g", C.c_void_p), ("ln1_b", C.c_void_p), ("ln2_g", C.c_void_p), ("ln2_b", C.c_void_p)]
+
+
 class ModelDesc(C.Structure):
     _fields_ = [("T", C.c_int), ("D", C.c_int), ("hidden", C.c_int), ("E", C.c_int), ("dtype", C.c_int),
                 ("L", C.c_int), ("blocks", C.POINTER(BlockParams)), ("F", C.c_int64), ("head_w", C.c_void_p),
@@ -73,6 +78,12 @@ _SIGNATURES = {
     "rm_moe_route": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _int, _int, _int, _int, _vp, _sz, _vp]),
     "rm_block_fwd": (_int, [_vp, C.POINTER(BlockParams), _vp, _i64, _int, _int, _int, _int, _int, _vp, _sz, _vp]),
     "rm_block_workspace_bytes": (_sz, [_int, _i64, _int, _int, _int, _int, _int]),
+    "rm_block_saved_bytes": (_sz, [_i64, _int, _int, _int, _int]),
+    "rm_block_fwd_train": (_int, [_vp, C.POINTER(BlockParams), _vp, _vp, _sz, _i64, _int, _int, _int, _int, _vp,
+                                  _sz, _vp]),
+    "rm_block_bwd_workspace_bytes": (_sz, [_i64, _int, _int, _int, _int]),
+    "rm_block_bwd": (_int, [_vp, C.POINTER(BlockParams), _vp, _sz, _vp, _vp, C.POINTER(BlockGrads), _i64, _int, _int,
+                            _int, _int, _vp, _sz, _vp]),
     "rm_model_fwd": (_int, [C.POINTER(ModelDesc), _vp, _vp, _vp, _vp, _i64, _vp, _sz, _vp]),
     "rm_model_workspace_bytes": (_sz, [C.POINTER(ModelDesc), _i64]),
     "rm_status_string": (C.c_char_p, [_int]),
@@ -278,6 +289,44 @@ def rm_block_fwd(x: torch.Tensor, p: dict, out: Optional[torch.Tensor] = None) -
     _check(lib.rm_block_fwd(_p(x), C.byref(bp), _p(y), B, T, D, hidden, E, _dt(x), _p(ws), ws.numel(),
                             _stream(x.device)))
     return y
+
+
+def rm_block_fwd_train(x: torch.Tensor, p: dict, out: Optional[torch.Tensor] = None):
+    """Dense block forward that also returns the buffer rm_block_bwd needs:
+    (x_out, saved)."""
+    lib = load()
+    B, T, D = x.shape
+    Hd = p["w1"].shape[1]
+    y = torch.empty_like(x) if out is None else out
+    saved = torch.empty(lib.rm_block_saved_bytes(B, T, D, Hd, _dt(x)), dtype=torch.uint8, device=x.device)
+    n = lib.rm_block_workspace_bytes(RM_BLOCK_DENSE, B, T, D, Hd, 0, _dt(x))
+    ws = _workspace(x.device, n)
+    st = _block_struct(p)
+    _check(lib.rm_block_fwd_train(_p(x), C.byref(st), _p(y), _p(saved), saved.numel(), B, T, D, Hd, _dt(x), _p(ws),
+                                  ws.numel(), _stream(x.device)))
+    return y, saved
+
+
+def rm_block_bwd(x: torch.Tensor, p: dict, saved: torch.Tensor, d_out: torch.Tensor):
+    """Dense block backward: (dx, grads) with grads a dict of fp32 tensors
+    named like the parameters (w1, b1, w2, b2, ln1_g, ln1_b, ln2_g, ln2_b)."""
+    lib = load()
+    B, T, D = x.shape
+    Hd = p["w1"].shape[1]
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"w1": torch.empty((T, Hd, D), **f32), "b1": torch.empty((T, Hd), **f32),
+         "w2": torch.empty((T, D, Hd), **f32), "b2": torch.empty((T, D), **f32),
+         "ln1_g": torch.empty(D, **f32), "ln1_b": torch.empty(D, **f32),
+         "ln2_g": torch.empty(D, **f32), "ln2_b": torch.empty(D, **f32)}
+    dx = torch.empty_like(x)
+    gs = BlockGrads(*[_p(g[k]) for k in ("w1", "b1", "w2", "b2", "ln1_g", "ln1_b", "ln2_g", "ln2_b")])
+    n = lib.rm_block_bwd_workspace_bytes(B, T, D, Hd, _dt(x))
+    ws = _workspace(dev, n)
+    st = _block_struct(p)
+    _check(lib.rm_block_bwd(_p(x), C.byref(st), _p(saved), saved.numel(), _p(d_out), _p(dx), C.byref(gs), B, T, D, Hd,
+                            _dt(x), _p(ws), ws.numel(), _stream(dev)))
+    return dx, g
 
 
 class Model:

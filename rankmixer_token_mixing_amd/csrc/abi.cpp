@@ -603,6 +603,210 @@ rm_status rm_block_fwd(const void* x, const rm_block_params* p, void* x_out, int
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// dense block training forward and backward
+
+namespace {
+
+// what the training forward keeps for the backward: S (token-major), U (the
+// W1 product + b1 before GELU, token-major [T][B][Hd]) and Z (the W2 product +
+// b2, [B][T][D])
+struct Saved {
+  void* S;
+  void* U;
+  void* Z;
+};
+size_t saved_carve(Carver& c, int64_t B, int T, int D, int Hd, int dt, Saved* w) {
+  Saved x;
+  x.S = c.take((size_t)B * T * D * elem_bytes(dt));
+  x.U = c.take((size_t)B * T * Hd * elem_bytes(dt));
+  x.Z = c.take((size_t)B * T * D * elem_bytes(dt));
+  if (w) *w = x;
+  return c.off;
+}
+
+int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
+
+// workspace of the backward; the K = batch products read the transposed
+// activations with rows padded to Bp = B rounded up to 64 (zero tail)
+struct BwdWs {
+  void *dV, *dVt, *W2t, *dH, *dU, *dUt, *Ht, *St, *W1t;
+  float *dSf, *dY1, *ln2p, *ln1p, *b2p, *b1p;
+};
+size_t bwd_carve(Carver& c, int64_t B, int T, int D, int Hd, int dt, BwdWs* w) {
+  const size_t e = elem_bytes(dt);
+  const int64_t Bp = pad64(B);
+  const int64_t rt = rm::transpose_row_tiles(B, Bp);
+  const int lg = rm::ln_bwd_grid(B, T);
+  BwdWs x;
+  x.dV = c.take((size_t)T * B * D * e);
+  x.dVt = c.take((size_t)T * D * Bp * e);
+  x.W2t = c.take((size_t)T * Hd * D * e);
+  x.dH = c.take((size_t)T * B * Hd * e);
+  x.dU = c.take((size_t)T * B * Hd * e);
+  x.dUt = c.take((size_t)T * Hd * Bp * e);
+  x.Ht = c.take((size_t)T * Hd * Bp * e);
+  x.St = c.take((size_t)T * D * Bp * e);
+  x.W1t = c.take((size_t)T * D * Hd * e);
+  x.dSf = (float*)c.take((size_t)T * B * D * 4);
+  x.dY1 = (float*)c.take((size_t)B * T * D * 4);
+  x.ln2p = (float*)c.take((size_t)lg * 2 * D * 4);
+  x.ln1p = (float*)c.take((size_t)lg * 2 * D * 4);
+  x.b2p = (float*)c.take((size_t)T * rt * D * 4);
+  x.b1p = (float*)c.take((size_t)T * rt * Hd * 4);
+  if (w) *w = x;
+  return c.off;
+}
+
+rm_status check_train_shape(const rm_block_params* p, int64_t B, int T, int D, int hidden, int dt) {
+  RM_TRY(check_block_params(p, dt));
+  if (p->kind != RM_BLOCK_DENSE) return fail(RM_ERR_UNSUPPORTED, "training supports dense blocks only");
+  RM_TRY(check_block_shape(RM_BLOCK_DENSE, B, T, D, hidden, 0, dt));
+  if (D > rm::ln_bwd_max_width())
+    return fail(RM_ERR_UNSUPPORTED, "D=%d is wider than the backward row kernels support (%d)", D, rm::ln_bwd_max_width());
+  if (B * T * (int64_t)hidden >= ((int64_t)1 << 31) || (int64_t)T * pad64(B) * hidden >= ((int64_t)1 << 31))
+    return fail(RM_ERR_UNSUPPORTED, "B*T*hidden too large");
+  return RM_OK;
+}
+
+}  // namespace
+
+size_t rm_block_saved_bytes(int64_t B, int T, int D, int hidden, int dtype) {
+  Carver c(nullptr);
+  return saved_carve(c, B, T, D, hidden, dtype, nullptr);
+}
+
+rm_status rm_block_fwd_train(const void* x, const rm_block_params* p, void* x_out, void* saved, size_t saved_bytes,
+                             int64_t B, int T, int D, int hidden, int dtype, void* ws, size_t ws_bytes, void* stream) {
+  RM_TRY(check_train_shape(p, B, T, D, hidden, dtype));
+  if (B == 0) return ok();
+  RM_TRY(check_ptr(x, "x")); RM_TRY(check_ptr(x_out, "x_out"));
+  if (x == x_out) return fail(RM_ERR_INVALID, "x_out must not alias x");
+  RM_TRY(check_ptr(saved, "saved"));
+  const size_t need_s = rm_block_saved_bytes(B, T, D, hidden, dtype);
+  if (saved_bytes < need_s) return fail(RM_ERR_WORKSPACE, "saved buffer %zu bytes, need %zu", saved_bytes, need_s);
+  RM_TRY(check_ptr(ws, "ws"));
+  const size_t need = rm_block_workspace_bytes(RM_BLOCK_DENSE, B, T, D, hidden, 0, dtype);
+  if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  Carver cs(saved);
+  Saved sv;
+  saved_carve(cs, B, T, D, hidden, dtype, &sv);
+  Carver c(ws);
+  BlockWs w;
+  block_ws(c, RM_BLOCK_DENSE, B, T, D, hidden, 0, dtype, &w);
+  const int64_t sb = D, sT = B * D;  // S is token-major
+  RM_TIMED("mix_ln1", st, RM_HIP(rm::launch_mix_ln(x, sv.S, p->ln1_g, p->ln1_b, B, T, D, dtype, true, st), "token mix + LayerNorm"));
+  rm::GemmArgs a1 = ffn1_args(sv.S, sb, sT, &p->pffn, sv.U, B, T, D, hidden, dtype);
+  a1.epi = rm::kEpiBias;  // keep U = W1 s + b1; GELU separately
+  RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block W1 product"));
+  RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.pffn.H, B * T * (int64_t)hidden, dtype, st), "GELU"));
+  rm::GemmArgs a2 = ffn2_args(w.pffn.H, &p->pffn, B, T, D, hidden, dtype);
+  a2.epi = rm::kEpiBias;
+  a2.C = sv.Z;
+  RM_TIMED("ffn2", st, RM_HIP(rm::launch_gemm(a2, st), "block W2 product"));
+  RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows(sv.Z, sv.S, sb, sT, T, x_out, p->ln2_g, p->ln2_b, B * T, D, dtype, st),
+                             "residual + LayerNorm 2"));
+  return ok();
+}
+
+size_t rm_block_bwd_workspace_bytes(int64_t B, int T, int D, int hidden, int dtype) {
+  Carver c(nullptr);
+  return bwd_carve(c, B, T, D, hidden, dtype, nullptr);
+}
+
+rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* saved, size_t saved_bytes, const void* d_out,
+                       void* dx, const rm_block_grads* g, int64_t B, int T, int D, int hidden, int dtype, void* ws,
+                       size_t ws_bytes, void* stream) {
+  RM_TRY(check_train_shape(p, B, T, D, hidden, dtype));
+  if (!g) return fail(RM_ERR_INVALID, "grads is NULL");
+  RM_TRY(check_ptr(g->w1, "grads.w1")); RM_TRY(check_ptr(g->b1, "grads.b1"));
+  RM_TRY(check_ptr(g->w2, "grads.w2")); RM_TRY(check_ptr(g->b2, "grads.b2"));
+  RM_TRY(check_ptr(g->ln1_g, "grads.ln1_g")); RM_TRY(check_ptr(g->ln1_b, "grads.ln1_b"));
+  RM_TRY(check_ptr(g->ln2_g, "grads.ln2_g")); RM_TRY(check_ptr(g->ln2_b, "grads.ln2_b"));
+  hipStream_t st = (hipStream_t)stream;
+  const int Hd = hidden;
+  if (B == 0) {
+    // an empty batch contributes nothing: every gradient is zero (a sum over
+    // no partials, written by a kernel rather than a memset)
+    const struct { float* p; int64_t n; } z[] = {{g->w1, (int64_t)T * Hd * D}, {g->b1, (int64_t)T * Hd},
+                                                 {g->w2, (int64_t)T * D * Hd}, {g->b2, (int64_t)T * D},
+                                                 {g->ln1_g, D}, {g->ln1_b, D}, {g->ln2_g, D}, {g->ln2_b, D}};
+    for (const auto& v : z) RM_HIP(rm::launch_sum_parts(v.p, v.p, nullptr, 1, 0, v.n, v.n, st), "zero grads");
+    return ok();
+  }
+  RM_TRY(check_ptr(x, "x")); RM_TRY(check_ptr(d_out, "d_out")); RM_TRY(check_ptr(dx, "dx"));
+  if (dx == x || dx == d_out) return fail(RM_ERR_INVALID, "dx must not alias x or d_out");
+  RM_TRY(check_ptr(saved, "saved"));
+  const size_t need_s = rm_block_saved_bytes(B, T, D, hidden, dtype);
+  if (saved_bytes < need_s) return fail(RM_ERR_WORKSPACE, "saved buffer %zu bytes, need %zu", saved_bytes, need_s);
+  RM_TRY(check_ptr(ws, "ws"));
+  const size_t need = rm_block_bwd_workspace_bytes(B, T, D, hidden, dtype);
+  if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  Carver cs(const_cast<void*>(saved));
+  Saved sv;
+  saved_carve(cs, B, T, D, hidden, dtype, &sv);
+  Carver c(ws);
+  BwdWs w;
+  bwd_carve(c, B, T, D, hidden, dtype, &w);
+  const int dt = dtype;
+  const int64_t Bp = pad64(B);
+  const int rt = rm::transpose_row_tiles(B, Bp);
+  const int lg = rm::ln_bwd_grid(B, T);
+  // X' = LN2(Z + S): dV = dY2 (token-major), gamma2 / beta2 partials
+  RM_TIMED("ln2_bwd", st, RM_HIP(rm::launch_ln_bwd(0, d_out, nullptr, nullptr, sv.Z, sv.S, p->ln2_g, w.dV, w.ln2p, B, T, D, dt, st), "LayerNorm 2 backward"));
+  // dV^T (rows padded to Bp) and the b2 partials
+  RM_TIMED("tr_dV", st, RM_HIP(rm::launch_transpose(0, w.dV, nullptr, w.dVt, nullptr, w.b2p, T, B, D, Bp, dt, st), "transpose dV"));
+  // W2^T [T][Hd][D]
+  RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->pffn.w2, nullptr, w.W2t, nullptr, nullptr, T, D, Hd, D, dt, st), "transpose W2"));
+  // dH = dV W2
+  rm::GemmArgs g1;
+  g1.dt = dt; g1.epi = rm::kEpiBias;
+  g1.M = (int)B; g1.N = Hd; g1.K = D; g1.G = T;
+  g1.A = w.dV; g1.a_gs = B * D; g1.a_rs = D;
+  g1.W = w.W2t; g1.b_gs = (int64_t)Hd * D;
+  g1.C = w.dH; g1.c_gs = B * Hd; g1.c_rs = Hd;
+  RM_TIMED("bwd_dH", st, RM_HIP(rm::launch_gemm(g1, st), "dH product"));
+  // dU = dH * GELU'(U), also transposed, with the b1 partials; H^T = GELU(U)^T
+  RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.b1p, T, B, Hd, Bp, dt, st), "GELU backward"));
+  RM_TIMED("tr_H", st, RM_HIP(rm::launch_transpose(1, sv.U, nullptr, w.Ht, nullptr, nullptr, T, B, Hd, Bp, dt, st), "transpose H"));
+  // dW2 = dV^T H (fp32)
+  rm::GemmArgs g2;
+  g2.dt = dt; g2.epi = rm::kEpiBiasF32;
+  g2.M = D; g2.N = Hd; g2.K = (int)Bp; g2.G = T;
+  g2.A = w.dVt; g2.a_gs = (int64_t)D * Bp; g2.a_rs = Bp;
+  g2.W = w.Ht; g2.b_gs = (int64_t)Hd * Bp;
+  g2.C = g->w2; g2.c_gs = (int64_t)D * Hd; g2.c_rs = Hd;
+  RM_TIMED("bwd_dW2", st, RM_HIP(rm::launch_gemm(g2, st), "dW2 product"));
+  // dW1 = dU^T S (fp32)
+  RM_TIMED("tr_S", st, RM_HIP(rm::launch_transpose(0, sv.S, nullptr, w.St, nullptr, nullptr, T, B, D, Bp, dt, st), "transpose S"));
+  rm::GemmArgs g3;
+  g3.dt = dt; g3.epi = rm::kEpiBiasF32;
+  g3.M = Hd; g3.N = D; g3.K = (int)Bp; g3.G = T;
+  g3.A = w.dUt; g3.a_gs = (int64_t)Hd * Bp; g3.a_rs = Bp;
+  g3.W = w.St; g3.b_gs = (int64_t)D * Bp;
+  g3.C = g->w1; g3.c_gs = (int64_t)Hd * D; g3.c_rs = D;
+  RM_TIMED("bwd_dW1", st, RM_HIP(rm::launch_gemm(g3, st), "dW1 product"));
+  // dS (W1 branch) = dU W1 (fp32, token-major)
+  RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->pffn.w1, nullptr, w.W1t, nullptr, nullptr, T, Hd, D, Hd, dt, st), "transpose W1"));
+  rm::GemmArgs g4;
+  g4.dt = dt; g4.epi = rm::kEpiBiasF32;
+  g4.M = (int)B; g4.N = D; g4.K = Hd; g4.G = T;
+  g4.A = w.dU; g4.a_gs = B * Hd; g4.a_rs = Hd;
+  g4.W = w.W1t; g4.b_gs = (int64_t)D * Hd;
+  g4.C = w.dSf; g4.c_gs = B * D; g4.c_rs = D;
+  RM_TIMED("bwd_dS", st, RM_HIP(rm::launch_gemm(g4, st), "dS product"));
+  // S = LN1(TM(X) + X) with dS = dV + dS_ffn; dX = dY1 + TM(dY1)
+  RM_TIMED("ln1_bwd", st, RM_HIP(rm::launch_ln_bwd(1, nullptr, w.dV, w.dSf, x, nullptr, p->ln1_g, w.dY1, w.ln1p, B, T, D, dt, st), "LayerNorm 1 backward"));
+  RM_TIMED("tm_add", st, RM_HIP(rm::launch_tm_add(w.dY1, dx, B, T, D, dt, st), "token mix backward"));
+  // fixed-order sums of the partials
+  RM_TIMED("sums_ln", st, RM_HIP(rm::launch_sum_parts(w.ln2p, g->ln2_g, g->ln2_b, 1, lg, 2 * (int64_t)D, D, st), "gamma2 / beta2"));
+  RM_TIMED("sums_ln", st, RM_HIP(rm::launch_sum_parts(w.ln1p, g->ln1_g, g->ln1_b, 1, lg, 2 * (int64_t)D, D, st), "gamma1 / beta1"));
+  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b2p, g->b2, nullptr, T, rt, D, D, st), "b2"));
+  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b1p, g->b1, nullptr, T, rt, Hd, Hd, st), "b1"));
+  return ok();
+}
+
 size_t rm_model_workspace_bytes(const rm_model_desc* m, int64_t B) {
   if (!m || (m->L > 0 && !m->blocks)) return 0;
   Carver c(nullptr);

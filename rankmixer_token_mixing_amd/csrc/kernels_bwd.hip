@@ -1,0 +1,427 @@
+// Kernels of the dense block backward (the chain rule through the block of
+// "Rankmixer: 硬件效率优化", section "RankMixer整体架构"; the pages print no
+// backward).  The four gradient products run on the grouped GEMM; these are
+// the HBM-bound pieces around them:
+//  * k_ln_bwd: LayerNorm backward, one row per wave, fp32 math, with the
+//    gamma / beta gradients accumulated per workgroup in a fixed order;
+//  * k_transpose: [G][R][C] -> [G][C][ldo] through a 64 x 64 LDS tile, with an
+//    elementwise op on the way (GELU, or the GELU derivative times an upstream
+//    gradient), an optional untransposed copy of the result and optional
+//    per-tile column sums (the bias gradients);
+//  * k_tm_add: dX = dY1 + TM(dY1), the token mix being its own transpose;
+//  * k_sum_parts: fixed-order sums of the per-workgroup / per-tile partials;
+//  * k_gelu_ew: H = GELU(U) for the training forward, which keeps U.
+// No floating-point atomics: every sum has one fixed order, so results are
+// bitwise reproducible.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rm {
+
+namespace {
+
+constexpr int kLnWaves = 4;       // rows (waves) per workgroup of k_ln_bwd
+constexpr int kLnBwdDmax = 4096;  // widest row: the waves' gamma/beta partials live in LDS (128 KB)
+__device__ __forceinline__ float ln_eps_b() { return 1e-5f; }
+
+// Phi(x) and phi(x) of the standard normal
+__device__ __forceinline__ float norm_cdf(float x) { return 0.5f * erfcf(-x * 0.70710678118654752f); }
+__device__ __forceinline__ float norm_pdf(float x) { return 0.3989422804014327f * expf(-0.5f * x * x); }
+// d/du GELU(u) = Phi(u) + u phi(u)
+__device__ __forceinline__ float gelu_grad(float u) { return norm_cdf(u) + u * norm_pdf(u); }
+
+struct LnBwdArgs {
+  const void* dout;    // mode 0: dL/dX' rows [B][T][D]
+  const void* dres;    // mode 1: dY2, token-major [T][B][D]
+  const float* dres32; // mode 1: the W1-branch gradient of S, token-major fp32
+  const void* z;       // mode 0: Z (W2 product + b2) [B][T][D];  mode 1: X [B][T][D]
+  const void* res;     // mode 0: S, token-major
+  const float* gamma;
+  void* dy;            // mode 0: dY2 token-major (dtype);  mode 1: dY1 [B][T][D] fp32
+  float* part;         // [gridDim.x][2][D]: sum of dout * xhat, sum of dout
+  int64_t B;
+  int T, D;
+};
+
+// LayerNorm backward.  Mode 0 (LN2): Y = Z + S, upstream dX'.  Mode 1 (LN1):
+// Y = TM(X) + X gathered as the forward does, upstream dY2 + dS_ffn.  With
+// xhat = (Y - mean) * rstd and g = upstream * gamma:
+//   dY = (g - mean(g) - xhat * mean(g * xhat)) * rstd.
+// Element k of mixed token t is element t*d + (k mod d) of token k / d.
+// The gamma / beta partials of each wave accumulate in its own LDS region
+// [2][D] (dynamic LDS, kLnWaves * 2 * D floats), so registers hold only the
+// row being processed.
+template <typename T, int VEC, int MAXI, int MODE>
+__global__ __launch_bounds__(kLnWaves* kWave) void k_ln_bwd(LnBwdArgs a) {
+  extern __shared__ float wpart[];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int D = a.D, T_ = a.T, d = D / T_;
+  const int nch = D / VEC;
+  const int64_t rows = a.B * T_;
+  for (int k = threadIdx.x; k < kLnWaves * 2 * D; k += kLnWaves * kWave) wpart[k] = 0.f;
+  __syncthreads();
+  float* pg = wpart + wave * 2 * D;
+  float* pb = pg + D;
+
+  for (int64_t row = (int64_t)blockIdx.x * kLnWaves + wave; row < rows; row += (int64_t)gridDim.x * kLnWaves) {
+    const int64_t b = row / T_;
+    const int t = (int)(row - b * T_);
+    const int64_t tm = (int64_t)t * a.B + b;  // token-major row index
+    float y[MAXI][VEC], up[MAXI][VEC];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nch) {
+        const int k = c * VEC;
+        float p[VEC], q[VEC];
+        if constexpr (MODE == 0) {
+          load_f32<T, VEC>((const T*)a.z + row * D + k, p);
+          load_f32<T, VEC>((const T*)a.res + tm * D + k, q);
+          load_f32<T, VEC>((const T*)a.dout + row * D + k, up[i]);
+        } else {
+          const T* xb = (const T*)a.z + b * (int64_t)T_ * D;
+          const int tp = k / d, j = k - tp * d;
+          load_f32<T, VEC>(xb + (int64_t)tp * D + t * d + j, p);
+          load_f32<T, VEC>(xb + (int64_t)t * D + k, q);
+          float r[VEC];
+          load_f32<T, VEC>((const T*)a.dres + tm * D + k, up[i]);
+          load_f32<float, VEC>(a.dres32 + tm * D + k, r);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) up[i][e] += r[e];
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          y[i][e] = p[e] + q[e];
+          sum += y[i][e];
+        }
+      }
+    }
+    const float mean = wave_sum(sum) / (float)D;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nch) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float q = y[i][e] - mean;
+          sq += q * q;
+        }
+      }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D + ln_eps_b());
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nch) {
+        const int k = c * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          y[i][e] = (y[i][e] - mean) * rstd;  // xhat from here on
+          const float g = up[i][e] * a.gamma[k + e];
+          sg += g;
+          sgx += g * y[i][e];
+          pg[k + e] += up[i][e] * y[i][e];
+          pb[k + e] += up[i][e];
+        }
+      }
+    }
+    const float mg = wave_sum(sg) / (float)D, mgx = wave_sum(sgx) / (float)D;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nch) {
+        const int k = c * VEC;
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = (up[i][e] * a.gamma[k + e] - mg - y[i][e] * mgx) * rstd;
+        if constexpr (MODE == 0)
+          store_from_f32<T, VEC>((T*)a.dy + tm * D + k, o);
+        else
+          store_from_f32<float, VEC>((float*)a.dy + row * D + k, o);
+      }
+    }
+  }
+  // workgroup partials: the waves' regions added in a fixed order
+  __syncthreads();
+  float* out = a.part + (int64_t)blockIdx.x * 2 * D;
+  for (int k = threadIdx.x; k < 2 * D; k += kLnWaves * kWave) {
+    float v = wpart[k];
+#pragma unroll
+    for (int w = 1; w < kLnWaves; ++w) v += wpart[w * 2 * D + k];
+    out[k] = v;
+  }
+}
+
+struct TrArgs {
+  const void* in;   // [G][R][C], rows of C elements
+  const void* aux;  // op 2: U, same layout as in
+  void* out;        // [G][C][ldo]: out[g][c][r] = op(in[g][r][c]), zero for R <= r < rows covered
+  void* direct;     // op 2, optional: op(in) in the input's layout
+  float* colsum;    // optional [G][row tiles][C]: per 64-row tile sums of op(in) over r
+  int64_t R, C, ldo;
+};
+
+// op 0: x;  op 1: GELU(x);  op 2: x * GELU'(aux)
+template <typename T, int OP>
+__global__ __launch_bounds__(256) void k_transpose(TrArgs a) {
+  __shared__ float tile[64][65];
+  const int tid = threadIdx.x;
+  const int64_t g = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const T* in = (const T*)a.in + g * a.R * a.C;
+  {
+    const int rl = tid >> 2, cl = (tid & 3) * 16;
+    const int64_t r = r0 + rl;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t c = c0 + cl + 8 * h;
+      float v[8];
+      if (r < a.R && c < a.C) {
+        load_f32<T, 8>(in + r * a.C + c, v);
+        if constexpr (OP == 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
+        } else if constexpr (OP == 2) {
+          float u[8];
+          load_f32<T, 8>((const T*)a.aux + g * a.R * a.C + r * a.C + c, u);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= gelu_grad(u[e]);
+          if (a.direct) store_from_f32<T, 8>((T*)a.direct + g * a.R * a.C + r * a.C + c, v);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[rl][cl + 8 * h + e] = v[e];
+    }
+  }
+  __syncthreads();
+  {
+    const int cl = tid >> 2, rl = (tid & 3) * 16;
+    const int64_t c = c0 + cl;
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t r = r0 + rl + 8 * h;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = tile[rl + 8 * h + e][cl];
+        s += v[e];
+      }
+      if (c < a.C && r < a.ldo) store_from_f32<T, 8>((T*)a.out + g * a.C * a.ldo + c * a.ldo + r, v);
+    }
+    if (a.colsum) {
+      s += __shfl_xor(s, 1, kWave);
+      s += __shfl_xor(s, 2, kWave);
+      if ((tid & 3) == 0 && c < a.C) a.colsum[(g * gridDim.y + blockIdx.y) * a.C + c] = s;
+    }
+  }
+}
+
+// dX[b,t,k] = dY1[b,t,k] + dY1[b, k/d, t*d + k%d]; VEC elements per thread
+// never straddle a head
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void k_tm_add(const float* __restrict__ dy, T* __restrict__ dx, int64_t B, int T_,
+                                                int D) {
+  const int64_t n = B * T_ * (int64_t)D / VEC;
+  const int d = D / T_;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = i * VEC;
+    const int64_t b = e0 / ((int64_t)T_ * D);
+    const int rem = (int)(e0 - b * T_ * (int64_t)D);
+    const int t = rem / D, k = rem - t * D;
+    const int tp = k / d, j = k - tp * d;
+    float p[VEC], q[VEC];
+    load_f32<float, VEC>(dy + e0, p);
+    load_f32<float, VEC>(dy + b * T_ * (int64_t)D + (int64_t)tp * D + t * d + j, q);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) p[e] += q[e];
+    store_from_f32<T, VEC>(dx + e0, p);
+  }
+}
+
+// out[g][c] = sum over p < P of part[(g * P + p) * C + c]; columns c < split
+// go to out0[g * split + c], the rest to out1[g * (C - split) + c - split].
+// A workgroup owns 64 columns of one g: lane group q < 4 sums p = q, q+4, ...
+// in order, then the four sums are added in order -- a fixed order throughout.
+__global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ part, float* __restrict__ out0,
+                                                   float* __restrict__ out1, int P, int64_t C, int64_t split) {
+  __shared__ float acc[4][64];
+  const int cl = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t g = blockIdx.y, c = (int64_t)blockIdx.x * 64 + cl;
+  float s = 0.f;
+  if (c < C) {
+    const float* p = part + g * P * C + c;
+    int i = q;
+    for (; i + 12 < P; i += 16) {
+      const float a0 = p[(int64_t)i * C], a1 = p[(int64_t)(i + 4) * C], a2 = p[(int64_t)(i + 8) * C],
+                  a3 = p[(int64_t)(i + 12) * C];
+      s += a0;
+      s += a1;
+      s += a2;
+      s += a3;
+    }
+    for (; i < P; i += 4) s += p[(int64_t)i * C];
+  }
+  acc[q][cl] = s;
+  __syncthreads();
+  if (q == 0 && c < C) {
+    const float v = ((acc[0][cl] + acc[1][cl]) + acc[2][cl]) + acc[3][cl];
+    if (c < split)
+      out0[g * split + c] = v;
+    else
+      out1[g * (C - split) + c - split] = v;
+  }
+}
+
+// H = GELU(U), 8 elements per thread
+template <typename T>
+__global__ __launch_bounds__(256) void k_gelu_ew(const T* __restrict__ u, T* __restrict__ h, int64_t n8) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    float v[8];
+    load_f32<T, 8>(u + i * 8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
+    store_from_f32<T, 8>(h + i * 8, v);
+  }
+}
+
+int ln_slots(int chunks) {
+  const int need = (chunks + kWave - 1) / kWave;
+  if (need <= 1) return 1;
+  if (need <= 2) return 2;
+  if (need <= 4) return 4;
+  if (need <= 8) return 8;
+  if (need <= 16) return 16;
+  return 0;
+}
+
+int chunk_of(int d, int eb) {
+  const int max_e = 16 / eb;
+  for (int v = max_e; v > 1; v >>= 1)
+    if (d % v == 0) return v;
+  return 1;
+}
+
+template <typename T, int VEC, int MODE>
+hipError_t ln_bwd_vec(const LnBwdArgs& a, int grid, hipStream_t s) {
+  const dim3 block(kLnWaves * kWave);
+  const size_t lds = (size_t)kLnWaves * 2 * a.D * sizeof(float);
+  switch (ln_slots(a.D / VEC)) {
+    case 1: hipLaunchKernelGGL((k_ln_bwd<T, VEC, 1, MODE>), dim3(grid), block, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_ln_bwd<T, VEC, 2, MODE>), dim3(grid), block, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_ln_bwd<T, VEC, 4, MODE>), dim3(grid), block, lds, s, a); break;
+    case 8: hipLaunchKernelGGL((k_ln_bwd<T, VEC, 8, MODE>), dim3(grid), block, lds, s, a); break;
+    case 16: hipLaunchKernelGGL((k_ln_bwd<T, VEC, 16, MODE>), dim3(grid), block, lds, s, a); break;
+    default: return hipErrorInvalidValue;  // a row wider than 1024 chunks
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int MODE>
+hipError_t ln_bwd_t(const LnBwdArgs& a, int grid, hipStream_t s) {
+  // mode 1 gathers within heads: chunks must not straddle one
+  const int vec = MODE == 0 ? 8 : chunk_of(a.D / a.T, (int)sizeof(T));
+  switch (vec) {
+    case 8: return ln_bwd_vec<T, 8, MODE>(a, grid, s);
+    case 4: return ln_bwd_vec<T, 4, MODE>(a, grid, s);
+    case 2: return ln_bwd_vec<T, 2, MODE>(a, grid, s);
+    default: return ln_bwd_vec<T, 1, MODE>(a, grid, s);
+  }
+}
+
+}  // namespace
+
+int ln_bwd_grid(int64_t B, int T) {
+  const int64_t rows = B * T;
+  const int64_t want = (rows + kLnWaves * 8 - 1) / (kLnWaves * 8);  // about 8 rows per wave
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, 2 * (int64_t)device_cus()));
+}
+
+int ln_bwd_max_width() { return kLnBwdDmax; }
+
+hipError_t launch_ln_bwd(int mode, const void* dout, const void* dres, const float* dres32, const void* z,
+                         const void* res, const float* gamma, void* dy, float* part, int64_t B, int T, int D, int dt,
+                         hipStream_t s) {
+  if (D > kLnBwdDmax || D % 8 || D % T) return hipErrorInvalidValue;
+  LnBwdArgs a{dout, dres, dres32, z, res, gamma, dy, part, B, T, D};
+  const int grid = ln_bwd_grid(B, T);
+  if (dt == kBF16)
+    return mode == 0 ? ln_bwd_t<bf16, 0>(a, grid, s) : ln_bwd_t<bf16, 1>(a, grid, s);
+  return mode == 0 ? ln_bwd_t<float, 0>(a, grid, s) : ln_bwd_t<float, 1>(a, grid, s);
+}
+
+int transpose_row_tiles(int64_t R, int64_t ldo) { return (int)((std::max(R, ldo) + 63) / 64); }
+
+hipError_t launch_transpose(int op, const void* in, const void* aux, void* out, void* direct, float* colsum, int G,
+                            int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s) {
+  if (C % 8 || ldo % 8 || ldo < R || G <= 0) return hipErrorInvalidValue;
+  if (R == 0 && ldo == 0) return hipSuccess;
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)transpose_row_tiles(R, ldo), (unsigned)G);
+  TrArgs a{in, aux, out, direct, colsum, R, C, ldo};
+  const dim3 block(256);
+  if (dt == kBF16) {
+    switch (op) {
+      case 0: hipLaunchKernelGGL((k_transpose<bf16, 0>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((k_transpose<bf16, 1>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((k_transpose<bf16, 2>), grid, block, 0, s, a); break;
+    }
+  } else {
+    switch (op) {
+      case 0: hipLaunchKernelGGL((k_transpose<float, 0>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((k_transpose<float, 1>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((k_transpose<float, 2>), grid, block, 0, s, a); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tm_add(const float* dy, void* dx, int64_t B, int T, int D, int dt, hipStream_t s) {
+  const int vec = chunk_of(D / T, 4);  // fp32 input: at most 4 elements per 16 bytes
+  const int64_t n = B * T * (int64_t)D / vec;
+  const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 65536)));
+  if (dt == kBF16) {
+    switch (vec) {
+      case 4: hipLaunchKernelGGL((k_tm_add<bf16, 4>), grid, dim3(256), 0, s, dy, (bf16*)dx, B, T, D); break;
+      case 2: hipLaunchKernelGGL((k_tm_add<bf16, 2>), grid, dim3(256), 0, s, dy, (bf16*)dx, B, T, D); break;
+      default: hipLaunchKernelGGL((k_tm_add<bf16, 1>), grid, dim3(256), 0, s, dy, (bf16*)dx, B, T, D); break;
+    }
+  } else {
+    switch (vec) {
+      case 4: hipLaunchKernelGGL((k_tm_add<float, 4>), grid, dim3(256), 0, s, dy, (float*)dx, B, T, D); break;
+      case 2: hipLaunchKernelGGL((k_tm_add<float, 2>), grid, dim3(256), 0, s, dy, (float*)dx, B, T, D); break;
+      default: hipLaunchKernelGGL((k_tm_add<float, 1>), grid, dim3(256), 0, s, dy, (float*)dx, B, T, D); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_parts(const float* part, float* out0, float* out1, int G, int P, int64_t C, int64_t split,
+                            hipStream_t s) {
+  if ((int64_t)G * C == 0) return hipSuccess;
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)G);
+  hipLaunchKernelGGL(k_sum_parts, grid, dim3(256), 0, s, part, out0, out1, P, C, split);
+  return hipGetLastError();
+}
+
+hipError_t launch_gelu_ew(const void* u, void* h, int64_t n, int dt, hipStream_t s) {
+  if (n % 8) return hipErrorInvalidValue;
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>((n8 + 255) / 256, 65536)));
+  if (dt == kBF16)
+    hipLaunchKernelGGL((k_gelu_ew<bf16>), grid, dim3(256), 0, s, (const bf16*)u, (bf16*)h, n8);
+  else
+    hipLaunchKernelGGL((k_gelu_ew<float>), grid, dim3(256), 0, s, (const float*)u, (float*)h, n8);
+  return hipGetLastError();
+}
+
+}  // namespace rm

@@ -98,6 +98,33 @@ struct GemmArgs {
 int gemm_tile_m(const GemmArgs& a);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
+// ---- dense block backward (kernels_bwd.hip) -----------------------------------
+
+// LayerNorm backward over rows (b, t).  mode 0: Y = z + res (z [B][T][D], res
+// token-major), upstream dout [B][T][D], dY written token-major in dt.  mode 1:
+// Y = TM(z) + z (z = X [B][T][D]), upstream dres (token-major, dt) + dres32
+// (token-major fp32), dY written [B][T][D] fp32.  part receives, per workgroup
+// g < ln_bwd_grid(B, T), the partial sums of dout * xhat and dout: part[g][2][D].
+int ln_bwd_grid(int64_t B, int T);
+int ln_bwd_max_width();
+hipError_t launch_ln_bwd(int mode, const void* dout, const void* dres, const float* dres32, const void* z,
+                         const void* res, const float* gamma, void* dy, float* part, int64_t B, int T, int D, int dt,
+                         hipStream_t s);
+// out[g][c][r] = op(in[g][r][c]) for r < ldo (zero for r >= R), in [G][R][C];
+// op 0 identity, 1 GELU, 2 in * GELU'(aux) (direct, if set, receives op(in) in
+// the input layout).  colsum, if set, receives [G][transpose_row_tiles][C]
+// sums of op(in) over each 64-row tile.  C and ldo multiples of 8, ldo >= R.
+int transpose_row_tiles(int64_t R, int64_t ldo);
+hipError_t launch_transpose(int op, const void* in, const void* aux, void* out, void* direct, float* colsum, int G,
+                            int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s);
+// dx = dy + TM(dy): dy fp32 [B][T][D], dx in dt
+hipError_t launch_tm_add(const float* dy, void* dx, int64_t B, int T, int D, int dt, hipStream_t s);
+// out[g][c] = sum_p part[g][p][c] (fixed order); c < split -> out0, else out1
+hipError_t launch_sum_parts(const float* part, float* out0, float* out1, int G, int P, int64_t C, int64_t split,
+                            hipStream_t s);
+// h = GELU(u), n elements (a multiple of 8)
+hipError_t launch_gelu_ew(const void* u, void* h, int64_t n, int dt, hipStream_t s);
+
 // ---- projection tokenizer (kernels_tokproj.hip) -------------------------------
 
 // x0[b][t][:] = W_t . bf16(pad(emb[b])[t*seg : (t+1)*seg]) + bias_t in one

@@ -200,3 +200,42 @@ def test_projection_tokenizer_errors(lib):
     assert lib.rm_tokenize_project(*args, 5000, 16, 320, 320, bd.RM_F32, *f32) == bd.RM_ERR_INVALID
     assert "b is NULL" in err(lib)
     assert lib.rm_tokenize_project(None, None, 0, 5000, 16, 320, 320, bd.RM_BF16, None, None, 0, None) == bd.RM_OK
+
+
+def _dense_bp():
+    bp = bd.BlockParams()
+    bp.kind = bd.RM_BLOCK_DENSE
+    bp.ln1_g = bp.ln1_b = bp.ln2_g = bp.ln2_b = A16
+    bp.pffn = _pffn()
+    return bp
+
+
+def test_training_entry_points_check_their_arguments(lib):
+    bp = _dense_bp()
+    sv = lib.rm_block_saved_bytes(64, 4, 64, 128, bd.RM_BF16)
+    assert sv >= 64 * 4 * (64 + 128 + 64) * 2
+    wsf = lib.rm_block_workspace_bytes(0, 64, 4, 64, 128, 0, bd.RM_BF16)
+    wsb = lib.rm_block_bwd_workspace_bytes(64, 4, 64, 128, bd.RM_BF16)
+    assert wsb > wsf
+    fwd = lambda *a: lib.rm_block_fwd_train(A16, C.byref(bp), A16 * 2, A16 * 3, *a)
+    assert fwd(sv - 1, 64, 4, 64, 128, bd.RM_BF16, A16 * 4, wsf, None) == bd.RM_ERR_WORKSPACE
+    assert "saved" in err(lib)
+    assert fwd(sv, 64, 4, 64, 128, bd.RM_BF16, A16 * 4, wsf - 1, None) == bd.RM_ERR_WORKSPACE
+    assert fwd(sv, 64, 4, 8192, 128, bd.RM_BF16, A16 * 4, 1 << 40, None) == bd.RM_ERR_UNSUPPORTED  # D > 4096
+    moe = bd.BlockParams()
+    moe.kind = bd.RM_BLOCK_MOE
+    moe.ln1_g = moe.ln1_b = moe.ln2_g = moe.ln2_b = A16
+    moe.moe = bd.MoeParams(A16, A16, A16, A16, A16, A16)
+    assert lib.rm_block_fwd_train(A16, C.byref(moe), A16 * 2, A16 * 3, sv, 64, 4, 64, 128, bd.RM_BF16, A16 * 4, wsf,
+                                  None) == bd.RM_ERR_UNSUPPORTED
+    assert "dense" in err(lib)
+    g = bd.BlockGrads(*([A16 * 5] * 8))
+    bwd = lambda dx, gg, ws_bytes: lib.rm_block_bwd(A16, C.byref(bp), A16 * 3, sv, A16 * 6, dx, gg, 64, 4, 64, 128,
+                                                    bd.RM_BF16, A16 * 4, ws_bytes, None)
+    assert bwd(A16 * 7, C.byref(g), wsb - 1) == bd.RM_ERR_WORKSPACE
+    assert bwd(A16, C.byref(g), wsb) == bd.RM_ERR_INVALID  # dx aliases x
+    assert "alias" in err(lib)
+    assert bwd(A16 * 7, None, wsb) == bd.RM_ERR_INVALID
+    g.b2 = None
+    assert bwd(A16 * 7, C.byref(g), wsb) == bd.RM_ERR_INVALID
+    assert "grads.b2" in err(lib)
