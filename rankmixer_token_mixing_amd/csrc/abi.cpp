@@ -756,9 +756,9 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   // X' = LN2(Z + S): dV = dY2 (token-major), gamma2 / beta2 partials
   RM_TIMED("ln2_bwd", st, RM_HIP(rm::launch_ln_bwd(0, d_out, nullptr, nullptr, sv.Z, sv.S, p->ln2_g, w.dV, w.ln2p, B, T, D, dt, st), "LayerNorm 2 backward"));
   // dV^T (rows padded to Bp) and the b2 partials
-  RM_TIMED("tr_dV", st, RM_HIP(rm::launch_transpose(0, w.dV, nullptr, w.dVt, nullptr, w.b2p, T, B, D, Bp, dt, st), "transpose dV"));
+  RM_TIMED("tr_dV", st, RM_HIP(rm::launch_transpose(0, w.dV, nullptr, w.dVt, nullptr, nullptr, w.b2p, T, B, D, Bp, dt, st), "transpose dV"));
   // W2^T [T][Hd][D]
-  RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->pffn.w2, nullptr, w.W2t, nullptr, nullptr, T, D, Hd, D, dt, st), "transpose W2"));
+  RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->pffn.w2, nullptr, w.W2t, nullptr, nullptr, nullptr, T, D, Hd, D, dt, st), "transpose W2"));
   // dH = dV W2
   rm::GemmArgs g1;
   g1.dt = dt; g1.epi = rm::kEpiBias;
@@ -767,9 +767,9 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   g1.W = w.W2t; g1.b_gs = (int64_t)Hd * D;
   g1.C = w.dH; g1.c_gs = B * Hd; g1.c_rs = Hd;
   RM_TIMED("bwd_dH", st, RM_HIP(rm::launch_gemm(g1, st), "dH product"));
-  // dU = dH * GELU'(U), also transposed, with the b1 partials; H^T = GELU(U)^T
-  RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.b1p, T, B, Hd, Bp, dt, st), "GELU backward"));
-  RM_TIMED("tr_H", st, RM_HIP(rm::launch_transpose(1, sv.U, nullptr, w.Ht, nullptr, nullptr, T, B, Hd, Bp, dt, st), "transpose H"));
+  // dU = dH * GELU'(U), also transposed, with the b1 partials, and H^T =
+  // GELU(U)^T from the same read of U
+  RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.Ht, w.b1p, T, B, Hd, Bp, dt, st), "GELU backward"));
   // dW2 = dV^T H (fp32)
   rm::GemmArgs g2;
   g2.dt = dt; g2.epi = rm::kEpiBiasF32;
@@ -779,7 +779,7 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   g2.C = g->w2; g2.c_gs = (int64_t)D * Hd; g2.c_rs = Hd;
   RM_TIMED("bwd_dW2", st, RM_HIP(rm::launch_gemm(g2, st), "dW2 product"));
   // dW1 = dU^T S (fp32)
-  RM_TIMED("tr_S", st, RM_HIP(rm::launch_transpose(0, sv.S, nullptr, w.St, nullptr, nullptr, T, B, D, Bp, dt, st), "transpose S"));
+  RM_TIMED("tr_S", st, RM_HIP(rm::launch_transpose(0, sv.S, nullptr, w.St, nullptr, nullptr, nullptr, T, B, D, Bp, dt, st), "transpose S"));
   rm::GemmArgs g3;
   g3.dt = dt; g3.epi = rm::kEpiBiasF32;
   g3.M = Hd; g3.N = D; g3.K = (int)Bp; g3.G = T;
@@ -788,7 +788,7 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   g3.C = g->w1; g3.c_gs = (int64_t)Hd * D; g3.c_rs = D;
   RM_TIMED("bwd_dW1", st, RM_HIP(rm::launch_gemm(g3, st), "dW1 product"));
   // dS (W1 branch) = dU W1 (fp32, token-major)
-  RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->pffn.w1, nullptr, w.W1t, nullptr, nullptr, T, Hd, D, Hd, dt, st), "transpose W1"));
+  RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->pffn.w1, nullptr, w.W1t, nullptr, nullptr, nullptr, T, Hd, D, Hd, dt, st), "transpose W1"));
   rm::GemmArgs g4;
   g4.dt = dt; g4.epi = rm::kEpiBiasF32;
   g4.M = (int)B; g4.N = D; g4.K = Hd; g4.G = T;

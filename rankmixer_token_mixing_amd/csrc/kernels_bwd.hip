@@ -163,6 +163,7 @@ struct TrArgs {
   const void* aux;  // op 2: U, same layout as in
   void* out;        // [G][C][ldo]: out[g][c][r] = op(in[g][r][c]), zero for R <= r < rows covered
   void* direct;     // op 2, optional: op(in) in the input's layout
+  void* out2;       // op 2, optional: GELU(aux) transposed like out
   float* colsum;    // optional [G][row tiles][C]: per 64-row tile sums of op(in) over r
   int64_t R, C, ldo;
 };
@@ -171,6 +172,7 @@ struct TrArgs {
 template <typename T, int OP>
 __global__ __launch_bounds__(256) void k_transpose(TrArgs a) {
   __shared__ float tile[64][65];
+  __shared__ float tile2[OP == 2 ? 64 : 1][65];
   const int tid = threadIdx.x;
   const int64_t g = blockIdx.z;
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
@@ -193,10 +195,17 @@ __global__ __launch_bounds__(256) void k_transpose(TrArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] *= gelu_grad(u[e]);
           if (a.direct) store_from_f32<T, 8>((T*)a.direct + g * a.R * a.C + r * a.C + c, v);
+          if (a.out2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tile2[rl][cl + 8 * h + e] = gelu_erf(u[e]);
         }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        if constexpr (OP == 2)
+          if (a.out2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tile2[rl][cl + 8 * h + e] = 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) tile[rl][cl + 8 * h + e] = v[e];
@@ -217,6 +226,13 @@ __global__ __launch_bounds__(256) void k_transpose(TrArgs a) {
         s += v[e];
       }
       if (c < a.C && r < a.ldo) store_from_f32<T, 8>((T*)a.out + g * a.C * a.ldo + c * a.ldo + r, v);
+      if constexpr (OP == 2) {
+        if (a.out2 && c < a.C && r < a.ldo) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = tile2[rl + 8 * h + e][cl];
+          store_from_f32<T, 8>((T*)a.out2 + g * a.C * a.ldo + c * a.ldo + r, v);
+        }
+      }
     }
     if (a.colsum) {
       s += __shfl_xor(s, 1, kWave);
@@ -361,12 +377,12 @@ hipError_t launch_ln_bwd(int mode, const void* dout, const void* dres, const flo
 
 int transpose_row_tiles(int64_t R, int64_t ldo) { return (int)((std::max(R, ldo) + 63) / 64); }
 
-hipError_t launch_transpose(int op, const void* in, const void* aux, void* out, void* direct, float* colsum, int G,
-                            int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s) {
+hipError_t launch_transpose(int op, const void* in, const void* aux, void* out, void* direct, void* out2,
+                            float* colsum, int G, int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s) {
   if (C % 8 || ldo % 8 || ldo < R || G <= 0) return hipErrorInvalidValue;
   if (R == 0 && ldo == 0) return hipSuccess;
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)transpose_row_tiles(R, ldo), (unsigned)G);
-  TrArgs a{in, aux, out, direct, colsum, R, C, ldo};
+  TrArgs a{in, aux, out, direct, out2, colsum, R, C, ldo};
   const dim3 block(256);
   if (dt == kBF16) {
     switch (op) {

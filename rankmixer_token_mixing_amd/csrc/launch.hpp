@@ -112,11 +112,12 @@ hipError_t launch_ln_bwd(int mode, const void* dout, const void* dres, const flo
                          hipStream_t s);
 // out[g][c][r] = op(in[g][r][c]) for r < ldo (zero for r >= R), in [G][R][C];
 // op 0 identity, 1 GELU, 2 in * GELU'(aux) (direct, if set, receives op(in) in
-// the input layout).  colsum, if set, receives [G][transpose_row_tiles][C]
-// sums of op(in) over each 64-row tile.  C and ldo multiples of 8, ldo >= R.
+// the input layout; out2, if set, receives GELU(aux) transposed like out).
+// colsum, if set, receives [G][transpose_row_tiles][C] sums of op(in) over
+// each 64-row tile.  C and ldo multiples of 8, ldo >= R.
 int transpose_row_tiles(int64_t R, int64_t ldo);
-hipError_t launch_transpose(int op, const void* in, const void* aux, void* out, void* direct, float* colsum, int G,
-                            int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s);
+hipError_t launch_transpose(int op, const void* in, const void* aux, void* out, void* direct, void* out2,
+                            float* colsum, int G, int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s);
 // dx = dy + TM(dy): dy fp32 [B][T][D], dx in dt
 hipError_t launch_tm_add(const float* dy, void* dx, int64_t B, int T, int D, int dt, hipStream_t s);
 // out[g][c] = sum_p part[g][p][c] (fixed order); c < split -> out0, else out1
