@@ -163,6 +163,34 @@ def pffn(S, w1, b1, w2, b2) -> np.ndarray:
     return V
 
 
+def silu(x) -> np.ndarray:
+    """SiLU (Swish with beta = 1): x * sigmoid(x)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def swiglu_pffn(S, w1, b1, w2, b2) -> np.ndarray:
+    """Per-token SwiGLU FFN ([TB] section 3.6, "SwiGLU D->4/3D", a drop-in for
+    the per-token FFN): for every token t,
+      v_t = W2_t (SiLU(Wg_t s_t + bg_t) * (Wu_t s_t + bu_t)) + b2_t,
+    '*' elementwise.  w1 [T, 2*Hs, D] holds the gate rows Wg_t (0 .. Hs-1) and
+    then the up rows Wu_t (Hs .. 2Hs-1); b1 [T, 2*Hs] likewise; w2 [T, D, Hs].
+    Reading: the pages name the variant only; it is taken with a bias on every
+    linear map, like the per-token FFN here (zero biases give the bias-free
+    form)."""
+    S = as_f64(S)
+    B, T, D = S.shape
+    Hs = w1.shape[1] // 2
+    V = np.empty((B, T, D))
+    for t in range(T):
+        W1 = as_f64(w1[t])
+        bb = as_f64(b1[t])
+        g = S[:, t, :] @ W1[:Hs].T + bb[:Hs]
+        u = S[:, t, :] @ W1[Hs:].T + bb[Hs:]
+        V[:, t, :] = (silu(g) * u) @ as_f64(w2[t]).T + as_f64(b2[t])
+    return V
+
+
 def moe_gates(S, wr, br) -> np.ndarray:
     """ReLU router ([FR] section "Sparse MoE扩展"; [WL] ReLU routing):
     G_{t,j} = ReLU(h(s_t))_j with h the per-token affine router.  Returns
@@ -202,11 +230,19 @@ def moe_relu_pffn(S, w1, b1, w2, b2, wr, br):
 def block_fwd(X, blk: dict) -> np.ndarray:
     """One RankMixer block ([FR] section "RankMixer整体架构", block equations):
     S = LN(TokenMixing(X) + X);  X' = LN(PFFN(S) + S).  A block whose params
-    hold a router ("wr") uses the ReLU-gated MoE in place of the PFFN."""
+    hold a router ("wr") uses the ReLU-gated MoE in place of the PFFN; one
+    marked "swiglu" uses the SwiGLU FFN.  A block marked "no_mix_norm" drops
+    the Add & Norm after the token mix ([TB] section 3.5, the variant that lost
+    it): S = TokenMixing(X)."""
     X = as_f64(X)
-    S = layer_norm(token_mix(X) + X, blk["ln1_g"], blk["ln1_b"])
+    if blk.get("no_mix_norm"):
+        S = token_mix(X)
+    else:
+        S = layer_norm(token_mix(X) + X, blk["ln1_g"], blk["ln1_b"])
     if "wr" in blk:
         V, _ = moe_relu_pffn(S, blk["w1"], blk["b1"], blk["w2"], blk["b2"], blk["wr"], blk["br"])
+    elif blk.get("swiglu"):
+        V = swiglu_pffn(S, blk["w1"], blk["b1"], blk["w2"], blk["b2"])
     else:
         V = pffn(S, blk["w1"], blk["b1"], blk["w2"], blk["b2"])
     return layer_norm(V + S, blk["ln2_g"], blk["ln2_b"])

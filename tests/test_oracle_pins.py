@@ -230,7 +230,7 @@ def test_pffn_locality():
 # brute force: every index written out, scalar math only
 
 
-def _bf_block(x, p, moe=None):
+def _bf_block(x, p, moe=None, swiglu=False, no_mix_norm=False):
     B, T, D = x.shape
     d = D // T
 
@@ -247,11 +247,20 @@ def _bf_block(x, p, moe=None):
         S = []
         for t in range(T):
             # element k of mixed token t is element (t*d + k%d) of token k//d
-            row = [x[b, k // d, t * d + k % d] + x[b, t, k] for k in range(D)]
-            S.append(ln(row, p["ln1_g"], p["ln1_b"]))
+            if no_mix_norm:
+                S.append([x[b, k // d, t * d + k % d] for k in range(D)])
+            else:
+                row = [x[b, k // d, t * d + k % d] + x[b, t, k] for k in range(D)]
+                S.append(ln(row, p["ln1_g"], p["ln1_b"]))
         for t in range(T):
             s = S[t]
-            if moe is None:
+            if swiglu:
+                Hs = p["w1"].shape[1] // 2
+                gate = [sum(p["w1"][t, n, k] * s[k] for k in range(D)) + p["b1"][t, n] for n in range(Hs)]
+                up = [sum(p["w1"][t, Hs + n, k] * s[k] for k in range(D)) + p["b1"][t, Hs + n] for n in range(Hs)]
+                h = [gate[n] / (1 + math.exp(-gate[n])) * up[n] for n in range(Hs)]
+                v = [sum(p["w2"][t, k, n] * h[n] for n in range(Hs)) + p["b2"][t, k] for k in range(D)]
+            elif moe is None:
                 Hd = p["w1"].shape[1]
                 h = [gel(sum(p["w1"][t, n, k] * s[k] for k in range(D)) + p["b1"][t, n]) for n in range(Hd)]
                 v = [sum(p["w2"][t, k, n] * h[n] for n in range(Hd)) + p["b2"][t, k] for k in range(D)]
@@ -294,6 +303,68 @@ def test_moe_block_matches_brute_force(T, D, E, He):
     blk.update(moe)
     x = rng.standard_normal((3, T, D))
     np.testing.assert_allclose(orc.block_fwd(x, blk), _bf_block(x, p, moe), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,D,Hs", [(1, 4, 6), (2, 4, 4), (4, 8, 12)])
+def test_swiglu_block_matches_brute_force(T, D, Hs):
+    # [TB] section 3.6: the SwiGLU per-token FFN in place of the GELU FFN
+    rng = _rng(30 + T)
+    p = _dense_params(rng, T, D, 2 * Hs)
+    p["w2"] = rng.standard_normal((T, D, Hs)) / math.sqrt(Hs)
+    p["swiglu"] = True
+    x = rng.standard_normal((2, T, D))
+    np.testing.assert_allclose(orc.block_fwd(x, p), _bf_block(x, p, swiglu=True), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,D,Hd", [(2, 4, 6), (4, 8, 16)])
+def test_no_mix_norm_block_matches_brute_force(T, D, Hd):
+    # [TB] section 3.5: the block without the Add & Norm after the token mix
+    rng = _rng(40 + T)
+    p = _dense_params(rng, T, D, Hd)
+    p["no_mix_norm"] = True
+    x = rng.standard_normal((2, T, D))
+    np.testing.assert_allclose(orc.block_fwd(x, p), _bf_block(x, p, no_mix_norm=True), rtol=0, atol=1e-12)
+
+
+def test_silu_matches_torch_and_closed_forms():
+    x = np.linspace(-30, 30, 121)
+    np.testing.assert_allclose(orc.silu(x), torch.nn.functional.silu(torch.from_numpy(x)).numpy(), rtol=1e-14,
+                               atol=1e-300)
+    assert orc.silu(0.0) == 0.0
+    assert orc.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+
+
+def test_swiglu_with_constant_up_branch_is_a_silu_ffn():
+    # Wu = 0, bu = 1: SwiGLU(s) = W2 SiLU(Wg s + bg) + b2, a plain FFN with SiLU (torch layers)
+    rng = _rng(50)
+    T, D, Hs = 3, 8, 10
+    w1 = np.concatenate([rng.standard_normal((T, Hs, D)), np.zeros((T, Hs, D))], axis=1)
+    b1 = np.concatenate([rng.standard_normal((T, Hs)), np.ones((T, Hs))], axis=1)
+    w2 = rng.standard_normal((T, D, Hs))
+    b2 = rng.standard_normal((T, D))
+    S = rng.standard_normal((4, T, D))
+    got = orc.swiglu_pffn(S, w1, b1, w2, b2)
+    for t in range(T):
+        with torch.no_grad():
+            h = torch.nn.functional.silu(torch.from_numpy(S[:, t]) @ torch.from_numpy(w1[t, :Hs]).T
+                                         + torch.from_numpy(b1[t, :Hs]))
+            ref = h @ torch.from_numpy(w2[t]).T + torch.from_numpy(b2[t])
+        np.testing.assert_allclose(got[:, t], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_no_mix_norm_T1_block_is_ffn_plus_residual_then_norm():
+    # T = 1 and no Add & Norm after the mix: S = X, X' = LN2(FFN(X) + X)
+    rng = _rng(51)
+    D, Hd = 16, 24
+    p = _dense_params(rng, 1, D, Hd)
+    p["no_mix_norm"] = True
+    x = rng.standard_normal((5, 1, D))
+    ffn = _torch_ffn(p["w1"][0], p["b1"][0], p["w2"][0], p["b2"][0])
+    with torch.no_grad():
+        xt = torch.from_numpy(x[:, 0])
+        ref = torch.nn.functional.layer_norm(ffn(xt) + xt, (D,), torch.from_numpy(p["ln2_g"]),
+                                             torch.from_numpy(p["ln2_b"]), 1e-5)
+    np.testing.assert_allclose(orc.block_fwd(x, p)[:, 0], ref.numpy(), rtol=0, atol=1e-12)
 
 
 # --------------------------------------------------------------------------
