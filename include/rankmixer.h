@@ -60,7 +60,11 @@ typedef enum rm_status {
 
 typedef enum rm_dtype { RM_F32 = 0, RM_BF16 = 1 } rm_dtype;
 
-typedef enum rm_block_kind { RM_BLOCK_DENSE = 0, RM_BLOCK_MOE = 1 } rm_block_kind;
+typedef enum rm_block_kind { RM_BLOCK_DENSE = 0, RM_BLOCK_MOE = 1, RM_BLOCK_SWIGLU = 2 } rm_block_kind;
+
+/* rm_block_params.flags: drop the Add & Norm after the token mix, S = TM(X)
+ * ([TB] section 3.5 reports the block that lost it) */
+#define RM_BLOCK_NO_MIX_NORM 1
 
 /* Per-token FFN of one block ([FR] "Per-Token FFN"; [WL] "Per-Token FFN"):
  *   v_t = W2_t GELU(W1_t s_t + b1_t) + b2_t,  t = 0..T-1, GELU the exact erf form.
@@ -89,7 +93,12 @@ typedef struct rm_moe_params {
 
 /* One block ([FR] "RankMixer整体架构", block equations):
  *   S = LN1(TokenMix(X) + X),   X' = LN2(F(S) + S),
- * F the per-token FFN (kind DENSE) or the ReLU MoE (kind MOE).  LayerNorm:
+ * F the per-token FFN (kind DENSE), the ReLU MoE (kind MOE) or the per-token
+ * SwiGLU FFN (kind SWIGLU, [TB] section 3.6 "SwiGLU D->4/3D"):
+ *   v_t = W2_t (SiLU(Wg_t s_t + bg_t) * (Wu_t s_t + bu_t)) + b2_t,
+ * its pffn.w1 [T][2*Hs][D] holding the gate rows Wg_t then the up rows Wu_t,
+ * pffn.b1 [T][2*Hs] likewise, pffn.w2 [T][D][Hs], hidden = Hs.  With flag
+ * RM_BLOCK_NO_MIX_NORM, S = TokenMix(X) (ln1_g / ln1_b unused).  LayerNorm:
  * biased variance over the D entries of one token, epsilon 1e-5. */
 typedef struct rm_block_params {
   int kind;                   /* rm_block_kind */
@@ -97,8 +106,9 @@ typedef struct rm_block_params {
   const float* ln1_b;         /* [D] */
   const float* ln2_g;         /* [D] */
   const float* ln2_b;         /* [D] */
-  rm_pffn_params pffn;        /* used when kind == RM_BLOCK_DENSE */
+  rm_pffn_params pffn;        /* used when kind == RM_BLOCK_DENSE or RM_BLOCK_SWIGLU */
   rm_moe_params moe;          /* used when kind == RM_BLOCK_MOE */
+  int flags;                  /* 0 or RM_BLOCK_NO_MIX_NORM */
 } rm_block_params;
 
 /* Gradients of one dense block: float32 device buffers, overwritten (not
@@ -221,7 +231,8 @@ size_t rm_model_workspace_bytes(const rm_model_desc* m, int64_t B);
  * b1 before GELU, the W2 product + b2; size rm_block_saved_bytes).  The output
  * equals rm_block_fwd's up to the rounding of the GELU input to dtype.
  *   Workspace: rm_block_workspace_bytes(RM_BLOCK_DENSE, B, T, D, hidden, 0, dtype).
- * Errors: an MoE block, D > 4096 -> RM_ERR_UNSUPPORTED (besides rm_block_fwd's). */
+ * Errors: a block that is not DENSE or has flags, D > 4096 -> RM_ERR_UNSUPPORTED
+ * (besides rm_block_fwd's). */
 size_t rm_block_saved_bytes(int64_t B, int T, int D, int hidden, int dtype);
 rm_status rm_block_fwd_train(const void* x, const rm_block_params* p, void* x_out, void* saved,
                              size_t saved_bytes, int64_t B, int T, int D, int hidden, int dtype,

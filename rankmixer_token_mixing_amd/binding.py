@@ -19,7 +19,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 
 RM_OK, RM_ERR_INVALID, RM_ERR_UNSUPPORTED, RM_ERR_WORKSPACE, RM_ERR_HIP = range(5)
 RM_F32, RM_BF16 = 0, 1
-RM_BLOCK_DENSE, RM_BLOCK_MOE = 0, 1
+RM_BLOCK_DENSE, RM_BLOCK_MOE, RM_BLOCK_SWIGLU = 0, 1, 2
+RM_BLOCK_NO_MIX_NORM = 1
 _DT = {torch.float32: RM_F32, torch.bfloat16: RM_BF16}
 
 
@@ -48,7 +49,7 @@ class MoeParams(C.Structure):
 
 class BlockParams(C.Structure):
     _fields_ = [("kind", C.c_int), ("ln1_g", C.c_void_p), ("ln1_b", C.c_void_p), ("ln2_g", C.c_void_p),
-                ("ln2_b", C.c_void_p), ("pffn", PffnParams), ("moe", MoeParams)]
+                ("ln2_b", C.c_void_p), ("pffn", PffnParams), ("moe", MoeParams), ("flags", C.c_int)]
 
 
 class BlockGrads(C.Structure):
@@ -183,9 +184,12 @@ def _moe_struct(p: dict) -> MoeParams:
 
 
 def _block_struct(p: dict) -> BlockParams:
+    """Block dict -> rm_block_params: a router ("wr") makes it an MoE block,
+    "swiglu": True a SwiGLU block, "no_mix_norm": True sets the flag."""
     moe = "wr" in p
     bp = BlockParams()
-    bp.kind = RM_BLOCK_MOE if moe else RM_BLOCK_DENSE
+    bp.kind = RM_BLOCK_MOE if moe else (RM_BLOCK_SWIGLU if p.get("swiglu") else RM_BLOCK_DENSE)
+    bp.flags = RM_BLOCK_NO_MIX_NORM if p.get("no_mix_norm") else 0
     bp.ln1_g, bp.ln1_b, bp.ln2_g, bp.ln2_b = _p(p["ln1_g"]), _p(p["ln1_b"]), _p(p["ln2_g"]), _p(p["ln2_b"])
     if moe:
         bp.moe = _moe_struct(p)
@@ -198,6 +202,8 @@ def _block_dims(p: dict):
     """(hidden, E) of a block's parameter dict."""
     if "wr" in p:
         return p["w1"].shape[2], p["w1"].shape[1]
+    if p.get("swiglu"):
+        return p["w1"].shape[1] // 2, 0
     return p["w1"].shape[1], 0
 
 
@@ -400,4 +406,5 @@ def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
 
 
 def upload_blocks(blocks: List[dict], device="cuda") -> List[dict]:
-    return [{k: to_device(v, device) for k, v in b.items()} for b in blocks]
+    """Arrays to device tensors; flags ("swiglu", "no_mix_norm") pass through."""
+    return [{k: (to_device(v, device) if isinstance(v, np.ndarray) else v) for k, v in b.items()} for b in blocks]

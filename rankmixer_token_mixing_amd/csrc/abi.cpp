@@ -202,16 +202,19 @@ size_t moe_ws(Carver& c, int64_t B, int T, int D, int E, int He, int dt, MoeWs* 
 
 struct BlockWs {
   void* S;
-  void* Z;  // W2 product + bias, activation dtype
+  void* Z;   // W2 product + bias, activation dtype
+  void* GU;  // SwiGLU: the gate | up product [T][B][2*Hs]
   PffnWs pffn;
   MoeWs moe;
 };
 size_t block_ws(Carver& c, int kind, int64_t B, int T, int D, int hidden, int E, int dt, BlockWs* w) {
   BlockWs x;
   x.S = c.take((size_t)B * T * D * elem_bytes(dt));
-  if (kind == RM_BLOCK_DENSE) {
+  x.GU = nullptr;
+  if (kind == RM_BLOCK_DENSE || kind == RM_BLOCK_SWIGLU) {
     x.Z = c.take((size_t)B * T * D * elem_bytes(dt));
     pffn_ws(c, B, T, hidden, dt, &x.pffn);
+    if (kind == RM_BLOCK_SWIGLU) x.GU = c.take((size_t)B * T * 2 * hidden * elem_bytes(dt));
   } else {
     x.Z = nullptr;
     moe_ws(c, B, T, D, E, hidden, dt, &x.moe);
@@ -301,7 +304,8 @@ rm_status check_block_params(const rm_block_params* p, int dt) {
   if (!p) return fail(RM_ERR_INVALID, "block params is NULL");
   RM_TRY(check_ptr(p->ln1_g, "ln1_g")); RM_TRY(check_ptr(p->ln1_b, "ln1_b"));
   RM_TRY(check_ptr(p->ln2_g, "ln2_g")); RM_TRY(check_ptr(p->ln2_b, "ln2_b"));
-  if (p->kind == RM_BLOCK_DENSE) {
+  if (p->flags & ~RM_BLOCK_NO_MIX_NORM) return fail(RM_ERR_UNSUPPORTED, "unknown block flags %d", p->flags);
+  if (p->kind == RM_BLOCK_DENSE || p->kind == RM_BLOCK_SWIGLU) {
     RM_TRY(check_ptr(p->pffn.w1, "pffn.w1")); RM_TRY(check_ptr(p->pffn.b1, "pffn.b1"));
     RM_TRY(check_ptr(p->pffn.w2, "pffn.w2")); RM_TRY(check_ptr(p->pffn.b2, "pffn.b2"));
   } else if (p->kind == RM_BLOCK_MOE) {
@@ -327,10 +331,29 @@ rm_status check_block_shape(int kind, int64_t B, int T, int D, int hidden, int E
 
 rm_status run_block(const void* x, const rm_block_params* p, void* xo, int64_t B, int T, int D, int hidden,
                     int E, int dt, const BlockWs& w, hipStream_t st) {
-  RM_TIMED("mix_ln1", st, RM_HIP(rm::launch_mix_ln(x, w.S, p->ln1_g, p->ln1_b, B, T, D, dt, true, st), "token mix + LayerNorm"));
-  const int64_t sb = D, sT = B * D;  // S is token-major
-  if (p->kind == RM_BLOCK_DENSE) {
-    RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(w.S, sb, sT, &p->pffn, w.pffn.H, B, T, D, hidden, dt), st), "block W1 product"));
+  int64_t sb, sT;  // S row (b, t) at b * sb + t * sT
+  if (p->flags & RM_BLOCK_NO_MIX_NORM) {
+    // S = TM(X), [B][T][D]
+    RM_TIMED("mix", st, RM_HIP(rm::launch_token_mix(x, w.S, B, T, D, dt, st), "token mix"));
+    sb = (int64_t)T * D;
+    sT = D;
+  } else {
+    // S = LN1(TM(X) + X), token-major so one token's rows are contiguous
+    RM_TIMED("mix_ln1", st, RM_HIP(rm::launch_mix_ln(x, w.S, p->ln1_g, p->ln1_b, B, T, D, dt, true, st), "token mix + LayerNorm"));
+    sb = D;
+    sT = B * D;
+  }
+  if (p->kind == RM_BLOCK_DENSE || p->kind == RM_BLOCK_SWIGLU) {
+    if (p->kind == RM_BLOCK_DENSE) {
+      RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(w.S, sb, sT, &p->pffn, w.pffn.H, B, T, D, hidden, dt), st), "block W1 product"));
+    } else {
+      // one product over the gate and up rows (N = 2*Hs, bias epilogue), then
+      // H = SiLU(G) * U
+      rm::GemmArgs a1 = ffn1_args(w.S, sb, sT, &p->pffn, w.GU, B, T, D, 2 * hidden, dt);
+      a1.epi = rm::kEpiBias;
+      RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block gate / up product"));
+      RM_TIMED("swiglu", st, RM_HIP(rm::launch_swiglu_ew(w.GU, w.pffn.H, B * T, hidden, dt, st), "SwiGLU"));
+    }
     rm::GemmArgs a2 = ffn2_args(w.pffn.H, &p->pffn, B, T, D, hidden, dt);
     // Z = W2 product + bias in the activation dtype; the residual S is added
     // inside LayerNorm 2 (fp32 arithmetic), which streams Z anyway, instead of
@@ -660,7 +683,8 @@ size_t bwd_carve(Carver& c, int64_t B, int T, int D, int Hd, int dt, BwdWs* w) {
 
 rm_status check_train_shape(const rm_block_params* p, int64_t B, int T, int D, int hidden, int dt) {
   RM_TRY(check_block_params(p, dt));
-  if (p->kind != RM_BLOCK_DENSE) return fail(RM_ERR_UNSUPPORTED, "training supports dense blocks only");
+  if (p->kind != RM_BLOCK_DENSE || p->flags)
+    return fail(RM_ERR_UNSUPPORTED, "training supports dense blocks (GELU FFN, Add & Norm after the mix) only");
   RM_TRY(check_block_shape(RM_BLOCK_DENSE, B, T, D, hidden, 0, dt));
   if (D > rm::ln_bwd_max_width())
     return fail(RM_ERR_UNSUPPORTED, "D=%d is wider than the backward row kernels support (%d)", D, rm::ln_bwd_max_width());

@@ -126,6 +126,11 @@ hipError_t launch_sum_parts(const float* part, float* out0, float* out1, int G, 
 // h = GELU(u), n elements (a multiple of 8)
 hipError_t launch_gelu_ew(const void* u, void* h, int64_t n, int dt, hipStream_t s);
 
+// ---- block variants (kernels_variants.hip) -------------------------------------
+
+// SwiGLU: h[r][j] = SiLU(gu[r][j]) * gu[r][Hs + j] over rows of 2*Hs (Hs % 8 == 0)
+hipError_t launch_swiglu_ew(const void* gu, void* h, int64_t rows, int Hs, int dt, hipStream_t s);
+
 // ---- projection tokenizer (kernels_tokproj.hip) -------------------------------
 
 // x0[b][t][:] = W_t . bf16(pad(emb[b])[t*seg : (t+1)*seg]) + bias_t in one

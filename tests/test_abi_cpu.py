@@ -239,3 +239,20 @@ def test_training_entry_points_check_their_arguments(lib):
     g.b2 = None
     assert bwd(A16 * 7, C.byref(g), wsb) == bd.RM_ERR_INVALID
     assert "grads.b2" in err(lib)
+
+
+def test_block_flags_and_variant_kinds(lib):
+    bp = _dense_bp()
+    bp.flags = 2  # not a known flag
+    assert lib.rm_block_fwd(A16, C.byref(bp), A16 * 2, 8, 4, 64, 128, 0, bd.RM_BF16, A16 * 3, 1 << 30,
+                            None) == bd.RM_ERR_UNSUPPORTED
+    assert "flags" in err(lib)
+    # the SwiGLU block needs room for the gate | up product as well
+    assert lib.rm_block_workspace_bytes(bd.RM_BLOCK_SWIGLU, 64, 4, 64, 128, 0, bd.RM_BF16) > \
+        lib.rm_block_workspace_bytes(bd.RM_BLOCK_DENSE, 64, 4, 64, 128, 0, bd.RM_BF16)
+    # training covers the plain dense block only
+    sv = lib.rm_block_saved_bytes(64, 4, 64, 128, bd.RM_BF16)
+    for kind, flags in ((bd.RM_BLOCK_SWIGLU, 0), (bd.RM_BLOCK_DENSE, bd.RM_BLOCK_NO_MIX_NORM)):
+        bp.kind, bp.flags = kind, flags
+        assert lib.rm_block_fwd_train(A16, C.byref(bp), A16 * 2, A16 * 3, sv, 64, 4, 64, 128, bd.RM_BF16, A16 * 4,
+                                      1 << 30, None) == bd.RM_ERR_UNSUPPORTED
