@@ -312,16 +312,111 @@ def bench_block_bwd(args) -> int:
     return 0
 
 
+def bench_variants(args) -> int:
+    """The block variants of the Taobao report on the 100M-class width (B=2048,
+    T=16, D=768, bf16): the SwiGLU block D -> 4/3 D (hidden 1024) is the timed
+    step; the GELU FFN block D -> 2D (hidden 1536, the same parameters and
+    flops per token) and both without the Add & Norm after the mix are timed
+    beside it the same way (one rm_block_fwd per step)."""
+    import torch
+    import synthetic_inputs as si
+    from rankmixer_token_mixing_amd import binding as bd
+    from rankmixer_token_mixing_amd import perfmodel as pm
+
+    B, T, D = 2048, 16, 768
+    Hs, Hd = 4 * D // 3, 2 * D
+    x = bd.to_device(si.make_inputs(si.Config("variants", B=B, T=T, D=D, L=0, dtype="bf16"), seed=1)["x"])
+    cases = {
+        "swiglu_4_3": si.make_variant_block(T, D, Hs, "bf16", swiglu=True, seed=2),
+        "gelu_2": si.make_variant_block(T, D, Hd, "bf16", seed=3),
+        "swiglu_4_3_no_mix_norm": si.make_variant_block(T, D, Hs, "bf16", swiglu=True, no_mix_norm=True, seed=2),
+        "gelu_2_no_mix_norm": si.make_variant_block(T, D, Hd, "bf16", no_mix_norm=True, seed=3),
+    }
+    flops = 6 * B * T * D * Hs  # = 4 * B * T * D * Hd for Hd = 2D: the same for every case
+    res = {}
+    main_prof = {}
+    for name, host_blk in cases.items():
+        blk = bd.upload_blocks([host_blk])[0]
+        y = torch.empty_like(x)
+        for _ in range(args.warmup):
+            bd.rm_block_fwd(x, blk, out=y)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            bd.rm_block_fwd(x, blk, out=y)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if name == "swiglu_4_3" and not args.no_profile:
+            # per-launch HIP events in a separate pass (their own overhead stays
+            # out of the timed steps)
+            bd.profile_enable(True)
+            for _ in range(args.steps):
+                bd.rm_block_fwd(x, blk, out=y)
+            torch.cuda.synchronize()
+            main_prof = bd.profile_read()
+            bd.profile_enable(False)
+        ms = el * 1e3 / args.steps
+        res[name] = {"ms": round(ms, 4), "samples_per_s": round(B / (ms * 1e-3), 1),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        log(f"{name}: {ms:.4f} ms")
+    kernels = {}
+    for nm, (tot_ms, n) in main_prof.items():
+        kernels[nm] = {"avg_ms": round(tot_ms / max(n, 1), 5), "launches": n, "total_ms": round(tot_ms, 3)}
+    roofline = None
+    if "ffn1" in kernels:
+        f1 = T * pm.gemm_flops(B, 2 * Hs, D)
+        ach = f1 / (kernels["ffn1"]["avg_ms"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "ffn1 (gate | up product)", "achieved": round(ach, 1),
+                    "peak": pm.PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / pm.PEAK_BF16_TFLOPS, 4),
+                    "flop_per_launch": f1, "traffic": None}
+    main = res["swiglu_4_3"]
+    rec = {
+        "metric": "samples/sec RankMixer SwiGLU block fwd (bf16) + % of MI355X MFMA peak",
+        "value": main["samples_per_s"],
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"SwiGLU block D -> 4/3 D: B={B}, T={T}, D={D}, hidden {Hs}, bf16",
+                   "B": B, "T": T, "D": D, "hidden": Hs, "step": "rm_block_fwd over the batch"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "variants": res,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import rankmixer_oracle as orc
+        xh = si.make_inputs(si.Config("variants", B=B, T=T, D=D, L=0, dtype="bf16"), seed=1)["x"]
+        rows = si.random_rows(B, 256, seed=99)
+        t0 = time.perf_counter()
+        orc.block_fwd(xh[rows], cases["swiglu_4_3"])
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": len(rows) / dt, "unit": "samples/s", "cores": os.cpu_count() or 1,
+                               "kind": "oracle",
+                               "sample": f"{len(rows)} of {B} samples through the SwiGLU block (fp64 numpy, {dt:.1f} s)"}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", help="workload (c3 is the benchmarked one)")
-    ap.add_argument("--op", default="model", choices=["model", "tokenize_project", "block_bwd"],
+    ap.add_argument("--op", default="model", choices=["model", "tokenize_project", "block_bwd", "block_variants"],
                     help="model: the block stack (default); tokenize_project: the projection "
                          "tokenizer alone on the pad-split model's embedding; block_bwd: the dense "
-                         "block backward on block 0 of the workload")
+                         "block backward on block 0 of the workload; block_variants: the SwiGLU "
+                         "(D -> 4/3 D) block beside the GELU FFN (D -> 2D) block of equal parameters and "
+                         "flops, with and without the Add & Norm after the mix")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="samples in the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-launch HIP events")
@@ -363,6 +458,8 @@ def main() -> int:
         return bench_project(args)
     if args.op == "block_bwd":
         return bench_block_bwd(args)
+    if args.op == "block_variants":
+        return bench_variants(args)
 
     cfg = si.CONFIGS[args.config]
     t0 = time.perf_counter()

@@ -347,12 +347,21 @@ rm_status run_block(const void* x, const rm_block_params* p, void* xo, int64_t B
     if (p->kind == RM_BLOCK_DENSE) {
       RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(w.S, sb, sT, &p->pffn, w.pffn.H, B, T, D, hidden, dt), st), "block W1 product"));
     } else {
-      // one product over the gate and up rows (N = 2*Hs, bias epilogue), then
-      // H = SiLU(G) * U
-      rm::GemmArgs a1 = ffn1_args(w.S, sb, sT, &p->pffn, w.GU, B, T, D, 2 * hidden, dt);
-      a1.epi = rm::kEpiBias;
-      RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block gate / up product"));
-      RM_TIMED("swiglu", st, RM_HIP(rm::launch_swiglu_ew(w.GU, w.pffn.H, B * T, hidden, dt, st), "SwiGLU"));
+      // one product over the gate and up rows (N = 2*Hs); on the pipelined
+      // kernel its epilogue pairs them and writes H = SiLU(G) * U directly,
+      // otherwise the product writes [G | U] and a pointwise pass combines
+      rm::GemmArgs a1 = ffn1_args(w.S, sb, sT, &p->pffn, w.pffn.H, B, T, D, 2 * hidden, dt);
+      a1.c_gs = B * hidden;
+      a1.c_rs = hidden;
+      a1.epi = rm::kEpiSwiglu;
+      if (rm::gemm_pipe_eligible(a1)) {
+        RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block gate / up product + SwiGLU"));
+      } else {
+        a1 = ffn1_args(w.S, sb, sT, &p->pffn, w.GU, B, T, D, 2 * hidden, dt);
+        a1.epi = rm::kEpiBias;
+        RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block gate / up product"));
+        RM_TIMED("swiglu", st, RM_HIP(rm::launch_swiglu_ew(w.GU, w.pffn.H, B * T, hidden, dt, st), "SwiGLU"));
+      }
     }
     rm::GemmArgs a2 = ffn2_args(w.pffn.H, &p->pffn, B, T, D, hidden, dt);
     // Z = W2 product + bias in the activation dtype; the residual S is added

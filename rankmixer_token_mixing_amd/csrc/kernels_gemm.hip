@@ -586,9 +586,16 @@ __device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileI
   for (int j = 0; j < FN; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int n = t.n0 + wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
-      bias[j][q] = (p.bias && n < p.N) ? *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + n)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int nl = wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
+      int n = t.n0 + nl;
+      bool ok = n < p.N;
+      if constexpr (EPI == kEpiSwiglu) {  // the tile's column -> gate / up row, as the W operand
+        const int hs = p.N / 2, h = t.n0 / 2 + (nl & (BN / 2 - 1));
+        n = nl < BN / 2 ? h : hs + h;
+        ok = h < hs;
+      }
+      bias[j][q] = (p.bias && ok) ? *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + n)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -609,15 +616,35 @@ __device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileI
         }
     }
     __syncthreads();
+    if constexpr (EPI == kEpiSwiglu) {
+      // output chunk c of a row: SiLU(gate chunk c) * (up chunk c + OCH/2), the
+      // row half the tile wide, so a pass covers twice the rows
 #pragma unroll
-    for (int pass = 0; pass < SROWS / RPP; ++pass) {
-      const int sr = pass * RPP + tid / OCH;
-      const int c = tid % OCH;
-      const uint4 val = *reinterpret_cast<const uint4*>(stage + sr * (BN * 2) + ((c ^ (sr & (OCH - 1))) * 16));
-      const int m = t.m0 + (sr / 64) * 128 + h * 64 + (sr % 64);
-      if (m < t.Mg && t.n0 + c * 8 < p.N)
-        *reinterpret_cast<uint4*>((bf16*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + t.n0 + c * 8) =
-            val;
+      for (int pass = 0; pass < SROWS / (2 * RPP); ++pass) {
+        const int sr = pass * 2 * RPP + tid / (OCH / 2);
+        const int c = tid % (OCH / 2);
+        const int m = t.m0 + (sr / 64) * 128 + h * 64 + (sr % 64);
+        const int hcol = t.n0 / 2 + c * 8;
+        float g[8], u[8];
+        load_f32<bf16, 8>(reinterpret_cast<const bf16*>(stage + sr * (BN * 2) + ((c ^ (sr & (OCH - 1))) * 16)), g);
+        load_f32<bf16, 8>(
+            reinterpret_cast<const bf16*>(stage + sr * (BN * 2) + (((c + OCH / 2) ^ (sr & (OCH - 1))) * 16)), u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) g[e] = g[e] / (1.0f + __expf(-g[e])) * u[e];
+        if (m < t.Mg && hcol < p.N / 2)
+          store_from_f32<bf16, 8>((bf16*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + hcol, g);
+      }
+    } else {
+#pragma unroll
+      for (int pass = 0; pass < SROWS / RPP; ++pass) {
+        const int sr = pass * RPP + tid / OCH;
+        const int c = tid % OCH;
+        const int m = t.m0 + (sr / 64) * 128 + h * 64 + (sr % 64);
+        const uint4 val = *reinterpret_cast<const uint4*>(stage + sr * (BN * 2) + ((c ^ (sr & (OCH - 1))) * 16));
+        if (m < t.Mg && t.n0 + c * 8 < p.N)
+          *reinterpret_cast<uint4*>((bf16*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + t.n0 + c * 8) =
+              val;
+      }
     }
     __syncthreads();  // staging is free again
   }
@@ -643,9 +670,16 @@ __device__ __forceinline__ void pipe_epilogue_f32(const KParams& p, const TileId
   for (int j = 0; j < FN; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int n = t.n0 + wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
-      bias[j][q] = (p.bias && n < p.N) ? *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + n)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int nl = wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
+      int n = t.n0 + nl;
+      bool ok = n < p.N;
+      if constexpr (EPI == kEpiSwiglu) {  // the tile's column -> gate / up row, as the W operand
+        const int hs = p.N / 2, h = t.n0 / 2 + (nl & (BN / 2 - 1));
+        n = nl < BN / 2 ? h : hs + h;
+        ok = h < hs;
+      }
+      bias[j][q] = (p.bias && ok) ? *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + n)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -757,7 +791,16 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i) {
       const int row = 8 * (wave + i * NW) + (lane >> 3);
-      const int n = min(t.n0 + row, p.N - 1);
+      int n;
+      if constexpr (EPI == kEpiSwiglu) {
+        // tile columns [0, BN/2) are gate rows h0 + c, [BN/2, BN) the matching
+        // up rows Hs + h0 + c (h0 = n0 / 2), so each gate/up pair is in the tile
+        const int hs = p.N / 2;
+        const int h = min(t.n0 / 2 + (row & (BN / 2 - 1)), hs - 1);
+        n = row < BN / 2 ? h : hs + h;
+      } else {
+        n = min(t.n0 + row, p.N - 1);
+      }
       vw[i] = (uint32_t)(((long long)n * K + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
     }
   };
@@ -837,7 +880,7 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
       issue_w(1, 0);
       issue_a(2, 1);
     }
-    if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias)
+    if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias || EPI == kEpiSwiglu)
       pipe_epilogue_bf16<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
     else
       pipe_epilogue_f32<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
@@ -914,7 +957,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   if (grid.x == 0) return hipSuccess;
   if (ragged && !((a.epi == kEpiBiasGelu && a.a_rowidx) || (a.epi == kEpiBiasScaleF32 && !a.a_rowidx)))
     return hipErrorInvalidValue;
-  if (!ragged && !(a.epi == kEpiBiasGelu || a.epi == kEpiBias || a.epi == kEpiBiasF32)) return hipErrorInvalidValue;
+  if (!ragged && !(a.epi == kEpiBiasGelu || a.epi == kEpiBias || a.epi == kEpiBiasF32 || a.epi == kEpiSwiglu))
+    return hipErrorInvalidValue;
 
   if constexpr (FM == 4 && FN == 2) {
     // the pipelined ring addresses operands by 32-bit byte offsets from the
@@ -940,12 +984,16 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
             hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasGelu, false, false>), grid2, block, 0, s, p);
             break;
           case kEpiBias: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBias, false, false>), grid2, block, 0, s, p); break;
+          case kEpiSwiglu:
+            hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiSwiglu, false, false>), grid2, block, 0, s, p);
+            break;
           default: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasF32, false, false>), grid2, block, 0, s, p); break;
         }
       }
       return hipGetLastError();
     }
   }
+  if (a.epi == kEpiSwiglu) return hipErrorInvalidValue;  // the pipelined kernel only
   if (ragged) {
     if (a.a_rowidx)
       launch_one<NWM, NWN, FM, FN, kEpiBiasGelu, true, true>(a, p, grid, s, ring);
@@ -977,6 +1025,13 @@ int device_cus() {
 }
 
 int gemm_tile_m(const GemmArgs& a) { return kCfgs[choose_cfg(a)].bm(); }
+
+bool gemm_pipe_eligible(const GemmArgs& a) {
+  const TileCfg& t = kCfgs[choose_cfg(a)];
+  if (!(t.fm == 4 && t.fn == 2) || a.dt != kBF16 || a.K % 64 || a.pipe == 0) return false;
+  const long long arows = a.row_off && !a.a_rowidx ? (long long)a.M * a.G : a.M;
+  return ((arows - 1) * a.a_rs + a.K) * 2 < (1LL << 32) && ((long long)(a.N - 1) * a.K + a.K) * 2 < (1LL << 32);
+}
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   switch (choose_cfg(a)) {

@@ -65,6 +65,10 @@ enum Epilogue {
   kEpiBias = 1,           // C(dt)  = acc + bias[n]
   kEpiBiasF32 = 2,        // C(f32) = acc + bias[n]
   kEpiBiasScaleF32 = 3,   // C(f32) = rowscale[m] * (acc + bias[n])
+  // C(dt)[m][h] = SiLU(acc_g + bias[h]) * (acc_u + bias[Hs + h]), h < Hs = N/2:
+  // W rows 0..Hs-1 are the gate rows, Hs..N-1 the up rows; C is Hs wide.
+  // Pipelined kernel only (gemm_pipe_eligible).
+  kEpiSwiglu = 4,
 };
 
 // C_g[m][n] = sum_k A_g[m][k] * W_g[n][k], g = 0..G-1, followed by an epilogue.
@@ -97,6 +101,8 @@ struct GemmArgs {
 // built for this).
 int gemm_tile_m(const GemmArgs& a);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// whether launch_gemm would run `a` on the hand-scheduled pipelined kernel
+bool gemm_pipe_eligible(const GemmArgs& a);
 
 // ---- dense block backward (kernels_bwd.hip) -----------------------------------
 

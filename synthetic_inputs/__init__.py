@@ -237,6 +237,32 @@ def make_proj_inputs(B: int, F: int, T: int, seg: int, D: int, dtype: str, seed:
     return {"emb": emb, "w": to_bf16_bits(w) if dtype == "bf16" else w, "b": b}
 
 
+def make_variant_block(T: int, D: int, hidden: int, dtype: str, swiglu: bool = False, no_mix_norm: bool = False,
+                       seed: int = 1) -> dict:
+    """One block of the [TB] variants with the workload recipe: W ~ N(0,
+    1/fan_in), zero biases, gamma = 1, beta = 0.  SwiGLU blocks get w1
+    [T, 2*hidden, D] (gate rows, then up rows) and w2 [T, D, hidden]."""
+    dr = _Drawer(seed)
+    bf = dtype == "bf16"
+    n1 = 2 * hidden if swiglu else hidden
+    blk = {
+        "w1": dr.normal((T, n1, D), 1.0 / D),
+        "b1": np.zeros((T, n1), np.float32),
+        "w2": dr.normal((T, D, hidden), 1.0 / hidden),
+        "b2": np.zeros((T, D), np.float32),
+        "ln1_g": np.ones(D, np.float32), "ln1_b": np.zeros(D, np.float32),
+        "ln2_g": np.ones(D, np.float32), "ln2_b": np.zeros(D, np.float32),
+    }
+    if bf:
+        blk["w1"] = to_bf16_bits(blk["w1"])
+        blk["w2"] = to_bf16_bits(blk["w2"])
+    if swiglu:
+        blk["swiglu"] = True
+    if no_mix_norm:
+        blk["no_mix_norm"] = True
+    return blk
+
+
 def random_rows(B: int, n: int, seed: int = 12345) -> np.ndarray:
     """A seeded, sorted subset of n sample indices that always holds 0 and B-1."""
     if n >= B:

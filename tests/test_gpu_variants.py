@@ -60,7 +60,8 @@ def _x(B, T, D, dtype, seed):
     ("f32", 64, 4, 64, 88),        # fp32, hidden not a multiple of 64
     ("bf16", 300, 4, 96, 128),     # 4/3 D, ragged batch
     ("bf16", 1, 2, 16, 24),        # one sample
-    ("bf16", 1024, 16, 768, 1024), # 4/3 D at the 100M-class width: pipelined products
+    ("bf16", 1024, 16, 768, 1024), # 4/3 D at the 100M-class width: fused SwiGLU epilogue
+    ("bf16", 1100, 16, 768, 1000), # fused epilogue with a ragged last gate/up tile and ragged batch
 ])
 def test_swiglu_block_matches_oracle(dtype, B, T, D, Hs):
     from rankmixer_token_mixing_amd import binding as bd
