@@ -20,7 +20,8 @@
  *    NULL where stated.
  *  - B is the batch size; B = 0 is an empty batch: the call checks its other
  *    arguments, returns RM_OK and enqueues nothing (data pointers may then be
- *    NULL), except rm_block_bwd, which writes zero gradients.  B < 0 is
+ *    NULL), except the backward calls, which write zero gradients, and
+ *    rm_moe_block_fwd_train, which writes a zero sparsity loss.  B < 0 is
  *    RM_ERR_INVALID.
  *  - Width limits of this build: D a multiple of 8 (and of T wherever tokens
  *    are mixed), hidden widths a multiple of 8, one [D] row per wavefront in
@@ -258,6 +259,73 @@ size_t rm_block_bwd_workspace_bytes(int64_t B, int T, int D, int hidden, int dty
 rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* saved, size_t saved_bytes,
                        const void* d_out, void* dx, const rm_block_grads* g, int64_t B, int T,
                        int D, int hidden, int dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradients of one MoE block trained with the dense-training / sparse-
+ * inference routers: float32 device buffers, overwritten by rm_moe_block_bwd. */
+typedef struct rm_moe_grads {
+  float* w1;        /* [T][E][He][D] */
+  float* b1;        /* [T][E][He] */
+  float* w2;        /* [T][E][D][He] */
+  float* b2;        /* [T][E][D] */
+  float* wr_train;  /* [T][E][D]  training router h_train */
+  float* br_train;  /* [T][E] */
+  float* wr_infer;  /* [T][E][D]  inference router h_infer (p->moe.wr) */
+  float* br_infer;  /* [T][E] */
+  float* ln1_g;     /* [D] */
+  float* ln1_b;     /* [D] */
+  float* ln2_g;     /* [D] */
+  float* ln2_b;     /* [D] */
+} rm_moe_grads;
+
+/* MoE block training forward with two routers per token ([FR] "Sparse
+ * MoE扩展", dense-training / sparse-inference; [WL] ReLU routing):
+ *   S = LN1(TM(X) + X);  G_train = ReLU(S_t Wr_train_t^T + br_train_t)
+ *   G_infer = ReLU(S_t Wr_t^T + br_t)   (Wr, br: the block's own router p->moe)
+ *   v_t = sum_j G_train[t, j] * (W2_tj GELU(W1_tj s_t + b1_tj) + b2_tj)
+ *   X' = LN2(v + S);  *l_reg = sum over b, t, j of G_infer[b, t, j]
+ * The training router routes; the inference router only feeds the sparsity
+ * loss L_reg (at inference, rm_block_fwd routes with p->moe alone).  Every
+ * expert runs on every token (dense training); a zero gate contributes zero.
+ *   x: [B][T][D] dtype; p: an MoE block without flags; wr_train: [T][E][D]
+ *   dtype device; br_train: [T][E] fp32 device; x_out: [B][T][D] dtype;
+ *   l_reg: one fp32 on the device; saved: the caller's buffer of
+ *   rm_moe_saved_bytes for rm_moe_block_bwd (S, the W1 products + b1, the
+ *   expert outputs, both gate sets, v).
+ *   Workspace: rm_moe_train_workspace_bytes(B, T, D, He, E, dtype).
+ * B = 0 writes *l_reg = 0.
+ * Errors: a block that is not MOE or has flags, D > 4096, T*E not a multiple
+ * of 8, B*T*E*He >= 2^31 -> RM_ERR_UNSUPPORTED; NULL pointers, x_out aliasing
+ * x -> RM_ERR_INVALID; a short saved buffer or workspace -> RM_ERR_WORKSPACE. */
+size_t rm_moe_saved_bytes(int64_t B, int T, int D, int He, int E, int dtype);
+size_t rm_moe_train_workspace_bytes(int64_t B, int T, int D, int He, int E, int dtype);
+rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const void* wr_train,
+                                 const float* br_train, void* x_out, float* l_reg, void* saved,
+                                 size_t saved_bytes, int64_t B, int T, int D, int He, int E, int dtype,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* MoE block backward of L = <d_out, X'> + lambda * L_reg, the chain rule
+ * through the equations of rm_moe_block_fwd_train (the pages print no
+ * backward).  L_reg is applied to h_infer only, so its gradient reaches
+ * h_infer's weights and bias and nothing else; the task loss reaches every
+ * parameter but h_infer:
+ *   dV = LNbwd2(d_out);  dy_tj = G_train[t, j] dV_t;  dG_tj = dV_t . y_tj
+ *   experts (per t, j): db2 = sum_b dy;  dW2 = dy^T H;  dU = (dy W2) * GELU'(U)
+ *              db1 = sum_b dU;  dW1 = dU^T S_t;  dS_t += dU W1
+ *   h_train:   dz = dG [G_train > 0];  dbr_train = sum_b dz;  dWr_train = dz^T S_t;
+ *              dS_t += dz Wr_train_t
+ *   h_infer:   dzi = lambda [G_infer > 0];  dbr = sum_b dzi;  dWr = dzi^T S_t
+ *   dS += dV;  dY1 = LNbwd1(dS);  dX = dY1 + TM(dY1)
+ * Arguments as rm_moe_block_fwd_train (saved from that call on the same x and
+ * parameters); d_out, dx: [B][T][D] dtype; g: fp32 gradients.  Products in
+ * dtype with fp32 accumulation; every sum over the batch in a fixed order.
+ * B = 0 writes zero gradients.
+ *   Workspace: rm_moe_train_workspace_bytes(B, T, D, He, E, dtype) (the same
+ *   size as the forward's; the two calls may share one buffer).
+ * Errors: as rm_moe_block_fwd_train; dx aliasing x or d_out -> RM_ERR_INVALID. */
+rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* wr_train,
+                           const float* br_train, float lambda, const void* saved, size_t saved_bytes,
+                           const void* d_out, void* dx, const rm_moe_grads* g, int64_t B, int T, int D,
+                           int He, int E, int dtype, void* ws, size_t ws_bytes, void* stream);
 
 /* Launch timing for benchmarks.  While enabled, every group of kernel
  * launches an entry point makes (the W1 product, the W2 product, a LayerNorm,

@@ -57,6 +57,11 @@ class BlockGrads(C.Structure):
                 ("ln1_g", C.c_void_p), ("ln1_b", C.c_void_p), ("ln2_g", C.c_void_p), ("ln2_b", C.c_void_p)]
 
 
+class MoeGrads(C.Structure):
+    _fields_ = [(k, C.c_void_p) for k in ("w1", "b1", "w2", "b2", "wr_train", "br_train", "wr_infer", "br_infer",
+                                          "ln1_g", "ln1_b", "ln2_g", "ln2_b")]
+
+
 class ModelDesc(C.Structure):
     _fields_ = [("T", C.c_int), ("D", C.c_int), ("hidden", C.c_int), ("E", C.c_int), ("dtype", C.c_int),
                 ("L", C.c_int), ("blocks", C.POINTER(BlockParams)), ("F", C.c_int64), ("head_w", C.c_void_p),
@@ -85,6 +90,12 @@ _SIGNATURES = {
     "rm_block_bwd_workspace_bytes": (_sz, [_i64, _int, _int, _int, _int]),
     "rm_block_bwd": (_int, [_vp, C.POINTER(BlockParams), _vp, _sz, _vp, _vp, C.POINTER(BlockGrads), _i64, _int, _int,
                             _int, _int, _vp, _sz, _vp]),
+    "rm_moe_saved_bytes": (_sz, [_i64, _int, _int, _int, _int, _int]),
+    "rm_moe_train_workspace_bytes": (_sz, [_i64, _int, _int, _int, _int, _int]),
+    "rm_moe_block_fwd_train": (_int, [_vp, C.POINTER(BlockParams), _vp, _vp, _vp, _vp, _vp, _sz, _i64, _int, _int,
+                                      _int, _int, _int, _vp, _sz, _vp]),
+    "rm_moe_block_bwd": (_int, [_vp, C.POINTER(BlockParams), _vp, _vp, C.c_float, _vp, _sz, _vp, _vp,
+                                C.POINTER(MoeGrads), _i64, _int, _int, _int, _int, _int, _vp, _sz, _vp]),
     "rm_model_fwd": (_int, [C.POINTER(ModelDesc), _vp, _vp, _vp, _vp, _i64, _vp, _sz, _vp]),
     "rm_model_workspace_bytes": (_sz, [C.POINTER(ModelDesc), _i64]),
     "rm_status_string": (C.c_char_p, [_int]),
@@ -332,6 +343,51 @@ def rm_block_bwd(x: torch.Tensor, p: dict, saved: torch.Tensor, d_out: torch.Ten
     st = _block_struct(p)
     _check(lib.rm_block_bwd(_p(x), C.byref(st), _p(saved), saved.numel(), _p(d_out), _p(dx), C.byref(gs), B, T, D, Hd,
                             _dt(x), _p(ws), ws.numel(), _stream(dev)))
+    return dx, g
+
+
+MOE_GRADS = ("w1", "b1", "w2", "b2", "wr_train", "br_train", "wr", "br", "ln1_g", "ln1_b", "ln2_g", "ln2_b")
+
+
+def rm_moe_block_fwd_train(x: torch.Tensor, p: dict, out: Optional[torch.Tensor] = None):
+    """MoE block training forward (dense-training / sparse-inference routers).
+    p: an MoE block dict (its "wr"/"br" are h_infer) plus "wr_train" [T][E][D]
+    in x's dtype and "br_train" [T][E] fp32.  Returns (x_out, l_reg [1] fp32,
+    saved)."""
+    lib = load()
+    B, T, D = x.shape
+    He, E = _block_dims(p)
+    y = torch.empty_like(x) if out is None else out
+    l_reg = torch.empty(1, dtype=torch.float32, device=x.device)
+    saved = torch.empty(max(lib.rm_moe_saved_bytes(B, T, D, He, E, _dt(x)), 16), dtype=torch.uint8, device=x.device)
+    ws = _workspace(x.device, lib.rm_moe_train_workspace_bytes(B, T, D, He, E, _dt(x)))
+    st = _block_struct(p)
+    _check(lib.rm_moe_block_fwd_train(_p(x), C.byref(st), _p(p["wr_train"]), _p(p["br_train"]), _p(y), _p(l_reg),
+                                      _p(saved), saved.numel(), B, T, D, He, E, _dt(x), _p(ws), ws.numel(),
+                                      _stream(x.device)))
+    return y, l_reg, saved
+
+
+def rm_moe_block_bwd(x: torch.Tensor, p: dict, saved: torch.Tensor, d_out: torch.Tensor, lam: float):
+    """MoE block backward of <d_out, x_out> + lam * L_reg: (dx, grads), grads
+    a dict of fp32 tensors named like the parameters (MOE_GRADS; "wr"/"br"
+    are h_infer's)."""
+    lib = load()
+    B, T, D = x.shape
+    He, E = _block_dims(p)
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    shapes = {"w1": (T, E, He, D), "b1": (T, E, He), "w2": (T, E, D, He), "b2": (T, E, D),
+              "wr_train": (T, E, D), "br_train": (T, E), "wr": (T, E, D), "br": (T, E),
+              "ln1_g": (D,), "ln1_b": (D,), "ln2_g": (D,), "ln2_b": (D,)}
+    g = {k: torch.empty(shapes[k], **f32) for k in MOE_GRADS}
+    dx = torch.empty_like(x)
+    gs = MoeGrads(*[_p(g[k]) for k in MOE_GRADS])
+    ws = _workspace(dev, lib.rm_moe_train_workspace_bytes(B, T, D, He, E, _dt(x)))
+    st = _block_struct(p)
+    _check(lib.rm_moe_block_bwd(_p(x), C.byref(st), _p(p["wr_train"]), _p(p["br_train"]), float(lam), _p(saved),
+                                saved.numel(), _p(d_out), _p(dx), C.byref(gs), B, T, D, He, E, _dt(x), _p(ws),
+                                ws.numel(), _stream(dev)))
     return dx, g
 
 

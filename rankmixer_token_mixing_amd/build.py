@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librankmixer.so")
-SOURCES = ["abi.cpp", "kernels_rows.hip", "kernels_moe.hip", "kernels_gemm.hip", "kernels_tokproj.hip", "kernels_bwd.hip", "kernels_variants.hip"]
+SOURCES = ["abi.cpp", "kernels_rows.hip", "kernels_moe.hip", "kernels_gemm.hip", "kernels_tokproj.hip", "kernels_bwd.hip", "kernels_variants.hip", "kernels_moe_train.hip"]
 ARCH = os.environ.get("RM_OFFLOAD_ARCH", "gfx950")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in the device code

@@ -840,6 +840,260 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// MoE block training with the dense-training / sparse-inference routers
+
+namespace {
+
+struct MoeSaved {
+  void* S;   // [T][B][D] token-major
+  void* U;   // [B][T*E][He]: W1 product + b1 of every (token, expert)
+  float* Y;  // [B][T*E][D]: expert outputs
+  float* Gt; // [B][T][E] training gates
+  float* Gi; // [B][T][E] inference gates
+  void* Z;   // [B][T][D]: sum_j G_train y_j
+};
+size_t moe_saved_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt, MoeSaved* w) {
+  const size_t e = elem_bytes(dt);
+  const int64_t TE = (int64_t)T * E;
+  MoeSaved x;
+  x.S = c.take((size_t)B * T * D * e);
+  x.U = c.take((size_t)B * TE * He * e);
+  x.Y = (float*)c.take((size_t)B * TE * D * 4);
+  x.Gt = (float*)c.take((size_t)B * TE * 4);
+  x.Gi = (float*)c.take((size_t)B * TE * 4);
+  x.Z = c.take((size_t)B * T * D * e);
+  if (w) *w = x;
+  return c.off;
+}
+
+struct MoeTrainWs {
+  void* H;  // forward: GELU(U), same layout
+  void *dV, *dy, *dz, *mask, *W2t, *dH, *dU, *dUt, *Ht, *dyt, *St, *W1tc, *dzt, *maskt;
+  float *dSr, *dSf, *dY1, *ln2p, *ln1p, *b2p, *b1p, *brtp, *brip;
+};
+size_t moe_train_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt, MoeTrainWs* w) {
+  const size_t e = elem_bytes(dt);
+  const int64_t TE = (int64_t)T * E, Bp = pad64(B);
+  const int64_t rt = rm::transpose_row_tiles(B, Bp);
+  const int lg = rm::ln_bwd_grid(B, T);
+  MoeTrainWs x;
+  x.H = c.take((size_t)B * TE * He * e);
+  x.dV = c.take((size_t)T * B * D * e);
+  x.dy = c.take((size_t)B * TE * D * e);
+  x.dz = c.take((size_t)B * TE * e);
+  x.mask = c.take((size_t)B * TE * e);
+  x.W2t = c.take((size_t)TE * He * D * e);
+  x.dH = c.take((size_t)B * TE * He * e);
+  x.dU = c.take((size_t)B * TE * He * e);
+  x.dUt = c.take((size_t)TE * He * Bp * e);
+  x.Ht = c.take((size_t)TE * He * Bp * e);
+  x.dyt = c.take((size_t)TE * D * Bp * e);
+  x.St = c.take((size_t)T * D * Bp * e);
+  x.W1tc = c.take((size_t)T * D * E * He * e);
+  x.dzt = c.take((size_t)TE * Bp * e);
+  x.maskt = c.take((size_t)TE * Bp * e);
+  x.dSr = (float*)c.take((size_t)T * B * D * 4);
+  x.dSf = (float*)c.take((size_t)T * B * D * 4);
+  x.dY1 = (float*)c.take((size_t)B * T * D * 4);
+  x.ln2p = (float*)c.take((size_t)lg * 2 * D * 4);
+  x.ln1p = (float*)c.take((size_t)lg * 2 * D * 4);
+  x.b2p = (float*)c.take((size_t)TE * rt * D * 4);
+  x.b1p = (float*)c.take((size_t)TE * rt * He * 4);
+  x.brtp = (float*)c.take((size_t)rt * TE * 4);
+  x.brip = (float*)c.take((size_t)rt * TE * 4);
+  if (w) *w = x;
+  return c.off;
+}
+
+rm_status check_moe_train(const rm_block_params* p, const void* wr_train, const float* br_train, int64_t B, int T,
+                          int D, int He, int E, int dt) {
+  RM_TRY(check_block_params(p, dt));
+  if (p->kind != RM_BLOCK_MOE || p->flags)
+    return fail(RM_ERR_UNSUPPORTED, "MoE training needs an MoE block with the Add & Norm after the mix");
+  RM_TRY(check_block_shape(RM_BLOCK_MOE, B, T, D, He, E, dt));
+  RM_TRY(check_ptr(wr_train, "wr_train")); RM_TRY(check_ptr(br_train, "br_train"));
+  if (D > rm::ln_bwd_max_width())
+    return fail(RM_ERR_UNSUPPORTED, "D=%d is wider than the backward row kernels support (%d)", D, rm::ln_bwd_max_width());
+  if (((int64_t)T * E) % 8) return fail(RM_ERR_UNSUPPORTED, "T*E=%lld must be a multiple of 8", (long long)T * E);
+  const int64_t TE = (int64_t)T * E;
+  if (B * TE * He >= ((int64_t)1 << 31) || TE * pad64(B) * He >= ((int64_t)1 << 31) || B * TE * D >= ((int64_t)1 << 31))
+    return fail(RM_ERR_UNSUPPORTED, "B*T*E*hidden too large");
+  return RM_OK;
+}
+
+}  // namespace
+
+size_t rm_moe_saved_bytes(int64_t B, int T, int D, int He, int E, int dtype) {
+  Carver c(nullptr);
+  return moe_saved_carve(c, B, T, D, E, He, dtype, nullptr);
+}
+
+size_t rm_moe_train_workspace_bytes(int64_t B, int T, int D, int He, int E, int dtype) {
+  Carver c(nullptr);
+  return moe_train_carve(c, B, T, D, E, He, dtype, nullptr);
+}
+
+rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const void* wr_train, const float* br_train,
+                                 void* x_out, float* l_reg, void* saved, size_t saved_bytes, int64_t B, int T, int D,
+                                 int He, int E, int dtype, void* ws, size_t ws_bytes, void* stream) {
+  RM_TRY(check_moe_train(p, wr_train, br_train, B, T, D, He, E, dtype));
+  RM_TRY(check_ptr(l_reg, "l_reg"));
+  hipStream_t st = (hipStream_t)stream;
+  if (B == 0) {
+    RM_HIP(rm::launch_sum_parts(l_reg, l_reg, nullptr, 1, 0, 1, 1, st), "zero loss");
+    return ok();
+  }
+  RM_TRY(check_ptr(x, "x")); RM_TRY(check_ptr(x_out, "x_out"));
+  if (x == x_out) return fail(RM_ERR_INVALID, "x_out must not alias x");
+  RM_TRY(check_ptr(saved, "saved"));
+  const size_t need_s = rm_moe_saved_bytes(B, T, D, He, E, dtype);
+  if (saved_bytes < need_s) return fail(RM_ERR_WORKSPACE, "saved buffer %zu bytes, need %zu", saved_bytes, need_s);
+  RM_TRY(check_ptr(ws, "ws"));
+  const size_t need = rm_moe_train_workspace_bytes(B, T, D, He, E, dtype);
+  if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  const int dt = dtype;
+  const int64_t TE = (int64_t)T * E;
+  Carver cs(saved);
+  MoeSaved sv;
+  moe_saved_carve(cs, B, T, D, E, He, dt, &sv);
+  Carver c(ws);
+  MoeTrainWs w;
+  moe_train_carve(c, B, T, D, E, He, dt, &w);
+  // S = LN1(TM(X) + X), token-major
+  RM_TIMED("mix_ln1", st, RM_HIP(rm::launch_mix_ln(x, sv.S, p->ln1_g, p->ln1_b, B, T, D, dt, true, st), "token mix + LayerNorm"));
+  // both routers' gates; the sparsity loss sums the inference gates
+  RM_TIMED("router", st, RM_HIP(rm::launch_moe_router(sv.S, D, B * D, wr_train, br_train, sv.Gt, B, T, D, E, dt, st), "training router"));
+  RM_TIMED("router", st, RM_HIP(rm::launch_moe_router(sv.S, D, B * D, p->moe.wr, p->moe.br, sv.Gi, B, T, D, E, dt, st), "inference router"));
+  RM_TIMED("l_reg", st, RM_HIP(rm::launch_sum_all(sv.Gi, l_reg, B * TE, st), "sparsity loss"));
+  // every expert densely: U = S W1^T + b1 over T*E groups (S shared by a token's experts)
+  rm::GemmArgs a1;
+  a1.dt = dt; a1.epi = rm::kEpiBias;
+  a1.M = (int)B; a1.N = He; a1.K = D; a1.G = (int)TE;
+  a1.A = sv.S; a1.a_gs = B * D; a1.a_rs = D; a1.a_gdiv = E;
+  a1.W = p->moe.w1; a1.b_gs = (int64_t)He * D;
+  a1.C = sv.U; a1.c_gs = He; a1.c_rs = TE * He;
+  a1.bias = p->moe.b1; a1.bias_gs = He;
+  RM_TIMED("moe_ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "expert W1 products"));
+  RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.H, B * TE * He, dt, st), "GELU"));
+  rm::GemmArgs a2;
+  a2.dt = dt; a2.epi = rm::kEpiBiasF32;
+  a2.M = (int)B; a2.N = D; a2.K = He; a2.G = (int)TE;
+  a2.A = w.H; a2.a_gs = He; a2.a_rs = TE * He;
+  a2.W = p->moe.w2; a2.b_gs = (int64_t)D * He;
+  a2.C = sv.Y; a2.c_gs = D; a2.c_rs = TE * D;
+  a2.bias = p->moe.b2; a2.bias_gs = D;
+  RM_TIMED("moe_ffn2", st, RM_HIP(rm::launch_gemm(a2, st), "expert W2 products"));
+  // Z = sum_j G_train y_j, then X' = LN2(Z + S)
+  RM_TIMED("combine", st, RM_HIP(rm::launch_moe_combine_dense(sv.Y, sv.Gt, sv.Z, B * T, E, D, dt, st), "expert combine"));
+  RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows(sv.Z, sv.S, D, B * D, T, x_out, p->ln2_g, p->ln2_b, B * T, D, dt, st),
+                             "residual + LayerNorm 2"));
+  return ok();
+}
+
+rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* wr_train, const float* br_train,
+                           float lambda, const void* saved, size_t saved_bytes, const void* d_out, void* dx,
+                           const rm_moe_grads* g, int64_t B, int T, int D, int He, int E, int dtype, void* ws,
+                           size_t ws_bytes, void* stream) {
+  RM_TRY(check_moe_train(p, wr_train, br_train, B, T, D, He, E, dtype));
+  if (!g) return fail(RM_ERR_INVALID, "grads is NULL");
+  const struct { float* p; const char* n; int64_t len; } outs[] = {
+      {g->w1, "grads.w1", (int64_t)T * E * He * D}, {g->b1, "grads.b1", (int64_t)T * E * He},
+      {g->w2, "grads.w2", (int64_t)T * E * D * He}, {g->b2, "grads.b2", (int64_t)T * E * D},
+      {g->wr_train, "grads.wr_train", (int64_t)T * E * D}, {g->br_train, "grads.br_train", (int64_t)T * E},
+      {g->wr_infer, "grads.wr_infer", (int64_t)T * E * D}, {g->br_infer, "grads.br_infer", (int64_t)T * E},
+      {g->ln1_g, "grads.ln1_g", D}, {g->ln1_b, "grads.ln1_b", D}, {g->ln2_g, "grads.ln2_g", D}, {g->ln2_b, "grads.ln2_b", D}};
+  for (const auto& o : outs) RM_TRY(check_ptr(o.p, o.n));
+  hipStream_t st = (hipStream_t)stream;
+  if (B == 0) {
+    for (const auto& o : outs) RM_HIP(rm::launch_sum_parts(o.p, o.p, nullptr, 1, 0, o.len, o.len, st), "zero grads");
+    return ok();
+  }
+  RM_TRY(check_ptr(x, "x")); RM_TRY(check_ptr(d_out, "d_out")); RM_TRY(check_ptr(dx, "dx"));
+  if (dx == x || dx == d_out) return fail(RM_ERR_INVALID, "dx must not alias x or d_out");
+  RM_TRY(check_ptr(saved, "saved"));
+  const size_t need_s = rm_moe_saved_bytes(B, T, D, He, E, dtype);
+  if (saved_bytes < need_s) return fail(RM_ERR_WORKSPACE, "saved buffer %zu bytes, need %zu", saved_bytes, need_s);
+  RM_TRY(check_ptr(ws, "ws"));
+  const size_t need = rm_moe_train_workspace_bytes(B, T, D, He, E, dtype);
+  if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  const int dt = dtype;
+  const int64_t TE = (int64_t)T * E, Bp = pad64(B);
+  const int rt = rm::transpose_row_tiles(B, Bp);
+  const int lg = rm::ln_bwd_grid(B, T);
+  Carver cs(const_cast<void*>(saved));
+  MoeSaved sv;
+  moe_saved_carve(cs, B, T, D, E, He, dt, &sv);
+  Carver c(ws);
+  MoeTrainWs w;
+  moe_train_carve(c, B, T, D, E, He, dt, &w);
+  // X' = LN2(Z + S): dV = dY2 (token-major)
+  RM_TIMED("ln2_bwd", st, RM_HIP(rm::launch_ln_bwd(0, d_out, nullptr, nullptr, sv.Z, sv.S, p->ln2_g, w.dV, w.ln2p, B, T, D, dt, st), "LayerNorm 2 backward"));
+  // gates: dy = G_train dV, dz (training router), mask (inference router), router input gradient
+  RM_TIMED("moe_rows", st, RM_HIP(rm::launch_moe_bwd_rows(w.dV, sv.Y, sv.Gt, sv.Gi, wr_train, w.dy, w.dz, w.mask, w.dSr, B, T, E, D, dt, st), "gate backward"));
+  // experts, densely over the T*E groups
+  RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->moe.w2, nullptr, w.W2t, nullptr, nullptr, nullptr, (int)TE, D, He, D, dt, st), "transpose W2"));
+  rm::GemmArgs g1;
+  g1.dt = dt; g1.epi = rm::kEpiBias;
+  g1.M = (int)B; g1.N = He; g1.K = D; g1.G = (int)TE;
+  g1.A = w.dy; g1.a_gs = D; g1.a_rs = TE * D;
+  g1.W = w.W2t; g1.b_gs = (int64_t)He * D;
+  g1.C = w.dH; g1.c_gs = He; g1.c_rs = TE * He;
+  RM_TIMED("bwd_dH", st, RM_HIP(rm::launch_gemm(g1, st), "expert dH products"));
+  RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.Ht, w.b1p, (int)TE, B, He, Bp, dt, st, He, TE * He), "GELU backward"));
+  RM_TIMED("tr_dy", st, RM_HIP(rm::launch_transpose(0, w.dy, nullptr, w.dyt, nullptr, nullptr, w.b2p, (int)TE, B, D, Bp, dt, st, D, TE * D), "transpose dy"));
+  rm::GemmArgs g2;
+  g2.dt = dt; g2.epi = rm::kEpiBiasF32;
+  g2.M = D; g2.N = He; g2.K = (int)Bp; g2.G = (int)TE;
+  g2.A = w.dyt; g2.a_gs = (int64_t)D * Bp; g2.a_rs = Bp;
+  g2.W = w.Ht; g2.b_gs = (int64_t)He * Bp;
+  g2.C = g->w2; g2.c_gs = (int64_t)D * He; g2.c_rs = He;
+  RM_TIMED("bwd_dW2", st, RM_HIP(rm::launch_gemm(g2, st), "expert dW2 products"));
+  RM_TIMED("tr_S", st, RM_HIP(rm::launch_transpose(0, sv.S, nullptr, w.St, nullptr, nullptr, nullptr, T, B, D, Bp, dt, st), "transpose S"));
+  rm::GemmArgs g3;
+  g3.dt = dt; g3.epi = rm::kEpiBiasF32;
+  g3.M = He; g3.N = D; g3.K = (int)Bp; g3.G = (int)TE;
+  g3.A = w.dUt; g3.a_gs = (int64_t)He * Bp; g3.a_rs = Bp;
+  g3.W = w.St; g3.b_gs = (int64_t)D * Bp; g3.b_gdiv = E;
+  g3.C = g->w1; g3.c_gs = (int64_t)He * D; g3.c_rs = D;
+  RM_TIMED("bwd_dW1", st, RM_HIP(rm::launch_gemm(g3, st), "expert dW1 products"));
+  // dS from the experts: per token one product over the E experts' hidden units
+  // concatenated along K (dU is [B][T][E*He], W1 per token viewed as [E*He][D])
+  RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->moe.w1, nullptr, w.W1tc, nullptr, nullptr, nullptr, T, (int64_t)E * He, D, (int64_t)E * He, dt, st), "transpose W1"));
+  rm::GemmArgs g4;
+  g4.dt = dt; g4.epi = rm::kEpiBiasF32;
+  g4.M = (int)B; g4.N = D; g4.K = E * He; g4.G = T;
+  g4.A = w.dU; g4.a_gs = (int64_t)E * He; g4.a_rs = TE * He;
+  g4.W = w.W1tc; g4.b_gs = (int64_t)D * E * He;
+  g4.C = w.dSf; g4.c_gs = B * D; g4.c_rs = D;
+  RM_TIMED("bwd_dS", st, RM_HIP(rm::launch_gemm(g4, st), "expert dS products"));
+  // routers: dWr = dz^T S (training), lambda * mask^T S (inference); biases from the column sums
+  RM_TIMED("tr_router", st, RM_HIP(rm::launch_transpose(0, w.dz, nullptr, w.dzt, nullptr, nullptr, w.brtp, 1, B, TE, Bp, dt, st), "transpose dz"));
+  RM_TIMED("tr_router", st, RM_HIP(rm::launch_transpose(0, w.mask, nullptr, w.maskt, nullptr, nullptr, w.brip, 1, B, TE, Bp, dt, st), "transpose mask"));
+  rm::GemmArgs g5;
+  g5.dt = dt; g5.epi = rm::kEpiBiasF32;
+  g5.M = E; g5.N = D; g5.K = (int)Bp; g5.G = T;
+  g5.A = w.dzt; g5.a_gs = (int64_t)E * Bp; g5.a_rs = Bp;
+  g5.W = w.St; g5.b_gs = (int64_t)D * Bp;
+  g5.C = g->wr_train; g5.c_gs = (int64_t)E * D; g5.c_rs = D;
+  RM_TIMED("bwd_router", st, RM_HIP(rm::launch_gemm(g5, st), "training router gradient"));
+  rm::GemmArgs g6 = g5;
+  g6.A = w.maskt;
+  g6.C = g->wr_infer;
+  RM_TIMED("bwd_router", st, RM_HIP(rm::launch_gemm(g6, st), "inference router gradient"));
+  RM_TIMED("bwd_router", st, RM_HIP(rm::launch_scale(g->wr_infer, TE * D, lambda, st), "lambda"));
+  // S = LN1(TM(X) + X) with dS = dY2 + experts + training router; dX = dY1 + TM(dY1)
+  RM_TIMED("ln1_bwd", st, RM_HIP(rm::launch_ln_bwd(1, nullptr, w.dV, w.dSf, x, nullptr, p->ln1_g, w.dY1, w.ln1p, B, T, D, dt, st, w.dSr), "LayerNorm 1 backward"));
+  RM_TIMED("tm_add", st, RM_HIP(rm::launch_tm_add(w.dY1, dx, B, T, D, dt, st), "token mix backward"));
+  RM_TIMED("sums_ln", st, RM_HIP(rm::launch_sum_parts(w.ln2p, g->ln2_g, g->ln2_b, 1, lg, 2 * (int64_t)D, D, st), "gamma2 / beta2"));
+  RM_TIMED("sums_ln", st, RM_HIP(rm::launch_sum_parts(w.ln1p, g->ln1_g, g->ln1_b, 1, lg, 2 * (int64_t)D, D, st), "gamma1 / beta1"));
+  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b2p, g->b2, nullptr, (int)TE, rt, D, D, st), "b2"));
+  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b1p, g->b1, nullptr, (int)TE, rt, He, He, st), "b1"));
+  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.brtp, g->br_train, nullptr, 1, rt, TE, TE, st), "training router bias"));
+  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.brip, g->br_infer, nullptr, 1, rt, TE, TE, st, lambda), "inference router bias"));
+  return ok();
+}
+
 size_t rm_model_workspace_bytes(const rm_model_desc* m, int64_t B) {
   if (!m || (m->L > 0 && !m->blocks)) return 0;
   Carver c(nullptr);

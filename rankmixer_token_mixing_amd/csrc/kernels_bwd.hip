@@ -36,6 +36,7 @@ struct LnBwdArgs {
   const void* dout;    // mode 0: dL/dX' rows [B][T][D]
   const void* dres;    // mode 1: dY2, token-major [T][B][D]
   const float* dres32; // mode 1: the W1-branch gradient of S, token-major fp32
+  const float* dres32b; // mode 1, optional: a further fp32 addend, token-major
   const void* z;       // mode 0: Z (W2 product + b2) [B][T][D];  mode 1: X [B][T][D]
   const void* res;     // mode 0: S, token-major
   const float* gamma;
@@ -92,6 +93,11 @@ __global__ __launch_bounds__(kLnWaves* kWave) void k_ln_bwd(LnBwdArgs a) {
           load_f32<float, VEC>(a.dres32 + tm * D + k, r);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) up[i][e] += r[e];
+          if (a.dres32b) {
+            load_f32<float, VEC>(a.dres32b + tm * D + k, r);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) up[i][e] += r[e];
+          }
         }
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
@@ -159,13 +165,13 @@ __global__ __launch_bounds__(kLnWaves* kWave) void k_ln_bwd(LnBwdArgs a) {
 }
 
 struct TrArgs {
-  const void* in;   // [G][R][C], rows of C elements
+  const void* in;   // [G][R][C]: element (g, r, c) at g * in_gs + r * in_rs + c
   const void* aux;  // op 2: U, same layout as in
   void* out;        // [G][C][ldo]: out[g][c][r] = op(in[g][r][c]), zero for R <= r < rows covered
   void* direct;     // op 2, optional: op(in) in the input's layout
   void* out2;       // op 2, optional: GELU(aux) transposed like out
   float* colsum;    // optional [G][row tiles][C]: per 64-row tile sums of op(in) over r
-  int64_t R, C, ldo;
+  int64_t R, C, ldo, in_gs, in_rs;
 };
 
 // op 0: x;  op 1: GELU(x);  op 2: x * GELU'(aux)
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(256) void k_transpose(TrArgs a) {
   const int tid = threadIdx.x;
   const int64_t g = blockIdx.z;
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const T* in = (const T*)a.in + g * a.R * a.C;
+  const T* in = (const T*)a.in + g * a.in_gs;
   {
     const int rl = tid >> 2, cl = (tid & 3) * 16;
     const int64_t r = r0 + rl;
@@ -185,16 +191,16 @@ __global__ __launch_bounds__(256) void k_transpose(TrArgs a) {
       const int64_t c = c0 + cl + 8 * h;
       float v[8];
       if (r < a.R && c < a.C) {
-        load_f32<T, 8>(in + r * a.C + c, v);
+        load_f32<T, 8>(in + r * a.in_rs + c, v);
         if constexpr (OP == 1) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
         } else if constexpr (OP == 2) {
           float u[8];
-          load_f32<T, 8>((const T*)a.aux + g * a.R * a.C + r * a.C + c, u);
+          load_f32<T, 8>((const T*)a.aux + g * a.in_gs + r * a.in_rs + c, u);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] *= gelu_grad(u[e]);
-          if (a.direct) store_from_f32<T, 8>((T*)a.direct + g * a.R * a.C + r * a.C + c, v);
+          if (a.direct) store_from_f32<T, 8>((T*)a.direct + g * a.in_gs + r * a.in_rs + c, v);
           if (a.out2)
 #pragma unroll
             for (int e = 0; e < 8; ++e) tile2[rl][cl + 8 * h + e] = gelu_erf(u[e]);
@@ -269,7 +275,8 @@ __global__ __launch_bounds__(256) void k_tm_add(const float* __restrict__ dy, T*
 // A workgroup owns 64 columns of one g: lane group q < 4 sums p = q, q+4, ...
 // in order, then the four sums are added in order -- a fixed order throughout.
 __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ part, float* __restrict__ out0,
-                                                   float* __restrict__ out1, int P, int64_t C, int64_t split) {
+                                                   float* __restrict__ out1, int P, int64_t C, int64_t split,
+                                                   float scale) {
   __shared__ float acc[4][64];
   const int cl = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int64_t g = blockIdx.y, c = (int64_t)blockIdx.x * 64 + cl;
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
   acc[q][cl] = s;
   __syncthreads();
   if (q == 0 && c < C) {
-    const float v = ((acc[0][cl] + acc[1][cl]) + acc[2][cl]) + acc[3][cl];
+    const float v = (((acc[0][cl] + acc[1][cl]) + acc[2][cl]) + acc[3][cl]) * scale;
     if (c < split)
       out0[g * split + c] = v;
     else
@@ -366,9 +373,9 @@ int ln_bwd_max_width() { return kLnBwdDmax; }
 
 hipError_t launch_ln_bwd(int mode, const void* dout, const void* dres, const float* dres32, const void* z,
                          const void* res, const float* gamma, void* dy, float* part, int64_t B, int T, int D, int dt,
-                         hipStream_t s) {
+                         hipStream_t s, const float* dres32b) {
   if (D > kLnBwdDmax || D % 8 || D % T) return hipErrorInvalidValue;
-  LnBwdArgs a{dout, dres, dres32, z, res, gamma, dy, part, B, T, D};
+  LnBwdArgs a{dout, dres, dres32, dres32b, z, res, gamma, dy, part, B, T, D};
   const int grid = ln_bwd_grid(B, T);
   if (dt == kBF16)
     return mode == 0 ? ln_bwd_t<bf16, 0>(a, grid, s) : ln_bwd_t<bf16, 1>(a, grid, s);
@@ -378,11 +385,15 @@ hipError_t launch_ln_bwd(int mode, const void* dout, const void* dres, const flo
 int transpose_row_tiles(int64_t R, int64_t ldo) { return (int)((std::max(R, ldo) + 63) / 64); }
 
 hipError_t launch_transpose(int op, const void* in, const void* aux, void* out, void* direct, void* out2,
-                            float* colsum, int G, int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s) {
+                            float* colsum, int G, int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s,
+                            int64_t in_gs, int64_t in_rs) {
   if (C % 8 || ldo % 8 || ldo < R || G <= 0) return hipErrorInvalidValue;
+  if (in_rs < 0) in_rs = C;
+  if (in_gs < 0) in_gs = R * in_rs;
+  if (in_rs % 8 || in_gs % 8 || in_rs < C) return hipErrorInvalidValue;
   if (R == 0 && ldo == 0) return hipSuccess;
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)transpose_row_tiles(R, ldo), (unsigned)G);
-  TrArgs a{in, aux, out, direct, out2, colsum, R, C, ldo};
+  TrArgs a{in, aux, out, direct, out2, colsum, R, C, ldo, in_gs, in_rs};
   const dim3 block(256);
   if (dt == kBF16) {
     switch (op) {
@@ -421,10 +432,10 @@ hipError_t launch_tm_add(const float* dy, void* dx, int64_t B, int T, int D, int
 }
 
 hipError_t launch_sum_parts(const float* part, float* out0, float* out1, int G, int P, int64_t C, int64_t split,
-                            hipStream_t s) {
+                            hipStream_t s, float scale) {
   if ((int64_t)G * C == 0) return hipSuccess;
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)G);
-  hipLaunchKernelGGL(k_sum_parts, grid, dim3(256), 0, s, part, out0, out1, P, C, split);
+  hipLaunchKernelGGL(k_sum_parts, grid, dim3(256), 0, s, part, out0, out1, P, C, split, scale);
   return hipGetLastError();
 }
 

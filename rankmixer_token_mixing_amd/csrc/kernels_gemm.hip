@@ -46,6 +46,7 @@ struct KParams {
   const int* a_rowidx;
   const void* W;
   long long b_gs;
+  int b_gdiv;
   void* C;
   long long c_gs, c_rs;
   const float* bias;
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_generic(KParams p) {
       a_chunk[i] = ((lane & 7) ^ ((row >> 1) & 7)) * EPC;
       asrc[i] = Ab + r * p.a_rs + a_chunk[i];
     }
-    const T* Bb = (const T*)p.W + (long long)t.g * p.b_gs;
+    const T* Bb = (const T*)p.W + (long long)(t.g / p.b_gdiv) * p.b_gs;
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i) {
       const int row = 8 * (wave + i * TL::NW) + (lane >> 3);
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
 
   const int K = p.K;
   const bf16* Ab = (const bf16*)p.A + (long long)(t.g / p.a_gdiv) * p.a_gs;
-  const bf16* Bb = (const bf16*)p.W + (long long)t.g * p.b_gs;
+  const bf16* Bb = (const bf16*)p.W + (long long)(t.g / p.b_gdiv) * p.b_gs;
   const bf16* asrc[A_DMA];
   const bf16* bsrc[B_DMA];
 #pragma unroll
@@ -780,7 +781,7 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
   uint32_t va[A_DMA], vw[B_DMA];
   auto setup = [&](const TileId& t) {
     Ab = (const char*)p.A + (long long)(t.g / p.a_gdiv) * p.a_gs * 2;
-    Bb = (const char*)p.W + (long long)t.g * p.b_gs * 2;
+    Bb = (const char*)p.W + (long long)(t.g / p.b_gdiv) * p.b_gs * 2;
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
       const int row = 8 * (wave + i * NW) + (lane >> 3);
@@ -924,7 +925,7 @@ int choose_cfg(const GemmArgs& a) {
 KParams make_params(const GemmArgs& a, int bm, int bn) {
   KParams p;
   p.A = a.A; p.a_gs = a.a_gs; p.a_rs = a.a_rs; p.a_gdiv = a.a_gdiv; p.a_rowidx = a.a_rowidx;
-  p.W = a.W; p.b_gs = a.b_gs;
+  p.W = a.W; p.b_gs = a.b_gs; p.b_gdiv = a.b_gdiv;
   p.C = a.C; p.c_gs = a.c_gs; p.c_rs = a.c_rs;
   p.bias = a.bias; p.bias_gs = a.bias_gs;
   p.rowscale = a.rowscale;

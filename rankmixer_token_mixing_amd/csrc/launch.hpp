@@ -74,7 +74,7 @@ enum Epilogue {
 // C_g[m][n] = sum_k A_g[m][k] * W_g[n][k], g = 0..G-1, followed by an epilogue.
 // Element offsets (not bytes).  Row m of A in group g sits at
 //   (g / a_gdiv) * a_gs + rowid(m) * a_rs,   rowid(m) = a_rowidx ? a_rowidx[base+m] : base+m
-// with base = row_off ? row_off[g] : 0; W_g row n at g * b_gs + n * K; output
+// with base = row_off ? row_off[g] : 0; W_g row n at (g / b_gdiv) * b_gs + n * K; output
 // row m of group g at (base + m) * c_rs + g * c_gs (the residual the same way
 // with r_rs / r_gs); bias of group g at g * bias_gs.
 struct GemmArgs {
@@ -83,7 +83,7 @@ struct GemmArgs {
   int M = 0, N = 0, K = 0, G = 0;
   const void* A = nullptr; int64_t a_gs = 0, a_rs = 0; int a_gdiv = 1;
   const int* a_rowidx = nullptr;
-  const void* W = nullptr; int64_t b_gs = 0;
+  const void* W = nullptr; int64_t b_gs = 0; int b_gdiv = 1;  // W group of g at (g / b_gdiv) * b_gs
   void* C = nullptr; int64_t c_gs = 0, c_rs = 0;
   const float* bias = nullptr; int64_t bias_gs = 0;
   const float* rowscale = nullptr;
@@ -115,20 +115,22 @@ int ln_bwd_grid(int64_t B, int T);
 int ln_bwd_max_width();
 hipError_t launch_ln_bwd(int mode, const void* dout, const void* dres, const float* dres32, const void* z,
                          const void* res, const float* gamma, void* dy, float* part, int64_t B, int T, int D, int dt,
-                         hipStream_t s);
+                         hipStream_t s, const float* dres32b = nullptr);
 // out[g][c][r] = op(in[g][r][c]) for r < ldo (zero for r >= R), in [G][R][C];
 // op 0 identity, 1 GELU, 2 in * GELU'(aux) (direct, if set, receives op(in) in
 // the input layout; out2, if set, receives GELU(aux) transposed like out).
 // colsum, if set, receives [G][transpose_row_tiles][C] sums of op(in) over
-// each 64-row tile.  C and ldo multiples of 8, ldo >= R.
+// each 64-row tile.  C and ldo multiples of 8, ldo >= R.  Input element
+// (g, r, c) at g * in_gs + r * in_rs + c (defaults: in_rs = C, in_gs = R * in_rs).
 int transpose_row_tiles(int64_t R, int64_t ldo);
 hipError_t launch_transpose(int op, const void* in, const void* aux, void* out, void* direct, void* out2,
-                            float* colsum, int G, int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s);
+                            float* colsum, int G, int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s,
+                            int64_t in_gs = -1, int64_t in_rs = -1);
 // dx = dy + TM(dy): dy fp32 [B][T][D], dx in dt
 hipError_t launch_tm_add(const float* dy, void* dx, int64_t B, int T, int D, int dt, hipStream_t s);
-// out[g][c] = sum_p part[g][p][c] (fixed order); c < split -> out0, else out1
+// out[g][c] = scale * sum_p part[g][p][c] (fixed order); c < split -> out0, else out1
 hipError_t launch_sum_parts(const float* part, float* out0, float* out1, int G, int P, int64_t C, int64_t split,
-                            hipStream_t s);
+                            hipStream_t s, float scale = 1.0f);
 // h = GELU(u), n elements (a multiple of 8)
 hipError_t launch_gelu_ew(const void* u, void* h, int64_t n, int dt, hipStream_t s);
 
@@ -136,6 +138,21 @@ hipError_t launch_gelu_ew(const void* u, void* h, int64_t n, int dt, hipStream_t
 
 // SwiGLU: h[r][j] = SiLU(gu[r][j]) * gu[r][Hs + j] over rows of 2*Hs (Hs % 8 == 0)
 hipError_t launch_swiglu_ew(const void* gu, void* h, int64_t rows, int Hs, int dt, hipStream_t s);
+
+// ---- MoE training, dense-training / sparse-inference (kernels_moe_train.hip) --
+
+// z[r][:] = sum_j gate[r][j] * y[r][j][:] over rows r < rows (y fp32 [rows][E][D])
+hipError_t launch_moe_combine_dense(const float* y, const float* gate, void* z, int64_t rows, int E, int D, int dt,
+                                    hipStream_t s);
+// per row (b, t): dy = G_train * dV, dz = (dV . y_j) [G_train > 0], mask =
+// [G_infer > 0], dsr = sum_j dz_j Wr_train[t][j] (see kernels_moe_train.hip)
+hipError_t launch_moe_bwd_rows(const void* dv, const float* y, const float* gt, const float* gi, const void* wr,
+                               void* dy, void* dz, void* mask, float* dsr, int64_t B, int T, int E, int D, int dt,
+                               hipStream_t s);
+// out[0] = sum of x[0 .. n), fixed order
+hipError_t launch_sum_all(const float* x, float* out, int64_t n, hipStream_t s);
+// x *= scale
+hipError_t launch_scale(float* x, int64_t n, float scale, hipStream_t s);
 
 // ---- projection tokenizer (kernels_tokproj.hip) -------------------------------
 

@@ -263,6 +263,27 @@ def make_variant_block(T: int, D: int, hidden: int, dtype: str, swiglu: bool = F
     return blk
 
 
+# Training-router bias of the dense-training / sparse-inference MoE: with the
+# same N(0, 1/D) weights the pre-activation is close to N(bias, 1), and a bias
+# of +Phi^-1(0.75) leaves about 75 % of the training gates positive (the
+# training router is the dense one; the inference router keeps
+# MOE_ROUTER_BIAS, about 25 %).
+MOE_TRAIN_ROUTER_BIAS = 0.6744897501960817
+
+
+def add_training_router(blk: dict, dtype: str, seed: int = 7, bias: float = MOE_TRAIN_ROUTER_BIAS) -> dict:
+    """A copy of MoE block ``blk`` with a training router: ``wr_train``
+    [T,E,D] ~ N(0, 1/D) (uint16 bf16 bits for bf16) and ``br_train`` [T,E]
+    filled with ``bias``."""
+    T, E, D = blk["wr"].shape
+    dr = _Drawer(seed)
+    w = dr.normal((T, E, D), 1.0 / D)
+    out = dict(blk)
+    out["wr_train"] = to_bf16_bits(w) if dtype == "bf16" else w
+    out["br_train"] = np.full((T, E), bias, np.float32)
+    return out
+
+
 def random_rows(B: int, n: int, seed: int = 12345) -> np.ndarray:
     """A seeded, sorted subset of n sample indices that always holds 0 and B-1."""
     if n >= B:

@@ -256,3 +256,43 @@ def test_block_flags_and_variant_kinds(lib):
         bp.kind, bp.flags = kind, flags
         assert lib.rm_block_fwd_train(A16, C.byref(bp), A16 * 2, A16 * 3, sv, 64, 4, 64, 128, bd.RM_BF16, A16 * 4,
                                       1 << 30, None) == bd.RM_ERR_UNSUPPORTED
+
+
+def test_moe_training_entry_points_check_their_arguments(lib):
+    # nothing here reaches a launch: every call fails its host-side checks
+    moe = bd.BlockParams()
+    moe.kind = bd.RM_BLOCK_MOE
+    moe.ln1_g = moe.ln1_b = moe.ln2_g = moe.ln2_b = A16
+    moe.moe = bd.MoeParams(A16, A16, A16, A16, A16, A16)
+    B, T, D, He, E = 64, 4, 64, 64, 4
+    sv = lib.rm_moe_saved_bytes(B, T, D, He, E, bd.RM_BF16)
+    # S, U, Y (fp32), both gate sets (fp32), Z
+    assert sv >= B * T * D * 2 + B * T * E * He * 2 + B * T * E * D * 4 + 2 * B * T * E * 4 + B * T * D * 2
+    ws = lib.rm_moe_train_workspace_bytes(B, T, D, He, E, bd.RM_BF16)
+    fwd = lambda p, l_reg, sb, wb, t=T, e=E: lib.rm_moe_block_fwd_train(
+        A16, C.byref(p), A16 * 2, A16 * 3, A16 * 4, l_reg, A16 * 5, sb, B, t, D, He, e, bd.RM_BF16, A16 * 6, wb, None)
+    assert fwd(moe, A16 * 7, sv - 1, ws) == bd.RM_ERR_WORKSPACE
+    assert "saved" in err(lib)
+    assert fwd(moe, A16 * 7, sv, ws - 1) == bd.RM_ERR_WORKSPACE
+    assert fwd(moe, None, sv, ws) == bd.RM_ERR_INVALID
+    assert "l_reg" in err(lib)
+    assert fwd(moe, A16 * 7, 1 << 40, 1 << 40, t=2, e=3) == bd.RM_ERR_UNSUPPORTED  # T*E = 6
+    assert "multiple of 8" in err(lib)
+    dense = _dense_bp()
+    assert fwd(dense, A16 * 7, sv, ws) == bd.RM_ERR_UNSUPPORTED
+    moe.flags = bd.RM_BLOCK_NO_MIX_NORM
+    assert fwd(moe, A16 * 7, sv, ws) == bd.RM_ERR_UNSUPPORTED
+    moe.flags = 0
+    assert lib.rm_moe_block_fwd_train(A16, C.byref(moe), None, A16 * 3, A16 * 4, A16 * 7, A16 * 5, sv, B, T, D, He,
+                                      E, bd.RM_BF16, A16 * 6, ws, None) == bd.RM_ERR_INVALID
+    assert "wr_train" in err(lib)
+    g = bd.MoeGrads(*([A16 * 8] * 12))
+    bwd = lambda dx, gg, wb: lib.rm_moe_block_bwd(A16, C.byref(moe), A16 * 3, A16 * 4, 0.5, A16 * 5, sv, A16 * 9, dx,
+                                                  gg, B, T, D, He, E, bd.RM_BF16, A16 * 6, wb, None)
+    assert bwd(A16 * 10, C.byref(g), ws - 1) == bd.RM_ERR_WORKSPACE
+    assert bwd(A16 * 9, C.byref(g), ws) == bd.RM_ERR_INVALID  # dx aliases d_out
+    assert "alias" in err(lib)
+    assert bwd(A16 * 10, None, ws) == bd.RM_ERR_INVALID
+    g.wr_infer = None
+    assert bwd(A16 * 10, C.byref(g), ws) == bd.RM_ERR_INVALID
+    assert "grads.wr_infer" in err(lib)
