@@ -312,6 +312,110 @@ def bench_block_bwd(args) -> int:
     return 0
 
 
+def bench_moe_train(args) -> int:
+    """Training of the ReLU-routed MoE block with the dense-training /
+    sparse-inference routers on block 0 of the MoE workload (c4: B=2048, T=16,
+    D=768, 8 experts of 768 -> 1536 -> 768 per token, bf16), the inference
+    router at about 25 % active gates and the training router at about 75 %.
+    A step is rm_moe_block_fwd_train + rm_moe_block_bwd (lambda = 0.01) on one
+    batch.  Every expert runs on every token in training, so the six expert
+    products (W1, W2 forward; dH, dW2, dW1, dS backward) are 2*B*D*He*T*E
+    flops each; the roofline is the dominant one against the bf16 MFMA peak."""
+    import torch
+    import synthetic_inputs as si
+    from rankmixer_token_mixing_amd import binding as bd
+    from rankmixer_token_mixing_amd import perfmodel as pm
+
+    cfg = si.CONFIGS["c4"]
+    t0 = time.perf_counter()
+    inputs = si.make_inputs(si.scaled(cfg, L=1))
+    blk_np = si.add_training_router(inputs["blocks"][0], cfg.dtype)
+    d_out_np = si.make_inputs(si.scaled(cfg, L=0), seed=100 + si.SEEDS[cfg.name])["x"]
+    log(f"generated {cfg.name} inputs in {time.perf_counter() - t0:.1f}s: {cfg.description}, training router added")
+    blk = bd.upload_blocks([blk_np])[0]
+    x = bd.to_device(inputs["x"])
+    d_out = bd.to_device(d_out_np)
+    B, T, D, E, He = cfg.B, cfg.T, cfg.D, cfg.E, cfg.He
+    lam = 0.01
+
+    def step():
+        _, _, saved = bd.rm_moe_block_fwd_train(x, blk)
+        bd.rm_moe_block_bwd(x, blk, saved, d_out, lam)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    bd.profile_enable(not args.no_profile)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = bd.profile_read() if not args.no_profile else {}
+    bd.profile_enable(False)
+    ms_step = elapsed * 1e3 / args.steps
+    gemm = T * E * pm.gemm_flops(B, He, D)  # each of the six expert products
+    products = ("moe_ffn1", "moe_ffn2", "bwd_dH", "bwd_dW2", "bwd_dW1", "bwd_dS")
+    kernels = {}
+    for name, (tot_ms, n) in prof.items():
+        avg = tot_ms / max(n, 1)
+        e = {"avg_ms": round(avg, 5), "launches": n, "total_ms": round(tot_ms, 3)}
+        if name in products:
+            e["tflops"] = round(gemm / (avg * 1e-3) / 1e12, 1)
+        kernels[name] = e
+    roofline = None
+    gk = {k: v for k, v in kernels.items() if k in products}
+    if gk:
+        dom = max(gk, key=lambda k: gk[k]["total_ms"])
+        ach = gemm / (gk[dom]["avg_ms"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": pm.PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / pm.PEAK_BF16_TFLOPS, 4), "flop_per_launch": gemm,
+                    "traffic": None}
+    step_tf = 6 * gemm / (ms_step * 1e-3) / 1e12
+    rec = {
+        "metric": "samples/sec RankMixer MoE block training step (bf16) + % of MI355X MFMA peak",
+        "value": round(B / (ms_step * 1e-3), 1),
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.description}: training of block 0 with a dense training router",
+                   "B": B, "T": T, "D": D, "E": E, "He": He, "lambda": lam,
+                   "step": "rm_moe_block_fwd_train + rm_moe_block_bwd over the batch"},
+        "roofline": roofline,
+        "step_tflops": round(step_tf, 1),
+        "step_frac_of_bf16_peak": round(step_tf / pm.PEAK_BF16_TFLOPS, 4),
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import moe_training as omt
+        n = min(B, 512)
+        rows = si.random_rows(B, n, seed=99)
+        t0 = time.perf_counter()
+        omt.dtsi_bwd(inputs["x"][rows], blk_np, d_out_np[rows], lam)
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([q.get("num_threads", 1) for q in threadpool_info() if q.get("user_api") == "blas"] or [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        rec["cpu_baseline"] = {"value": n / dt, "unit": "samples/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"{n} of {B} samples (fp64 numpy training forward + backward of block 0, "
+                                         f"{dt:.1f} s); the work is linear in the samples, so the rate is "
+                                         f"per-sample exact"}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def bench_variants(args) -> int:
     """The block variants of the Taobao report on the 100M-class width (B=2048,
     T=16, D=768, bf16): the SwiGLU block D -> 4/3 D (hidden 1024) is the timed
@@ -411,12 +515,13 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", help="workload (c3 is the benchmarked one)")
-    ap.add_argument("--op", default="model", choices=["model", "tokenize_project", "block_bwd", "block_variants"],
+    ap.add_argument("--op", default="model", choices=["model", "tokenize_project", "block_bwd", "block_variants", "moe_train"],
                     help="model: the block stack (default); tokenize_project: the projection "
                          "tokenizer alone on the pad-split model's embedding; block_bwd: the dense "
                          "block backward on block 0 of the workload; block_variants: the SwiGLU "
                          "(D -> 4/3 D) block beside the GELU FFN (D -> 2D) block of equal parameters and "
-                         "flops, with and without the Add & Norm after the mix")
+                         "flops, with and without the Add & Norm after the mix; moe_train: training "
+                         "step of the MoE block with dense-training / sparse-inference routers")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="samples in the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-launch HIP events")
@@ -460,6 +565,8 @@ def main() -> int:
         return bench_block_bwd(args)
     if args.op == "block_variants":
         return bench_variants(args)
+    if args.op == "moe_train":
+        return bench_moe_train(args)
 
     cfg = si.CONFIGS[args.config]
     t0 = time.perf_counter()

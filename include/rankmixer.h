@@ -317,7 +317,9 @@ rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const 
  *   dS += dV;  dY1 = LNbwd1(dS);  dX = dY1 + TM(dY1)
  * Arguments as rm_moe_block_fwd_train (saved from that call on the same x and
  * parameters); d_out, dx: [B][T][D] dtype; g: fp32 gradients.  Products in
- * dtype with fp32 accumulation; every sum over the batch in a fixed order.
+ * dtype with fp32 accumulation (bf16: the expert outputs y, dV, dy, dH and dU
+ * are stored in bf16 between kernels); every sum over the batch in a fixed
+ * order.
  * B = 0 writes zero gradients.
  *   Workspace: rm_moe_train_workspace_bytes(B, T, D, He, E, dtype) (the same
  *   size as the forward's; the two calls may share one buffer).

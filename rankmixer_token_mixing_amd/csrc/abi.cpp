@@ -848,7 +848,7 @@ namespace {
 struct MoeSaved {
   void* S;   // [T][B][D] token-major
   void* U;   // [B][T*E][He]: W1 product + b1 of every (token, expert)
-  float* Y;  // [B][T*E][D]: expert outputs
+  void* Y;   // [B][T*E][D]: expert outputs
   float* Gt; // [B][T][E] training gates
   float* Gi; // [B][T][E] inference gates
   void* Z;   // [B][T][D]: sum_j G_train y_j
@@ -859,7 +859,7 @@ size_t moe_saved_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt
   MoeSaved x;
   x.S = c.take((size_t)B * T * D * e);
   x.U = c.take((size_t)B * TE * He * e);
-  x.Y = (float*)c.take((size_t)B * TE * D * 4);
+  x.Y = c.take((size_t)B * TE * D * e);
   x.Gt = (float*)c.take((size_t)B * TE * 4);
   x.Gi = (float*)c.take((size_t)B * TE * 4);
   x.Z = c.take((size_t)B * T * D * e);
@@ -870,7 +870,7 @@ size_t moe_saved_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt
 struct MoeTrainWs {
   void* H;  // forward: GELU(U), same layout
   void *dV, *dy, *dz, *mask, *W2t, *dH, *dU, *dUt, *Ht, *dyt, *St, *W1tc, *dzt, *maskt;
-  float *dSr, *dSf, *dY1, *ln2p, *ln1p, *b2p, *b1p, *brtp, *brip;
+  float *dSr, *dSf, *dY1, *ln2p, *ln1p, *b2p, *b1p, *brtp, *brip, *lpart;
 };
 size_t moe_train_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt, MoeTrainWs* w) {
   const size_t e = elem_bytes(dt);
@@ -902,6 +902,7 @@ size_t moe_train_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt
   x.b1p = (float*)c.take((size_t)TE * rt * He * 4);
   x.brtp = (float*)c.take((size_t)rt * TE * 4);
   x.brip = (float*)c.take((size_t)rt * TE * 4);
+  x.lpart = (float*)c.take((size_t)rm::kSumParts * 4);
   if (w) *w = x;
   return c.off;
 }
@@ -965,7 +966,7 @@ rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const 
   // both routers' gates; the sparsity loss sums the inference gates
   RM_TIMED("router", st, RM_HIP(rm::launch_moe_router(sv.S, D, B * D, wr_train, br_train, sv.Gt, B, T, D, E, dt, st), "training router"));
   RM_TIMED("router", st, RM_HIP(rm::launch_moe_router(sv.S, D, B * D, p->moe.wr, p->moe.br, sv.Gi, B, T, D, E, dt, st), "inference router"));
-  RM_TIMED("l_reg", st, RM_HIP(rm::launch_sum_all(sv.Gi, l_reg, B * TE, st), "sparsity loss"));
+  RM_TIMED("l_reg", st, RM_HIP(rm::launch_sum_all(sv.Gi, l_reg, B * TE, w.lpart, st), "sparsity loss"));
   // every expert densely: U = S W1^T + b1 over T*E groups (S shared by a token's experts)
   rm::GemmArgs a1;
   a1.dt = dt; a1.epi = rm::kEpiBias;
@@ -977,7 +978,7 @@ rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const 
   RM_TIMED("moe_ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "expert W1 products"));
   RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.H, B * TE * He, dt, st), "GELU"));
   rm::GemmArgs a2;
-  a2.dt = dt; a2.epi = rm::kEpiBiasF32;
+  a2.dt = dt; a2.epi = rm::kEpiBias;
   a2.M = (int)B; a2.N = D; a2.K = He; a2.G = (int)TE;
   a2.A = w.H; a2.a_gs = He; a2.a_rs = TE * He;
   a2.W = p->moe.w2; a2.b_gs = (int64_t)D * He;

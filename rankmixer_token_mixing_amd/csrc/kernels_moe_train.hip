@@ -8,7 +8,7 @@
 //  * k_moe_bwd_rows: per row, dG_j = dV . y_j, dy_j = G_j dV, the training
 //    router's dz_j = dG_j [G_j > 0], its input gradient sum_j dz_j Wr_j, and the
 //    inference router's mask [G_infer > 0];
-//  * k_sum_all: the sparsity loss, one fixed-order sum.
+//  * k_sum_all: the sparsity loss, a fixed-order sum in two passes.
 #include <algorithm>
 
 #include "common.hpp"
@@ -20,22 +20,22 @@ namespace {
 
 constexpr int kRowWaves = 4;
 
-// z[b][t][:] = sum_j G[b][t][j] * y[b][t][j][:]  (y fp32 [B][T][E][D], z in T)
+// z[b][t][:] = sum_j G[b][t][j] * y[b][t][j][:]  (y [B][T][E][D] and z in T, fp32 sums)
 template <typename T>
-__global__ __launch_bounds__(kRowWaves* kWave) void k_moe_combine_dense(const float* __restrict__ y,
+__global__ __launch_bounds__(kRowWaves* kWave) void k_moe_combine_dense(const T* __restrict__ y,
                                                                           const float* __restrict__ gate,
                                                                           T* __restrict__ z, int64_t rows, int E,
                                                                           int D) {
   const int64_t row = (int64_t)blockIdx.x * kRowWaves + threadIdx.x / kWave;
   if (row >= rows) return;
   const int lane = lane_id();
-  const float* yr = y + row * E * (int64_t)D;
+  const T* yr = y + row * E * (int64_t)D;
   for (int k = lane * 4; k < D; k += kWave * 4) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < E; ++j) {
       const float g = gate[row * E + j];
       float v[4];
-      load_f32<float, 4>(yr + (int64_t)j * D + k, v);
+      load_f32<T, 4>(yr + (int64_t)j * D + k, v);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = fmaf(g, v[e], acc[e]);
     }
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kRowWaves* kWave) void k_moe_combine_dense(const fl
 
 struct MoeBwdArgs {
   const void* dv;      // dY2, token-major [T][B][D] (dtype)
-  const float* y;      // expert outputs [B][T][E][D] fp32
+  const void* y;       // expert outputs [B][T][E][D] (dtype)
   const float* gt;     // G_train [B][T][E]
   const float* gi;     // G_infer [B][T][E]
   const void* wr;      // training router [T][E][D] (dtype)
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kRowWaves* kWave) void k_moe_bwd_rows(MoeBwdArgs a)
   const int t = (int)(row - b * a.T);
   const int D = a.D, E = a.E;
   const T* dvr = (const T*)a.dv + ((int64_t)t * a.B + b) * D;
-  const float* yr = a.y + row * E * (int64_t)D;
+  const T* yr = (const T*)a.y + row * E * (int64_t)D;
   float my_dz = 0.f;  // lane j keeps dz_j (E <= 32, checked)
   for (int j = 0; j < E; ++j) {
     const float g = a.gt[row * E + j];
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kRowWaves* kWave) void k_moe_bwd_rows(MoeBwdArgs a)
     for (int k = lane * 4; k < D; k += kWave * 4) {
       float dv[4], yv[4], o[4];
       load_f32<T, 4>(dvr + k, dv);
-      load_f32<float, 4>(yr + (int64_t)j * D + k, yv);
+      load_f32<T, 4>(yr + (int64_t)j * D + k, yv);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         part = fmaf(dv[e], yv[e], part);
@@ -105,18 +105,21 @@ __global__ __launch_bounds__(kRowWaves* kWave) void k_moe_bwd_rows(MoeBwdArgs a)
   }
 }
 
-// out[0] = sum of x[0 .. n) in a fixed order (one workgroup)
-__global__ __launch_bounds__(256) void k_sum_all(const float* __restrict__ x, float* __restrict__ out, int64_t n) {
+// out[blockIdx.x] = sum of x[blockIdx.x * chunk, min(n, (blockIdx.x + 1) * chunk))
+// in a fixed order
+__global__ __launch_bounds__(256) void k_sum_all(const float* __restrict__ x, float* __restrict__ out, int64_t n,
+                                                 int64_t chunk) {
   __shared__ float red[256];
+  const int64_t lo = (int64_t)blockIdx.x * chunk, hi = std::min<int64_t>(n, lo + chunk);
   float s = 0.f;
-  for (int64_t i = threadIdx.x; i < n; i += 256) s += x[i];
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) s += x[i];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w >= 1; w >>= 1) {
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[0] = red[0];
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0];
 }
 
 // x[i] *= s
@@ -129,20 +132,20 @@ dim3 rows_grid(int64_t rows) { return dim3((unsigned)((rows + kRowWaves - 1) / k
 
 }  // namespace
 
-hipError_t launch_moe_combine_dense(const float* y, const float* gate, void* z, int64_t rows, int E, int D, int dt,
+hipError_t launch_moe_combine_dense(const void* y, const float* gate, void* z, int64_t rows, int E, int D, int dt,
                                     hipStream_t s) {
   if (D % 4) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
   if (dt == kBF16)
-    hipLaunchKernelGGL(k_moe_combine_dense<bf16>, rows_grid(rows), dim3(kRowWaves * kWave), 0, s, y, gate, (bf16*)z,
-                       rows, E, D);
+    hipLaunchKernelGGL(k_moe_combine_dense<bf16>, rows_grid(rows), dim3(kRowWaves * kWave), 0, s, (const bf16*)y,
+                       gate, (bf16*)z, rows, E, D);
   else
-    hipLaunchKernelGGL(k_moe_combine_dense<float>, rows_grid(rows), dim3(kRowWaves * kWave), 0, s, y, gate,
-                       (float*)z, rows, E, D);
+    hipLaunchKernelGGL(k_moe_combine_dense<float>, rows_grid(rows), dim3(kRowWaves * kWave), 0, s, (const float*)y,
+                       gate, (float*)z, rows, E, D);
   return hipGetLastError();
 }
 
-hipError_t launch_moe_bwd_rows(const void* dv, const float* y, const float* gt, const float* gi, const void* wr,
+hipError_t launch_moe_bwd_rows(const void* dv, const void* y, const float* gt, const float* gi, const void* wr,
                                void* dy, void* dz, void* mask, float* dsr, int64_t B, int T, int E, int D, int dt,
                                hipStream_t s) {
   if (D % 4 || E < 1 || E > 32) return hipErrorInvalidValue;
@@ -155,8 +158,15 @@ hipError_t launch_moe_bwd_rows(const void* dv, const float* y, const float* gt, 
   return hipGetLastError();
 }
 
-hipError_t launch_sum_all(const float* x, float* out, int64_t n, hipStream_t s) {
-  hipLaunchKernelGGL(k_sum_all, dim3(1), dim3(256), 0, s, x, out, n);
+int sum_all_parts(int64_t n) { return (int)std::max<int64_t>(1, std::min<int64_t>(kSumParts, (n + 4095) / 4096)); }
+
+hipError_t launch_sum_all(const float* x, float* out, int64_t n, float* part, hipStream_t s) {
+  // pass 1: up to kSumParts workgroups over contiguous chunks; pass 2: one
+  // workgroup over the partial sums
+  const int np = sum_all_parts(n);
+  const int64_t chunk = (n + np - 1) / np;
+  hipLaunchKernelGGL(k_sum_all, dim3(np), dim3(256), 0, s, x, part, n, std::max<int64_t>(chunk, 1));
+  hipLaunchKernelGGL(k_sum_all, dim3(1), dim3(256), 0, s, part, out, (int64_t)np, (int64_t)np);
   return hipGetLastError();
 }
 

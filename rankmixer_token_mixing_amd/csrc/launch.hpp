@@ -141,16 +141,19 @@ hipError_t launch_swiglu_ew(const void* gu, void* h, int64_t rows, int Hs, int d
 
 // ---- MoE training, dense-training / sparse-inference (kernels_moe_train.hip) --
 
-// z[r][:] = sum_j gate[r][j] * y[r][j][:] over rows r < rows (y fp32 [rows][E][D])
-hipError_t launch_moe_combine_dense(const float* y, const float* gate, void* z, int64_t rows, int E, int D, int dt,
+// z[r][:] = sum_j gate[r][j] * y[r][j][:] over rows r < rows (y [rows][E][D], y and z in dt)
+hipError_t launch_moe_combine_dense(const void* y, const float* gate, void* z, int64_t rows, int E, int D, int dt,
                                     hipStream_t s);
 // per row (b, t): dy = G_train * dV, dz = (dV . y_j) [G_train > 0], mask =
 // [G_infer > 0], dsr = sum_j dz_j Wr_train[t][j] (see kernels_moe_train.hip)
-hipError_t launch_moe_bwd_rows(const void* dv, const float* y, const float* gt, const float* gi, const void* wr,
+hipError_t launch_moe_bwd_rows(const void* dv, const void* y, const float* gt, const float* gi, const void* wr,
                                void* dy, void* dz, void* mask, float* dsr, int64_t B, int T, int E, int D, int dt,
                                hipStream_t s);
-// out[0] = sum of x[0 .. n), fixed order
-hipError_t launch_sum_all(const float* x, float* out, int64_t n, hipStream_t s);
+// out[0] = sum of x[0 .. n), fixed order, through part[sum_all_parts(n)]
+// partial sums (part at most kSumParts floats)
+constexpr int kSumParts = 512;
+int sum_all_parts(int64_t n);
+hipError_t launch_sum_all(const float* x, float* out, int64_t n, float* part, hipStream_t s);
 // x *= scale
 hipError_t launch_scale(float* x, int64_t n, float scale, hipStream_t s);
 

@@ -266,8 +266,8 @@ def test_moe_training_entry_points_check_their_arguments(lib):
     moe.moe = bd.MoeParams(A16, A16, A16, A16, A16, A16)
     B, T, D, He, E = 64, 4, 64, 64, 4
     sv = lib.rm_moe_saved_bytes(B, T, D, He, E, bd.RM_BF16)
-    # S, U, Y (fp32), both gate sets (fp32), Z
-    assert sv >= B * T * D * 2 + B * T * E * He * 2 + B * T * E * D * 4 + 2 * B * T * E * 4 + B * T * D * 2
+    # S, U, Y, both gate sets (fp32), Z
+    assert sv >= B * T * D * 2 + B * T * E * He * 2 + B * T * E * D * 2 + 2 * B * T * E * 4 + B * T * D * 2
     ws = lib.rm_moe_train_workspace_bytes(B, T, D, He, E, bd.RM_BF16)
     fwd = lambda p, l_reg, sb, wb, t=T, e=E: lib.rm_moe_block_fwd_train(
         A16, C.byref(p), A16 * 2, A16 * 3, A16 * 4, l_reg, A16 * 5, sb, B, t, D, He, e, bd.RM_BF16, A16 * 6, wb, None)

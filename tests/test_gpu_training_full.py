@@ -1,0 +1,92 @@
+"""GPU parity of the two training paths at the benchmarked sizes, in the
+launch configuration the benchmark times (one call over the whole batch):
+the dense block backward on block 0 of the ~1B-class workload (B=1024, T=32,
+D=1536, hidden 6144) and the MoE block training step on block 0 of the MoE
+workload (B=2048, T=16, D=768, 8 experts of 768 -> 1536 -> 768) with its
+training router.  The oracle evaluates sampled samples: the forward output and
+dX of a sample depend on that sample alone, so the sampled rows are exact.
+Weight gradients sum over the batch and are compared element by element at
+the smaller sizes of test_gpu_backward / test_gpu_moe_training.
+
+For dX of the MoE block, the ReLU gates decide which router terms exist; the
+kernels take the decision in fp32 from bf16 S (rounding error of a router
+pre-activation ~1e-3 here), the oracle in fp64, so dX is compared on sampled
+samples whose pre-activations (fp64) all lie at least 0.01 from zero."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic_inputs as si
+from oracle import block_backward as bw
+from oracle import moe_training as mt
+from oracle import rankmixer_oracle as orc
+from tests.gpu_util import TOL, ensure_lib, host, note, rel_l2_rows
+
+pytestmark = pytest.mark.gpu
+
+KINK_MARGIN = 0.01
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    note(f"[gpu] {request.node.nodeid}")
+
+
+def _workload(name):
+    cfg = si.CONFIGS[name]
+    inputs = si.make_inputs(si.scaled(cfg, L=1))
+    d_out = si.make_inputs(si.scaled(cfg, L=0), seed=100 + si.SEEDS[name])["x"]
+    return cfg, inputs, d_out
+
+
+def test_dense_backward_full_size_sampled():
+    from rankmixer_token_mixing_amd import binding as bd
+    cfg, inputs, d_out_np = _workload("c3")
+    blk_np = inputs["blocks"][0]
+    blk = bd.upload_blocks([blk_np])[0]
+    x = bd.to_device(inputs["x"])
+    note(f"[gpu] rm_block_fwd_train + rm_block_bwd, {cfg.description}, block 0")
+    y, saved = bd.rm_block_fwd_train(x, blk)
+    dx, _ = bd.rm_block_bwd(x, blk, saved, bd.to_device(d_out_np))
+    torch.cuda.synchronize()
+    rows = si.random_rows(cfg.B, 8)
+    xr = inputs["x"][rows]
+    assert rel_l2_rows(host(y)[rows], orc.block_fwd(xr, blk_np)) <= TOL["bf16"]
+    ref = bw.block_bwd(xr, blk_np, d_out_np[rows])
+    err = rel_l2_rows(host(dx)[rows], ref["dX"])
+    assert err <= TOL["bf16"], f"dX {err:.3e}"
+
+
+def test_moe_training_full_size_sampled():
+    from rankmixer_token_mixing_amd import binding as bd
+    cfg, inputs, d_out_np = _workload("c4")
+    blk_np = si.add_training_router(inputs["blocks"][0], cfg.dtype)
+    blk = bd.upload_blocks([blk_np])[0]
+    x = bd.to_device(inputs["x"])
+    lam = 0.01
+    note(f"[gpu] rm_moe_block_fwd_train + rm_moe_block_bwd, {cfg.description}, block 0")
+    y, l_reg, saved = bd.rm_moe_block_fwd_train(x, blk)
+    dx, _ = bd.rm_moe_block_bwd(x, blk, saved, bd.to_device(d_out_np), lam)
+    torch.cuda.synchronize()
+    # the sparsity loss sums the inference gates over the whole batch
+    S = orc.layer_norm(orc.token_mix(inputs["x"]) + orc.as_f64(inputs["x"]), blk_np["ln1_g"], blk_np["ln1_b"])
+    l_ref = orc.moe_gates(S, blk_np["wr"], blk_np["br"]).sum()
+    assert abs(float(host(l_reg)[0]) - l_ref) <= 1e-3 * l_ref
+    # forward output on sampled samples (a gate near zero contributes ~0 either way)
+    rows = si.random_rows(cfg.B, 8)
+    f = mt.dtsi_fwd_saved(inputs["x"][rows], blk_np)
+    assert rel_l2_rows(host(y)[rows], f["out"]) <= TOL["bf16"]
+    # dX on sampled samples clear of the ReLU kink
+    cand = si.random_rows(cfg.B, 96, seed=777)
+    fc = mt.dtsi_fwd_saved(inputs["x"][cand], blk_np)
+    margin = np.minimum(np.abs(fc["Zt"]).min(axis=(1, 2)), np.abs(fc["Zi"]).min(axis=(1, 2)))
+    clear = cand[margin > KINK_MARGIN][:8]
+    assert len(clear) >= 4, f"only {len(clear)} of {len(cand)} sampled samples clear of the kink"
+    ref = mt.dtsi_bwd(inputs["x"][clear], blk_np, d_out_np[clear], lam)
+    err = rel_l2_rows(host(dx)[clear], ref["dX"])
+    assert err <= TOL["bf16"], f"dX {err:.3e}"
