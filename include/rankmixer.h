@@ -25,8 +25,11 @@
  *    RM_ERR_INVALID.
  *  - Width limits of this build: D a multiple of 8 (and of T wherever tokens
  *    are mixed), hidden widths a multiple of 8, one [D] row per wavefront in
- *    registers (D <= 8192 when D/T is a multiple of 8; the FFN and MoE calls
- *    and blocks with an MoE: D <= 4096); MoE: 1 <= E <= 32, T*E <= 4096.
+ *    registers, at most 1024 16-byte chunks of one head width (bf16:
+ *    D <= 8192 when D/T is a multiple of 8; fp32: D <= 4096 when D/T is a
+ *    multiple of 4; narrower heads allow proportionally less); the FFN and
+ *    MoE calls, blocks with an MoE and the training calls: D <= 4096; MoE:
+ *    1 <= E <= 32, T*E <= 4096.
  *    Larger shapes are RM_ERR_UNSUPPORTED.
  *  - The caller owns every buffer, including the workspace `ws`, sized with
  *    the matching rm_*_workspace_bytes call.  The library never allocates,

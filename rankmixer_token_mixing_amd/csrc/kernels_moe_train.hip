@@ -92,16 +92,24 @@ __global__ __launch_bounds__(kRowWaves* kWave) void k_moe_bwd_rows(MoeBwdArgs a)
   }
   const T* wr = (const T*)a.wr + (int64_t)t * E * D;
   float* out = a.dsr + ((int64_t)t * a.B + b) * D;
-  for (int k = lane * 4; k < D; k += kWave * 4) {
+  // the chunk loop runs the same trip count on every lane, so the broadcast
+  // of lane j's dz happens with the whole wave active (lanes past D only skip
+  // the memory accesses)
+  const int nch = (D + kWave * 4 - 1) / (kWave * 4);
+  for (int c = 0; c < nch; ++c) {
+    const int k = c * kWave * 4 + lane * 4;
+    const bool in = k < D;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < E; ++j) {
       const float dzj = __shfl(my_dz, j, kWave);
-      float w[4];
-      load_f32<T, 4>(wr + (int64_t)j * D + k, w);
+      if (in) {
+        float w[4];
+        load_f32<T, 4>(wr + (int64_t)j * D + k, w);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(dzj, w[e], acc[e]);
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(dzj, w[e], acc[e]);
+      }
     }
-    store_from_f32<float, 4>(out + k, acc);
+    if (in) store_from_f32<float, 4>(out + k, acc);
   }
 }
 
