@@ -178,7 +178,7 @@ size_t pffn_ws(Carver& c, int64_t B, int T, int Hd, int dt, PffnWs* w) {
 struct MoeWs {
   rm::MoeWork mw;
   void* Hc;
-  float* Yc;
+  void* Yc;  // gate-scaled expert outputs of the compacted rows, activation dtype
   int max_mtiles;
 };
 size_t moe_ws(Carver& c, int64_t B, int T, int D, int E, int He, int dt, MoeWs* w) {
@@ -195,7 +195,7 @@ size_t moe_ws(Carver& c, int64_t B, int T, int D, int E, int He, int dt, MoeWs* 
   x.mw.gatec = (float*)c.take(nmax * 4);
   x.mw.pos = (int*)c.take(nmax * 4);
   x.Hc = c.take((size_t)nmax * He * elem_bytes(dt));
-  x.Yc = (float*)c.take((size_t)nmax * D * 4);
+  x.Yc = c.take((size_t)nmax * D * elem_bytes(dt));
   if (w) *w = x;
   return c.off;
 }
@@ -284,7 +284,7 @@ rm_status run_moe(const void* s, int64_t sb, int64_t sT, const rm_moe_params* p,
   RM_TIMED("moe_ffn1", st, RM_HIP(rm::launch_gemm(a, st), "moe W1 product"));
   rm::GemmArgs b;
   b.dt = dt;
-  b.epi = rm::kEpiBiasScaleF32;
+  b.epi = rm::kEpiBiasScale;
   b.M = (int)B; b.N = D; b.K = He; b.G = G;
   b.A = w.Hc; b.a_gs = 0; b.a_rs = He;
   b.W = p->w2; b.b_gs = (int64_t)D * He;

@@ -85,7 +85,8 @@ template <> struct Mma<float> {
 
 template <int EPI, typename T>
 struct OutType {
-  typedef typename std::conditional<EPI == kEpiBiasGelu || EPI == kEpiBias, T, float>::type type;
+  typedef typename std::conditional<EPI == kEpiBiasGelu || EPI == kEpiBias || EPI == kEpiBiasScale, T, float>::type
+      type;
 };
 
 // which tile this workgroup owns
@@ -129,7 +130,7 @@ __device__ __forceinline__ void epi4(const KParams& p, const TileId& t, int m, i
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = gelu_erf(v[e]);
   }
-  if constexpr (EPI == kEpiBiasScaleF32) {
+  if constexpr (EPI == kEpiBiasScale) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] *= scale;
   }
@@ -147,7 +148,7 @@ __device__ __forceinline__ void store_direct(const KParams& p, const TileId& t, 
     if (m >= t.Mg) continue;
     const long long orow = (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs;
     float scale = 1.f;
-    if constexpr (EPI == kEpiBiasScaleF32) scale = p.rowscale[t.row_base + m];
+    if constexpr (EPI == kEpiBiasScale) scale = p.rowscale[t.row_base + m];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -598,6 +599,13 @@ __device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileI
       bias[j][q] = (p.bias && ok) ? *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + n)
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  // kEpiBiasScale: the gate of each accumulator row block's row (rows past
+  // the group's end read its last row and are never stored)
+  float scale[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (EPI == kEpiBiasScale) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) scale[i] = p.rowscale[t.row_base + min(t.m0 + wm * 128 + i * 32 + lr, t.Mg - 1)];
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -611,7 +619,7 @@ __device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileI
           const int nl = wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
           float v[4] = {acc[i][j][4 * q + 0] + bias[j][q].x, acc[i][j][4 * q + 1] + bias[j][q].y,
                         acc[i][j][4 * q + 2] + bias[j][q].z, acc[i][j][4 * q + 3] + bias[j][q].w};
-          epi4<EPI, bf16>(p, t, 0, 0, 1.f, v);
+          epi4<EPI, bf16>(p, t, 0, 0, scale[i], v);
           const int phys = (nl >> 3) ^ (sr & (OCH - 1));
           store_from_f32<bf16, 4>(reinterpret_cast<bf16*>(stage + sr * (BN * 2) + phys * 16 + (nl & 7) * 2), v);
         }
@@ -685,20 +693,13 @@ __device__ __forceinline__ void pipe_epilogue_f32(const KParams& p, const TileId
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int sr = wm * 32 + lr;
-    float scale = 1.f;  // kEpiBiasScaleF32: the row's gate
-    if constexpr (EPI == kEpiBiasScaleF32) {
-      const int m = t.m0 + wm * 128 + i * 32 + lr;
-      scale = m < t.Mg ? p.rowscale[t.row_base + m] : 0.f;
-    }
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cix = (wn * FN * 32 + j * 32 + 8 * q + 4 * lh) >> 2;
-        const float4 v = make_float4((acc[i][j][4 * q + 0] + bias[j][q].x) * scale,
-                                     (acc[i][j][4 * q + 1] + bias[j][q].y) * scale,
-                                     (acc[i][j][4 * q + 2] + bias[j][q].z) * scale,
-                                     (acc[i][j][4 * q + 3] + bias[j][q].w) * scale);
+        const float4 v = make_float4(acc[i][j][4 * q + 0] + bias[j][q].x, acc[i][j][4 * q + 1] + bias[j][q].y,
+                                     acc[i][j][4 * q + 2] + bias[j][q].z, acc[i][j][4 * q + 3] + bias[j][q].w);
         *reinterpret_cast<float4*>(stage + sr * (BN * 4) + ((cix ^ (sr & 15)) * 16)) = v;
       }
     __syncthreads();
@@ -881,7 +882,7 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
       issue_w(1, 0);
       issue_a(2, 1);
     }
-    if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias || EPI == kEpiSwiglu)
+    if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias || EPI == kEpiSwiglu || EPI == kEpiBiasScale)
       pipe_epilogue_bf16<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
     else
       pipe_epilogue_f32<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
@@ -956,7 +957,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const dim3 grid(ragged ? (unsigned)((long long)a.max_mtiles * p.tiles_n)
                          : (unsigned)((long long)a.G * p.tiles_m * p.tiles_n));
   if (grid.x == 0) return hipSuccess;
-  if (ragged && !((a.epi == kEpiBiasGelu && a.a_rowidx) || (a.epi == kEpiBiasScaleF32 && !a.a_rowidx)))
+  if (ragged && !((a.epi == kEpiBiasGelu && a.a_rowidx) || (a.epi == kEpiBiasScale && !a.a_rowidx)))
     return hipErrorInvalidValue;
   if (!ragged && !(a.epi == kEpiBiasGelu || a.epi == kEpiBias || a.epi == kEpiBiasF32 || a.epi == kEpiSwiglu))
     return hipErrorInvalidValue;
@@ -978,7 +979,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
         if (a.a_rowidx)
           hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasGelu, true, true>), grid2, block, 0, s, p);
         else
-          hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasScaleF32, true, false>), grid2, block, 0, s, p);
+          hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasScale, true, false>), grid2, block, 0, s, p);
       } else {
         switch (a.epi) {
           case kEpiBiasGelu:
@@ -999,7 +1000,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
     if (a.a_rowidx)
       launch_one<NWM, NWN, FM, FN, kEpiBiasGelu, true, true>(a, p, grid, s, ring);
     else
-      launch_one<NWM, NWN, FM, FN, kEpiBiasScaleF32, true, false>(a, p, grid, s, ring);
+      launch_one<NWM, NWN, FM, FN, kEpiBiasScale, true, false>(a, p, grid, s, ring);
   } else {
     switch (a.epi) {
       case kEpiBiasGelu: launch_one<NWM, NWN, FM, FN, kEpiBiasGelu, false, false>(a, p, grid, s, ring); break;

@@ -26,7 +26,9 @@ int pick_slots(int chunks) {
   return 0;
 }
 
-// gates[b,t,j] = max(0, Wr[t,j,:] . s[b,t,:] + br[t,j]); one wave per (b, t)
+// gates[b,t,j] = max(0, Wr[t,j,:] . s[b,t,:] + br[t,j]); one wave per (b, t),
+// the waves walking the samples of one token together so that token's router
+// rows stay in the near caches
 template <typename T, int VEC, int MAXI>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_router(const T* __restrict__ s, int64_t sb, int64_t st,
                                                                   const T* __restrict__ wr,
@@ -36,8 +38,8 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_router(const T* __res
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
   if (row >= B * T_) return;
   const int lane = lane_id();
-  const int t = (int)(row % T_);
-  const int64_t b = row / T_;
+  const int t = (int)(row / B);
+  const int64_t b = row - (int64_t)t * B;
   const int nch = D / VEC;
   const T* sr = s + b * sb + t * st;
   float v[MAXI][VEC];
@@ -60,7 +62,103 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_router(const T* __res
       }
     }
     const float z = wave_sum(acc) + br[t * E + j];
-    if (lane == j % kWave) gates[row * E + j] = z > 0.f ? z : 0.f;
+    if (lane == j % kWave) gates[(b * T_ + t) * E + j] = z > 0.f ? z : 0.f;
+  }
+}
+
+// The same gates for E <= 8 experts with the token's router rows staged in
+// LDS: workgroup (x, t) takes samples [16x, 16x + 16) of token t, a wave four
+// of them, whose S rows it loads at once (clamped addresses, so the loads
+// issue back to back).  Each lane forms its partial dot products for all
+// experts and rows; per row a butterfly that halves the experts per lane at
+// each of the first three exchange steps (32, 16, 8 lanes apart) and then sums
+// across the remaining 8 lanes reduces the 8 partial sums in 6 exchanges.
+constexpr int kRouterRowsPerWave = 4;
+constexpr int kRouterRows = 4 * kRouterRowsPerWave;  // samples per workgroup (4 waves)
+constexpr int kRouterMaxE = 8;
+constexpr int kRouterLds = 65536;  // bytes of router rows staged per workgroup
+
+template <typename T, int VEC, int MAXI>
+__global__ __launch_bounds__(256) void k_router_lds(const T* __restrict__ s, int64_t sb, int64_t st,
+                                                    const T* __restrict__ wr, const float* __restrict__ br,
+                                                    float* __restrict__ gates, int64_t B, int T_, int D, int E) {
+  constexpr int R = kRouterRowsPerWave;
+  extern __shared__ uint4 wl_raw[];
+  const T* wl = reinterpret_cast<const T*>(wl_raw);
+  const int t = blockIdx.y;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(wr + (int64_t)t * E * D);
+    const int n16 = E * D * (int)sizeof(T) / 16;
+    for (int i = threadIdx.x; i < n16; i += 256) wl_raw[i] = src[i];
+  }
+  const int nch = D / VEC;
+  const int64_t b0 = (int64_t)blockIdx.x * kRouterRows + wave * R;
+  float v[R][MAXI][VEC];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t b = b0 + r < B ? b0 + r : B - 1;
+    const T* sr = s + b * sb + t * st;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int c = lane + i * kWave;
+      load_f32<T, VEC>(sr + (c < nch ? c : nch - 1) * VEC, v[r][i]);
+    }
+  }
+  __syncthreads();
+  float acc[R][kRouterMaxE];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < kRouterMaxE; ++j) acc[r][j] = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+#pragma unroll
+      for (int j = 0; j < kRouterMaxE; ++j) {
+        if (j < E) {
+          float q[VEC];
+          load_f32<T, VEC>(wl + j * D + c * VEC, q);
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[r][j] = fmaf(v[r][i][e], q[e], acc[r][j]);
+        }
+      }
+    }
+  }
+  const int e_of = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    // 8 -> 4 -> 2 -> 1 experts per lane, then the sum over 8 lanes
+    float* a = acc[r];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool hi = lane & 32;
+      const float keep = hi ? a[k + 4] : a[k], give = hi ? a[k] : a[k + 4];
+      a[k] = keep + __shfl_xor(give, 32, kWave);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const bool hi = lane & 16;
+      const float keep = hi ? a[k + 2] : a[k], give = hi ? a[k] : a[k + 2];
+      a[k] = keep + __shfl_xor(give, 16, kWave);
+    }
+    {
+      const bool hi = lane & 8;
+      const float keep = hi ? a[1] : a[0], give = hi ? a[0] : a[1];
+      a[0] = keep + __shfl_xor(give, 8, kWave);
+    }
+    float z = a[0];
+    z += __shfl_xor(z, 1, kWave);
+    z += __shfl_xor(z, 2, kWave);
+    z += __shfl_xor(z, 4, kWave);
+    const int64_t b = b0 + r;
+    if ((lane & 7) == 0 && e_of < E && b < B) {
+      z += br[t * E + e_of];
+      gates[(b * T_ + t) * E + e_of] = z > 0.f ? z : 0.f;
+    }
   }
 }
 
@@ -159,8 +257,8 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const float* __restrict__ g
 }
 
 // v = sum_j y[pos[b,t,j]] (fixed j order); out = ln ? LN(v + s) : v
-template <typename T, int MAXI>
-__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_moe_combine(const float* __restrict__ y,
+template <typename T, int VEC, int MAXI>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_moe_combine(const T* __restrict__ y,
                                                                        const int* __restrict__ pos,
                                                                        const T* __restrict__ s, int64_t sb,
                                                                        int64_t st, int T_,
@@ -168,7 +266,6 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_moe_combine(const flo
                                                                        const float* __restrict__ beta,
                                                                        T* __restrict__ out, int64_t rows_n,
                                                                        int D, int E, int ln) {
-  constexpr int VEC = 4;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
   if (row >= rows_n) return;
   const int lane = lane_id();
@@ -181,13 +278,13 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_moe_combine(const flo
   for (int j = 0; j < E; ++j) {
     const int p = pos[row * E + j];
     if (p < 0) continue;
-    const float* yr = y + (int64_t)p * D;
+    const T* yr = y + (int64_t)p * D;
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
       const int c = lane + i * kWave;
       if (c < nch) {
         float q[VEC];
-        load_f32<float, VEC>(yr + c * VEC, q);
+        load_f32<T, VEC>(yr + c * VEC, q);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) v[i][e] += q[e];
       }
@@ -261,21 +358,42 @@ hipError_t router_t(const void* s, int64_t sb, int64_t sT, const void* wr, const
   return hipGetLastError();
 }
 
+template <typename T, int VEC>
+hipError_t router_lds_t(const void* s, int64_t sb, int64_t sT, const void* wr, const float* br, float* gates,
+                        int64_t B, int T_, int D, int E, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  const dim3 grid((unsigned)((B + kRouterRows - 1) / kRouterRows), (unsigned)T_), block(256);
+  const size_t lds = (size_t)E * D * sizeof(T);
+  const T* ss = (const T*)s;
+  const T* ww = (const T*)wr;
+  switch (pick_slots(D / VEC)) {
+    case 0: return hipErrorInvalidValue;
+    case 1: hipLaunchKernelGGL((k_router_lds<T, VEC, 1>), grid, block, lds, st, ss, sb, sT, ww, br, gates, B, T_, D, E); break;
+    case 2: hipLaunchKernelGGL((k_router_lds<T, VEC, 2>), grid, block, lds, st, ss, sb, sT, ww, br, gates, B, T_, D, E); break;
+    case 4: hipLaunchKernelGGL((k_router_lds<T, VEC, 4>), grid, block, lds, st, ss, sb, sT, ww, br, gates, B, T_, D, E); break;
+    case 8: hipLaunchKernelGGL((k_router_lds<T, VEC, 8>), grid, block, lds, st, ss, sb, sT, ww, br, gates, B, T_, D, E); break;
+    default: hipLaunchKernelGGL((k_router_lds<T, VEC, 16>), grid, block, lds, st, ss, sb, sT, ww, br, gates, B, T_, D, E); break;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
-hipError_t combine_t(const float* y, const int* pos, const void* s, int64_t sb, int64_t sT, const float* g,
+hipError_t combine_t(const void* yv, const int* pos, const void* s, int64_t sb, int64_t sT, const float* g,
                      const float* b, void* out, int64_t B, int T_, int D, int E, bool ln, hipStream_t st) {
   const int64_t rows = B * T_;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
   const T* ss = (const T*)s;
+  const T* y = (const T*)yv;
   T* oo = (T*)out;
   const int l = ln ? 1 : 0;
-  switch (pick_slots(D / 4)) {
+  constexpr int VEC = sizeof(T) == 2 ? 8 : 4;  // 16-byte chunks
+  switch (pick_slots(D / VEC)) {
     case 0: return hipErrorInvalidValue;
-    case 1: hipLaunchKernelGGL((k_moe_combine<T, 1>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
-    case 2: hipLaunchKernelGGL((k_moe_combine<T, 2>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
-    case 4: hipLaunchKernelGGL((k_moe_combine<T, 4>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
-    case 8: hipLaunchKernelGGL((k_moe_combine<T, 8>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
-    default: hipLaunchKernelGGL((k_moe_combine<T, 16>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
+    case 1: hipLaunchKernelGGL((k_moe_combine<T, VEC, 1>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
+    case 2: hipLaunchKernelGGL((k_moe_combine<T, VEC, 2>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
+    case 4: hipLaunchKernelGGL((k_moe_combine<T, VEC, 4>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
+    case 8: hipLaunchKernelGGL((k_moe_combine<T, VEC, 8>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
+    default: hipLaunchKernelGGL((k_moe_combine<T, VEC, 16>), grid, block, 0, st, y, pos, ss, sb, sT, T_, g, b, oo, rows, D, E, l); break;
   }
   return hipGetLastError();
 }
@@ -284,6 +402,13 @@ hipError_t combine_t(const float* y, const int* pos, const void* s, int64_t sb, 
 
 hipError_t launch_moe_router(const void* s, int64_t sb, int64_t sT, const void* wr, const float* br, float* gates,
                              int64_t B, int T, int D, int E, int dt, hipStream_t st) {
+  // the staged kernel keeps four S rows per lane in registers: up to four
+  // 16-byte chunks of each
+  const int eb = dt == kBF16 ? 2 : 4;
+  if (E <= kRouterMaxE && (int64_t)E * D * eb <= kRouterLds && D * eb <= 4 * kWave * 16) {
+    if (dt == kBF16) return router_lds_t<bf16, 8>(s, sb, sT, wr, br, gates, B, T, D, E, st);
+    return router_lds_t<float, 4>(s, sb, sT, wr, br, gates, B, T, D, E, st);
+  }
   if (dt == kBF16) return router_t<bf16, 8>(s, sb, sT, wr, br, gates, B, T, D, E, st);
   return router_t<float, 4>(s, sb, sT, wr, br, gates, B, T, D, E, st);
 }
@@ -297,7 +422,7 @@ hipError_t launch_moe_compact(const MoeWork& w, int64_t B, int T, int E, int bm,
   return hipGetLastError();
 }
 
-hipError_t launch_moe_combine(const float* y, const int* pos, const void* s, int64_t sb, int64_t sT, const float* g,
+hipError_t launch_moe_combine(const void* y, const int* pos, const void* s, int64_t sb, int64_t sT, const float* g,
                               const float* b, void* out, int64_t B, int T, int D, int E, bool ln, int dt,
                               hipStream_t st) {
   if (dt == kBF16) return combine_t<bf16>(y, pos, s, sb, sT, g, b, out, B, T, D, E, ln, st);

@@ -51,7 +51,7 @@ hipError_t launch_moe_router(const void* s, int64_t sb, int64_t st_, const void*
                              float* gates, int64_t B, int T, int D, int E, int dt, hipStream_t st);
 hipError_t launch_moe_compact(const MoeWork& w, int64_t B, int T, int E, int bm, hipStream_t st);
 // v[b,t,:] = sum_j y[pos[b,t,j], :]; if ln: out = LN(v + s) else out = v
-hipError_t launch_moe_combine(const float* y, const int* pos, const void* s, int64_t sb, int64_t st_,
+hipError_t launch_moe_combine(const void* y, const int* pos, const void* s, int64_t sb, int64_t st_,
                               const float* g, const float* b, void* out, int64_t B, int T, int D,
                               int E, bool ln, int dt, hipStream_t st);
 
@@ -64,7 +64,7 @@ enum Epilogue {
   kEpiBiasGelu = 0,       // C(dt)  = GELU(acc + bias[n])
   kEpiBias = 1,           // C(dt)  = acc + bias[n]
   kEpiBiasF32 = 2,        // C(f32) = acc + bias[n]
-  kEpiBiasScaleF32 = 3,   // C(f32) = rowscale[m] * (acc + bias[n])
+  kEpiBiasScale = 3,      // C(dt)  = rowscale[m] * (acc + bias[n])
   // C(dt)[m][h] = SiLU(acc_g + bias[h]) * (acc_u + bias[Hs + h]), h < Hs = N/2:
   // W rows 0..Hs-1 are the gate rows, Hs..N-1 the up rows; C is Hs wide.
   // Pipelined kernel only (gemm_pipe_eligible).
