@@ -847,7 +847,7 @@ namespace {
 
 struct MoeSaved {
   void* S;   // [T][B][D] token-major
-  void* U;   // [B][T*E][He]: W1 product + b1 of every (token, expert)
+  void* U;   // [T*E][B][He]: W1 product + b1 of every (token, expert), group-major
   void* Y;   // [B][T*E][D]: expert outputs
   float* Gt; // [B][T][E] training gates
   float* Gi; // [B][T][E] inference gates
@@ -867,6 +867,9 @@ size_t moe_saved_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt
   return c.off;
 }
 
+// group-major [T*E][B][*]: H, dy, dH (so each (token, expert) slice is
+// contiguous for its product and its transpose); dU [B][T][E*He] (one K axis
+// over a token's experts for the dS product)
 struct MoeTrainWs {
   void* H;  // forward: GELU(U), same layout
   void *dV, *dy, *dz, *mask, *W2t, *dH, *dU, *dUt, *Ht, *dyt, *St, *W1tc, *dzt, *maskt;
@@ -973,14 +976,14 @@ rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const 
   a1.M = (int)B; a1.N = He; a1.K = D; a1.G = (int)TE;
   a1.A = sv.S; a1.a_gs = B * D; a1.a_rs = D; a1.a_gdiv = E;
   a1.W = p->moe.w1; a1.b_gs = (int64_t)He * D;
-  a1.C = sv.U; a1.c_gs = He; a1.c_rs = TE * He;
+  a1.C = sv.U; a1.c_gs = B * He; a1.c_rs = He;
   a1.bias = p->moe.b1; a1.bias_gs = He;
   RM_TIMED("moe_ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "expert W1 products"));
   RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.H, B * TE * He, dt, st), "GELU"));
   rm::GemmArgs a2;
   a2.dt = dt; a2.epi = rm::kEpiBias;
   a2.M = (int)B; a2.N = D; a2.K = He; a2.G = (int)TE;
-  a2.A = w.H; a2.a_gs = He; a2.a_rs = TE * He;
+  a2.A = w.H; a2.a_gs = B * He; a2.a_rs = He;
   a2.W = p->moe.w2; a2.b_gs = (int64_t)D * He;
   a2.C = sv.Y; a2.c_gs = D; a2.c_rs = TE * D;
   a2.bias = p->moe.b2; a2.bias_gs = D;
@@ -1037,12 +1040,13 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
   rm::GemmArgs g1;
   g1.dt = dt; g1.epi = rm::kEpiBias;
   g1.M = (int)B; g1.N = He; g1.K = D; g1.G = (int)TE;
-  g1.A = w.dy; g1.a_gs = D; g1.a_rs = TE * D;
+  g1.A = w.dy; g1.a_gs = B * D; g1.a_rs = D;
   g1.W = w.W2t; g1.b_gs = (int64_t)He * D;
-  g1.C = w.dH; g1.c_gs = He; g1.c_rs = TE * He;
+  g1.C = w.dH; g1.c_gs = B * He; g1.c_rs = He;
   RM_TIMED("bwd_dH", st, RM_HIP(rm::launch_gemm(g1, st), "expert dH products"));
-  RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.Ht, w.b1p, (int)TE, B, He, Bp, dt, st, He, TE * He), "GELU backward"));
-  RM_TIMED("tr_dy", st, RM_HIP(rm::launch_transpose(0, w.dy, nullptr, w.dyt, nullptr, nullptr, w.b2p, (int)TE, B, D, Bp, dt, st, D, TE * D), "transpose dy"));
+  // dH and U are group-major; dU also goes out [B][T][E*He] for the dS product
+  RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.Ht, w.b1p, (int)TE, B, He, Bp, dt, st, -1, -1, He, TE * He), "GELU backward"));
+  RM_TIMED("tr_dy", st, RM_HIP(rm::launch_transpose(0, w.dy, nullptr, w.dyt, nullptr, nullptr, w.b2p, (int)TE, B, D, Bp, dt, st), "transpose dy"));
   rm::GemmArgs g2;
   g2.dt = dt; g2.epi = rm::kEpiBiasF32;
   g2.M = D; g2.N = He; g2.K = (int)Bp; g2.G = (int)TE;

@@ -98,6 +98,27 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return fmaf(-a, tail, fmaxf(x, 0.0f));
 }
 
+// GELU(x) as gelu_erf and its derivative Phi(x) + x phi(x) from the same tail:
+// Phi(x) = 1 - Phi(-a) for x >= 0, Phi(-a) otherwise, and
+// phi(x) = exp2(-log2(e) x^2 / 2) / sqrt(2 pi).  In fp32 the derivative is
+// within 1.4e-6 of the exact one (the fitted tail is 1.3e-6 off Phi(0) = 1/2,
+// which GELU itself, weighted by |x|, does not see).
+__device__ __forceinline__ void gelu_and_grad(float x, float& g, float& dg) {
+  const float a = fabsf(x);
+  const float ac = fminf(a, 5.5f);
+  float p = fmaf(3.4890897950390354e-05f, ac, -0.0007811335963197052f);
+  p = fmaf(p, ac, 0.008104033768177032f);
+  p = fmaf(p, ac, -0.053417619317770004f);
+  p = fmaf(p, ac, 0.2625527083873749f);
+  p = fmaf(p, ac, -1.1511831283569336f);
+  p = fmaf(p, ac, -0.9999961853027344f);
+  const float e0 = x * -0.7213475204444817f * x;
+  const float tail = __builtin_amdgcn_exp2f(p + e0);  // Phi(-a)
+  g = fmaf(-a, tail, fmaxf(x, 0.0f));
+  const float cdf = x >= 0.0f ? 1.0f - tail : tail;
+  dg = fmaf(x, 0.3989422804014327f * __builtin_amdgcn_exp2f(e0), cdf);
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup ids are handed to the 8 XCDs round-robin (id % 8).  Map the ids
 // of one XCD to a contiguous range of logical tiles so that tiles sharing

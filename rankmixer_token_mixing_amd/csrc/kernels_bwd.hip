@@ -26,12 +26,6 @@ constexpr int kLnWaves = 4;       // rows (waves) per workgroup of k_ln_bwd
 constexpr int kLnBwdDmax = 4096;  // widest row: the waves' gamma/beta partials live in LDS (128 KB)
 __device__ __forceinline__ float ln_eps_b() { return 1e-5f; }
 
-// Phi(x) and phi(x) of the standard normal
-__device__ __forceinline__ float norm_cdf(float x) { return 0.5f * erfcf(-x * 0.70710678118654752f); }
-__device__ __forceinline__ float norm_pdf(float x) { return 0.3989422804014327f * expf(-0.5f * x * x); }
-// d/du GELU(u) = Phi(u) + u phi(u)
-__device__ __forceinline__ float gelu_grad(float u) { return norm_cdf(u) + u * norm_pdf(u); }
-
 struct LnBwdArgs {
   const void* dout;    // mode 0: dL/dX' rows [B][T][D]
   const void* dres;    // mode 1: dY2, token-major [T][B][D]
@@ -168,10 +162,10 @@ struct TrArgs {
   const void* in;   // [G][R][C]: element (g, r, c) at g * in_gs + r * in_rs + c
   const void* aux;  // op 2: U, same layout as in
   void* out;        // [G][C][ldo]: out[g][c][r] = op(in[g][r][c]), zero for R <= r < rows covered
-  void* direct;     // op 2, optional: op(in) in the input's layout
+  void* direct;     // op 2, optional: op(in), element (g, r, c) at g * dir_gs + r * dir_rs + c
   void* out2;       // op 2, optional: GELU(aux) transposed like out
   float* colsum;    // optional [G][row tiles][C]: per 64-row tile sums of op(in) over r
-  int64_t R, C, ldo, in_gs, in_rs;
+  int64_t R, C, ldo, in_gs, in_rs, dir_gs, dir_rs;
 };
 
 // op 0: x;  op 1: GELU(x);  op 2: x * GELU'(aux)
@@ -199,11 +193,16 @@ __global__ __launch_bounds__(256) void k_transpose(TrArgs a) {
           float u[8];
           load_f32<T, 8>((const T*)a.aux + g * a.in_gs + r * a.in_rs + c, u);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= gelu_grad(u[e]);
-          if (a.direct) store_from_f32<T, 8>((T*)a.direct + g * a.in_gs + r * a.in_rs + c, v);
+          for (int e = 0; e < 8; ++e) {
+            float gu, dgu;
+            gelu_and_grad(u[e], gu, dgu);
+            v[e] *= dgu;
+            u[e] = gu;
+          }
+          if (a.direct) store_from_f32<T, 8>((T*)a.direct + g * a.dir_gs + r * a.dir_rs + c, v);
           if (a.out2)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) tile2[rl][cl + 8 * h + e] = gelu_erf(u[e]);
+            for (int e = 0; e < 8; ++e) tile2[rl][cl + 8 * h + e] = u[e];
         }
       } else {
 #pragma unroll
@@ -386,14 +385,17 @@ int transpose_row_tiles(int64_t R, int64_t ldo) { return (int)((std::max(R, ldo)
 
 hipError_t launch_transpose(int op, const void* in, const void* aux, void* out, void* direct, void* out2,
                             float* colsum, int G, int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s,
-                            int64_t in_gs, int64_t in_rs) {
+                            int64_t in_gs, int64_t in_rs, int64_t dir_gs, int64_t dir_rs) {
   if (C % 8 || ldo % 8 || ldo < R || G <= 0) return hipErrorInvalidValue;
   if (in_rs < 0) in_rs = C;
   if (in_gs < 0) in_gs = R * in_rs;
   if (in_rs % 8 || in_gs % 8 || in_rs < C) return hipErrorInvalidValue;
+  if (dir_rs < 0) dir_rs = in_rs;
+  if (dir_gs < 0) dir_gs = in_gs;
+  if (dir_rs % 8 || dir_gs % 8 || dir_rs < C) return hipErrorInvalidValue;
   if (R == 0 && ldo == 0) return hipSuccess;
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)transpose_row_tiles(R, ldo), (unsigned)G);
-  TrArgs a{in, aux, out, direct, out2, colsum, R, C, ldo, in_gs, in_rs};
+  TrArgs a{in, aux, out, direct, out2, colsum, R, C, ldo, in_gs, in_rs, dir_gs, dir_rs};
   const dim3 block(256);
   if (dt == kBF16) {
     switch (op) {

@@ -49,7 +49,7 @@ struct MoeBwdArgs {
   const float* gt;     // G_train [B][T][E]
   const float* gi;     // G_infer [B][T][E]
   const void* wr;      // training router [T][E][D] (dtype)
-  void* dy;            // [B][T][E][D] dtype: G_train * dV
+  void* dy;            // [T][E][B][D] dtype: G_train * dV, (token, expert)-major
   void* dz;            // [B][T][E] dtype: dL/dz_train
   void* mask;          // [B][T][E] dtype: [G_infer > 0]
   float* dsr;          // [T][B][D] fp32: sum_j dz_j Wr[t][j]
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kRowWaves* kWave) void k_moe_bwd_rows(MoeBwdArgs a)
         part = fmaf(dv[e], yv[e], part);
         o[e] = g * dv[e];
       }
-      store_from_f32<T, 4>((T*)a.dy + (row * E + j) * (int64_t)D + k, o);
+      store_from_f32<T, 4>((T*)a.dy + (((int64_t)t * E + j) * a.B + b) * D + k, o);
     }
     const float dg = wave_sum(part);
     if (lane == j) my_dz = g > 0.f ? dg : 0.f;

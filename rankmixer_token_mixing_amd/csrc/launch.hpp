@@ -117,15 +117,16 @@ hipError_t launch_ln_bwd(int mode, const void* dout, const void* dres, const flo
                          const void* res, const float* gamma, void* dy, float* part, int64_t B, int T, int D, int dt,
                          hipStream_t s, const float* dres32b = nullptr);
 // out[g][c][r] = op(in[g][r][c]) for r < ldo (zero for r >= R), in [G][R][C];
-// op 0 identity, 1 GELU, 2 in * GELU'(aux) (direct, if set, receives op(in) in
-// the input layout; out2, if set, receives GELU(aux) transposed like out).
-// colsum, if set, receives [G][transpose_row_tiles][C] sums of op(in) over
-// each 64-row tile.  C and ldo multiples of 8, ldo >= R.  Input element
-// (g, r, c) at g * in_gs + r * in_rs + c (defaults: in_rs = C, in_gs = R * in_rs).
+// op 0 identity, 1 GELU, 2 in * GELU'(aux) (direct, if set, receives op(in);
+// out2, if set, receives GELU(aux) transposed like out).  colsum, if set,
+// receives [G][transpose_row_tiles][C] sums of op(in) over each 64-row tile.
+// C and ldo multiples of 8, ldo >= R.  Input (and aux) element (g, r, c) at
+// g * in_gs + r * in_rs + c (defaults: in_rs = C, in_gs = R * in_rs); direct
+// element (g, r, c) at g * dir_gs + r * dir_rs + c (defaults: the input's).
 int transpose_row_tiles(int64_t R, int64_t ldo);
 hipError_t launch_transpose(int op, const void* in, const void* aux, void* out, void* direct, void* out2,
                             float* colsum, int G, int64_t R, int64_t C, int64_t ldo, int dt, hipStream_t s,
-                            int64_t in_gs = -1, int64_t in_rs = -1);
+                            int64_t in_gs = -1, int64_t in_rs = -1, int64_t dir_gs = -1, int64_t dir_rs = -1);
 // dx = dy + TM(dy): dy fp32 [B][T][D], dx in dt
 hipError_t launch_tm_add(const float* dy, void* dx, int64_t B, int T, int D, int dt, hipStream_t s);
 // out[g][c] = scale * sum_p part[g][p][c] (fixed order); c < split -> out0, else out1
@@ -144,8 +145,9 @@ hipError_t launch_swiglu_ew(const void* gu, void* h, int64_t rows, int Hs, int d
 // z[r][:] = sum_j gate[r][j] * y[r][j][:] over rows r < rows (y [rows][E][D], y and z in dt)
 hipError_t launch_moe_combine_dense(const void* y, const float* gate, void* z, int64_t rows, int E, int D, int dt,
                                     hipStream_t s);
-// per row (b, t): dy = G_train * dV, dz = (dV . y_j) [G_train > 0], mask =
-// [G_infer > 0], dsr = sum_j dz_j Wr_train[t][j] (see kernels_moe_train.hip)
+// per row (b, t): dy = G_train * dV (written [T][E][B][D]), dz = (dV . y_j)
+// [G_train > 0], mask = [G_infer > 0], dsr = sum_j dz_j Wr_train[t][j] (see
+// kernels_moe_train.hip)
 hipError_t launch_moe_bwd_rows(const void* dv, const void* y, const float* gt, const float* gi, const void* wr,
                                void* dy, void* dz, void* mask, float* dsr, int64_t B, int T, int E, int D, int dt,
                                hipStream_t s);
