@@ -105,6 +105,24 @@ def block0_protocol(bd, blocks, x0, B: int, flop_block, peak: float) -> dict:
     return rec
 
 
+def moe_active_rows(bd, blocks, x0, D: int) -> list:
+    """Active (sample, token, expert) rows of each MoE block on this batch, for
+    the flop count: block l's input comes from the library's own blocks, its S
+    = LN1(TM(X) + X) from the library's token mix and torch's fp32 LayerNorm
+    (bookkeeping only; a gate within rounding of zero may be counted on the
+    other side), and the count from the library's router and compaction."""
+    import torch
+    x = x0
+    counts = []
+    for blk in blocks:
+        y1 = bd.rm_token_mix(x).float() + x.float()
+        s = torch.nn.functional.layer_norm(y1, (D,), blk["ln1_g"], blk["ln1_b"], eps=1e-5).to(x.dtype)
+        _, offsets, _ = bd.rm_moe_route(s, blk["wr"], blk["br"])
+        counts.append(int(offsets[-1].item()))
+        x = bd.rm_block_fwd(x, blk)
+    return counts
+
+
 def cpu_baseline(inputs, L: int, n_rows: int) -> dict:
     import numpy as np
     from oracle import rankmixer_oracle as orc
@@ -604,10 +622,16 @@ def main() -> int:
     value = cfg.B * L / (elapsed / args.steps)
 
     # algorithmic work of each launch group (one launch group = one block's worth)
+    x0 = bd.rm_tokenize_padsplit(inp, cfg.T, cfg.D, out_dtype=dtype) if cfg.F else inp
+    active = None
     if cfg.E:
-        gemm_flops = None
+        # either expert product, averaged over the blocks: 2 * active rows * He * D
+        active = moe_active_rows(bd, blocks, x0, cfg.D)
+        gemm_flops = int(round(2 * (sum(active) / len(active)) * hidden * cfg.D))
+        prod_names = ("moe_ffn1", "moe_ffn2")
     else:
         gemm_flops = cfg.T * pm.gemm_flops(cfg.B, hidden, cfg.D)  # either product of one block
+        prod_names = ("ffn1", "ffn2")
     eb = pm.ELEM_BYTES[cfg.dtype]
     row_bytes = {  # compulsory HBM bytes per launch
         "mix_ln1": 2 * cfg.B * cfg.T * cfg.D * eb,
@@ -617,7 +641,7 @@ def main() -> int:
     for name, (tot_ms, n) in prof.items():
         avg = tot_ms / max(n, 1)
         e = {"avg_ms": round(avg, 5), "launches": n, "total_ms": round(tot_ms, 3)}
-        if gemm_flops and name in ("ffn1", "ffn2"):
+        if gemm_flops and name in prod_names:
             e["tflops"] = round(gemm_flops / (avg * 1e-3) / 1e12, 1)
         if name in row_bytes:
             e["gbs"] = round(row_bytes[name] / (avg * 1e-3) / 1e9, 1)
@@ -627,7 +651,7 @@ def main() -> int:
     if kernels:
         dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
         avg_s = kernels[dom]["avg_ms"] * 1e-3
-        if gemm_flops and dom in ("ffn1", "ffn2"):
+        if gemm_flops and dom in prod_names:
             ach = gemm_flops / avg_s / 1e12
             roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1),
                         "peak": pm.PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else pm.PEAK_FP32_MFMA_TFLOPS,
@@ -641,9 +665,13 @@ def main() -> int:
         if roofline is not None:
             roofline["traffic"] = committed_traffic(cfg.name, dom)
 
-    block_flops = pm.block_flops(cfg.B, cfg.T, cfg.D, hidden) if not cfg.E else None
-    step_tflops = block_flops * L / (ms_step * 1e-3) / 1e12 if block_flops else None
-    x0 = bd.rm_tokenize_padsplit(inp, cfg.T, cfg.D, out_dtype=dtype) if cfg.F else inp
+    if cfg.E:
+        flops_l = [pm.moe_flops(a, cfg.B, cfg.T, cfg.D, cfg.E, hidden) for a in active]
+        block_flops = flops_l[0]
+        step_tflops = sum(flops_l) / (ms_step * 1e-3) / 1e12
+    else:
+        block_flops = pm.block_flops(cfg.B, cfg.T, cfg.D, hidden)
+        step_tflops = block_flops * L / (ms_step * 1e-3) / 1e12
     block0 = block0_protocol(bd, blocks, x0, cfg.B, block_flops, pm.PEAK_BF16_TFLOPS)
     log(f"block 0 alone: {block0['ms']} ms")
 
@@ -672,6 +700,9 @@ def main() -> int:
         "kernels": kernels,
         "block0_fwd": block0,
     }
+    if active is not None:
+        rec["moe_active_rows"] = {"per_block": active, "of": cfg.B * cfg.T * cfg.E,
+                                  "note": "flops count active (sample, token, expert) rows only"}
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(inputs, L, args.cpu_rows)
