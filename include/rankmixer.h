@@ -340,9 +340,13 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
  * off (creating events is a host-side cost; leave it off outside timing).
  * rm_profile_count() is the number of names recorded; rm_profile_read(i, ...)
  * waits for entry i's events and returns its name, the summed event-to-event
- * time in ms and the number of launch groups.  Not thread-safe against
- * concurrent launches on other threads. */
+ * time in ms and the number of launch groups.  rm_profile_only(name)
+ * restricts recording to the groups of that name (NULL or "": every group),
+ * so a timed region can carry events around one kernel only; it persists
+ * across rm_profile_enable calls.  Not thread-safe against concurrent
+ * launches on other threads. */
 int rm_profile_enable(int on);
+int rm_profile_only(const char* name);
 int rm_profile_count(void);
 int rm_profile_read(int idx, char* name, size_t name_len, double* total_ms, int* launches);
 

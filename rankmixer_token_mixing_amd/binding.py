@@ -102,6 +102,7 @@ _SIGNATURES = {
     "rm_last_error": (C.c_char_p, []),
     "rm_version": (C.c_char_p, []),
     "rm_profile_enable": (_int, [_int]),
+    "rm_profile_only": (_int, [C.c_char_p]),
     "rm_profile_count": (_int, []),
     "rm_profile_read": (_int, [_int, C.c_char_p, _sz, C.POINTER(C.c_double), C.POINTER(C.c_int)]),
 }
@@ -435,6 +436,11 @@ def rm_model_fwd(model: Model, inp: torch.Tensor, want_x: bool = True, want_pool
 
 def profile_enable(on: bool = True) -> None:
     _check(load().rm_profile_enable(1 if on else 0))
+
+
+def profile_only(name: Optional[str] = None) -> None:
+    """Record only the launch groups called `name` (None: every group)."""
+    _check(load().rm_profile_only(name.encode() if name else None))
 
 
 def profile_read() -> Dict[str, tuple]:

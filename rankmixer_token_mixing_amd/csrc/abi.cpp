@@ -47,6 +47,7 @@ struct ProfEntry {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+std::string g_prof_only;  // non-empty: record only launch groups of this name
 std::vector<std::string> g_prof_names;
 std::map<std::string, ProfEntry> g_prof;
 
@@ -55,7 +56,7 @@ struct ProfScope {
   hipStream_t st;
   const char* name;
   ProfScope(const char* n, hipStream_t s) : st(s), name(n) {
-    if (!g_prof_on) return;
+    if (!g_prof_on || (!g_prof_only.empty() && g_prof_only != n)) return;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
       a = b = nullptr;
       return;
@@ -428,6 +429,12 @@ int rm_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   prof_clear();
   g_prof_on = on != 0;
+  return RM_OK;
+}
+
+int rm_profile_only(const char* name) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_only = name ? name : "";
   return RM_OK;
 }
 
