@@ -655,6 +655,7 @@ def main() -> int:
     row_bytes = {  # compulsory HBM bytes per launch
         "mix_ln1": 2 * cfg.B * cfg.T * cfg.D * eb,
         "ln2": cfg.B * cfg.T * cfg.D * 3 * eb,  # Z and the residual S in, X' out
+        "ln2_mix_ln1": cfg.B * cfg.T * cfg.D * 3 * eb,  # Z and S in, the next block's S out
     }
     def table(prof):
         kern = {}

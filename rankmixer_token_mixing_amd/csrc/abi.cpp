@@ -330,10 +330,18 @@ rm_status check_block_shape(int kind, int64_t B, int T, int D, int hidden, int E
   return RM_OK;
 }
 
+// One block X -> xo.  s_given: S = LN1(TM(X) + X) is already in w.S
+// (token-major; x is not read).  next: instead of LN2 into xo, run the block
+// boundary, which leaves the next block's S in w.S (the block's output is not
+// materialised); the caller checks fusable_boundary first.
 rm_status run_block(const void* x, const rm_block_params* p, void* xo, int64_t B, int T, int D, int hidden,
-                    int E, int dt, const BlockWs& w, hipStream_t st) {
+                    int E, int dt, const BlockWs& w, hipStream_t st, bool s_given = false,
+                    const rm_block_params* next = nullptr) {
   int64_t sb, sT;  // S row (b, t) at b * sb + t * sT
-  if (p->flags & RM_BLOCK_NO_MIX_NORM) {
+  if (s_given) {
+    sb = D;
+    sT = B * D;
+  } else if (p->flags & RM_BLOCK_NO_MIX_NORM) {
     // S = TM(X), [B][T][D]
     RM_TIMED("mix", st, RM_HIP(rm::launch_token_mix(x, w.S, B, T, D, dt, st), "token mix"));
     sb = (int64_t)T * D;
@@ -371,11 +379,28 @@ rm_status run_block(const void* x, const rm_block_params* p, void* xo, int64_t B
     a2.epi = rm::kEpiBias;
     a2.C = w.Z;
     RM_TIMED("ffn2", st, RM_HIP(rm::launch_gemm(a2, st), "block W2 product"));
+    if (next) {
+      RM_TIMED("ln2_mix_ln1", st, RM_HIP(rm::launch_ln_mix_ln(w.Z, w.S, p->ln2_g, p->ln2_b, next->ln1_g, next->ln1_b,
+                                                              B, T, D, dt, st),
+                                         "LayerNorm 2 + next block's token mix + LayerNorm 1"));
+      return RM_OK;
+    }
     RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows(w.Z, w.S, sb, sT, T, xo, p->ln2_g, p->ln2_b, B * T, D, dt, st),
                                "residual + LayerNorm 2"));
     return RM_OK;
   }
   return run_moe(w.S, sb, sT, &p->moe, xo, nullptr, p->ln2_g, p->ln2_b, B, T, D, E, hidden, dt, w.moe, st);
+}
+
+// whether block l's LN2 and block l + 1's mix + LN1 run as one boundary pass
+// (block l a dense or SwiGLU block, neither block without the Add & Norm
+// after the mix, and the sample's T rows fit in LDS)
+bool fusable_boundary(const rm_model_desc* m, int l) {
+  if (l + 1 >= m->L) return false;
+  const rm_block_params& a = m->blocks[l];
+  const rm_block_params& b = m->blocks[l + 1];
+  return (a.kind == RM_BLOCK_DENSE || a.kind == RM_BLOCK_SWIGLU) && a.flags == 0 && b.flags == 0 &&
+         rm::ln_mix_ln_supported(m->T, m->D, m->dtype);
 }
 
 size_t model_ws(Carver& c, const rm_model_desc* m, int64_t B, void** x0, void** x1, BlockWs* bw) {
@@ -1156,15 +1181,23 @@ rm_status rm_model_fwd(const rm_model_desc* m, const void* in, void* x_out, floa
     cur = buf[0];
     next = 1;
   }
+  // every block kind carves S first, so S sits at the same address for all
+  // blocks and a boundary pass can leave the next block's S there
+  bool s_given = false;
   for (int l = 0; l < m->L; ++l) {
     void* dst = (l == m->L - 1 && x_out) ? x_out : buf[next];
     // a block workspace sized for the largest kind; re-carve for this kind
     Carver bc(bw.S);
     BlockWs w;
     block_ws(bc, m->blocks[l].kind, B, T, D, m->hidden, m->E, dt, &w);
-    RM_TRY(run_block(cur, &m->blocks[l], dst, B, T, D, m->hidden, m->E, dt, w, st));
-    cur = dst;
-    next ^= 1;
+    const bool fuse = fusable_boundary(m, l);
+    RM_TRY(run_block(cur, &m->blocks[l], dst, B, T, D, m->hidden, m->E, dt, w, st, s_given,
+                     fuse ? &m->blocks[l + 1] : nullptr));
+    s_given = fuse;
+    if (!fuse) {
+      cur = dst;
+      next ^= 1;
+    }
   }
   if (x_out && cur != x_out) RM_HIP(hipMemcpyAsync(x_out, cur, (size_t)B * T * D * elem_bytes(dt), hipMemcpyDeviceToDevice, st), "copy x_out");
   if (m->head_w) RM_TIMED("pool_logit", st, RM_HIP(rm::launch_pool_logit(cur, m->head_w, m->head_c, pooled, logits, B, T, D, dt, st), "pool + logit"));

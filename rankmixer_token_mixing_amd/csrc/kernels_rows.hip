@@ -225,6 +225,134 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const T* __re
 }
 
 // ---------------------------------------------------------------------------
+// Block boundary: the LN2 of one block and the mix + LN1 of the next, per
+// sample in one workgroup.  Phase 1: X'[t] = LN2(Z[b][t] + S[t][b]) for every
+// token t of sample b, rounded to the activation type as the block output is,
+// into LDS (row pitch D plus one head, so the gathers of phase 2 walk the
+// banks).  Phase 2: S'[h][b] = LN1(TM(X')[h] + X'[h]) from LDS, written over
+// S (token-major; only this workgroup touches sample b's rows, and every
+// read of them happens before the barrier).  X' never goes to HBM.
+constexpr int kBndThreads = 1024;
+constexpr int kBndLdsMax = 128 * 1024;
+
+template <typename T, int VEC, int MAXI>
+__global__ __launch_bounds__(kBndThreads) void k_ln_mix_ln(const T* __restrict__ z, T* s,
+                                                           const float* __restrict__ g2,
+                                                           const float* __restrict__ be2,
+                                                           const float* __restrict__ g1,
+                                                           const float* __restrict__ be1, int64_t B, int T_,
+                                                           int D, int pitch) {
+  extern __shared__ uint4 bnd_lds[];
+  T* xl = reinterpret_cast<T*>(bnd_lds);
+  const int NW = blockDim.x / kWave;  // T/2 waves (at most 16): two rows each
+  const int64_t b = blockIdx.x;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int d = D / T_, nch = D / VEC;
+  // phase 1, two rows per wave at a time: every load of both rows is issued
+  // before any is used (chunk indices past the row re-read its last chunk and
+  // are left out of the sums and stores)
+  for (int t0 = wave; t0 < T_; t0 += 2 * NW) {
+    const int tr[2] = {t0, t0 + NW < T_ ? t0 + NW : t0};
+    float v[2][MAXI][VEC], q[2][MAXI][VEC];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const T* zr = z + (b * T_ + tr[r]) * (int64_t)D;
+      const T* sr = s + ((int64_t)tr[r] * B + b) * D;
+#pragma unroll
+      for (int i = 0; i < MAXI; ++i) {
+        const int c = min(lane + i * kWave, nch - 1);
+        load_f32<T, VEC>(zr + c * VEC, v[r][i]);
+        load_f32<T, VEC>(sr + c * VEC, q[r][i]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (r == 1 && t0 + NW >= T_) break;
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < MAXI; ++i) {
+        const bool in = lane + i * kWave < nch;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          v[r][i][e] += q[r][i][e];
+          sum += in ? v[r][i][e] : 0.f;
+        }
+      }
+      const float mean = wave_sum(sum) / (float)D;
+      float sq = 0.f;
+#pragma unroll
+      for (int i = 0; i < MAXI; ++i) {
+        const bool in = lane + i * kWave < nch;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float dv = v[r][i][e] - mean;
+          sq += in ? dv * dv : 0.f;
+        }
+      }
+      const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D + ln_eps());
+#pragma unroll
+      for (int i = 0; i < MAXI; ++i) {
+        const int c = lane + i * kWave;
+        if (c < nch) {
+          const int k = c * VEC;
+          float o[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) o[e] = (v[r][i][e] - mean) * rstd * g2[k + e] + be2[k + e];
+          store_from_f32<T, VEC>(xl + tr[r] * pitch + k, o);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int h = wave; h < T_; h += NW) {
+    float v[MAXI][VEC];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nch) {
+        const int k = c * VEC;
+        const int tp = k / d, j = k - tp * d;
+        float m[VEC], r[VEC];
+        load_f32<T, VEC>(xl + tp * pitch + h * d + j, m);
+        load_f32<T, VEC>(xl + h * pitch + k, r);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          v[i][e] = m[e] + r[e];
+          sum += v[i][e];
+        }
+      }
+    }
+    const float mean = wave_sum(sum) / (float)D;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nch) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float q = v[i][e] - mean;
+          sq += q * q;
+        }
+      }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D + ln_eps());
+    T* orow = s + ((int64_t)h * B + b) * D;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nch) {
+        const int k = c * VEC;
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = (v[i][e] - mean) * rstd * g1[k + e] + be1[k + e];
+        store_from_f32<T, VEC>(orow + k, o);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // pooled[b,k] = (1/T) sum_t x[b,t,k];  logit[b] = sum_k w[k] pooled[b,k] + c
 
 template <typename T, int VEC>
@@ -367,6 +495,59 @@ hipError_t launch_mix_ln(const void* x, void* so, const float* g, const float* b
     case 4: return mix_ln_vec<float, 4>(x, so, g, b, B, T, D, tm, s);
     case 2: return mix_ln_vec<float, 2>(x, so, g, b, B, T, D, tm, s);
     default: return mix_ln_vec<float, 1>(x, so, g, b, B, T, D, tm, s);
+  }
+}
+
+namespace {
+// LDS row pitch of the boundary kernel in elements: D plus one head rounded
+// up to 16 bytes
+int bnd_pitch(int T, int D, int eb) { return D + ((D / T * eb + 15) / 16 * 16) / eb; }
+
+template <typename T, int VEC>
+hipError_t ln_mix_ln_vec(const void* z, void* s, const float* g2, const float* b2, const float* g1,
+                         const float* b1, int64_t B, int T_, int D, hipStream_t st) {
+  const int pitch = bnd_pitch(T_, D, (int)sizeof(T));
+  const size_t lds = (size_t)T_ * pitch * sizeof(T);
+  const int nw = std::min(kBndThreads / kWave, std::max(1, (T_ + 1) / 2));
+  const dim3 grid((unsigned)B), block(nw * kWave);
+  const T* zz = (const T*)z;
+  T* ss = (T*)s;
+  switch (pick_maxi(D / VEC)) {
+    case 0: return hipErrorInvalidValue;
+    case 1: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 1>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
+    case 2: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 2>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
+    case 4: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 4>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
+    default: return hipErrorInvalidValue;  // wider rows: see ln_mix_ln_supported
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+bool ln_mix_ln_supported(int T, int D, int dt) {
+  // the sample's rows fit in LDS, and a row is at most 4 chunks per lane (the
+  // 16 waves of a workgroup hold two rows each in 128 registers)
+  const int eb = dt == kBF16 ? 2 : 4;
+  return row_width_supported(T, D, dt) && (size_t)T * bnd_pitch(T, D, eb) * eb <= (size_t)kBndLdsMax &&
+         pick_maxi(D / chunk_elems(D / T, eb)) <= 4;
+}
+
+hipError_t launch_ln_mix_ln(const void* z, void* s, const float* g2, const float* b2, const float* g1,
+                            const float* b1, int64_t B, int T, int D, int dt, hipStream_t st) {
+  if (!ln_mix_ln_supported(T, D, dt)) return hipErrorInvalidValue;
+  if (B == 0) return hipSuccess;
+  const int d = D / T;
+  if (dt == kBF16) {
+    switch (chunk_elems(d, 2)) {
+      case 8: return ln_mix_ln_vec<bf16, 8>(z, s, g2, b2, g1, b1, B, T, D, st);
+      case 4: return ln_mix_ln_vec<bf16, 4>(z, s, g2, b2, g1, b1, B, T, D, st);
+      case 2: return ln_mix_ln_vec<bf16, 2>(z, s, g2, b2, g1, b1, B, T, D, st);
+      default: return ln_mix_ln_vec<bf16, 1>(z, s, g2, b2, g1, b1, B, T, D, st);
+    }
+  }
+  switch (chunk_elems(d, 4)) {
+    case 4: return ln_mix_ln_vec<float, 4>(z, s, g2, b2, g1, b1, B, T, D, st);
+    case 2: return ln_mix_ln_vec<float, 2>(z, s, g2, b2, g1, b1, B, T, D, st);
+    default: return ln_mix_ln_vec<float, 1>(z, s, g2, b2, g1, b1, B, T, D, st);
   }
 }
 

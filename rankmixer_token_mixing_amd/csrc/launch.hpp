@@ -30,6 +30,13 @@ hipError_t launch_mix_ln(const void* x, void* s_out, const float* g, const float
 // elements
 hipError_t launch_ln_rows(const void* z, const void* res, int64_t res_bs, int64_t res_ts, int Tn, void* out,
                           const float* g, const float* b, int64_t rows, int D, int dt, hipStream_t s);
+// block boundary: S' = LN1'(TM(X') + X') with X' = LN2(Z + S), per sample in
+// one workgroup; Z [B][T][D], S token-major, overwritten by S' (token-major).
+// X' stays in LDS (T rows of D + one head), so only shapes that fit are
+// supported.
+bool ln_mix_ln_supported(int T, int D, int dt);
+hipError_t launch_ln_mix_ln(const void* z, void* s, const float* g2, const float* b2, const float* g1,
+                            const float* b1, int64_t B, int T, int D, int dt, hipStream_t st);
 // pooled[b] = mean_t x[b,t,:]; logit[b] = w . pooled[b] + c
 hipError_t launch_pool_logit(const void* x, const float* w, float c, float* pooled, float* logits,
                              int64_t B, int T, int D, int dt, hipStream_t s);
