@@ -52,6 +52,7 @@ KERNEL_SOURCES = {
     "ffn2": ("kernels_gemm.hip", "frag.hpp", "common.hpp"),
     "mix_ln1": ("kernels_rows.hip", "common.hpp"),
     "ln2": ("kernels_rows.hip", "common.hpp"),
+    "ln2_mix_ln1": ("kernels_rows.hip", "common.hpp"),
     "tokenize_proj": ("kernels_tokproj.hip", "frag.hpp", "common.hpp"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_fwd_{config}_traffic.json")
