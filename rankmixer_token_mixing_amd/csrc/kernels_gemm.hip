@@ -56,6 +56,7 @@ struct KParams {
   const int* tiles;
   const int* ntiles;
   int M, N, K, G, tiles_m, tiles_n;
+  int n_fast;  // dense: consecutive tiles walk the N tiles of one M row (else the M tiles of one N column)
 };
 
 // 16 zero bytes: the source of every chunk that lies past K
@@ -109,13 +110,15 @@ __device__ __forceinline__ bool tile_id(const KParams& p, TileId& t) {
     t.Mg = p.row_off[t.g + 1] - (int)t.row_base;
   } else {
     // consecutive ids (one XCD after xcd_remap) walk the M tiles of one N
-    // column first, so concurrently running tiles share W panels and A panels
+    // column first (or, n_fast, the N tiles of one M row), so concurrently
+    // running tiles share W panels and A panels
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int per = p.tiles_m * p.tiles_n;
     t.g = lid / per;
     const int r = lid - t.g * per;
-    const int tn = r / p.tiles_m;
-    t.m0 = (r - tn * p.tiles_m) * BM;
+    const int tn = p.n_fast ? r % p.tiles_n : r / p.tiles_m;
+    const int tm = p.n_fast ? r / p.tiles_n : r - tn * p.tiles_m;
+    t.m0 = tm * BM;
     t.n0 = tn * BN;
     t.row_base = 0;
     t.Mg = p.M;
@@ -746,8 +749,9 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
   if (v >= ntile) return;
 
   // logical tile of virtual id v: consecutive ids of one XCD walk the M tiles
-  // of one N column first (dense) or the N tiles of one (group, m0) (ragged),
-  // so concurrently running tiles share operand panels
+  // of one N column first (dense; n_fast: the N tiles of one M row) or the N
+  // tiles of one (group, m0) (ragged), so concurrently running tiles share
+  // operand panels
   auto tile_of = [&](int vv, TileId& t) {
     const int lid = xcd_remap(vv, ntile);
     if constexpr (RAGGED) {
@@ -761,8 +765,9 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
       const int per = p.tiles_m * p.tiles_n;
       t.g = lid / per;
       const int r = lid - t.g * per;
-      const int tn = r / p.tiles_m;
-      t.m0 = (r - tn * p.tiles_m) * BM;
+      const int tn = p.n_fast ? r % p.tiles_n : r / p.tiles_m;
+      const int tm = p.n_fast ? r / p.tiles_n : r - tn * p.tiles_m;
+      t.m0 = tm * BM;
       t.n0 = tn * BN;
       t.row_base = 0;
       t.Mg = p.M;
@@ -934,6 +939,10 @@ KParams make_params(const GemmArgs& a, int bm, int bn) {
   p.M = a.M; p.N = a.N; p.K = a.K; p.G = a.G;
   p.tiles_m = ceil_div(a.M, bm);
   p.tiles_n = ceil_div(a.N, bn);
+  // tile order: the operand whose panels of one group take less space is the
+  // one cycled (kept in L2 across the walk), the other is read once per panel
+  const double a_panels = (double)p.tiles_m * bm * a.K, w_panels = (double)p.tiles_n * bn * a.K;
+  p.n_fast = !a.row_off && w_panels < a_panels ? 1 : 0;
   return p;
 }
 
