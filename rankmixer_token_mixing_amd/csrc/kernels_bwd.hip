@@ -158,6 +158,11 @@ __global__ __launch_bounds__(kLnWaves* kWave) void k_ln_bwd(LnBwdArgs a) {
   }
 }
 
+// 64-row tiles covering max(R, ldo) rows (the column-sum partials)
+__host__ __device__ __forceinline__ int transpose_row_tiles_dev(int64_t R, int64_t ldo) {
+  return (int)(((R > ldo ? R : ldo) + 63) / 64);
+}
+
 struct TrArgs {
   const void* in;   // [G][R][C]: element (g, r, c) at g * in_gs + r * in_rs + c
   const void* aux;  // op 2: U, same layout as in
@@ -244,6 +249,115 @@ __global__ __launch_bounds__(256) void k_transpose(TrArgs a) {
       s += __shfl_xor(s, 2, kWave);
       if ((tid & 3) == 0 && c < a.C) a.colsum[(g * gridDim.y + blockIdx.y) * a.C + c] = s;
     }
+  }
+}
+
+// The GELU-derivative pass (op 2) in bf16, 128 x 128 tiles (256-byte row
+// segments on both sides).  Phase 1: each thread loads 8 chunks of 8 elements
+// of dH and U (rows tid/16 + 16i, columns (tid%16)*8), forms dU = dH GELU'(U),
+// stores it directly (direct), keeps GELU(U) in registers and writes dU as
+// bf16 into an LDS tile of row pitch 136.  Phase 2: each thread reads 32 rows
+// of two adjacent columns (one 32-bit LDS read per row) and writes two
+// 64-byte pieces of output rows; the per-64-row column sums come from the
+// rounded values.  With out2, phase 2 runs a second time over GELU(U).  The 16-byte chunks of a row are
+// XOR-swizzled by 4 x (row / 32 mod 4), so the four 32-row blocks a wave reads
+// in phase 2 fall on disjoint banks.
+constexpr int kTr = 128;       // tile edge
+constexpr int kTrPitch = 136;  // LDS row pitch (elements)
+
+// LDS element index of (row, column) in the swizzled tile
+__device__ __forceinline__ int tr_lds(int row, int col) {
+  return row * kTrPitch + (((col >> 3) ^ (((row >> 5) & 3) << 2)) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(lo)) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(hi)) << 16);
+}
+
+__global__ __launch_bounds__(256) void k_gelu_bwd_t128(TrArgs a) {
+  __shared__ __align__(16) bf16 tile[kTr * kTrPitch];
+  const int tid = threadIdx.x;
+  const int64_t g = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * kTr, c0 = (int64_t)blockIdx.x * kTr;
+  const bf16* in = (const bf16*)a.in + g * a.in_gs;
+  const int ch = tid % 16;                 // column chunk of phase 1
+  const int64_t cc = c0 + ch * 8;
+  uint4 keep[8];                           // GELU(aux) of the 8 chunks, packed
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rl = tid / 16 + 16 * i;
+    const int64_t r = r0 + rl;
+    float v[8];
+    const bool ok = r < a.R && cc < a.C;
+    if (ok) {
+      float u[8];
+      load_f32<bf16, 8>(in + r * a.in_rs + cc, v);
+      load_f32<bf16, 8>((const bf16*)a.aux + g * a.in_gs + r * a.in_rs + cc, u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float gu, dgu;
+        gelu_and_grad(u[e], gu, dgu);
+        v[e] *= dgu;
+        u[e] = gu;
+      }
+      if (a.direct) store_from_f32<bf16, 8>((bf16*)a.direct + g * a.dir_gs + r * a.dir_rs + cc, v);
+      keep[i] = make_uint4(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]), pack_bf16x2(u[4], u[5]),
+                           pack_bf16x2(u[6], u[7]));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      keep[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    *reinterpret_cast<uint4*>(tile + tr_lds(rl, ch * 8)) =
+        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7]));
+  }
+  __syncthreads();
+  // phase 2: columns cl, cl + 1 of the tile, rows q*32 .. q*32 + 31
+  const int cl = (tid / 4) * 2, q = tid % 4;
+  const int nrt = transpose_row_tiles_dev(a.R, a.ldo);
+  auto out_pass = [&](bf16* out, bool sums) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float lo[8], hi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + tr_lds(q * 32 + k * 8 + e, cl));
+        lo[e] = __uint_as_float(w << 16);
+        hi[e] = __uint_as_float(w & 0xffff0000u);
+        s0 += lo[e];
+        s1 += hi[e];
+      }
+      const int64_t r = r0 + q * 32 + k * 8;
+      if (r < a.ldo) {
+        if (c0 + cl < a.C) store_from_f32<bf16, 8>(out + g * a.C * a.ldo + (c0 + cl) * a.ldo + r, lo);
+        if (c0 + cl + 1 < a.C) store_from_f32<bf16, 8>(out + g * a.C * a.ldo + (c0 + cl + 1) * a.ldo + r, hi);
+      }
+    }
+    if (sums) {
+      // the two threads of one 64-row half are adjacent lanes
+      s0 += __shfl_xor(s0, 1, kWave);
+      s1 += __shfl_xor(s1, 1, kWave);
+      const int half = (int)(blockIdx.y * 2) + q / 2;
+      if ((q & 1) == 0 && half < nrt) {
+        float* cs = a.colsum + (g * nrt + half) * a.C;
+        if (c0 + cl < a.C) cs[c0 + cl] = s0;
+        if (c0 + cl + 1 < a.C) cs[c0 + cl + 1] = s1;
+      }
+    }
+  };
+  out_pass((bf16*)a.out, a.colsum != nullptr);
+  if (a.out2) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rl = tid / 16 + 16 * i;
+      *reinterpret_cast<uint4*>(tile + tr_lds(rl, ch * 8)) = keep[i];
+    }
+    __syncthreads();
+    out_pass((bf16*)a.out2, false);
   }
 }
 
@@ -398,10 +512,13 @@ hipError_t launch_transpose(int op, const void* in, const void* aux, void* out, 
   TrArgs a{in, aux, out, direct, out2, colsum, R, C, ldo, in_gs, in_rs, dir_gs, dir_rs};
   const dim3 block(256);
   if (dt == kBF16) {
+    // the GELU-derivative pass (two inputs, up to three outputs) runs faster in
+    // 128 x 128 tiles; plain transposes in 64 x 64 ones (measured)
+    const dim3 g128((unsigned)((C + kTr - 1) / kTr), (unsigned)((std::max(R, ldo) + kTr - 1) / kTr), (unsigned)G);
     switch (op) {
       case 0: hipLaunchKernelGGL((k_transpose<bf16, 0>), grid, block, 0, s, a); break;
       case 1: hipLaunchKernelGGL((k_transpose<bf16, 1>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((k_transpose<bf16, 2>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL(k_gelu_bwd_t128, g128, block, 0, s, a); break;
     }
   } else {
     switch (op) {
