@@ -762,10 +762,18 @@ rm_status rm_block_fwd_train(const void* x, const rm_block_params* p, void* x_ou
   block_ws(c, RM_BLOCK_DENSE, B, T, D, hidden, 0, dtype, &w);
   const int64_t sb = D, sT = B * D;  // S is token-major
   RM_TIMED("mix_ln1", st, RM_HIP(rm::launch_mix_ln(x, sv.S, p->ln1_g, p->ln1_b, B, T, D, dtype, true, st), "token mix + LayerNorm"));
+  // keep U = W1 s + b1 (saved) and H = GELU(U): both from the product's
+  // epilogue on the pipelined kernel, else a separate GELU pass
   rm::GemmArgs a1 = ffn1_args(sv.S, sb, sT, &p->pffn, sv.U, B, T, D, hidden, dtype);
-  a1.epi = rm::kEpiBias;  // keep U = W1 s + b1; GELU separately
-  RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block W1 product"));
-  RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.pffn.H, B * T * (int64_t)hidden, dtype, st), "GELU"));
+  a1.epi = rm::kEpiBiasGeluDual;
+  a1.C2 = w.pffn.H;
+  if (rm::gemm_pipe_eligible(a1)) {
+    RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block W1 product + GELU"));
+  } else {
+    a1.epi = rm::kEpiBias;
+    RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block W1 product"));
+    RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.pffn.H, B * T * (int64_t)hidden, dtype, st), "GELU"));
+  }
   rm::GemmArgs a2 = ffn2_args(w.pffn.H, &p->pffn, B, T, D, hidden, dtype);
   a2.epi = rm::kEpiBias;
   a2.C = sv.Z;
@@ -1010,8 +1018,15 @@ rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const 
   a1.W = p->moe.w1; a1.b_gs = (int64_t)He * D;
   a1.C = sv.U; a1.c_gs = B * He; a1.c_rs = He;
   a1.bias = p->moe.b1; a1.bias_gs = He;
-  RM_TIMED("moe_ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "expert W1 products"));
-  RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.H, B * TE * He, dt, st), "GELU"));
+  a1.epi = rm::kEpiBiasGeluDual;  // U (saved) and H = GELU(U) from one epilogue where the kernel allows
+  a1.C2 = w.H;
+  if (rm::gemm_pipe_eligible(a1)) {
+    RM_TIMED("moe_ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "expert W1 products + GELU"));
+  } else {
+    a1.epi = rm::kEpiBias;
+    RM_TIMED("moe_ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "expert W1 products"));
+    RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.H, B * TE * He, dt, st), "GELU"));
+  }
   rm::GemmArgs a2;
   a2.dt = dt; a2.epi = rm::kEpiBias;
   a2.M = (int)B; a2.N = D; a2.K = He; a2.G = (int)TE;

@@ -49,6 +49,7 @@ struct KParams {
   int b_gdiv;
   void* C;
   long long c_gs, c_rs;
+  void* C2;  // kEpiBiasGeluDual: GELU(C), same layout as C
   const float* bias;
   long long bias_gs;
   const float* rowscale;
@@ -86,8 +87,9 @@ template <> struct Mma<float> {
 
 template <int EPI, typename T>
 struct OutType {
-  typedef typename std::conditional<EPI == kEpiBiasGelu || EPI == kEpiBias || EPI == kEpiBiasScale, T, float>::type
-      type;
+  typedef typename std::conditional<EPI == kEpiBiasGelu || EPI == kEpiBias || EPI == kEpiBiasScale ||
+                                        EPI == kEpiBiasGeluDual,
+                                    T, float>::type type;
 };
 
 // which tile this workgroup owns
@@ -653,9 +655,18 @@ __device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileI
         const int c = tid % OCH;
         const int m = t.m0 + (sr / 64) * 128 + h * 64 + (sr % 64);
         const uint4 val = *reinterpret_cast<const uint4*>(stage + sr * (BN * 2) + ((c ^ (sr & (OCH - 1))) * 16));
-        if (m < t.Mg && t.n0 + c * 8 < p.N)
-          *reinterpret_cast<uint4*>((bf16*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + t.n0 + c * 8) =
-              val;
+        if (m < t.Mg && t.n0 + c * 8 < p.N) {
+          const long long off = (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + t.n0 + c * 8;
+          *reinterpret_cast<uint4*>((bf16*)p.C + off) = val;
+          if constexpr (EPI == kEpiBiasGeluDual) {
+            // GELU of the stored (rounded) pre-activation, as a separate pass would
+            float u[8];
+            load_f32<bf16, 8>(reinterpret_cast<const bf16*>(&val), u);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = gelu_erf(u[e]);
+            store_from_f32<bf16, 8>((bf16*)p.C2 + off, u);
+          }
+        }
       }
     }
     __syncthreads();  // staging is free again
@@ -887,7 +898,8 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
       issue_w(1, 0);
       issue_a(2, 1);
     }
-    if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias || EPI == kEpiSwiglu || EPI == kEpiBiasScale)
+    if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias || EPI == kEpiSwiglu || EPI == kEpiBiasScale ||
+                  EPI == kEpiBiasGeluDual)
       pipe_epilogue_bf16<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
     else
       pipe_epilogue_f32<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
@@ -932,7 +944,7 @@ KParams make_params(const GemmArgs& a, int bm, int bn) {
   KParams p;
   p.A = a.A; p.a_gs = a.a_gs; p.a_rs = a.a_rs; p.a_gdiv = a.a_gdiv; p.a_rowidx = a.a_rowidx;
   p.W = a.W; p.b_gs = a.b_gs; p.b_gdiv = a.b_gdiv;
-  p.C = a.C; p.c_gs = a.c_gs; p.c_rs = a.c_rs;
+  p.C = a.C; p.c_gs = a.c_gs; p.c_rs = a.c_rs; p.C2 = a.C2;
   p.bias = a.bias; p.bias_gs = a.bias_gs;
   p.rowscale = a.rowscale;
   p.row_off = a.row_off; p.tiles = a.tiles; p.ntiles = a.ntiles;
@@ -968,7 +980,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   if (grid.x == 0) return hipSuccess;
   if (ragged && !((a.epi == kEpiBiasGelu && a.a_rowidx) || (a.epi == kEpiBiasScale && !a.a_rowidx)))
     return hipErrorInvalidValue;
-  if (!ragged && !(a.epi == kEpiBiasGelu || a.epi == kEpiBias || a.epi == kEpiBiasF32 || a.epi == kEpiSwiglu))
+  if (!ragged && !(a.epi == kEpiBiasGelu || a.epi == kEpiBias || a.epi == kEpiBiasF32 || a.epi == kEpiSwiglu ||
+                   (a.epi == kEpiBiasGeluDual && a.C2)))
     return hipErrorInvalidValue;
 
   if constexpr (FM == 4 && FN == 2) {
@@ -998,13 +1011,16 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
           case kEpiSwiglu:
             hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiSwiglu, false, false>), grid2, block, 0, s, p);
             break;
+          case kEpiBiasGeluDual:
+            hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasGeluDual, false, false>), grid2, block, 0, s, p);
+            break;
           default: hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasF32, false, false>), grid2, block, 0, s, p); break;
         }
       }
       return hipGetLastError();
     }
   }
-  if (a.epi == kEpiSwiglu) return hipErrorInvalidValue;  // the pipelined kernel only
+  if (a.epi == kEpiSwiglu || a.epi == kEpiBiasGeluDual) return hipErrorInvalidValue;  // the pipelined kernel only
   if (ragged) {
     if (a.a_rowidx)
       launch_one<NWM, NWN, FM, FN, kEpiBiasGelu, true, true>(a, p, grid, s, ring);

@@ -76,6 +76,9 @@ enum Epilogue {
   // W rows 0..Hs-1 are the gate rows, Hs..N-1 the up rows; C is Hs wide.
   // Pipelined kernel only (gemm_pipe_eligible).
   kEpiSwiglu = 4,
+  // C(dt) = acc + bias[n] and C2(dt) = GELU(C) (same layout; training keeps
+  // the pre-activation).  Pipelined kernel only.
+  kEpiBiasGeluDual = 5,
 };
 
 // C_g[m][n] = sum_k A_g[m][k] * W_g[n][k], g = 0..G-1, followed by an epilogue.
@@ -92,6 +95,7 @@ struct GemmArgs {
   const int* a_rowidx = nullptr;
   const void* W = nullptr; int64_t b_gs = 0; int b_gdiv = 1;  // W group of g at (g / b_gdiv) * b_gs
   void* C = nullptr; int64_t c_gs = 0, c_rs = 0;
+  void* C2 = nullptr;  // kEpiBiasGeluDual
   const float* bias = nullptr; int64_t bias_gs = 0;
   const float* rowscale = nullptr;
   // ragged mode (MoE): group g has row_off[g+1]-row_off[g] rows; the tiles
