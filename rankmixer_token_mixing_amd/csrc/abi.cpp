@@ -701,7 +701,7 @@ size_t bwd_carve(Carver& c, int64_t B, int T, int D, int Hd, int dt, BwdWs* w) {
   const size_t e = elem_bytes(dt);
   const int64_t Bp = pad64(B);
   const int64_t rt = rm::transpose_row_tiles(B, Bp);
-  const int lg = rm::ln_bwd_grid(B, T);
+  const int lg = rm::ln_bwd_grid(B, T, D);
   BwdWs x;
   x.dV = c.take((size_t)T * B * D * e);
   x.dVt = c.take((size_t)T * D * Bp * e);
@@ -825,7 +825,7 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   const int dt = dtype;
   const int64_t Bp = pad64(B);
   const int rt = rm::transpose_row_tiles(B, Bp);
-  const int lg = rm::ln_bwd_grid(B, T);
+  const int lg = rm::ln_bwd_grid(B, T, D);
   // X' = LN2(Z + S): dV = dY2 (token-major), gamma2 / beta2 partials
   RM_TIMED("ln2_bwd", st, RM_HIP(rm::launch_ln_bwd(0, d_out, nullptr, nullptr, sv.Z, sv.S, p->ln2_g, w.dV, w.ln2p, B, T, D, dt, st), "LayerNorm 2 backward"));
   // dV^T (rows padded to Bp) and the b2 partials
@@ -919,7 +919,7 @@ size_t moe_train_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt
   const size_t e = elem_bytes(dt);
   const int64_t TE = (int64_t)T * E, Bp = pad64(B);
   const int64_t rt = rm::transpose_row_tiles(B, Bp);
-  const int lg = rm::ln_bwd_grid(B, T);
+  const int lg = rm::ln_bwd_grid(B, T, D);
   MoeTrainWs x;
   x.H = c.take((size_t)B * TE * He * e);
   x.dV = c.take((size_t)T * B * D * e);
@@ -1071,7 +1071,7 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
   const int dt = dtype;
   const int64_t TE = (int64_t)T * E, Bp = pad64(B);
   const int rt = rm::transpose_row_tiles(B, Bp);
-  const int lg = rm::ln_bwd_grid(B, T);
+  const int lg = rm::ln_bwd_grid(B, T, D);
   Carver cs(const_cast<void*>(saved));
   MoeSaved sv;
   moe_saved_carve(cs, B, T, D, E, He, dt, &sv);

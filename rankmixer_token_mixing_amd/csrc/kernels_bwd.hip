@@ -385,32 +385,37 @@ __global__ __launch_bounds__(256) void k_tm_add(const float* __restrict__ dy, T*
 
 // out[g][c] = sum over p < P of part[(g * P + p) * C + c]; columns c < split
 // go to out0[g * split + c], the rest to out1[g * (C - split) + c - split].
-// A workgroup owns 64 columns of one g: lane group q < 4 sums p = q, q+4, ...
-// in order, then the four sums are added in order -- a fixed order throughout.
-__global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ part, float* __restrict__ out0,
-                                                   float* __restrict__ out1, int P, int64_t C, int64_t split,
-                                                   float scale) {
-  __shared__ float acc[4][64];
+// A workgroup owns 64 columns of one g: lane group q < S sums p = q, q + S,
+// ... in order, then the group sums are added in order -- a fixed order
+// throughout (S = 16 for many partials, 4 for few).
+template <int S>
+__global__ __launch_bounds__(64 * S) void k_sum_parts(const float* __restrict__ part, float* __restrict__ out0,
+                                                      float* __restrict__ out1, int P, int64_t C, int64_t split,
+                                                      float scale) {
+  __shared__ float acc[S][64];
   const int cl = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int64_t g = blockIdx.y, c = (int64_t)blockIdx.x * 64 + cl;
   float s = 0.f;
   if (c < C) {
     const float* p = part + g * P * C + c;
     int i = q;
-    for (; i + 12 < P; i += 16) {
-      const float a0 = p[(int64_t)i * C], a1 = p[(int64_t)(i + 4) * C], a2 = p[(int64_t)(i + 8) * C],
-                  a3 = p[(int64_t)(i + 12) * C];
+    for (; i + 3 * S < P; i += 4 * S) {
+      const float a0 = p[(int64_t)i * C], a1 = p[(int64_t)(i + S) * C], a2 = p[(int64_t)(i + 2 * S) * C],
+                  a3 = p[(int64_t)(i + 3 * S) * C];
       s += a0;
       s += a1;
       s += a2;
       s += a3;
     }
-    for (; i < P; i += 4) s += p[(int64_t)i * C];
+    for (; i < P; i += S) s += p[(int64_t)i * C];
   }
   acc[q][cl] = s;
   __syncthreads();
   if (q == 0 && c < C) {
-    const float v = (((acc[0][cl] + acc[1][cl]) + acc[2][cl]) + acc[3][cl]) * scale;
+    float v = acc[0][cl];
+#pragma unroll
+    for (int k = 1; k < S; ++k) v += acc[k][cl];
+    v *= scale;
     if (c < split)
       out0[g * split + c] = v;
     else
@@ -476,10 +481,15 @@ hipError_t ln_bwd_t(const LnBwdArgs& a, int grid, hipStream_t s) {
 
 }  // namespace
 
-int ln_bwd_grid(int64_t B, int T) {
+int ln_bwd_grid(int64_t B, int T, int D) {
+  // as many workgroups as fit on every CU at once (their per-wave gamma /
+  // beta partials take kLnWaves * 2 * D floats of LDS; at most 8 per CU),
+  // but at least ~8 rows per wave
   const int64_t rows = B * T;
-  const int64_t want = (rows + kLnWaves * 8 - 1) / (kLnWaves * 8);  // about 8 rows per wave
-  return (int)std::max<int64_t>(1, std::min<int64_t>(want, 2 * (int64_t)device_cus()));
+  const int64_t lds = (int64_t)kLnWaves * 2 * std::max(D, 8) * 4;
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / lds));
+  const int64_t want = (rows + kLnWaves * 8 - 1) / (kLnWaves * 8);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, per_cu * (int64_t)device_cus()));
 }
 
 int ln_bwd_max_width() { return kLnBwdDmax; }
@@ -489,7 +499,7 @@ hipError_t launch_ln_bwd(int mode, const void* dout, const void* dres, const flo
                          hipStream_t s, const float* dres32b) {
   if (D > kLnBwdDmax || D % 8 || D % T) return hipErrorInvalidValue;
   LnBwdArgs a{dout, dres, dres32, dres32b, z, res, gamma, dy, part, B, T, D};
-  const int grid = ln_bwd_grid(B, T);
+  const int grid = ln_bwd_grid(B, T, D);
   if (dt == kBF16)
     return mode == 0 ? ln_bwd_t<bf16, 0>(a, grid, s) : ln_bwd_t<bf16, 1>(a, grid, s);
   return mode == 0 ? ln_bwd_t<float, 0>(a, grid, s) : ln_bwd_t<float, 1>(a, grid, s);
@@ -554,7 +564,10 @@ hipError_t launch_sum_parts(const float* part, float* out0, float* out1, int G, 
                             hipStream_t s, float scale) {
   if ((int64_t)G * C == 0) return hipSuccess;
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)G);
-  hipLaunchKernelGGL(k_sum_parts, grid, dim3(256), 0, s, part, out0, out1, P, C, split, scale);
+  if (P >= 64)
+    hipLaunchKernelGGL(k_sum_parts<16>, grid, dim3(64 * 16), 0, s, part, out0, out1, P, C, split, scale);
+  else
+    hipLaunchKernelGGL(k_sum_parts<4>, grid, dim3(64 * 4), 0, s, part, out0, out1, P, C, split, scale);
   return hipGetLastError();
 }
 

@@ -121,8 +121,8 @@ bool gemm_pipe_eligible(const GemmArgs& a);
 // token-major), upstream dout [B][T][D], dY written token-major in dt.  mode 1:
 // Y = TM(z) + z (z = X [B][T][D]), upstream dres (token-major, dt) + dres32
 // (token-major fp32), dY written [B][T][D] fp32.  part receives, per workgroup
-// g < ln_bwd_grid(B, T), the partial sums of dout * xhat and dout: part[g][2][D].
-int ln_bwd_grid(int64_t B, int T);
+// g < ln_bwd_grid(B, T, D), the partial sums of dout * xhat and dout: part[g][2][D].
+int ln_bwd_grid(int64_t B, int T, int D);
 int ln_bwd_max_width();
 hipError_t launch_ln_bwd(int mode, const void* dout, const void* dres, const float* dres32, const void* z,
                          const void* res, const float* gamma, void* dy, float* part, int64_t B, int T, int D, int dt,
