@@ -830,15 +830,19 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   RM_TIMED("ln2_bwd", st, RM_HIP(rm::launch_ln_bwd(0, d_out, nullptr, nullptr, sv.Z, sv.S, p->ln2_g, w.dV, w.ln2p, B, T, D, dt, st), "LayerNorm 2 backward"));
   // dV^T (rows padded to Bp) and the b2 partials
   RM_TIMED("tr_dV", st, RM_HIP(rm::launch_transpose(0, w.dV, nullptr, w.dVt, nullptr, nullptr, w.b2p, T, B, D, Bp, dt, st), "transpose dV"));
-  // W2^T [T][Hd][D]
-  RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->pffn.w2, nullptr, w.W2t, nullptr, nullptr, nullptr, T, D, Hd, D, dt, st), "transpose W2"));
-  // dH = dV W2
+  // dH = dV W2: W2_t [D][Hd] is the product's W read K-major where the
+  // kernel allows, else W2^T [T][Hd][D] first
   rm::GemmArgs g1;
   g1.dt = dt; g1.epi = rm::kEpiBias;
   g1.M = (int)B; g1.N = Hd; g1.K = D; g1.G = T;
   g1.A = w.dV; g1.a_gs = B * D; g1.a_rs = D;
-  g1.W = w.W2t; g1.b_gs = (int64_t)Hd * D;
+  g1.W = p->pffn.w2; g1.b_gs = (int64_t)Hd * D; g1.w_kmajor = 1;
   g1.C = w.dH; g1.c_gs = B * Hd; g1.c_rs = Hd;
+  if (!rm::gemm_wt_eligible(g1)) {
+    RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->pffn.w2, nullptr, w.W2t, nullptr, nullptr, nullptr, T, D, Hd, D, dt, st), "transpose W2"));
+    g1.W = w.W2t;
+    g1.w_kmajor = 0;
+  }
   RM_TIMED("bwd_dH", st, RM_HIP(rm::launch_gemm(g1, st), "dH product"));
   // dU = dH * GELU'(U), also transposed, with the b1 partials, and H^T =
   // GELU(U)^T from the same read of U
@@ -860,14 +864,19 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   g3.W = w.St; g3.b_gs = (int64_t)D * Bp;
   g3.C = g->w1; g3.c_gs = (int64_t)Hd * D; g3.c_rs = D;
   RM_TIMED("bwd_dW1", st, RM_HIP(rm::launch_gemm(g3, st), "dW1 product"));
-  // dS (W1 branch) = dU W1 (fp32, token-major)
-  RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->pffn.w1, nullptr, w.W1t, nullptr, nullptr, nullptr, T, Hd, D, Hd, dt, st), "transpose W1"));
+  // dS (W1 branch) = dU W1 (fp32, token-major): W1_t [Hd][D] read K-major
+  // where the kernel allows, else W1^T first
   rm::GemmArgs g4;
   g4.dt = dt; g4.epi = rm::kEpiBiasF32;
   g4.M = (int)B; g4.N = D; g4.K = Hd; g4.G = T;
   g4.A = w.dU; g4.a_gs = B * Hd; g4.a_rs = Hd;
-  g4.W = w.W1t; g4.b_gs = (int64_t)D * Hd;
+  g4.W = p->pffn.w1; g4.b_gs = (int64_t)D * Hd; g4.w_kmajor = 1;
   g4.C = w.dSf; g4.c_gs = B * D; g4.c_rs = D;
+  if (!rm::gemm_wt_eligible(g4)) {
+    RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->pffn.w1, nullptr, w.W1t, nullptr, nullptr, nullptr, T, Hd, D, Hd, dt, st), "transpose W1"));
+    g4.W = w.W1t;
+    g4.w_kmajor = 0;
+  }
   RM_TIMED("bwd_dS", st, RM_HIP(rm::launch_gemm(g4, st), "dS product"));
   // S = LN1(TM(X) + X) with dS = dV + dS_ffn; dX = dY1 + TM(dY1)
   RM_TIMED("ln1_bwd", st, RM_HIP(rm::launch_ln_bwd(1, nullptr, w.dV, w.dSf, x, nullptr, p->ln1_g, w.dY1, w.ln1p, B, T, D, dt, st), "LayerNorm 1 backward"));

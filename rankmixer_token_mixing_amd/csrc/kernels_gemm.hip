@@ -359,9 +359,27 @@ struct Ring {
   static_assert(A_DMA < 16, "vmcnt field");
 };
 
-template <int NWM, int NWN, int FM, int FN, int EPI, bool RAGGED, bool AIDX>
+// W panel stored K-major (WT): the 64 k-rows of a stage hold BN elements
+// each, their 16-byte chunks XOR-swizzled by wt_swz(row) (multiples of four
+// chunks), so the four 4-row x 16-column blocks a transposed fragment read
+// takes from rows k, k + 8 (two lane groups each) fall on disjoint banks.
+__device__ __forceinline__ int wt_swz(int r) { return 4 * ((r & 3) | (((r >> 3) & 1) << 2)); }
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+// 4 bf16 of one column over 4 rows (ds_read_b64_tr_b16): within each group of
+// 16 lanes, lane i receives element i % 4 of the chunks lanes i/4, 4 + i/4,
+// 8 + i/4 and 12 + i/4 point at -- with lanes 4e..4e+3 pointing at the four
+// 4-element pieces of row e, column i of the 4 x 16 block
+__device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v*)(const_cast<char*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
+
+template <int NWM, int NWN, int FM, int FN, int EPI, bool RAGGED, bool AIDX, bool WT = false>
 __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
   typedef Ring<NWM, NWN, FM, FN> RG;
+  static_assert(!WT || (RG::BN == 256 && !RAGGED), "K-major W: 256-column tiles, dense");
   constexpr int BM = RG::BM, BN = RG::BN, BK = RG::BK, NW = RG::NW;
   constexpr int A_DMA = RG::A_DMA, B_DMA = RG::B_DMA;
 
@@ -399,9 +417,19 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
   }
 #pragma unroll
   for (int i = 0; i < B_DMA; ++i) {
-    const int row = 8 * (wave + i * NW) + (lane >> 3);
-    const int n = min(t.n0 + row, p.N - 1);
-    bsrc[i] = Bb + (long long)n * K + ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+    if constexpr (WT) {
+      // 1 KB block (wave + i*NW) of the [64][BN] panel: k-row r, chunk c of
+      // the LDS row holds the row's global chunk c ^ wt_swz(r); columns past
+      // N re-read the row's last chunk
+      const int q = (wave + i * NW) * 64 + lane;
+      const int r = q / (BN / 8), c = q % (BN / 8);
+      const int n = min(t.n0 + ((c ^ wt_swz(r)) * 8), p.N - 8);
+      bsrc[i] = Bb + (long long)r * p.N + n;
+    } else {
+      const int row = 8 * (wave + i * NW) + (lane >> 3);
+      const int n = min(t.n0 + row, p.N - 1);
+      bsrc[i] = Bb + (long long)n * K + ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+    }
   }
   const int nk_real = K / BK;
   // k-slices past the end re-read the last slice; they land in slots no
@@ -414,7 +442,7 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
                                        0, 0);
   };
   auto issueB = [&](uint4* dst, int kt) {
-    const int koff = min(kt, nk_real - 1) * BK;
+    const long long koff = (long long)min(kt, nk_real - 1) * BK * (WT ? p.N : 1);
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i)
       __builtin_amdgcn_global_load_lds((global_cvoid*)(bsrc[i] + koff), (lds_void*)(dst + (wave + i * NW) * 64), 16,
@@ -437,8 +465,27 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
     auto ld = [&](int kk, int b) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) af[b][i] = As[swz(wm * FM * 32 + i * 32 + lr, kk * 2 + lh)];
+      if constexpr (WT) {
+        // lane group g4 = lane/16: k rows 8*(g4/2) .. +7 of this k-step,
+        // columns 16*(g4%2) .. +15 of block j; lane i16 addresses row i16/4
+        // of each 4-row block, columns 4*(i16%4) .. +3
+        const int g4 = lane >> 4, i16 = lane & 15;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[b][j] = Bs[swz(wn * FN * 32 + j * 32 + lr, kk * 2 + lh)];
+        for (int j = 0; j < FN; ++j) {
+          const int col = wn * FN * 32 + j * 32 + (g4 & 1) * 16 + 4 * (i16 & 3);
+          uint2 h[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int r = kk * 16 + (g4 >> 1) * 8 + hh * 4 + (i16 >> 2);
+            h[hh] = lds_read_tr16(reinterpret_cast<const char*>(Bs) + r * (BN * 2) +
+                                  (((col >> 3) ^ wt_swz(r)) << 4) + (col & 7) * 2);
+          }
+          bfr[b][j] = make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[b][j] = Bs[swz(wn * FN * 32 + j * 32 + lr, kk * 2 + lh)];
+      }
     };
     auto mm = [&](int b) {
 #pragma unroll
@@ -980,6 +1027,29 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   if (grid.x == 0) return hipSuccess;
   if (ragged && !((a.epi == kEpiBiasGelu && a.a_rowidx) || (a.epi == kEpiBiasScale && !a.a_rowidx)))
     return hipErrorInvalidValue;
+  if (a.w_kmajor) {
+    // W stored [K][N] per group: the compiler-scheduled ring with transposed
+    // fragment reads, 256 x 256 tiles only
+    if constexpr (FM == 4 && FN == 2 && NWN == 4) {
+      if (!ring || ragged) return hipErrorInvalidValue;
+      const dim3 block(NWM * NWN * kWave);
+      switch (a.epi) {
+        case kEpiBiasGelu:
+          hipLaunchKernelGGL((k_gemm_ring<NWM, NWN, FM, FN, kEpiBiasGelu, false, false, true>), grid, block, 0, s, p);
+          break;
+        case kEpiBias:
+          hipLaunchKernelGGL((k_gemm_ring<NWM, NWN, FM, FN, kEpiBias, false, false, true>), grid, block, 0, s, p);
+          break;
+        case kEpiBiasF32:
+          hipLaunchKernelGGL((k_gemm_ring<NWM, NWN, FM, FN, kEpiBiasF32, false, false, true>), grid, block, 0, s, p);
+          break;
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (!ragged && !(a.epi == kEpiBiasGelu || a.epi == kEpiBias || a.epi == kEpiBiasF32 || a.epi == kEpiSwiglu ||
                    (a.epi == kEpiBiasGeluDual && a.C2)))
     return hipErrorInvalidValue;
@@ -1053,6 +1123,13 @@ int device_cus() {
 
 int gemm_tile_m(const GemmArgs& a) { return kCfgs[choose_cfg(a)].bm(); }
 
+bool gemm_wt_eligible(const GemmArgs& a) {
+  if (a.dt != kBF16 || a.K % 64 || a.row_off || a.N % 8 || a.N < 256) return false;
+  GemmArgs b = a;
+  b.w_kmajor = 0;
+  return choose_cfg(b) == 0;
+}
+
 bool gemm_pipe_eligible(const GemmArgs& a) {
   const TileCfg& t = kCfgs[choose_cfg(a)];
   if (!(t.fm == 4 && t.fn == 2) || a.dt != kBF16 || a.K % 64 || a.pipe == 0) return false;
@@ -1061,6 +1138,7 @@ bool gemm_pipe_eligible(const GemmArgs& a) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+  if (a.w_kmajor) return gemm_wt_eligible(a) ? launch_cfg<2, 4, 4, 2>(a, s) : hipErrorInvalidValue;
   switch (choose_cfg(a)) {
     case 0: return launch_cfg<2, 4, 4, 2>(a, s);
     case 1: return launch_cfg<2, 2, 4, 2>(a, s);

@@ -105,6 +105,10 @@ struct GemmArgs {
   const int* tiles = nullptr;
   const int* ntiles = nullptr;
   int max_mtiles = 0;
+  // W group stored K-major, [K][N] (element (k, n) at (g / b_gdiv) * b_gs +
+  // k * N + n): the compiler-scheduled ring with transposed LDS fragment
+  // reads, where gemm_wt_eligible (bf16, K % 64 == 0, dense, 256 x 256 tiles)
+  int w_kmajor = 0;
   int tile_cfg = -1;  // -1: choose automatically
   int pipe = -1;      // 0: never use the hand-scheduled ring (for comparisons)
 };
@@ -114,6 +118,8 @@ int gemm_tile_m(const GemmArgs& a);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // whether launch_gemm would run `a` on the hand-scheduled pipelined kernel
 bool gemm_pipe_eligible(const GemmArgs& a);
+// whether launch_gemm takes `a` with a K-major W (w_kmajor)
+bool gemm_wt_eligible(const GemmArgs& a);
 
 // ---- dense block backward (kernels_bwd.hip) -----------------------------------
 

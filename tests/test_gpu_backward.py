@@ -73,6 +73,8 @@ def _run(dtype, B, T, D, Hd, seed):
     ("bf16", 1, 2, 16, 32),       # one sample
     ("bf16", 1024, 8, 256, 1024), # pipelined products (K = batch = 1024)
     ("f32", 17, 8, 40, 24),       # heads of width 5: odd gathers
+    ("bf16", 1024, 16, 256, 2048),  # dH reads W2 K-major (transposed fragment reads, 256 x 256 tiles)
+    ("bf16", 1000, 32, 1024, 1024),  # ragged batch, dH and dS both read W K-major
 ])
 def test_block_backward_matches_oracle(dtype, B, T, D, Hd):
     blk, x, d_out, y, dx, g = _run(dtype, B, T, D, Hd, seed=B + T)
