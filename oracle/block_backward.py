@@ -16,9 +16,9 @@ The pages train this block (their cost figures are training flops) but print
 no backward; every function below is the chain rule applied to one forward
 equation, written out in float64 numpy per token, nothing fused or reordered.
 Given dX' = dL/dX' for some loss L it returns dL/dX and the gradients of every
-parameter.  Readings (listed in the design doc): the token mix is a permutation
-that is its own inverse when H = T, so its transpose is itself; the MoE block
-has no backward here.
+parameter.  Readings: the token mix is a permutation that is its own
+inverse when H = T, so its transpose is itself; the MoE block's backward
+(with its two routers) is in ``moe_training``.
 
 Parity pins (tests/test_oracle_backward_pins.py): central finite differences
 of the forward oracle on small blocks for every output, LayerNorm gradient

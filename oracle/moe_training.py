@@ -15,10 +15,10 @@ h_infer, both affine maps R^D -> R^{N_e}:
     L = L_task + lambda * L_reg
 
 and only h_infer is subject to L_reg.  At inference only h_infer routes (the
-forward of ``rankmixer_oracle.block_fwd`` with wr/br = h_infer).  Readings
-(listed in the design doc): L_reg's gradient reaches h_infer's weights and bias
-only, not S ("only applied to h_infer"); L_task reaches everything but
-h_infer, which does not take part in the training forward.
+forward of ``rankmixer_oracle.block_fwd`` with wr/br = h_infer).  Readings:
+L_reg's gradient reaches h_infer's weights and bias only, not S (the pages
+restrict the regulariser to h_infer); L_task reaches everything but h_infer,
+which does not take part in the training forward.
 
 Every function is the chain rule through one forward equation, in float64.
 Parity pins (tests/test_oracle_moe_training_pins.py): central finite

@@ -19,7 +19,7 @@ Pages cited (titles as printed on them):
   [TB]  "淘宝闪购-爆品团精排 Scaling Up 迭代实践" (BestBlogs.dev report)
   [SX]  "重新理解 RankMixer：扩参为什么有效，又为什么划算？" (sxkj888.cn blog)
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * LayerNorm: epsilon 1e-5, biased variance over the D entries of one token,
     one gamma/beta pair of length D per LayerNorm.
   * GELU is the exact erf form x * Phi(x).
