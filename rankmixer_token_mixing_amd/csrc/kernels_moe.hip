@@ -275,19 +275,46 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_moe_combine(const T* 
   for (int i = 0; i < MAXI; ++i)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) v[i][e] = 0.f;
-  for (int j = 0; j < E; ++j) {
-    const int p = pos[row * E + j];
-    if (p < 0) continue;
-    const T* yr = y + (int64_t)p * D;
+  // the row's active experts as a wave-uniform bit mask (lane j < E holds
+  // pos[row][j]); two rows of y are loaded per step, both issued before
+  // either is added, and added in expert order
+  const int pj = lane < E ? pos[row * E + lane] : -1;
+  // the residual row, loaded ahead of the expert rows
+  float r[MAXI][VEC];
+  if (ln) {
+    const T* sr = s + (row / T_) * sb + (row % T_) * st;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) load_f32<T, VEC>(sr + min(lane + i * kWave, nch - 1) * VEC, r[i]);
+  }
+  unsigned long long act = __ballot(pj >= 0);
+  while (act) {
+    const int j0 = __builtin_ctzll(act);
+    act &= act - 1;
+    const int p0 = __shfl(pj, j0, kWave);
+    int p1 = -1;
+    if (act) {
+      const int j1 = __builtin_ctzll(act);
+      act &= act - 1;
+      p1 = __shfl(pj, j1, kWave);
+    }
+    const T* y0 = y + (int64_t)p0 * D;
+    const T* y1 = y + (int64_t)(p1 >= 0 ? p1 : p0) * D;
+    float q0[MAXI][VEC], q1[MAXI][VEC];
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-      const int c = lane + i * kWave;
-      if (c < nch) {
-        float q[VEC];
-        load_f32<T, VEC>(yr + c * VEC, q);
+      const int c = min(lane + i * kWave, nch - 1);
+      load_f32<T, VEC>(y0 + c * VEC, q0[i]);
+      load_f32<T, VEC>(y1 + c * VEC, q1[i]);
+    }
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) v[i][e] += q[e];
-      }
+    for (int i = 0; i < MAXI; ++i)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[i][e] += q0[i][e];
+    if (p1 >= 0) {
+#pragma unroll
+      for (int i = 0; i < MAXI; ++i)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[i][e] += q1[i][e];
     }
   }
   T* orow = out + row * (int64_t)D;
@@ -299,17 +326,14 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_moe_combine(const T* 
     }
     return;
   }
-  const T* sr = s + (row / T_) * sb + (row % T_) * st;
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     const int c = lane + i * kWave;
     if (c < nch) {
-      float q[VEC];
-      load_f32<T, VEC>(sr + c * VEC, q);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        v[i][e] += q[e];
+        v[i][e] += r[i][e];
         sum += v[i][e];
       }
     }
