@@ -77,46 +77,38 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 // GELU, exact form x * Phi(x) with Phi the standard normal CDF, written as
 //   GELU(x) = max(x, 0) - |x| Phi(-|x|)
 // (for x >= 0, x Phi(x) = x - x Phi(-x); for x < 0 it is x Phi(-|x|)).  The
-// tail is Phi(-a) = exp2(P(min(a, 5.5)) - log2(e) a^2 / 2), P a degree-6
-// polynomial fitted to log2 Phi(-a) + log2(e) a^2 / 2 on [0, 5.5] by
-// weighted least squares (gelu_fit.py prints the coefficients and the error).
-// In fp32 the result is within 2.5e-7 of the exact GELU everywhere and within
-// 1.1e-5 relative wherever |GELU| > 1e-3 -- tighter than Abramowitz & Stegun
-// 7.1.26 evaluated the same way (3.3e-7, 1.7e-4), at eleven ALU ops and one
-// transcendental (exp2) instead of twelve and two (exp2, rcp).
+// tail is Phi(-a) = exp2(P(min(a, 6.5))), P a degree-6 polynomial fitted to
+// log2 Phi(-a) on [0, 6.5] by weighted least squares (gelu_fit.py prints the
+// coefficients and the error); the Gaussian's -log2(e) a^2 / 2 is P's square
+// term.  In fp32 the result is within 2.5e-7 of the exact GELU for |x| <= 9
+// (|x| * 4e-11 beyond, the clamped tail) and within 1.3e-5 relative wherever
+// |GELU| > 1e-3, at nine ALU ops and one transcendental (exp2).
+
+__device__ __forceinline__ float phi_tail_log2(float ac) {
+  float p = fmaf(3.4358014090685174e-05f, ac, -0.000775179301854223f);
+  p = fmaf(p, ac, 0.008079172112047672f);
+  p = fmaf(p, ac, -0.05336913466453552f);
+  p = fmaf(p, ac, -0.4588397741317749f);
+  p = fmaf(p, ac, -1.1511653661727905f);
+  return fmaf(p, ac, -0.9999982714653015f);
+}
 
 __device__ __forceinline__ float gelu_erf(float x) {
   const float a = fabsf(x);
-  const float ac = fminf(a, 5.5f);
-  float p = fmaf(3.4890897950390354e-05f, ac, -0.0007811335963197052f);
-  p = fmaf(p, ac, 0.008104033768177032f);
-  p = fmaf(p, ac, -0.053417619317770004f);
-  p = fmaf(p, ac, 0.2625527083873749f);
-  p = fmaf(p, ac, -1.1511831283569336f);
-  p = fmaf(p, ac, -0.9999961853027344f);
-  const float tail = __builtin_amdgcn_exp2f(fmaf(x * -0.7213475204444817f, x, p));  // Phi(-a)
+  const float tail = __builtin_amdgcn_exp2f(phi_tail_log2(fminf(a, 6.5f)));  // Phi(-a)
   return fmaf(-a, tail, fmaxf(x, 0.0f));
 }
 
 // GELU(x) as gelu_erf and its derivative Phi(x) + x phi(x) from the same tail:
 // Phi(x) = 1 - Phi(-a) for x >= 0, Phi(-a) otherwise, and
 // phi(x) = exp2(-log2(e) x^2 / 2) / sqrt(2 pi).  In fp32 the derivative is
-// within 1.4e-6 of the exact one (the fitted tail is 1.3e-6 off Phi(0) = 1/2,
-// which GELU itself, weighted by |x|, does not see).
+// within 7e-7 of the exact one.
 __device__ __forceinline__ void gelu_and_grad(float x, float& g, float& dg) {
   const float a = fabsf(x);
-  const float ac = fminf(a, 5.5f);
-  float p = fmaf(3.4890897950390354e-05f, ac, -0.0007811335963197052f);
-  p = fmaf(p, ac, 0.008104033768177032f);
-  p = fmaf(p, ac, -0.053417619317770004f);
-  p = fmaf(p, ac, 0.2625527083873749f);
-  p = fmaf(p, ac, -1.1511831283569336f);
-  p = fmaf(p, ac, -0.9999961853027344f);
-  const float e0 = x * -0.7213475204444817f * x;
-  const float tail = __builtin_amdgcn_exp2f(p + e0);  // Phi(-a)
+  const float tail = __builtin_amdgcn_exp2f(phi_tail_log2(fminf(a, 6.5f)));  // Phi(-a)
   g = fmaf(-a, tail, fmaxf(x, 0.0f));
   const float cdf = x >= 0.0f ? 1.0f - tail : tail;
-  dg = fmaf(x, 0.3989422804014327f * __builtin_amdgcn_exp2f(e0), cdf);
+  dg = fmaf(x, 0.3989422804014327f * __builtin_amdgcn_exp2f(x * -0.7213475204444817f * x), cdf);
 }
 
 // ---------------------------------------------------------------------------
