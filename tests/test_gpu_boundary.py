@@ -98,6 +98,9 @@ def test_mixed_kinds():
     ("bf16", 65, 32, 64, 32),   # heads of width 2
     ("bf16", 9, 1, 64, 96),     # T = 1
     ("bf16", 513, 16, 320, 64),  # the pad-split model's width
+    ("bf16", 600, 32, 1536, 32),  # the ~1B-class shape: three chunks per lane, the LDS nearly full
+    ("bf16", 70, 64, 128, 32),    # T > 32: each wave normalises several pairs of rows
+    ("bf16", 40, 16, 2048, 32),   # four chunks per lane
 ])
 def test_dense_stacks(dtype, B, T, D, H):
     blocks = [_block("dense", T, D, H, dtype, 20 + i) for i in range(3)]
