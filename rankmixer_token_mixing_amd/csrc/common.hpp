@@ -93,10 +93,15 @@ __device__ __forceinline__ float phi_tail_log2(float ac) {
   return fmaf(p, ac, -0.9999982714653015f);
 }
 
+// The clamps take their operand as it is -- v_med3_f32 for min(a, 6.5) and an
+// integer max for max(x, 0) (a float's bits ordered as a signed integer put
+// every negative value below +0) -- where fminf / fmaxf would first
+// canonicalize a value that comes straight out of an MFMA (one more
+// instruction per value in a product's epilogue).
 __device__ __forceinline__ float gelu_erf(float x) {
   const float a = fabsf(x);
-  const float tail = __builtin_amdgcn_exp2f(phi_tail_log2(fminf(a, 6.5f)));  // Phi(-a)
-  return fmaf(-a, tail, fmaxf(x, 0.0f));
+  const float tail = __builtin_amdgcn_exp2f(phi_tail_log2(__builtin_amdgcn_fmed3f(a, 0.0f, 6.5f)));  // Phi(-a)
+  return fmaf(-a, tail, __int_as_float(max(__float_as_int(x), 0)));
 }
 
 // GELU(x) as gelu_erf and its derivative Phi(x) + x phi(x) from the same tail:

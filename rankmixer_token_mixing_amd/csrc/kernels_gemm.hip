@@ -621,21 +621,16 @@ __device__ __forceinline__ void dma1(uint32_t m0v, const void* sb, uint32_t voff
                : "m0");
 }
 
-// bf16 epilogue of the persistent pipelined ring, in two halves through
-// slots 3 and 4 (the next tile's first slices are already landing in slots
-// 0-2): half h holds accumulator rows i = 2h, 2h+1 of every wave, i.e. tile
-// rows wm*128 + 64h .. +63, at staging row wm*64 + (i-2h)*32 + lr.
-template <int NWM, int NWN, int FN, int EPI>
-__device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileId& t, const floatx16 (&acc)[4][FN],
-                                                   int wave, int lane, char* stage) {
-  constexpr int BN = NWN * FN * 32, NT = NWM * NWN * kWave;
-  constexpr int OCH = BN / 8;       // 16-byte chunks per output row
-  constexpr int RPP = NT / OCH;     // staging rows per store pass
-  constexpr int SROWS = NWM * 64;   // staging rows per half
-  const int wm = wave / NWN, wn = wave % NWN;
-  const int lr = lane & 31, lh = lane >> 5;
-  const int tid = threadIdx.x;
-  float4 bias[FN][4];
+// Start value of the pipelined kernel's accumulators: the bias of each
+// accumulator's column (zero without bias), so the epilogue adds nothing.
+// Register 4q+e of block (i, j) holds column wn*FN*32 + j*32 + 8q + 4lh + e
+// for every i; each block gets its own load (volatile: no shared load plus
+// register copies), 4 * FN 16-byte loads per row block and lane.
+template <int NWN, int FN, int EPI>
+__device__ __forceinline__ void pipe_acc_bias(const KParams& p, const TileId& t, floatx16 (&acc)[4][FN], int wave,
+                                              int lane) {
+  constexpr int BN = NWN * FN * 32;
+  const int wn = wave % NWN, lh = lane >> 5;
 #pragma unroll
   for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -648,9 +643,35 @@ __device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileI
         n = nl < BN / 2 ? h : hs + h;
         ok = h < hs;
       }
-      bias[j][q] = (p.bias && ok) ? *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + n)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      // columns past N and products without bias read the zero block
+      const volatile float4* src = reinterpret_cast<const volatile float4*>(
+          p.bias && ok ? (const void*)(p.bias + (long long)t.g * p.bias_gs + n) : (const void*)&g_zero_chunk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4 b;
+        b.x = src->x; b.y = src->y; b.z = src->z; b.w = src->w;
+        acc[i][j][4 * q + 0] = b.x;
+        acc[i][j][4 * q + 1] = b.y;
+        acc[i][j][4 * q + 2] = b.z;
+        acc[i][j][4 * q + 3] = b.w;
+      }
     }
+}
+
+// bf16 epilogue of the persistent pipelined ring, in two halves through
+// slots 3 and 4 (the next tile's first slices are already landing in slots
+// 0-2): half h holds accumulator rows i = 2h, 2h+1 of every wave, i.e. tile
+// rows wm*128 + 64h .. +63, at staging row wm*64 + (i-2h)*32 + lr.
+template <int NWM, int NWN, int FN, int EPI, typename Init>
+__device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileId& t, const floatx16 (&acc)[4][FN],
+                                                   int wave, int lane, char* stage, Init& init_next) {
+  constexpr int BN = NWN * FN * 32, NT = NWM * NWN * kWave;
+  constexpr int OCH = BN / 8;       // 16-byte chunks per output row
+  constexpr int RPP = NT / OCH;     // staging rows per store pass
+  constexpr int SROWS = NWM * 64;   // staging rows per half
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int tid = threadIdx.x;
   // kEpiBiasScale: the gate of each accumulator row block's row (rows past
   // the group's end read its last row and are never stored)
   float scale[4] = {1.f, 1.f, 1.f, 1.f};
@@ -669,13 +690,13 @@ __device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileI
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int nl = wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
-          float v[4] = {acc[i][j][4 * q + 0] + bias[j][q].x, acc[i][j][4 * q + 1] + bias[j][q].y,
-                        acc[i][j][4 * q + 2] + bias[j][q].z, acc[i][j][4 * q + 3] + bias[j][q].w};
+          float v[4] = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
           epi4<EPI, bf16>(p, t, 0, 0, scale[i], v);
           const int phys = (nl >> 3) ^ (sr & (OCH - 1));
           store_from_f32<bf16, 4>(reinterpret_cast<bf16*>(stage + sr * (BN * 2) + phys * 16 + (nl & 7) * 2), v);
         }
     }
+    if (h == 1) init_next();  // the accumulators are read for the last time above
     __syncthreads();
     if constexpr (EPI == kEpiSwiglu) {
       // output chunk c of a row: SiLU(gate chunk c) * (up chunk c + OCH/2), the
@@ -724,9 +745,9 @@ __device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileI
 // slots 3 and 4: quarter i holds accumulator row block i of every wave, tile
 // rows wm*128 + 32i + lr at staging row wm*32 + lr, BN*4 bytes per row in
 // 16-byte chunks XOR-swizzled by (row mod 16); each store writes a whole row.
-template <int NWM, int NWN, int FN, int EPI>
+template <int NWM, int NWN, int FN, int EPI, typename Init>
 __device__ __forceinline__ void pipe_epilogue_f32(const KParams& p, const TileId& t, const floatx16 (&acc)[4][FN],
-                                                  int wave, int lane, char* stage) {
+                                                  int wave, int lane, char* stage, Init& init_next) {
   constexpr int FM = 4, BN = NWN * FN * 32, NT = NWM * NWN * kWave;
   constexpr int OCH = BN / 4;      // 16-byte chunks per output row
   constexpr int RPP = NT / OCH;    // staging rows per store pass
@@ -735,22 +756,6 @@ __device__ __forceinline__ void pipe_epilogue_f32(const KParams& p, const TileId
   const int wm = wave / NWN, wn = wave % NWN;
   const int lr = lane & 31, lh = lane >> 5;
   const int tid = threadIdx.x;
-  float4 bias[FN][4];
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int nl = wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
-      int n = t.n0 + nl;
-      bool ok = n < p.N;
-      if constexpr (EPI == kEpiSwiglu) {  // the tile's column -> gate / up row, as the W operand
-        const int hs = p.N / 2, h = t.n0 / 2 + (nl & (BN / 2 - 1));
-        n = nl < BN / 2 ? h : hs + h;
-        ok = h < hs;
-      }
-      bias[j][q] = (p.bias && ok) ? *reinterpret_cast<const float4*>(p.bias + (long long)t.g * p.bias_gs + n)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int sr = wm * 32 + lr;
@@ -759,10 +764,11 @@ __device__ __forceinline__ void pipe_epilogue_f32(const KParams& p, const TileId
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cix = (wn * FN * 32 + j * 32 + 8 * q + 4 * lh) >> 2;
-        const float4 v = make_float4(acc[i][j][4 * q + 0] + bias[j][q].x, acc[i][j][4 * q + 1] + bias[j][q].y,
-                                     acc[i][j][4 * q + 2] + bias[j][q].z, acc[i][j][4 * q + 3] + bias[j][q].w);
+        const float4 v = make_float4(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]);
         *reinterpret_cast<float4*>(stage + sr * (BN * 4) + ((cix ^ (sr & 15)) * 16)) = v;
       }
+    if (i == FM - 1) init_next();  // the accumulators are read for the last time above
     __syncthreads();
 #pragma unroll
     for (int pass = 0; pass < SROWS / RPP; ++pass) {
@@ -899,13 +905,8 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
   issue_a(2, 1);
 
   floatx16 acc[FM][FN];
+  pipe_acc_bias<NWN, FN, EPI>(p, t, acc, wave, lane);
   for (;;) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     // W_1 -> 3; then all but W_1 has landed (A_0, W_0, A_1 and any stores)
     issue_w(3, 1);
     wait_vmcnt<B_DMA>();
@@ -945,11 +946,15 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
       issue_w(1, 0);
       issue_a(2, 1);
     }
+    // the next tile's accumulators start from its bias once this tile's are read
+    auto init_next = [&]() {
+      if (more) pipe_acc_bias<NWN, FN, EPI>(p, t, acc, wave, lane);
+    };
     if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias || EPI == kEpiSwiglu || EPI == kEpiBiasScale ||
                   EPI == kEpiBiasGeluDual)
-      pipe_epilogue_bf16<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
+      pipe_epilogue_bf16<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB, init_next);
     else
-      pipe_epilogue_f32<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB);
+      pipe_epilogue_f32<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB, init_next);
     if (!more) break;
   }
 }
