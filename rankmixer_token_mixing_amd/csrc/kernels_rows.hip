@@ -32,6 +32,11 @@ int pick_maxi(int chunks) {
   return 0;
 }
 
+// as pick_maxi, but exactly 3 slots where a row needs 3 (rows of 129-192
+// chunks, e.g. D = 1536 in 16-byte chunks): the block-boundary pass holds two
+// rows per lane and then needs 108 registers instead of 128
+int pick_maxi3(int chunks) { return (chunks + kWave - 1) / kWave == 3 ? 3 : pick_maxi(chunks); }
+
 // ---------------------------------------------------------------------------
 // pad-split tokenizer: x0[b][i] = i < F ? cast(emb[b][i]) : 0, i < T*D.
 // Each thread writes 4 consecutive outputs of one sample.
@@ -512,8 +517,9 @@ hipError_t ln_mix_ln_vec(const void* z, void* s, const float* g2, const float* b
   const dim3 grid((unsigned)B), block(nw * kWave);
   const T* zz = (const T*)z;
   T* ss = (T*)s;
-  switch (pick_maxi(D / VEC)) {
+  switch (pick_maxi3(D / VEC)) {
     case 0: return hipErrorInvalidValue;
+    case 3: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 3>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
     case 1: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 1>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
     case 2: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 2>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
     case 4: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 4>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
