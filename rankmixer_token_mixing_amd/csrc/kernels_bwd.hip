@@ -61,16 +61,55 @@ __global__ __launch_bounds__(kLnWaves* kWave) void k_ln_bwd(LnBwdArgs a) {
   float* pg = wpart + wave * 2 * D;
   float* pb = pg + D;
 
-  for (int64_t row = (int64_t)blockIdx.x * kLnWaves + wave; row < rows; row += (int64_t)gridDim.x * kLnWaves) {
+  // LN2 rows of at most three chunks per lane: the next row's chunks are
+  // loaded while this one is reduced (3 * MAXI raw registers; the gamma /
+  // beta partials already hold occupancy at three workgroups per CU)
+  constexpr bool PF = MODE == 0 && MAXI <= 3;
+  typedef typename RawVec<(int)sizeof(T) * VEC>::type raw_t;
+  raw_t nz[PF ? MAXI : 1], nr[PF ? MAXI : 1], nd[PF ? MAXI : 1];
+  const int64_t stride = (int64_t)gridDim.x * kLnWaves;
+  auto fetch = [&](int64_t rw) {
+    if constexpr (PF) {
+      const int64_t bb = rw / T_;
+      const int64_t tmm = (rw - bb * T_) * a.B + bb;
+#pragma unroll
+      for (int i = 0; i < MAXI; ++i) {
+        const int k = min(lane + i * kWave, nch - 1) * VEC;  // past the row: its last chunk, unused
+        nz[i] = *reinterpret_cast<const raw_t*>((const T*)a.z + rw * D + k);
+        nr[i] = *reinterpret_cast<const raw_t*>((const T*)a.res + tmm * D + k);
+        nd[i] = *reinterpret_cast<const raw_t*>((const T*)a.dout + rw * D + k);
+      }
+    }
+  };
+  if (PF && (int64_t)blockIdx.x * kLnWaves + wave < rows) fetch((int64_t)blockIdx.x * kLnWaves + wave);
+
+  for (int64_t row = (int64_t)blockIdx.x * kLnWaves + wave; row < rows; row += stride) {
     const int64_t b = row / T_;
     const int t = (int)(row - b * T_);
     const int64_t tm = (int64_t)t * a.B + b;  // token-major row index
     float y[MAXI][VEC], up[MAXI][VEC];
     float sum = 0.f;
+    if constexpr (PF) {
+#pragma unroll
+      for (int i = 0; i < MAXI; ++i) {
+        Vec<T, VEC> vz, vr, vd;
+        vz.raw = nz[i];
+        vr.raw = nr[i];
+        vd.raw = nd[i];
+        const bool in = lane + i * kWave < nch;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          y[i][e] = to_f32(vz.e[e]) + to_f32(vr.e[e]);
+          up[i][e] = to_f32(vd.e[e]);
+          sum += in ? y[i][e] : 0.f;
+        }
+      }
+      if (row + stride < rows) fetch(row + stride);
+    }
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
       const int c = lane + i * kWave;
-      if (c < nch) {
+      if (!PF && c < nch) {
         const int k = c * VEC;
         float p[VEC], q[VEC];
         if constexpr (MODE == 0) {
@@ -456,8 +495,10 @@ template <typename T, int VEC, int MODE>
 hipError_t ln_bwd_vec(const LnBwdArgs& a, int grid, hipStream_t s) {
   const dim3 block(kLnWaves * kWave);
   const size_t lds = (size_t)kLnWaves * 2 * a.D * sizeof(float);
-  switch (ln_slots(a.D / VEC)) {
+  const int need = (a.D / VEC + kWave - 1) / kWave;
+  switch (MODE == 0 && need == 3 ? 3 : ln_slots(a.D / VEC)) {
     case 1: hipLaunchKernelGGL((k_ln_bwd<T, VEC, 1, MODE>), dim3(grid), block, lds, s, a); break;
+    case 3: hipLaunchKernelGGL((k_ln_bwd<T, VEC, 3, MODE>), dim3(grid), block, lds, s, a); break;
     case 2: hipLaunchKernelGGL((k_ln_bwd<T, VEC, 2, MODE>), dim3(grid), block, lds, s, a); break;
     case 4: hipLaunchKernelGGL((k_ln_bwd<T, VEC, 4, MODE>), dim3(grid), block, lds, s, a); break;
     case 8: hipLaunchKernelGGL((k_ln_bwd<T, VEC, 8, MODE>), dim3(grid), block, lds, s, a); break;
