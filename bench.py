@@ -112,6 +112,83 @@ def block0_protocol(bd, blocks, x0, B: int, flop_block, peak: float) -> dict:
     return rec
 
 
+def measure_ceilings(bd, copy_mib: int = 100, pairs: int = 6) -> dict:
+    """The chip's own ceilings, from the library's probes (tracked source):
+    the bf16 MFMA loop on random operands (TFLOP/s over 10 launches of ~2 ms
+    after 3 warm-up launches), and a copy of copy_mib MiB timed cold (each copy
+    reads and writes buffers that the copies of the other `pairs` - 1 buffer
+    pairs have pushed out of the 256 MB last-level cache) and warm (the same
+    pair again and again); GB/s count bytes read + bytes written."""
+    import statistics
+    import torch
+    lib = bd.load()
+    frags = torch.randn(lib.rm_probe_mfma_frag_bytes() // 2, device="cuda").to(torch.bfloat16)
+    out = torch.empty(lib.rm_probe_mfma_out_floats(), dtype=torch.float32, device="cuda")
+    iters = 600
+    for _ in range(3):
+        bd.probe_mfma_bf16(frags, out, iters)
+    ms = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bd.probe_mfma_bf16(frags, out, iters)
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    mfma = lib.rm_probe_mfma_flop(iters) / (statistics.median(ms) * 1e-3) / 1e12
+    n = copy_mib << 20
+    bufs = [(torch.empty(n, dtype=torch.uint8, device="cuda"), torch.empty(n, dtype=torch.uint8, device="cuda"))
+            for _ in range(pairs)]
+    for a, b in bufs:
+        a.fill_(1)
+        b.fill_(2)
+
+    def timed_copy(a, b):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bd.probe_copy(a, b, n)
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1)
+
+    cold = [timed_copy(*bufs[i % pairs]) for i in range(2 * pairs)][pairs:]
+    warm = [timed_copy(*bufs[0]) for _ in range(10)][2:]
+    del bufs
+    return {"mfma_bf16_random_tflops": round(mfma, 1),
+            "copy_cold_gbs": round(2 * n / (statistics.median(cold) * 1e-3) / 1e9, 1),
+            "copy_warm_gbs": round(2 * n / (statistics.median(warm) * 1e-3) / 1e9, 1),
+            "copy_bytes": 2 * n,
+            "how": "librankmixer probes: rm_probe_mfma_bf16 (8 waves per CU of v_mfma_f32_32x32x16_bf16 on "
+                   "random bf16 fragments, median of 10 launches) and rm_probe_copy (median per copy, cold: "
+                   f"round-robin over {pairs} buffer pairs)"}
+
+
+def with_ceiling(roofline, ceil: dict):
+    """The roofline object with the measured ceiling of its bound beside the
+    data-sheet peak."""
+    if roofline is None or not ceil:
+        return roofline
+    c = ceil["mfma_bf16_random_tflops"] if roofline["bound"] == "mfma" else ceil["copy_cold_gbs"]
+    roofline["measured_ceiling"] = c
+    roofline["frac_of_measured_ceiling"] = round(roofline["achieved"] / c, 4)
+    return roofline
+
+
+def bench_ceilings(args) -> int:
+    import torch
+    from rankmixer_token_mixing_amd import binding as bd
+    from rankmixer_token_mixing_amd import perfmodel as pm
+    c = measure_ceilings(bd)
+    rec = {"metric": "MI355X ceilings measured by the library's probes", "value": c["mfma_bf16_random_tflops"],
+           "unit": "TFLOP/s", "n_gpus": 1, "higher_is_better": True, "data": "synthetic (random bf16)",
+           "dtype": "bf16", "config": {"workload": "MFMA loop and HBM copy probes"},
+           "mfma_frac_of_spec": round(c["mfma_bf16_random_tflops"] / pm.PEAK_BF16_TFLOPS, 4),
+           "copy_cold_frac_of_spec": round(c["copy_cold_gbs"] / pm.PEAK_HBM_GBS, 4),
+           "copy_warm_frac_of_spec": round(c["copy_warm_gbs"] / pm.PEAK_HBM_GBS, 4), **c}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def moe_active_rows(bd, blocks, x0, D: int) -> list:
     """Active (sample, token, expert) rows of each MoE block on this batch, for
     the flop count: block l's input comes from the library's own blocks, its S
@@ -540,13 +617,16 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", help="workload (c3 is the benchmarked one)")
-    ap.add_argument("--op", default="model", choices=["model", "tokenize_project", "block_bwd", "block_variants", "moe_train"],
+    ap.add_argument("--op", default="model",
+                    choices=["model", "tokenize_project", "block_bwd", "block_variants", "moe_train", "ceilings"],
                     help="model: the block stack (default); tokenize_project: the projection "
                          "tokenizer alone on the pad-split model's embedding; block_bwd: the dense "
                          "block backward on block 0 of the workload; block_variants: the SwiGLU "
                          "(D -> 4/3 D) block beside the GELU FFN (D -> 2D) block of equal parameters and "
                          "flops, with and without the Add & Norm after the mix; moe_train: training "
-                         "step of the MoE block with dense-training / sparse-inference routers")
+                         "step of the MoE block with dense-training / sparse-inference routers; "
+                         "ceilings: the MFMA-loop and HBM-copy probes alone")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the probes after the timed steps")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="samples in the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-launch HIP events")
@@ -570,6 +650,7 @@ def main() -> int:
     if not os.path.exists(bd.lib_path()):
         from rankmixer_token_mixing_amd.build import build
         build()
+    bd.check_fresh()  # never time a library built from other sources than the tree's
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 1
@@ -592,6 +673,8 @@ def main() -> int:
         return bench_variants(args)
     if args.op == "moe_train":
         return bench_moe_train(args)
+    if args.op == "ceilings":
+        return bench_ceilings(args)
 
     cfg = si.CONFIGS[args.config]
     t0 = time.perf_counter()
@@ -700,6 +783,10 @@ def main() -> int:
         step_tflops = block_flops * L / (ms_step * 1e-3) / 1e12
     block0 = block0_protocol(bd, blocks, x0, cfg.B, block_flops, pm.PEAK_BF16_TFLOPS)
     log(f"block 0 alone: {block0['ms']} ms")
+    ceil = None if args.no_ceilings else measure_ceilings(bd)
+    roofline = with_ceiling(roofline, ceil)
+    if ceil:
+        block0["frac_of_measured_mfma_ceiling"] = round(block0.get("tflops", 0) / ceil["mfma_bf16_random_tflops"], 4)
 
     rec = {
         "metric": METRIC,
@@ -728,6 +815,7 @@ def main() -> int:
                         "warm-up; the timed steps carry events around the dominant kernel only (its average is "
                         "the roofline's)",
         "block0_fwd": block0,
+        "ceilings": ceil,
     }
     if active is not None:
         rec["moe_active_rows"] = {"per_block": active, "of": cfg.B * cfg.T * cfg.E,

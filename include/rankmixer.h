@@ -113,6 +113,15 @@ typedef struct rm_block_params {
   rm_pffn_params pffn;        /* used when kind == RM_BLOCK_DENSE or RM_BLOCK_SWIGLU */
   rm_moe_params moe;          /* used when kind == RM_BLOCK_MOE */
   int flags;                  /* 0 or RM_BLOCK_NO_MIX_NORM */
+  /* The block's own widths, which size every weight above: hidden = Hd
+   * (DENSE), Hs (SWIGLU) or He (MOE); E = experts per token (MOE), else 0.
+   * rm_model_fwd sizes and runs each block from these two fields, so the
+   * blocks of one stack may differ in kind, hidden width and expert count.
+   * The single-block calls take hidden and E as arguments; there, 0 in a
+   * field means "as the argument", and a non-zero field that differs from
+   * the argument is RM_ERR_INVALID. */
+  int hidden;
+  int E;
 } rm_block_params;
 
 /* Gradients of one dense block: float32 device buffers, overwritten (not
@@ -132,9 +141,7 @@ typedef struct rm_block_grads {
  * with an optional pad-split tokenizer in front and optional mean pooling
  * plus a D -> 1 logit behind ([WL]: the last block's tokens are averaged). */
 typedef struct rm_model_desc {
-  int T, D;
-  int hidden;                 /* Hd = kD for dense blocks, He for MoE blocks */
-  int E;                      /* experts per token (MoE blocks), else 0 */
+  int T, D;                   /* tokens and token width, shared by every block */
   int dtype;                  /* rm_dtype of activations and weight matrices */
   int L;                      /* number of blocks */
   const rm_block_params* blocks; /* host array of L block descriptors */
@@ -220,7 +227,9 @@ rm_status rm_block_fwd(const void* x, const rm_block_params* p, void* x_out, int
                        void* stream);
 size_t rm_block_workspace_bytes(int kind, int64_t B, int T, int D, int hidden, int E, int dtype);
 
-/* The whole stack.
+/* The whole stack.  Block l is sized from its own descriptor
+ * (m->blocks[l].hidden and .E, which must be set: hidden > 0, E in 1..32 for
+ * MoE blocks and 0 otherwise), so its weights must have exactly those widths.
  *   in:     m->F > 0: emb [B][F] fp32 device; else x0 [B][T][D] dtype device.
  *   x_out:  [B][T][D] dtype device output of the last block, or NULL.
  *   pooled: [B][D] fp32 device output of the token mean, or NULL (needs head_w).
@@ -349,6 +358,40 @@ int rm_profile_enable(int on);
 int rm_profile_only(const char* name);
 int rm_profile_count(void);
 int rm_profile_read(int idx, char* name, size_t name_len, double* total_ms, int* launches);
+
+/* Measurement probes: the chip's own ceilings, which bench.py reports beside
+ * the data-sheet peaks (not part of the method).
+ * rm_probe_mfma_bf16: eight waves per compute unit (two per SIMD) that do
+ * nothing but v_mfma_f32_32x32x16_bf16, the grouped products' instruction,
+ * on the random bf16 operands in `frags` (device, rm_probe_mfma_frag_bytes()
+ * bytes, the caller's random bits): each wave holds 16 fragments and eight
+ * 32x32 fp32 accumulators and runs iters rounds of 64 MFMAs, every MFMA on a
+ * different pair of fragments; out (device, rm_probe_mfma_out_floats() fp32)
+ * receives one sum per lane so nothing is optimised away.
+ * rm_probe_mfma_flop(iters) is the launch's flop count (32768 per MFMA).
+ * rm_probe_copy: dst[0..bytes) = src[0..bytes) with 16-byte loads and stores
+ * (bytes a multiple of 16; src, dst 16-byte aligned, not overlapping).
+ * Errors: NULL or misaligned pointers, iters < 1 -> RM_ERR_INVALID. */
+size_t rm_probe_mfma_frag_bytes(void);
+int64_t rm_probe_mfma_out_floats(void);
+double rm_probe_mfma_flop(int iters);
+rm_status rm_probe_mfma_bf16(const void* frags, float* out, int iters, void* stream);
+rm_status rm_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+/* Host-side audit of what the launches would read (needs no GPU).  While
+ * enabled (rm_audit_enable(1), per process), every entry point checks its
+ * arguments as usual but enqueues nothing; instead, for each launch it would
+ * make, it records every caller-owned buffer that launch reads -- the
+ * weights, biases, LayerNorm vectors, router, logit head and the input
+ * activations -- as (name, base pointer, bytes past the base the launch reads
+ * at most).  The extents come from the same arguments the launch would get,
+ * so a caller can check them against its allocations.  rm_audit_enable clears
+ * the record; rm_audit_count() is the number of records; rm_audit_read(i,
+ * ...) returns record i (RM_ERR_INVALID past the end).  Not thread-safe
+ * against concurrent calls on other threads. */
+int rm_audit_enable(int on);
+int rm_audit_count(void);
+int rm_audit_read(int idx, char* name, size_t name_len, uint64_t* base, uint64_t* bytes);
 
 /* Text of a status code; never NULL. */
 const char* rm_status_string(int status);

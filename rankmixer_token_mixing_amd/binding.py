@@ -49,7 +49,8 @@ class MoeParams(C.Structure):
 
 class BlockParams(C.Structure):
     _fields_ = [("kind", C.c_int), ("ln1_g", C.c_void_p), ("ln1_b", C.c_void_p), ("ln2_g", C.c_void_p),
-                ("ln2_b", C.c_void_p), ("pffn", PffnParams), ("moe", MoeParams), ("flags", C.c_int)]
+                ("ln2_b", C.c_void_p), ("pffn", PffnParams), ("moe", MoeParams), ("flags", C.c_int),
+                ("hidden", C.c_int), ("E", C.c_int)]
 
 
 class BlockGrads(C.Structure):
@@ -63,9 +64,8 @@ class MoeGrads(C.Structure):
 
 
 class ModelDesc(C.Structure):
-    _fields_ = [("T", C.c_int), ("D", C.c_int), ("hidden", C.c_int), ("E", C.c_int), ("dtype", C.c_int),
-                ("L", C.c_int), ("blocks", C.POINTER(BlockParams)), ("F", C.c_int64), ("head_w", C.c_void_p),
-                ("head_c", C.c_float)]
+    _fields_ = [("T", C.c_int), ("D", C.c_int), ("dtype", C.c_int), ("L", C.c_int),
+                ("blocks", C.POINTER(BlockParams)), ("F", C.c_int64), ("head_w", C.c_void_p), ("head_c", C.c_float)]
 
 
 _vp, _i64, _int, _sz = C.c_void_p, C.c_int64, C.c_int, C.c_size_t
@@ -101,6 +101,14 @@ _SIGNATURES = {
     "rm_status_string": (C.c_char_p, [_int]),
     "rm_last_error": (C.c_char_p, []),
     "rm_version": (C.c_char_p, []),
+    "rm_probe_mfma_frag_bytes": (_sz, []),
+    "rm_probe_mfma_out_floats": (_i64, []),
+    "rm_probe_mfma_flop": (C.c_double, [_int]),
+    "rm_probe_mfma_bf16": (_int, [_vp, _vp, _int, _vp]),
+    "rm_probe_copy": (_int, [_vp, _vp, _sz, _vp]),
+    "rm_audit_enable": (_int, [_int]),
+    "rm_audit_count": (_int, []),
+    "rm_audit_read": (_int, [_int, C.c_char_p, _sz, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]),
     "rm_profile_enable": (_int, [_int]),
     "rm_profile_only": (_int, [C.c_char_p]),
     "rm_profile_count": (_int, []),
@@ -131,6 +139,17 @@ def load():
                 fn.argtypes = args
             _lib = lib
     return _lib
+
+
+def check_fresh() -> None:
+    """Raise if the loaded library was built from other sources than the
+    ones in this tree (rm_version carries the hash of what it was built from)."""
+    from rankmixer_token_mixing_amd.build import source_hash
+    built = load().rm_version().decode().rsplit(" src ", 1)[-1]
+    want = source_hash()
+    if built != want:
+        raise RankMixerError(RM_ERR_HIP, f"{lib_path()} was built from sources {built}, the tree holds {want}: "
+                                         "rebuild with `python -m rankmixer_token_mixing_amd.build`")
 
 
 def _check(status: int) -> None:
@@ -197,11 +216,13 @@ def _moe_struct(p: dict) -> MoeParams:
 
 def _block_struct(p: dict) -> BlockParams:
     """Block dict -> rm_block_params: a router ("wr") makes it an MoE block,
-    "swiglu": True a SwiGLU block, "no_mix_norm": True sets the flag."""
+    "swiglu": True a SwiGLU block, "no_mix_norm": True sets the flag; hidden
+    and E are the block's own widths, read off its weights."""
     moe = "wr" in p
     bp = BlockParams()
     bp.kind = RM_BLOCK_MOE if moe else (RM_BLOCK_SWIGLU if p.get("swiglu") else RM_BLOCK_DENSE)
     bp.flags = RM_BLOCK_NO_MIX_NORM if p.get("no_mix_norm") else 0
+    bp.hidden, bp.E = _block_dims(p)
     bp.ln1_g, bp.ln1_b, bp.ln2_g, bp.ln2_b = _p(p["ln1_g"]), _p(p["ln1_b"]), _p(p["ln2_g"]), _p(p["ln2_b"])
     if moe:
         bp.moe = _moe_struct(p)
@@ -213,10 +234,33 @@ def _block_struct(p: dict) -> BlockParams:
 def _block_dims(p: dict):
     """(hidden, E) of a block's parameter dict."""
     if "wr" in p:
-        return p["w1"].shape[2], p["w1"].shape[1]
+        return int(p["w1"].shape[2]), int(p["w1"].shape[1])
     if p.get("swiglu"):
-        return p["w1"].shape[1] // 2, 0
-    return p["w1"].shape[1], 0
+        return int(p["w1"].shape[1]) // 2, 0
+    return int(p["w1"].shape[1]), 0
+
+
+def check_block(p: dict, T: int, D: int, dtype) -> None:
+    """Every tensor of a block dict has the shape and dtype its widths imply
+    (the C side sees only pointers, so a short tensor would be read past its
+    end): weight matrices in the activation dtype, vectors fp32."""
+    hidden, E = _block_dims(p)
+    if "wr" in p:
+        shapes = {"wr": (T, E, D), "br": (T, E), "w1": (T, E, hidden, D), "b1": (T, E, hidden),
+                  "w2": (T, E, D, hidden), "b2": (T, E, D)}
+        mats = ("wr", "w1", "w2")
+    else:
+        n1 = 2 * hidden if p.get("swiglu") else hidden
+        shapes = {"w1": (T, n1, D), "b1": (T, n1), "w2": (T, D, hidden), "b2": (T, D)}
+        mats = ("w1", "w2")
+    shapes.update({k: (D,) for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b")})
+    for k, shp in shapes.items():
+        t = p[k]
+        if tuple(t.shape) != shp:
+            raise ValueError(f"block tensor {k} has shape {tuple(t.shape)}, expected {shp}")
+        want = dtype if k in mats else torch.float32
+        if t.dtype != want:
+            raise ValueError(f"block tensor {k} is {t.dtype}, expected {want}")
 
 
 # ---------------------------------------------------------------------------
@@ -299,6 +343,7 @@ def rm_moe_route(s: torch.Tensor, wr: torch.Tensor, br: torch.Tensor):
 def rm_block_fwd(x: torch.Tensor, p: dict, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     lib = load()
     B, T, D = x.shape
+    check_block(p, T, D, x.dtype)
     hidden, E = _block_dims(p)
     bp = _block_struct(p)
     y = torch.empty_like(x) if out is None else out
@@ -398,15 +443,14 @@ class Model:
     def __init__(self, blocks: Sequence[dict], T: int, D: int, dtype=torch.bfloat16, F: int = 0,
                  head: Optional[dict] = None):
         self.blocks = list(blocks)
-        hidden, E = _block_dims(self.blocks[0]) if self.blocks else (8, 0)
+        # each block carries its own hidden width and expert count
         for b in self.blocks:
-            h, e = _block_dims(b)
-            if "wr" in b:
-                E = e
-            hidden = h
+            check_block(b, T, D, dtype)
+        if head is not None and (tuple(head["w"].shape) != (D,) or head["w"].dtype != torch.float32):
+            raise ValueError("head w must be a [D] fp32 tensor")
         self._arr = (BlockParams * max(1, len(self.blocks)))(*[_block_struct(b) for b in self.blocks])
         self.head = head
-        self.desc = ModelDesc(T, D, hidden, E, _DT[dtype], len(self.blocks), self._arr, F,
+        self.desc = ModelDesc(T, D, _DT[dtype], len(self.blocks), self._arr, F,
                               _p(head["w"]) if head else None, float(head["c"]) if head else 0.0)
         self.T, self.D, self.dtype, self.F = T, D, dtype, F
 
@@ -432,6 +476,16 @@ def rm_model_fwd(model: Model, inp: torch.Tensor, want_x: bool = True, want_pool
     _check(lib.rm_model_fwd(C.byref(model.desc), _p(inp), _p(res.get("x")), _p(res.get("pooled")),
                             _p(res.get("logit")), B, _p(ws), ws.numel(), _stream(dev)))
     return res
+
+
+def probe_mfma_bf16(frags: torch.Tensor, out: torch.Tensor, iters: int) -> None:
+    """The MFMA ceiling probe (see rm_probe_mfma_bf16); frags: random bytes of
+    rm_probe_mfma_frag_bytes(), out: rm_probe_mfma_out_floats() fp32."""
+    _check(load().rm_probe_mfma_bf16(_p(frags), _p(out), iters, _stream(frags.device)))
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int) -> None:
+    _check(load().rm_probe_copy(_p(src), _p(dst), nbytes, _stream(src.device)))
 
 
 def profile_enable(on: bool = True) -> None:

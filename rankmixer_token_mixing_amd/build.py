@@ -9,6 +9,7 @@ cross-compiles the device code.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -19,7 +20,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librankmixer.so")
-SOURCES = ["abi.cpp", "kernels_rows.hip", "kernels_moe.hip", "kernels_gemm.hip", "kernels_tokproj.hip", "kernels_bwd.hip", "kernels_variants.hip", "kernels_moe_train.hip"]
+SOURCES = ["abi.cpp", "kernels_rows.hip", "kernels_moe.hip", "kernels_gemm.hip", "kernels_tokproj.hip", "kernels_bwd.hip", "kernels_variants.hip", "kernels_moe_train.hip", "kernels_probe.hip"]
 ARCH = os.environ.get("RM_OFFLOAD_ARCH", "gfx950")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in the device code
@@ -29,6 +30,29 @@ HIPCC_FLAGS = [
 ]
 
 
+def source_hash() -> str:
+    """sha256 (first 16 hex digits) of every C/C++/HIP source and header the
+    library is built from; the build bakes it into rm_version()."""
+    root = os.path.dirname(PKG)
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp", ".hpp")))
+    files.append(os.path.join(root, "include", "rankmixer.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def library_is_fresh(path: str = LIB) -> bool:
+    """Whether the library at `path` exists and was built from the tree's
+    current sources (its rm_version string carries their hash)."""
+    if not os.path.exists(path):
+        return False
+    with open(path, "rb") as fh:
+        return (" src " + source_hash()).encode() in fh.read()
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -36,9 +60,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librankmixer.so)")
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, src_hash: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, f'-DRM_SRC_HASH="{src_hash}"', "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
@@ -49,8 +73,9 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     t0 = time.time()
+    src_hash = source_hash()
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda f: _compile(f, src_hash), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -3,6 +3,8 @@
 // frees or synchronises; every check runs before the first launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -39,6 +41,27 @@ rm_status hip_status(hipError_t e, const char* what) {
 }
 
 // ---------------------------------------------------------------------------
+// host-side audit (rm_audit_*): while it is on, nothing is enqueued; each
+// launch site records the caller-owned buffers its launch would read and the
+// bytes past their base it would read at most, from the launch's own arguments
+
+struct AuditRec {
+  std::string name;
+  uint64_t base, bytes;
+};
+std::mutex g_audit_mu;
+std::atomic<bool> g_audit{false};
+std::vector<AuditRec> g_audit_recs;
+
+bool auditing() { return g_audit.load(std::memory_order_relaxed); }
+
+void audit(const std::string& name, const void* base, int64_t bytes) {
+  if (!auditing() || !base) return;
+  std::lock_guard<std::mutex> lk(g_audit_mu);
+  g_audit_recs.push_back({name, (uint64_t)(uintptr_t)base, (uint64_t)(bytes > 0 ? bytes : 0)});
+}
+
+// ---------------------------------------------------------------------------
 // optional launch timing (rm_profile_*): a pair of HIP events around every
 // launch group, recorded on the stream the kernels go to
 
@@ -56,7 +79,7 @@ struct ProfScope {
   hipStream_t st;
   const char* name;
   ProfScope(const char* n, hipStream_t s) : st(s), name(n) {
-    if (!g_prof_on || (!g_prof_only.empty() && g_prof_only != n)) return;
+    if (!g_prof_on || auditing() || (!g_prof_only.empty() && g_prof_only != n)) return;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
       a = b = nullptr;
       return;
@@ -92,7 +115,11 @@ void prof_clear() {
     if (_st != RM_OK) return _st;        \
   } while (0)
 
-#define RM_HIP(expr, what) RM_TRY(hip_status((expr), (what)))
+// a HIP call (launch, copy); skipped, not evaluated, while auditing
+#define RM_HIP(expr, what)                                   \
+  do {                                                       \
+    if (!auditing()) RM_TRY(hip_status((expr), (what)));     \
+  } while (0)
 #define RM_PROF_CAT2(a, b) a##b
 #define RM_PROF_CAT(a, b) RM_PROF_CAT2(a, b)
 // time the launches of the enclosing statement under `name`
@@ -146,6 +173,34 @@ rm_status check_moe_shape(int64_t B, int T, int E) {
   if (E < 1 || E > 32) return fail(RM_ERR_UNSUPPORTED, "E=%d experts per token (supported: 1..32)", E);
   if ((int64_t)T * E > 4096) return fail(RM_ERR_UNSUPPORTED, "T*E=%lld lists (supported: <= 4096)", (long long)T * E);
   if (B * T * E >= ((int64_t)1 << 31)) return fail(RM_ERR_UNSUPPORTED, "B*T*E too large");
+  return RM_OK;
+}
+
+// One grouped product.  While auditing, it records instead how far each
+// operand the launch reads extends: A rows below M per group (gathered rows
+// index samples below M), or below M * G for the compacted rows of a ragged
+// product; W group g at (g / b_gdiv) * b_gs, N * K elements; the bias of group
+// g at g * bias_gs, N floats.
+rm_status gemm_go(const char* name, const rm::GemmArgs& a, hipStream_t st) {
+  if (auditing()) {
+    if (a.G <= 0 || a.M <= 0 || a.N <= 0 || a.K <= 0) return RM_OK;
+    const int64_t e = elem_bytes(a.dt);
+    const int64_t arows = a.row_off && !a.a_rowidx ? (int64_t)a.M * a.G : a.M;
+    const std::string n(name);
+    audit(n + ".A", a.A, (((int64_t)(a.G - 1) / a.a_gdiv) * a.a_gs + (arows - 1) * a.a_rs + a.K) * e);
+    audit(n + ".W", a.W, (((int64_t)(a.G - 1) / a.b_gdiv) * a.b_gs + (int64_t)a.N * a.K) * e);
+    if (a.bias) audit(n + ".bias", a.bias, ((int64_t)(a.G - 1) * a.bias_gs + a.N) * 4);
+    return RM_OK;
+  }
+  return hip_status(rm::launch_gemm(a, st), name);
+}
+
+// a block's widths given as arguments must agree with its descriptor's own
+// (0 there: as the argument)
+rm_status check_block_dims(const rm_block_params* p, int hidden, int E) {
+  if (p->hidden && p->hidden != hidden)
+    return fail(RM_ERR_INVALID, "block params hidden=%d differ from the argument hidden=%d", p->hidden, hidden);
+  if (p->E && p->E != E) return fail(RM_ERR_INVALID, "block params E=%d differ from the argument E=%d", p->E, E);
   return RM_OK;
 }
 
@@ -256,11 +311,11 @@ rm::GemmArgs ffn2_args(const void* H, const rm_pffn_params* p, int64_t B, int T,
 
 rm_status run_pffn(const void* s, const rm_pffn_params* p, void* v, int64_t B, int T, int D, int Hd, int dt,
                    const PffnWs& w, hipStream_t st) {
-  RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(s, (int64_t)T * D, D, p, w.H, B, T, D, Hd, dt), st), "pffn W1 product"));
+  RM_TIMED("ffn1", st, RM_TRY(gemm_go("pffn W1 product", ffn1_args(s, (int64_t)T * D, D, p, w.H, B, T, D, Hd, dt), st)));
   rm::GemmArgs a2 = ffn2_args(w.H, p, B, T, D, Hd, dt);
   a2.epi = rm::kEpiBias;
   a2.C = v;
-  RM_TIMED("ffn2", st, RM_HIP(rm::launch_gemm(a2, st), "pffn W2 product"));
+  RM_TIMED("ffn2", st, RM_TRY(gemm_go("pffn W2 product", a2, st)));
   return RM_OK;
 }
 
@@ -269,6 +324,9 @@ rm_status run_moe(const void* s, int64_t sb, int64_t sT, const rm_moe_params* p,
                   const float* ln_g, const float* ln_b, int64_t B, int T, int D, int E, int He, int dt, MoeWs w,
                   hipStream_t st) {
   if (gates_out) w.mw.gates = gates_out;
+  const int64_t e = elem_bytes(dt);
+  audit("moe_router.wr", p->wr, (int64_t)T * E * D * e);
+  audit("moe_router.br", p->br, (int64_t)T * E * 4);
   RM_TIMED("moe_router", st, RM_HIP(rm::launch_moe_router(s, sb, sT, p->wr, p->br, w.mw.gates, B, T, D, E, dt, st), "moe router"));
   RM_TIMED("moe_compact", st, RM_HIP(rm::launch_moe_compact(w.mw, B, T, E, kMoeTileM, st), "moe compaction"));
   const int G = T * E;
@@ -282,7 +340,7 @@ rm_status run_moe(const void* s, int64_t sb, int64_t sT, const rm_moe_params* p,
   a.bias = p->b1; a.bias_gs = He;
   a.row_off = w.mw.offsets; a.tiles = w.mw.tiles; a.ntiles = w.mw.ntiles; a.max_mtiles = w.max_mtiles;
   if (rm::gemm_tile_m(a) != kMoeTileM) return fail(RM_ERR_HIP, "internal: MoE tile size mismatch");
-  RM_TIMED("moe_ffn1", st, RM_HIP(rm::launch_gemm(a, st), "moe W1 product"));
+  RM_TIMED("moe_ffn1", st, RM_TRY(gemm_go("moe W1 product", a, st)));
   rm::GemmArgs b;
   b.dt = dt;
   b.epi = rm::kEpiBiasScale;
@@ -294,7 +352,9 @@ rm_status run_moe(const void* s, int64_t sb, int64_t sT, const rm_moe_params* p,
   b.rowscale = w.mw.gatec;
   b.row_off = w.mw.offsets; b.tiles = w.mw.tiles; b.ntiles = w.mw.ntiles; b.max_mtiles = w.max_mtiles;
   if (rm::gemm_tile_m(b) != kMoeTileM) return fail(RM_ERR_HIP, "internal: MoE tile size mismatch");
-  RM_TIMED("moe_ffn2", st, RM_HIP(rm::launch_gemm(b, st), "moe W2 product"));
+  RM_TIMED("moe_ffn2", st, RM_TRY(gemm_go("moe W2 product", b, st)));
+  audit("moe_combine.ln_g", ln_g, (int64_t)D * 4);
+  audit("moe_combine.ln_b", ln_b, (int64_t)D * 4);
   RM_TIMED("moe_combine", st,
            RM_HIP(rm::launch_moe_combine(w.Yc, w.mw.pos, s, sb, sT, ln_g, ln_b, out, B, T, D, E, ln_g != nullptr, dt, st),
                   "moe combine"));
@@ -343,18 +403,22 @@ rm_status run_block(const void* x, const rm_block_params* p, void* xo, int64_t B
     sT = B * D;
   } else if (p->flags & RM_BLOCK_NO_MIX_NORM) {
     // S = TM(X), [B][T][D]
+    audit("mix.x", x, B * T * D * (int64_t)elem_bytes(dt));
     RM_TIMED("mix", st, RM_HIP(rm::launch_token_mix(x, w.S, B, T, D, dt, st), "token mix"));
     sb = (int64_t)T * D;
     sT = D;
   } else {
     // S = LN1(TM(X) + X), token-major so one token's rows are contiguous
+    audit("mix_ln1.x", x, B * T * D * (int64_t)elem_bytes(dt));
+    audit("mix_ln1.ln1_g", p->ln1_g, (int64_t)D * 4);
+    audit("mix_ln1.ln1_b", p->ln1_b, (int64_t)D * 4);
     RM_TIMED("mix_ln1", st, RM_HIP(rm::launch_mix_ln(x, w.S, p->ln1_g, p->ln1_b, B, T, D, dt, true, st), "token mix + LayerNorm"));
     sb = D;
     sT = B * D;
   }
   if (p->kind == RM_BLOCK_DENSE || p->kind == RM_BLOCK_SWIGLU) {
     if (p->kind == RM_BLOCK_DENSE) {
-      RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(ffn1_args(w.S, sb, sT, &p->pffn, w.pffn.H, B, T, D, hidden, dt), st), "block W1 product"));
+      RM_TIMED("ffn1", st, RM_TRY(gemm_go("block W1 product", ffn1_args(w.S, sb, sT, &p->pffn, w.pffn.H, B, T, D, hidden, dt), st)));
     } else {
       // one product over the gate and up rows (N = 2*Hs); on the pipelined
       // kernel its epilogue pairs them and writes H = SiLU(G) * U directly,
@@ -364,11 +428,11 @@ rm_status run_block(const void* x, const rm_block_params* p, void* xo, int64_t B
       a1.c_rs = hidden;
       a1.epi = rm::kEpiSwiglu;
       if (rm::gemm_pipe_eligible(a1)) {
-        RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block gate / up product + SwiGLU"));
+        RM_TIMED("ffn1", st, RM_TRY(gemm_go("block gate / up product + SwiGLU", a1, st)));
       } else {
         a1 = ffn1_args(w.S, sb, sT, &p->pffn, w.GU, B, T, D, 2 * hidden, dt);
         a1.epi = rm::kEpiBias;
-        RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block gate / up product"));
+        RM_TIMED("ffn1", st, RM_TRY(gemm_go("block gate / up product", a1, st)));
         RM_TIMED("swiglu", st, RM_HIP(rm::launch_swiglu_ew(w.GU, w.pffn.H, B * T, hidden, dt, st), "SwiGLU"));
       }
     }
@@ -378,13 +442,19 @@ rm_status run_block(const void* x, const rm_block_params* p, void* xo, int64_t B
     // by loads in the product's epilogue
     a2.epi = rm::kEpiBias;
     a2.C = w.Z;
-    RM_TIMED("ffn2", st, RM_HIP(rm::launch_gemm(a2, st), "block W2 product"));
+    RM_TIMED("ffn2", st, RM_TRY(gemm_go("block W2 product", a2, st)));
     if (next) {
+      audit("ln2_mix_ln1.ln2_g", p->ln2_g, (int64_t)D * 4);
+      audit("ln2_mix_ln1.ln2_b", p->ln2_b, (int64_t)D * 4);
+      audit("ln2_mix_ln1.ln1_g", next->ln1_g, (int64_t)D * 4);
+      audit("ln2_mix_ln1.ln1_b", next->ln1_b, (int64_t)D * 4);
       RM_TIMED("ln2_mix_ln1", st, RM_HIP(rm::launch_ln_mix_ln(w.Z, w.S, p->ln2_g, p->ln2_b, next->ln1_g, next->ln1_b,
                                                               B, T, D, dt, st),
                                          "LayerNorm 2 + next block's token mix + LayerNorm 1"));
       return RM_OK;
     }
+    audit("ln2.ln2_g", p->ln2_g, (int64_t)D * 4);
+    audit("ln2.ln2_b", p->ln2_b, (int64_t)D * 4);
     RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows(w.Z, w.S, sb, sT, T, xo, p->ln2_g, p->ln2_b, B * T, D, dt, st),
                                "residual + LayerNorm 2"));
     return RM_OK;
@@ -403,30 +473,24 @@ bool fusable_boundary(const rm_model_desc* m, int l) {
          rm::ln_mix_ln_supported(m->T, m->D, m->dtype);
 }
 
-size_t model_ws(Carver& c, const rm_model_desc* m, int64_t B, void** x0, void** x1, BlockWs* bw) {
+// Two [B][T][D] ping-pong buffers, then one block region large enough for
+// the largest block of the stack, each block sized from its own kind, hidden
+// width and expert count; every block carves its own layout from the region's
+// start (S first, so a boundary pass can leave the next block's S there).
+size_t model_ws(Carver& c, const rm_model_desc* m, int64_t B, void** x0, void** x1, void** blk) {
   const size_t xb = (size_t)B * m->T * m->D * elem_bytes(m->dtype);
   void* a = c.take(xb);
   void* b = c.take(xb);
   if (x0) *x0 = a;
   if (x1) *x1 = b;
-  // one block workspace, sized for the largest block kind present
-  size_t start = c.off, best = 0;
-  int best_kind = RM_BLOCK_DENSE;
+  size_t best = 0;
   for (int l = 0; l < m->L; ++l) {
+    const rm_block_params& p = m->blocks[l];
     Carver probe(nullptr);
-    probe.off = start;
-    const size_t end = block_ws(probe, m->blocks[l].kind, B, m->T, m->D, m->hidden, m->E, m->dtype, nullptr);
-    if (end - start > best) {
-      best = end - start;
-      best_kind = m->blocks[l].kind;
-    }
+    best = std::max(best, block_ws(probe, p.kind, B, m->T, m->D, p.hidden, p.E, m->dtype, nullptr));
   }
-  if (m->L > 0) {
-    Carver real = c;
-    block_ws(real, best_kind, B, m->T, m->D, m->hidden, m->E, m->dtype, bw);
-    // a block workspace of the other kind is carved from the same region
-    c.off = start + best;
-  }
+  void* r = c.take(best);
+  if (blk) *blk = r;
   return c.off;
 }
 
@@ -448,7 +512,57 @@ const char* rm_status_string(int st) {
 
 const char* rm_last_error(void) { return g_last_error.c_str(); }
 
-const char* rm_version(void) { return "rankmixer-mi355x 0.1 (gfx950)"; }
+#ifndef RM_SRC_HASH
+#define RM_SRC_HASH "unknown"
+#endif
+// the build passes the hash of the sources it compiled
+const char* rm_version(void) { return "rankmixer-mi355x 0.2 (gfx950) src " RM_SRC_HASH; }
+
+size_t rm_probe_mfma_frag_bytes(void) { return (size_t)rm::kProbeFragBytes; }
+
+int64_t rm_probe_mfma_out_floats(void) { return (int64_t)rm::probe_mfma_waves() * 64; }
+
+double rm_probe_mfma_flop(int iters) { return (double)rm::probe_mfma_waves() * iters * 64 * 32768.0; }
+
+rm_status rm_probe_mfma_bf16(const void* frags, float* out, int iters, void* stream) {
+  RM_TRY(check_ptr(frags, "frags"));
+  RM_TRY(check_ptr(out, "out"));
+  if (iters < 1) return fail(RM_ERR_INVALID, "iters=%d must be positive", iters);
+  RM_HIP(rm::launch_probe_mfma(frags, out, iters, (hipStream_t)stream), "MFMA probe");
+  return ok();
+}
+
+rm_status rm_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  RM_TRY(check_ptr(src, "src"));
+  RM_TRY(check_ptr(dst, "dst"));
+  if (bytes % 16) return fail(RM_ERR_INVALID, "bytes=%zu must be a multiple of 16", bytes);
+  const char *a = (const char*)src, *b = (const char*)dst;
+  if (a < b + bytes && b < a + bytes) return fail(RM_ERR_INVALID, "src and dst overlap");
+  if (bytes) RM_HIP(rm::launch_probe_copy(src, dst, (long long)(bytes / 16), (hipStream_t)stream), "copy probe");
+  return ok();
+}
+
+int rm_audit_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_audit_mu);
+  g_audit_recs.clear();
+  g_audit.store(on != 0, std::memory_order_relaxed);
+  return RM_OK;
+}
+
+int rm_audit_count(void) {
+  std::lock_guard<std::mutex> lk(g_audit_mu);
+  return (int)g_audit_recs.size();
+}
+
+int rm_audit_read(int idx, char* name, size_t name_len, uint64_t* base, uint64_t* bytes) {
+  std::lock_guard<std::mutex> lk(g_audit_mu);
+  if (idx < 0 || idx >= (int)g_audit_recs.size() || !name || !base || !bytes)
+    return fail(RM_ERR_INVALID, "audit record %d does not exist", idx);
+  snprintf(name, name_len, "%s", g_audit_recs[idx].name.c_str());
+  *base = g_audit_recs[idx].base;
+  *bytes = g_audit_recs[idx].bytes;
+  return RM_OK;
+}
 
 int rm_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -494,6 +608,7 @@ rm_status rm_tokenize_padsplit(const float* emb, int64_t B, int64_t F, int T, in
   if (B == 0) return ok();  // empty batch: nothing to do
   RM_TRY(check_ptr(emb, "emb"));
   RM_TRY(check_ptr(x0, "x0"));
+  audit("tokenize.emb", emb, B * F * 4);
   RM_TIMED("tokenize", (hipStream_t)stream, RM_HIP(rm::launch_tokenize_padsplit(emb, B, F, T, D, out_dtype, x0, (hipStream_t)stream), "tokenize"));
   return ok();
 }
@@ -535,7 +650,10 @@ rm_status rm_tokenize_project(const float* emb, const rm_proj_params* p, int64_t
   if (need) RM_TRY(check_ptr(ws, "ws"));
   if (ws_bytes < need) return fail(RM_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
+  audit("tokenize.emb", emb, B * F * 4);
   if (fused) {
+    audit("tokenize_proj.W", p->w, (int64_t)T * D * seg * elem_bytes(dtype));
+    audit("tokenize_proj.bias", p->b, (int64_t)T * D * 4);
     RM_TIMED("tokenize_proj", st,
              RM_HIP(rm::launch_tokenize_project(emb, p->w, p->b, x0, B, F, T, seg, D, st), "tokenize projection"));
     return ok();
@@ -549,7 +667,7 @@ rm_status rm_tokenize_project(const float* emb, const rm_proj_params* p, int64_t
   a.W = p->w; a.b_gs = (int64_t)D * seg;
   a.C = x0; a.c_gs = D; a.c_rs = (int64_t)T * D;
   a.bias = p->b; a.bias_gs = D;
-  RM_TIMED("tokenize_proj", st, RM_HIP(rm::launch_gemm(a, st), "tokenize projection"));
+  RM_TIMED("tokenize_proj", st, RM_TRY(gemm_go("tokenize projection", a, st)));
   return ok();
 }
 
@@ -561,6 +679,7 @@ rm_status rm_token_mix(const void* x, void* y, int64_t B, int T, int D, int dtyp
   RM_TRY(check_ptr(x, "x"));
   RM_TRY(check_ptr(y, "y"));
   if (x == y) return fail(RM_ERR_INVALID, "y must not alias x");
+  audit("token_mix.x", x, B * T * D * (int64_t)elem_bytes(dtype));
   RM_TIMED("token_mix", (hipStream_t)stream, RM_HIP(rm::launch_token_mix(x, y, B, T, D, dtype, (hipStream_t)stream), "token mix"));
   return ok();
 }
@@ -640,6 +759,9 @@ rm_status rm_moe_route(const void* s, const void* wr, const float* br, float* ga
   w.mw.offsets = offsets;
   w.mw.rows = rows;
   hipStream_t st = (hipStream_t)stream;
+  audit("moe_router.s", s, B * T * D * (int64_t)elem_bytes(dtype));
+  audit("moe_router.wr", wr, (int64_t)T * E * D * elem_bytes(dtype));
+  audit("moe_router.br", br, (int64_t)T * E * 4);
   RM_HIP(rm::launch_moe_router(s, (int64_t)T * D, D, wr, br, gates, B, T, D, E, dtype, st), "moe router");
   RM_HIP(rm::launch_moe_compact(w.mw, B, T, E, kMoeTileM, st), "moe compaction");
   return ok();
@@ -653,6 +775,7 @@ size_t rm_block_workspace_bytes(int kind, int64_t B, int T, int D, int hidden, i
 rm_status rm_block_fwd(const void* x, const rm_block_params* p, void* x_out, int64_t B, int T, int D, int hidden,
                        int E, int dtype, void* ws, size_t ws_bytes, void* stream) {
   RM_TRY(check_block_params(p, dtype));
+  RM_TRY(check_block_dims(p, hidden, E));
   RM_TRY(check_block_shape(p->kind, B, T, D, hidden, E, dtype));
   if (B == 0) return ok();
   RM_TRY(check_ptr(x, "x")); RM_TRY(check_ptr(x_out, "x_out"));
@@ -724,6 +847,7 @@ size_t bwd_carve(Carver& c, int64_t B, int T, int D, int Hd, int dt, BwdWs* w) {
 
 rm_status check_train_shape(const rm_block_params* p, int64_t B, int T, int D, int hidden, int dt) {
   RM_TRY(check_block_params(p, dt));
+  RM_TRY(check_block_dims(p, hidden, 0));
   if (p->kind != RM_BLOCK_DENSE || p->flags)
     return fail(RM_ERR_UNSUPPORTED, "training supports dense blocks (GELU FFN, Add & Norm after the mix) only");
   RM_TRY(check_block_shape(RM_BLOCK_DENSE, B, T, D, hidden, 0, dt));
@@ -761,6 +885,11 @@ rm_status rm_block_fwd_train(const void* x, const rm_block_params* p, void* x_ou
   BlockWs w;
   block_ws(c, RM_BLOCK_DENSE, B, T, D, hidden, 0, dtype, &w);
   const int64_t sb = D, sT = B * D;  // S is token-major
+  audit("mix_ln1.x", x, B * T * D * (int64_t)elem_bytes(dtype));
+  audit("mix_ln1.ln1_g", p->ln1_g, (int64_t)D * 4);
+  audit("mix_ln1.ln1_b", p->ln1_b, (int64_t)D * 4);
+  audit("ln2.ln2_g", p->ln2_g, (int64_t)D * 4);
+  audit("ln2.ln2_b", p->ln2_b, (int64_t)D * 4);
   RM_TIMED("mix_ln1", st, RM_HIP(rm::launch_mix_ln(x, sv.S, p->ln1_g, p->ln1_b, B, T, D, dtype, true, st), "token mix + LayerNorm"));
   // keep U = W1 s + b1 (saved) and H = GELU(U): both from the product's
   // epilogue on the pipelined kernel, else a separate GELU pass
@@ -768,16 +897,16 @@ rm_status rm_block_fwd_train(const void* x, const rm_block_params* p, void* x_ou
   a1.epi = rm::kEpiBiasGeluDual;
   a1.C2 = w.pffn.H;
   if (rm::gemm_pipe_eligible(a1)) {
-    RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block W1 product + GELU"));
+    RM_TIMED("ffn1", st, RM_TRY(gemm_go("block W1 product + GELU", a1, st)));
   } else {
     a1.epi = rm::kEpiBias;
-    RM_TIMED("ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "block W1 product"));
+    RM_TIMED("ffn1", st, RM_TRY(gemm_go("block W1 product", a1, st)));
     RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.pffn.H, B * T * (int64_t)hidden, dtype, st), "GELU"));
   }
   rm::GemmArgs a2 = ffn2_args(w.pffn.H, &p->pffn, B, T, D, hidden, dtype);
   a2.epi = rm::kEpiBias;
   a2.C = sv.Z;
-  RM_TIMED("ffn2", st, RM_HIP(rm::launch_gemm(a2, st), "block W2 product"));
+  RM_TIMED("ffn2", st, RM_TRY(gemm_go("block W2 product", a2, st)));
   RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows(sv.Z, sv.S, sb, sT, T, x_out, p->ln2_g, p->ln2_b, B * T, D, dtype, st),
                              "residual + LayerNorm 2"));
   return ok();
@@ -826,6 +955,10 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   const int64_t Bp = pad64(B);
   const int rt = rm::transpose_row_tiles(B, Bp);
   const int lg = rm::ln_bwd_grid(B, T, D);
+  audit("ln_bwd.x", x, B * T * D * (int64_t)elem_bytes(dt));
+  audit("ln_bwd.d_out", d_out, B * T * D * (int64_t)elem_bytes(dt));
+  audit("ln_bwd.ln2_g", p->ln2_g, (int64_t)D * 4);
+  audit("ln_bwd.ln1_g", p->ln1_g, (int64_t)D * 4);
   // X' = LN2(Z + S): dV = dY2 (token-major), gamma2 / beta2 partials
   RM_TIMED("ln2_bwd", st, RM_HIP(rm::launch_ln_bwd(0, d_out, nullptr, nullptr, sv.Z, sv.S, p->ln2_g, w.dV, w.ln2p, B, T, D, dt, st), "LayerNorm 2 backward"));
   // dV^T (rows padded to Bp) and the b2 partials
@@ -839,11 +972,12 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   g1.W = p->pffn.w2; g1.b_gs = (int64_t)Hd * D; g1.w_kmajor = 1;
   g1.C = w.dH; g1.c_gs = B * Hd; g1.c_rs = Hd;
   if (!rm::gemm_wt_eligible(g1)) {
+    audit("tr_W2.W", p->pffn.w2, (int64_t)T * D * Hd * elem_bytes(dt));
     RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->pffn.w2, nullptr, w.W2t, nullptr, nullptr, nullptr, T, D, Hd, D, dt, st), "transpose W2"));
     g1.W = w.W2t;
     g1.w_kmajor = 0;
   }
-  RM_TIMED("bwd_dH", st, RM_HIP(rm::launch_gemm(g1, st), "dH product"));
+  RM_TIMED("bwd_dH", st, RM_TRY(gemm_go("dH product", g1, st)));
   // dU = dH * GELU'(U), also transposed, with the b1 partials, and H^T =
   // GELU(U)^T from the same read of U
   RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.Ht, w.b1p, T, B, Hd, Bp, dt, st), "GELU backward"));
@@ -854,7 +988,7 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   g2.A = w.dVt; g2.a_gs = (int64_t)D * Bp; g2.a_rs = Bp;
   g2.W = w.Ht; g2.b_gs = (int64_t)Hd * Bp;
   g2.C = g->w2; g2.c_gs = (int64_t)D * Hd; g2.c_rs = Hd;
-  RM_TIMED("bwd_dW2", st, RM_HIP(rm::launch_gemm(g2, st), "dW2 product"));
+  RM_TIMED("bwd_dW2", st, RM_TRY(gemm_go("dW2 product", g2, st)));
   // dW1 = dU^T S (fp32)
   RM_TIMED("tr_S", st, RM_HIP(rm::launch_transpose(0, sv.S, nullptr, w.St, nullptr, nullptr, nullptr, T, B, D, Bp, dt, st), "transpose S"));
   rm::GemmArgs g3;
@@ -863,7 +997,7 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   g3.A = w.dUt; g3.a_gs = (int64_t)Hd * Bp; g3.a_rs = Bp;
   g3.W = w.St; g3.b_gs = (int64_t)D * Bp;
   g3.C = g->w1; g3.c_gs = (int64_t)Hd * D; g3.c_rs = D;
-  RM_TIMED("bwd_dW1", st, RM_HIP(rm::launch_gemm(g3, st), "dW1 product"));
+  RM_TIMED("bwd_dW1", st, RM_TRY(gemm_go("dW1 product", g3, st)));
   // dS (W1 branch) = dU W1 (fp32, token-major): W1_t [Hd][D] read K-major
   // where the kernel allows, else W1^T first
   rm::GemmArgs g4;
@@ -873,11 +1007,12 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   g4.W = p->pffn.w1; g4.b_gs = (int64_t)D * Hd; g4.w_kmajor = 1;
   g4.C = w.dSf; g4.c_gs = B * D; g4.c_rs = D;
   if (!rm::gemm_wt_eligible(g4)) {
+    audit("tr_W1.W", p->pffn.w1, (int64_t)T * Hd * D * elem_bytes(dt));
     RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->pffn.w1, nullptr, w.W1t, nullptr, nullptr, nullptr, T, Hd, D, Hd, dt, st), "transpose W1"));
     g4.W = w.W1t;
     g4.w_kmajor = 0;
   }
-  RM_TIMED("bwd_dS", st, RM_HIP(rm::launch_gemm(g4, st), "dS product"));
+  RM_TIMED("bwd_dS", st, RM_TRY(gemm_go("dS product", g4, st)));
   // S = LN1(TM(X) + X) with dS = dV + dS_ffn; dX = dY1 + TM(dY1)
   RM_TIMED("ln1_bwd", st, RM_HIP(rm::launch_ln_bwd(1, nullptr, w.dV, w.dSf, x, nullptr, p->ln1_g, w.dY1, w.ln1p, B, T, D, dt, st), "LayerNorm 1 backward"));
   RM_TIMED("tm_add", st, RM_HIP(rm::launch_tm_add(w.dY1, dx, B, T, D, dt, st), "token mix backward"));
@@ -962,6 +1097,7 @@ size_t moe_train_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt
 rm_status check_moe_train(const rm_block_params* p, const void* wr_train, const float* br_train, int64_t B, int T,
                           int D, int He, int E, int dt) {
   RM_TRY(check_block_params(p, dt));
+  RM_TRY(check_block_dims(p, He, E));
   if (p->kind != RM_BLOCK_MOE || p->flags)
     return fail(RM_ERR_UNSUPPORTED, "MoE training needs an MoE block with the Add & Norm after the mix");
   RM_TRY(check_block_shape(RM_BLOCK_MOE, B, T, D, He, E, dt));
@@ -1016,6 +1152,15 @@ rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const 
   // S = LN1(TM(X) + X), token-major
   RM_TIMED("mix_ln1", st, RM_HIP(rm::launch_mix_ln(x, sv.S, p->ln1_g, p->ln1_b, B, T, D, dt, true, st), "token mix + LayerNorm"));
   // both routers' gates; the sparsity loss sums the inference gates
+  audit("mix_ln1.x", x, B * T * D * (int64_t)elem_bytes(dt));
+  audit("mix_ln1.ln1_g", p->ln1_g, (int64_t)D * 4);
+  audit("mix_ln1.ln1_b", p->ln1_b, (int64_t)D * 4);
+  audit("router.wr_train", wr_train, (int64_t)T * E * D * elem_bytes(dt));
+  audit("router.br_train", br_train, (int64_t)T * E * 4);
+  audit("router.wr", p->moe.wr, (int64_t)T * E * D * elem_bytes(dt));
+  audit("router.br", p->moe.br, (int64_t)T * E * 4);
+  audit("ln2.ln2_g", p->ln2_g, (int64_t)D * 4);
+  audit("ln2.ln2_b", p->ln2_b, (int64_t)D * 4);
   RM_TIMED("router", st, RM_HIP(rm::launch_moe_router(sv.S, D, B * D, wr_train, br_train, sv.Gt, B, T, D, E, dt, st), "training router"));
   RM_TIMED("router", st, RM_HIP(rm::launch_moe_router(sv.S, D, B * D, p->moe.wr, p->moe.br, sv.Gi, B, T, D, E, dt, st), "inference router"));
   RM_TIMED("l_reg", st, RM_HIP(rm::launch_sum_all(sv.Gi, l_reg, B * TE, w.lpart, st), "sparsity loss"));
@@ -1030,10 +1175,10 @@ rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const 
   a1.epi = rm::kEpiBiasGeluDual;  // U (saved) and H = GELU(U) from one epilogue where the kernel allows
   a1.C2 = w.H;
   if (rm::gemm_pipe_eligible(a1)) {
-    RM_TIMED("moe_ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "expert W1 products + GELU"));
+    RM_TIMED("moe_ffn1", st, RM_TRY(gemm_go("expert W1 products + GELU", a1, st)));
   } else {
     a1.epi = rm::kEpiBias;
-    RM_TIMED("moe_ffn1", st, RM_HIP(rm::launch_gemm(a1, st), "expert W1 products"));
+    RM_TIMED("moe_ffn1", st, RM_TRY(gemm_go("expert W1 products", a1, st)));
     RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.H, B * TE * He, dt, st), "GELU"));
   }
   rm::GemmArgs a2;
@@ -1043,7 +1188,7 @@ rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const 
   a2.W = p->moe.w2; a2.b_gs = (int64_t)D * He;
   a2.C = sv.Y; a2.c_gs = D; a2.c_rs = TE * D;
   a2.bias = p->moe.b2; a2.bias_gs = D;
-  RM_TIMED("moe_ffn2", st, RM_HIP(rm::launch_gemm(a2, st), "expert W2 products"));
+  RM_TIMED("moe_ffn2", st, RM_TRY(gemm_go("expert W2 products", a2, st)));
   // Z = sum_j G_train y_j, then X' = LN2(Z + S)
   RM_TIMED("combine", st, RM_HIP(rm::launch_moe_combine_dense(sv.Y, sv.Gt, sv.Z, B * T, E, D, dt, st), "expert combine"));
   RM_TIMED("ln2", st, RM_HIP(rm::launch_ln_rows(sv.Z, sv.S, D, B * D, T, x_out, p->ln2_g, p->ln2_b, B * T, D, dt, st),
@@ -1090,6 +1235,13 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
   // X' = LN2(Z + S): dV = dY2 (token-major)
   RM_TIMED("ln2_bwd", st, RM_HIP(rm::launch_ln_bwd(0, d_out, nullptr, nullptr, sv.Z, sv.S, p->ln2_g, w.dV, w.ln2p, B, T, D, dt, st), "LayerNorm 2 backward"));
   // gates: dy = G_train dV, dz (training router), mask (inference router), router input gradient
+  audit("ln_bwd.x", x, B * T * D * (int64_t)elem_bytes(dt));
+  audit("ln_bwd.d_out", d_out, B * T * D * (int64_t)elem_bytes(dt));
+  audit("ln_bwd.ln2_g", p->ln2_g, (int64_t)D * 4);
+  audit("ln_bwd.ln1_g", p->ln1_g, (int64_t)D * 4);
+  audit("moe_rows.wr_train", wr_train, (int64_t)T * E * D * elem_bytes(dt));
+  audit("tr_W2.W", p->moe.w2, TE * D * He * elem_bytes(dt));
+  audit("tr_W1.W", p->moe.w1, TE * He * D * elem_bytes(dt));
   RM_TIMED("moe_rows", st, RM_HIP(rm::launch_moe_bwd_rows(w.dV, sv.Y, sv.Gt, sv.Gi, wr_train, w.dy, w.dz, w.mask, w.dSr, B, T, E, D, dt, st), "gate backward"));
   // experts, densely over the T*E groups
   RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->moe.w2, nullptr, w.W2t, nullptr, nullptr, nullptr, (int)TE, D, He, D, dt, st), "transpose W2"));
@@ -1099,7 +1251,7 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
   g1.A = w.dy; g1.a_gs = B * D; g1.a_rs = D;
   g1.W = w.W2t; g1.b_gs = (int64_t)He * D;
   g1.C = w.dH; g1.c_gs = B * He; g1.c_rs = He;
-  RM_TIMED("bwd_dH", st, RM_HIP(rm::launch_gemm(g1, st), "expert dH products"));
+  RM_TIMED("bwd_dH", st, RM_TRY(gemm_go("expert dH products", g1, st)));
   // dH and U are group-major; dU also goes out [B][T][E*He] for the dS product
   RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.Ht, w.b1p, (int)TE, B, He, Bp, dt, st, -1, -1, He, TE * He), "GELU backward"));
   RM_TIMED("tr_dy", st, RM_HIP(rm::launch_transpose(0, w.dy, nullptr, w.dyt, nullptr, nullptr, w.b2p, (int)TE, B, D, Bp, dt, st), "transpose dy"));
@@ -1109,7 +1261,7 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
   g2.A = w.dyt; g2.a_gs = (int64_t)D * Bp; g2.a_rs = Bp;
   g2.W = w.Ht; g2.b_gs = (int64_t)He * Bp;
   g2.C = g->w2; g2.c_gs = (int64_t)D * He; g2.c_rs = He;
-  RM_TIMED("bwd_dW2", st, RM_HIP(rm::launch_gemm(g2, st), "expert dW2 products"));
+  RM_TIMED("bwd_dW2", st, RM_TRY(gemm_go("expert dW2 products", g2, st)));
   RM_TIMED("tr_S", st, RM_HIP(rm::launch_transpose(0, sv.S, nullptr, w.St, nullptr, nullptr, nullptr, T, B, D, Bp, dt, st), "transpose S"));
   rm::GemmArgs g3;
   g3.dt = dt; g3.epi = rm::kEpiBiasF32;
@@ -1117,7 +1269,7 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
   g3.A = w.dUt; g3.a_gs = (int64_t)He * Bp; g3.a_rs = Bp;
   g3.W = w.St; g3.b_gs = (int64_t)D * Bp; g3.b_gdiv = E;
   g3.C = g->w1; g3.c_gs = (int64_t)He * D; g3.c_rs = D;
-  RM_TIMED("bwd_dW1", st, RM_HIP(rm::launch_gemm(g3, st), "expert dW1 products"));
+  RM_TIMED("bwd_dW1", st, RM_TRY(gemm_go("expert dW1 products", g3, st)));
   // dS from the experts: per token one product over the E experts' hidden units
   // concatenated along K (dU is [B][T][E*He], W1 per token viewed as [E*He][D])
   RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->moe.w1, nullptr, w.W1tc, nullptr, nullptr, nullptr, T, (int64_t)E * He, D, (int64_t)E * He, dt, st), "transpose W1"));
@@ -1127,7 +1279,7 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
   g4.A = w.dU; g4.a_gs = (int64_t)E * He; g4.a_rs = TE * He;
   g4.W = w.W1tc; g4.b_gs = (int64_t)D * E * He;
   g4.C = w.dSf; g4.c_gs = B * D; g4.c_rs = D;
-  RM_TIMED("bwd_dS", st, RM_HIP(rm::launch_gemm(g4, st), "expert dS products"));
+  RM_TIMED("bwd_dS", st, RM_TRY(gemm_go("expert dS products", g4, st)));
   // routers: dWr = dz^T S (training), lambda * mask^T S (inference); biases from the column sums
   RM_TIMED("tr_router", st, RM_HIP(rm::launch_transpose(0, w.dz, nullptr, w.dzt, nullptr, nullptr, w.brtp, 1, B, TE, Bp, dt, st), "transpose dz"));
   RM_TIMED("tr_router", st, RM_HIP(rm::launch_transpose(0, w.mask, nullptr, w.maskt, nullptr, nullptr, w.brip, 1, B, TE, Bp, dt, st), "transpose mask"));
@@ -1137,11 +1289,11 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
   g5.A = w.dzt; g5.a_gs = (int64_t)E * Bp; g5.a_rs = Bp;
   g5.W = w.St; g5.b_gs = (int64_t)D * Bp;
   g5.C = g->wr_train; g5.c_gs = (int64_t)E * D; g5.c_rs = D;
-  RM_TIMED("bwd_router", st, RM_HIP(rm::launch_gemm(g5, st), "training router gradient"));
+  RM_TIMED("bwd_router", st, RM_TRY(gemm_go("training router gradient", g5, st)));
   rm::GemmArgs g6 = g5;
   g6.A = w.maskt;
   g6.C = g->wr_infer;
-  RM_TIMED("bwd_router", st, RM_HIP(rm::launch_gemm(g6, st), "inference router gradient"));
+  RM_TIMED("bwd_router", st, RM_TRY(gemm_go("inference router gradient", g6, st)));
   RM_TIMED("bwd_router", st, RM_HIP(rm::launch_scale(g->wr_infer, TE * D, lambda, st), "lambda"));
   // S = LN1(TM(X) + X) with dS = dY2 + experts + training router; dX = dY1 + TM(dY1)
   RM_TIMED("ln1_bwd", st, RM_HIP(rm::launch_ln_bwd(1, nullptr, w.dV, w.dSf, x, nullptr, p->ln1_g, w.dY1, w.ln1p, B, T, D, dt, st, w.dSr), "LayerNorm 1 backward"));
@@ -1167,15 +1319,15 @@ rm_status rm_model_fwd(const rm_model_desc* m, const void* in, void* x_out, floa
   if (m->L < 0) return fail(RM_ERR_INVALID, "L=%d must not be negative", m->L);
   if (m->L > 0 && !m->blocks) return fail(RM_ERR_INVALID, "blocks is NULL");
   RM_TRY(check_shape(B, m->T, m->D, m->dtype));
-  bool any_moe = false;
+  // every block is sized from its own descriptor
   for (int l = 0; l < m->L; ++l) {
-    RM_TRY(check_block_params(&m->blocks[l], m->dtype));
-    any_moe |= m->blocks[l].kind == RM_BLOCK_MOE;
-  }
-  if (m->L > 0) RM_TRY(check_hidden(m->hidden));
-  if (any_moe) {
-    RM_TRY(check_moe_shape(B, m->T, m->E));
-    if (m->D > 4096) return fail(RM_ERR_UNSUPPORTED, "D=%d is wider than the MoE row kernels support (4096)", m->D);
+    const rm_block_params& p = m->blocks[l];
+    RM_TRY(check_block_params(&p, m->dtype));
+    if (p.hidden <= 0) return fail(RM_ERR_INVALID, "block %d: hidden=%d must be set (> 0)", l, p.hidden);
+    if (p.kind == RM_BLOCK_MOE ? p.E <= 0 : p.E != 0)
+      return fail(RM_ERR_INVALID, "block %d: E=%d (MoE blocks need E > 0, other blocks E = 0)", l, p.E);
+    const rm_status st = check_block_shape(p.kind, B, m->T, m->D, p.hidden, p.E, m->dtype);
+    if (st != RM_OK) return fail(st, "block %d: %s", l, g_last_error.c_str());
   }
   if (m->F < 0) return fail(RM_ERR_INVALID, "F must not be negative");
   if (m->F > (int64_t)m->T * m->D) return fail(RM_ERR_UNSUPPORTED, "F=%lld floats do not fit in T*D", (long long)m->F);
@@ -1195,12 +1347,13 @@ rm_status rm_model_fwd(const rm_model_desc* m, const void* in, void* x_out, floa
   hipStream_t st = (hipStream_t)stream;
   Carver c(ws);
   void* buf[2];
-  BlockWs bw;
-  model_ws(c, m, B, &buf[0], &buf[1], &bw);
+  void* blk_region;
+  model_ws(c, m, B, &buf[0], &buf[1], &blk_region);
   const int T = m->T, D = m->D, dt = m->dtype;
   const void* cur = in;
   int next = 0;
   if (m->F > 0) {
+    audit("tokenize.emb", in, B * m->F * 4);
     RM_TIMED("tokenize", st, RM_HIP(rm::launch_tokenize_padsplit((const float*)in, B, m->F, T, D, dt, buf[0], st), "tokenize"));
     cur = buf[0];
     next = 1;
@@ -1210,13 +1363,13 @@ rm_status rm_model_fwd(const rm_model_desc* m, const void* in, void* x_out, floa
   bool s_given = false;
   for (int l = 0; l < m->L; ++l) {
     void* dst = (l == m->L - 1 && x_out) ? x_out : buf[next];
-    // a block workspace sized for the largest kind; re-carve for this kind
-    Carver bc(bw.S);
+    // this block's own layout in the shared region
+    const rm_block_params& p = m->blocks[l];
+    Carver bc(blk_region);
     BlockWs w;
-    block_ws(bc, m->blocks[l].kind, B, T, D, m->hidden, m->E, dt, &w);
+    block_ws(bc, p.kind, B, T, D, p.hidden, p.E, dt, &w);
     const bool fuse = fusable_boundary(m, l);
-    RM_TRY(run_block(cur, &m->blocks[l], dst, B, T, D, m->hidden, m->E, dt, w, st, s_given,
-                     fuse ? &m->blocks[l + 1] : nullptr));
+    RM_TRY(run_block(cur, &p, dst, B, T, D, p.hidden, p.E, dt, w, st, s_given, fuse ? &m->blocks[l + 1] : nullptr));
     s_given = fuse;
     if (!fuse) {
       cur = dst;
@@ -1224,6 +1377,7 @@ rm_status rm_model_fwd(const rm_model_desc* m, const void* in, void* x_out, floa
     }
   }
   if (x_out && cur != x_out) RM_HIP(hipMemcpyAsync(x_out, cur, (size_t)B * T * D * elem_bytes(dt), hipMemcpyDeviceToDevice, st), "copy x_out");
+  audit("pool_logit.head_w", m->head_w, (int64_t)D * 4);
   if (m->head_w) RM_TIMED("pool_logit", st, RM_HIP(rm::launch_pool_logit(cur, m->head_w, m->head_c, pooled, logits, B, T, D, dt, st), "pool + logit"));
   return ok();
 }

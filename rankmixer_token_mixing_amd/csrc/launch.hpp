@@ -186,4 +186,13 @@ hipError_t launch_tokenize_project(const float* emb, const void* w, const float*
                                    int T, int seg, int D, hipStream_t s);
 int tokenize_project_max_seg();
 
+// ---- measurement probes (kernels_probe.hip) ------------------------------------
+
+// waves of one probe_mfma launch (8 per compute unit); frags holds 64 sets of
+// 16 fragments of 64 lanes x 16 bytes
+int probe_mfma_waves();
+constexpr long long kProbeFragBytes = 64LL * 16 * 64 * 16;
+hipError_t launch_probe_mfma(const void* frags, float* out, int iters, hipStream_t s);
+hipError_t launch_probe_copy(const void* src, void* dst, long long n16, hipStream_t s);
+
 }  // namespace rm

@@ -21,10 +21,10 @@ def note(msg: str) -> None:
 
 
 def ensure_lib():
+    """The built library, refusing one built from other sources than the
+    tree's (GPU runs never compile: build on the host first)."""
     from rankmixer_token_mixing_amd import binding as bd
-    if not os.path.exists(bd.lib_path()):
-        from rankmixer_token_mixing_amd.build import build
-        build()
+    bd.check_fresh()
     assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
     return bd.load()
 

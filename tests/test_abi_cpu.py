@@ -15,9 +15,10 @@ HEADER = os.path.join(ROOT, "include", "rankmixer.h")
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(bd.lib_path()):
-        from rankmixer_token_mixing_amd.build import build
+    from rankmixer_token_mixing_amd.build import build, library_is_fresh
+    if not library_is_fresh(bd.lib_path()):
         build()
+    bd.check_fresh()
     return bd.load()
 
 
@@ -118,8 +119,9 @@ def test_block_and_model_errors(lib):
     need = lib.rm_block_workspace_bytes(0, 8, 4, 64, 128, 0, bd.RM_BF16)
     assert lib.rm_block_fwd(A16, C.byref(bp), A16 * 2, 8, 4, 64, 128, 0, bd.RM_BF16, A16 * 3, need - 1,
                             None) == bd.RM_ERR_WORKSPACE
+    bp.hidden = 128
     arr = (bd.BlockParams * 1)(bp)
-    m = bd.ModelDesc(4, 64, 128, 0, bd.RM_BF16, 1, arr, 0, None, 0.0)
+    m = bd.ModelDesc(4, 64, bd.RM_BF16, 1, arr, 0, None, 0.0)
     need = lib.rm_model_workspace_bytes(C.byref(m), 8)
     assert need >= lib.rm_block_workspace_bytes(0, 8, 4, 64, 128, 0, bd.RM_BF16)
     assert lib.rm_model_fwd(C.byref(m), A16, None, None, A16 * 2, 8, A16 * 3, need, None) == bd.RM_ERR_INVALID
@@ -149,8 +151,9 @@ def test_empty_batch_is_a_no_op(lib):
     bp.ln1_g = bp.ln1_b = bp.ln2_g = bp.ln2_b = A16
     bp.pffn = _pffn()
     assert lib.rm_block_fwd(None, C.byref(bp), None, 0, 4, 64, 128, 0, bd.RM_BF16, None, 0, None) == bd.RM_OK
+    bp.hidden = 128
     arr = (bd.BlockParams * 1)(bp)
-    m = bd.ModelDesc(4, 64, 128, 0, bd.RM_BF16, 1, arr, 0, None, 0.0)
+    m = bd.ModelDesc(4, 64, bd.RM_BF16, 1, arr, 0, None, 0.0)
     assert lib.rm_model_fwd(C.byref(m), None, None, None, None, 0, None, 0, None) == bd.RM_OK
 
 

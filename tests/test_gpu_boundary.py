@@ -114,6 +114,19 @@ def test_block_without_mix_norm_breaks_the_fusion():
     _check(blocks, 200, T, D, "bf16", 3)
 
 
+@pytest.mark.parametrize("dtype,B,T,D,spec", [
+    # SwiGLU, then an MoE block with E = 4 and no Add & Norm after its mix,
+    # then an MoE block with E = 8 (heads of 19, one-element row chunks in fp32)
+    ("f32", 329, 32, 608, [("swiglu", 24, 0, False), ("moe", 24, 4, True), ("moe", 24, 8, False)]),
+    # hidden widths and expert counts that differ from block to block
+    ("bf16", 300, 8, 128, [("dense", 256, 0, False), ("swiglu", 48, 0, False), ("moe", 32, 3, False),
+                           ("moe", 64, 6, False), ("dense", 128, 0, False)]),
+])
+def test_blocks_sized_from_their_own_descriptors(dtype, B, T, D, spec):
+    blocks = [_block(k, T, D, H, dtype, 50 + i, E=E or 4, no_mix_norm=nmn) for i, (k, H, E, nmn) in enumerate(spec)]
+    _check(blocks, B, T, D, dtype, 5)
+
+
 def test_row_too_wide_for_the_boundary_pass():
     # 16 rows of 8192 bf16 do not fit in LDS: LayerNorm 2 and the next mix run
     # as separate kernels

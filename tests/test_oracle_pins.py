@@ -17,7 +17,16 @@ import torch
 from oracle import rankmixer_oracle as orc
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _torch_float64():
+    """torch references in this module compute in fp64, like the oracle; the
+    default dtype is restored for the modules after it."""
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 def _golden(name):
