@@ -123,3 +123,24 @@ def block_bwd(X, blk: dict, d_out) -> dict:
     dX = dY1 + token_mix(dY1)
     return {"dX": dX, "w1": dw1, "b1": db1, "w2": dw2, "b2": db2,
             "ln1_g": dg1, "ln1_b": db1n, "ln2_g": dg2, "ln2_b": db2n}
+
+
+def block_bwd_token(X, blk: dict, d_out, t: int) -> dict:
+    """The parameter gradients of token t alone (w1[t], b1[t], w2[t], b2[t]),
+    summed over the whole batch, from token t's own forward: S needs the whole
+    token mix of every sample, but U_t, H_t, V_t, Y2_t and LN2's backward
+    involve token t's rows only (LN2 normalises each (sample, token) row by
+    itself), so this is exact at any batch size for a fraction of
+    ``block_bwd``'s work."""
+    X = as_f64(X)
+    d_out = as_f64(d_out)
+    S = layer_norm(token_mix(X) + X, blk["ln1_g"], blk["ln1_b"])
+    S_t = S[:, t, :]
+    W1 = as_f64(blk["w1"][t])
+    W2 = as_f64(blk["w2"][t])
+    U = S_t @ W1.T + as_f64(blk["b1"][t])
+    H = gelu(U)
+    Y2 = H @ W2.T + as_f64(blk["b2"][t]) + S_t
+    dV, _, _ = layer_norm_bwd(d_out[:, t, :], Y2, blk["ln2_g"])
+    dU = (dV @ W2) * gelu_grad(U)
+    return {"w1": dU.T @ S_t, "b1": dU.sum(axis=0), "w2": dV.T @ H, "b2": dV.sum(axis=0)}

@@ -105,3 +105,51 @@ def dtsi_bwd(X, blk: dict, d_out, lam: float) -> dict:
     g["dX"] = dY1 + token_mix(dY1)
     g["ln1_g"], g["ln1_b"], g["ln2_g"], g["ln2_b"] = dg1, db1n, dg2, db2n
     return g
+
+
+def dtsi_bwd_token(X, blk: dict, d_out, lam: float, t: int, train_on=None, infer_on=None) -> dict:
+    """The parameter gradients of token t alone -- its experts (w1[t], b1[t],
+    w2[t], b2[t], all E of them), its training router (wr_train[t],
+    br_train[t]) and its inference router (wr[t], br[t]) -- summed over the
+    whole batch, from token t's own forward.  S needs every sample's whole
+    token mix; the rest involves token t's rows only (LN2 normalises each row
+    by itself), so this is exact at any batch size.
+
+    train_on / infer_on ([B, E] booleans, optional) are the ReLU decisions
+    z > 0 of the two routers for token t, for a caller that must take them in
+    another precision than this fp64 evaluation (a decision, unlike a value,
+    does not converge as the precision grows; the gates' values stay fp64).
+    Also returned: "dG" [B, E], the task loss's gradient with respect to each
+    sample's training gate of token t (what one decision adds to the router's
+    gradients, times s_t)."""
+    X = as_f64(X)
+    d_out = as_f64(d_out)
+    E = blk["w1"].shape[1]
+    S = layer_norm(token_mix(X) + X, blk["ln1_g"], blk["ln1_b"])
+    S_t = S[:, t]
+    Zt = S_t @ as_f64(blk["wr_train"][t]).T + as_f64(blk["br_train"][t])
+    Zi = S_t @ as_f64(blk["wr"][t]).T + as_f64(blk["br"][t])
+    on_t = Zt > 0 if train_on is None else np.asarray(train_on, dtype=bool)
+    on_i = Zi > 0 if infer_on is None else np.asarray(infer_on, dtype=bool)
+    Gt = np.where(on_t, Zt, 0.0)
+    U = [S_t @ as_f64(blk["w1"][t, j]).T + as_f64(blk["b1"][t, j]) for j in range(E)]
+    Yx = [gelu(U[j]) @ as_f64(blk["w2"][t, j]).T + as_f64(blk["b2"][t, j]) for j in range(E)]
+    V = sum(Gt[:, j:j + 1] * Yx[j] for j in range(E))
+    dV, _, _ = layer_norm_bwd(d_out[:, t], V + S_t, blk["ln2_g"])
+    g = {k: np.zeros(np.shape(blk[k])[1:]) for k in ("w1", "b1", "w2", "b2", "wr_train", "br_train", "wr", "br")}
+    dG = np.stack([(dV * Yx[j]).sum(axis=1) for j in range(E)], axis=1)
+    for j in range(E):
+        dy = Gt[:, j:j + 1] * dV
+        g["b2"][j] = dy.sum(axis=0)
+        g["w2"][j] = dy.T @ gelu(U[j])
+        dU = (dy @ as_f64(blk["w2"][t, j])) * gelu_grad(U[j])
+        g["b1"][j] = dU.sum(axis=0)
+        g["w1"][j] = dU.T @ S_t
+    dz = dG * on_t
+    g["br_train"] = dz.sum(axis=0)
+    g["wr_train"] = dz.T @ S_t
+    dzi = lam * on_i
+    g["br"] = dzi.sum(axis=0)
+    g["wr"] = dzi.T @ S_t
+    g["dG"] = dG
+    return g

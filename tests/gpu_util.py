@@ -52,3 +52,25 @@ def rel_l2(y, ref) -> float:
 def host(t: torch.Tensor) -> np.ndarray:
     """device tensor -> float64 numpy (exact for bf16 and fp32)."""
     return t.detach().to(torch.float64).cpu().numpy()
+
+
+def rel_l2_groups(y, ref, n_lead: int, floor: float = 0.25) -> float:
+    """max over the groups indexed by the leading n_lead axes (the token t, or
+    the (token, expert) pair) of each group's L2 error, relative to the
+    larger of the group's own norm and `floor` times the root-mean-square
+    group norm.  An error confined to one group's tile is not diluted by the
+    others; the floor keeps a group whose gradient nearly cancels (one sample,
+    a gate barely open) from being judged on the rounding of that
+    cancellation, while a wrong tile still reads as an O(1) error."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert y.shape == ref.shape, (y.shape, ref.shape)
+    k = int(np.prod(ref.shape[:n_lead]))
+    y = y.reshape(k, -1)
+    ref = ref.reshape(k, -1)
+    num = np.linalg.norm(y - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    rms = float(np.sqrt(np.mean(den * den)))
+    if rms == 0.0:
+        return 0.0 if not num.any() else float("inf")
+    return float((num / np.maximum(den, floor * rms)).max())

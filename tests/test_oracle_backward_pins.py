@@ -129,3 +129,20 @@ def test_moe_block_is_rejected():
     blk["wr"] = np.zeros((2, 2, 4))
     with pytest.raises(ValueError):
         bw.block_bwd(np.zeros((1, 2, 4)), blk, np.zeros((1, 2, 4)))
+
+
+@pytest.mark.parametrize("B,T,D,Hd,t", [(4, 3, 6, 5, 1), (3, 2, 4, 8, 0), (5, 4, 8, 6, 3)])
+def test_single_token_gradients_match_finite_differences(B, T, D, Hd, t):
+    # token t's parameter gradients over the whole batch, from token t's own
+    # forward: central differences of L = sum(d_out * X') in token t's weights,
+    # and the t-slices of the whole backward
+    rng = np.random.default_rng(40 + t)
+    X = rng.standard_normal((B, T, D))
+    blk = _block(T, D, Hd, 20 + t)
+    d_out = rng.standard_normal((B, T, D))
+    got = bw.block_bwd_token(X, blk, d_out, t)
+    full = bw.block_bwd(X, blk, d_out)
+    for k in ("w1", "b1", "w2", "b2"):
+        sl = blk[k][t]
+        np.testing.assert_allclose(got[k], _fd(lambda: _loss(X, blk, d_out), sl), rtol=1e-6, atol=1e-7, err_msg=k)
+        np.testing.assert_allclose(got[k], full[k][t], rtol=1e-12, atol=1e-12, err_msg=k)

@@ -87,3 +87,52 @@ def test_sparsity_loss_sums_the_inference_gates():
                 z = sum(blk["wr"][t, j, k] * s[k] for k in range(4)) + blk["br"][t, j]
                 total += max(0.0, z)
     assert f["l_reg"] == pytest.approx(total, rel=1e-12)
+
+
+@pytest.mark.parametrize("B,T,D,E,He,t,seed", [(3, 2, 4, 3, 5, 1, 0), (4, 3, 6, 2, 4, 0, 2)])
+def test_single_token_gradients_match_finite_differences(B, T, D, E, He, t, seed):
+    # token t's expert and router gradients over the whole batch, from token
+    # t's own forward: central differences of the task loss (experts, training
+    # router) and of lambda * L_reg (inference router), and the t-slices of
+    # the whole backward
+    rng = np.random.default_rng(seed + 30)
+    X = rng.standard_normal((B, T, D))
+    blk = _blk(T, D, E, He, seed + 3)
+    d_out = rng.standard_normal((B, T, D))
+    lam = 0.7
+    f = mt.dtsi_fwd_saved(X, blk)
+    assert np.abs(f["Zt"]).min() > 1e-3 and np.abs(f["Zi"]).min() > 1e-3
+    got = mt.dtsi_bwd_token(X, blk, d_out, lam, t)
+    full = mt.dtsi_bwd(X, blk, d_out, lam)
+    task = lambda: float((mt.dtsi_fwd_saved(X, blk)["out"] * d_out).sum())
+    reg = lambda: lam * mt.dtsi_fwd_saved(X, blk)["l_reg"]
+    for k in ("w1", "b1", "w2", "b2", "wr_train", "br_train"):
+        np.testing.assert_allclose(got[k], _fd(task, blk[k][t]), rtol=1e-6, atol=1e-7, err_msg=k)
+    for k in ("wr", "br"):
+        np.testing.assert_allclose(got[k], _fd(reg, blk[k][t]), rtol=1e-6, atol=1e-7, err_msg=k)
+    for k in got:
+        if k != "dG":
+            np.testing.assert_allclose(got[k], full[k][t], rtol=1e-12, atol=1e-12, err_msg=k)
+
+
+def test_single_token_gate_gradient_matches_finite_differences():
+    # dG[b, j] = d L_task / d G_train[b, t, j]: with one sample in the batch a
+    # shift of br_train[t, j] moves that one gate by the same amount while it
+    # is on, so central differences in br_train give dG wherever z > 0; a
+    # large training-router bias switches every gate on
+    B, T, D, E, He, t = 3, 2, 6, 3, 4, 1
+    rng = np.random.default_rng(41)
+    X = rng.standard_normal((B, T, D))
+    d_out = rng.standard_normal((B, T, D))
+    for shift in (0.0, 10.0):
+        blk = _blk(T, D, E, He, 7)
+        blk["br_train"] = blk["br_train"] + shift
+        dG = mt.dtsi_bwd_token(X, blk, d_out, 0.3, t)["dG"]
+        zt = mt.dtsi_fwd_saved(X, blk)["Zt"][:, t]
+        assert np.abs(zt).min() > 1e-3
+        if shift:
+            assert (zt > 0).all()
+        for b in range(B):
+            task = lambda: float((mt.dtsi_fwd_saved(X[b:b + 1], blk)["out"] * d_out[b:b + 1]).sum())
+            fd = _fd(task, blk["br_train"][t])
+            np.testing.assert_allclose(fd, dG[b] * (zt[b] > 0), rtol=1e-6, atol=1e-7)
