@@ -611,6 +611,71 @@ def bench_variants(args) -> int:
     return 0
 
 
+def bench_epilogue_overlap(args) -> int:
+    """The two epilogue modes of the bf16 products (rm_set_epilogue_overlap)
+    on the per-token FFN of block 0 of the ~1B-class workload (B=1024, T=32,
+    D=1536, hidden 6144): rm_pffn_fwd with the epilogue after each tile (0,
+    the default) and inside the next tile's main loop (1), alternated over
+    several rounds so box drift hits both; per-launch HIP events give the W1
+    product (bias + GELU) and the W2 product (bias) apart."""
+    import torch
+    import synthetic_inputs as si
+    from rankmixer_token_mixing_amd import binding as bd
+    from rankmixer_token_mixing_amd import perfmodel as pm
+
+    cfg = si.CONFIGS["c3"]
+    B, T, D = cfg.B, cfg.T, cfg.D
+    Hd = cfg.hidden
+    blk = bd.upload_blocks([si.make_inputs(si.scaled(cfg, L=1))["blocks"][0]])[0]
+    p = {k: blk[k] for k in ("w1", "b1", "w2", "b2")}
+    g = torch.Generator(device="cuda").manual_seed(5)
+    s = torch.randn(B, T, D, device="cuda", generator=g).to(torch.bfloat16)  # LayerNorm-scaled operand
+    out = torch.empty_like(s)
+    flop = {"ffn1": T * pm.gemm_flops(B, Hd, D), "ffn2": T * pm.gemm_flops(B, D, Hd)}
+    acc = {m: {"ffn1": [0.0, 0], "ffn2": [0.0, 0]} for m in (0, 1)}
+    rounds = 4
+    for r in range(rounds):
+        for mode in (0, 1):
+            bd.set_epilogue_overlap(bool(mode))
+            for _ in range(args.warmup):
+                bd.rm_pffn_fwd(s, p, out=out)
+            torch.cuda.synchronize()
+            bd.profile_enable(True)
+            for _ in range(args.steps):
+                bd.rm_pffn_fwd(s, p, out=out)
+            torch.cuda.synchronize()
+            prof = bd.profile_read()
+            bd.profile_enable(False)
+            for k in ("ffn1", "ffn2"):
+                acc[mode][k][0] += prof[k][0]
+                acc[mode][k][1] += prof[k][1]
+        log(f"round {r + 1}/{rounds} done")
+    bd.set_epilogue_overlap(False)
+    res = {}
+    for mode, name in ((0, "after_tile"), (1, "overlapped")):
+        res[name] = {}
+        for k in ("ffn1", "ffn2"):
+            ms = acc[mode][k][0] / acc[mode][k][1]
+            tf = flop[k] / (ms * 1e-3) / 1e12
+            res[name][k] = {"avg_ms": round(ms, 5), "launches": acc[mode][k][1], "tflops": round(tf, 1),
+                            "frac": round(tf / pm.PEAK_BF16_TFLOPS, 4)}
+    base = res["after_tile"]["ffn1"]
+    rec = {
+        "metric": "W1 product TFLOP/s (bias + GELU epilogue), per-token FFN of block 0, bf16",
+        "value": base["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(base["avg_ms"], 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"rm_pffn_fwd B={B}, T={T}, D={D}, hidden {Hd}, bf16, both epilogue modes",
+                   "B": B, "T": T, "D": D, "hidden": Hd, "rounds": rounds},
+        "modes": res,
+        "overlapped_over_after_tile": {k: round(res["after_tile"][k]["avg_ms"] / res["overlapped"][k]["avg_ms"], 4)
+                                       for k in ("ffn1", "ffn2")},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -618,14 +683,17 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", help="workload (c3 is the benchmarked one)")
     ap.add_argument("--op", default="model",
-                    choices=["model", "tokenize_project", "block_bwd", "block_variants", "moe_train", "ceilings"],
+                    choices=["model", "tokenize_project", "block_bwd", "block_variants", "moe_train", "ceilings",
+                             "epilogue_overlap"],
                     help="model: the block stack (default); tokenize_project: the projection "
                          "tokenizer alone on the pad-split model's embedding; block_bwd: the dense "
                          "block backward on block 0 of the workload; block_variants: the SwiGLU "
                          "(D -> 4/3 D) block beside the GELU FFN (D -> 2D) block of equal parameters and "
                          "flops, with and without the Add & Norm after the mix; moe_train: training "
                          "step of the MoE block with dense-training / sparse-inference routers; "
-                         "ceilings: the MFMA-loop and HBM-copy probes alone")
+                         "ceilings: the MFMA-loop and HBM-copy probes alone; epilogue_overlap: the W1 "
+                         "and W2 products of block 0 with the epilogue after each tile and inside the "
+                         "next tile's main loop")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the probes after the timed steps")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="samples in the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -675,6 +743,8 @@ def main() -> int:
         return bench_moe_train(args)
     if args.op == "ceilings":
         return bench_ceilings(args)
+    if args.op == "epilogue_overlap":
+        return bench_epilogue_overlap(args)
 
     cfg = si.CONFIGS[args.config]
     t0 = time.perf_counter()

@@ -378,6 +378,25 @@ double rm_probe_mfma_flop(int iters);
 rm_status rm_probe_mfma_bf16(const void* frags, float* out, int iters, void* stream);
 rm_status rm_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
+/* How the bf16 grouped products finish a tile (bias, GELU, packing to bf16,
+ * stores).  0 (the default): after the tile's main loop, by every wave of the
+ * workgroup.  1: inside the next tile's main loop, four output values per
+ * MFMA k-step, so the epilogue's ALU work and stores issue while the matrix
+ * cores run (a deferred epilogue), for the products that qualify: dense
+ * operands, a bias, bias + GELU or bias + GELU keeping the pre-activation
+ * epilogue, K a multiple of 64 and at least 1024, M and N at least 256, edge
+ * tiles that recompute at most 1/8 of the area; the others run as with 0.
+ * Both modes compute the same products within bf16 output rounding (mode 1
+ * adds the bias at the end of the tile, mode 0 starts from it).  Applies to
+ * launches made after the call, process-wide.  Measured on MI355X the
+ * deferred epilogue is slower (the products are power-limited, and overlap
+ * does not lower a tile's energy), so 0 stays the default; mode 1 is kept
+ * for measurement (bench.py --op epilogue_overlap).
+ * Errors: on not 0 or 1 -> RM_ERR_INVALID.  rm_get_epilogue_overlap returns
+ * the current mode. */
+rm_status rm_set_epilogue_overlap(int on);
+int rm_get_epilogue_overlap(void);
+
 /* Host-side audit of what the launches would read (needs no GPU).  While
  * enabled (rm_audit_enable(1), per process), every entry point checks its
  * arguments as usual but enqueues nothing; instead, for each launch it would

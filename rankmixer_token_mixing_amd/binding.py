@@ -106,6 +106,8 @@ _SIGNATURES = {
     "rm_probe_mfma_flop": (C.c_double, [_int]),
     "rm_probe_mfma_bf16": (_int, [_vp, _vp, _int, _vp]),
     "rm_probe_copy": (_int, [_vp, _vp, _sz, _vp]),
+    "rm_set_epilogue_overlap": (_int, [_int]),
+    "rm_get_epilogue_overlap": (_int, []),
     "rm_audit_enable": (_int, [_int]),
     "rm_audit_count": (_int, []),
     "rm_audit_read": (_int, [_int, C.c_char_p, _sz, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]),
@@ -486,6 +488,15 @@ def probe_mfma_bf16(frags: torch.Tensor, out: torch.Tensor, iters: int) -> None:
 
 def probe_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int) -> None:
     _check(load().rm_probe_copy(_p(src), _p(dst), nbytes, _stream(src.device)))
+
+
+def set_epilogue_overlap(on: bool) -> None:
+    """The bf16 products' epilogue mode (rm_set_epilogue_overlap)."""
+    _check(load().rm_set_epilogue_overlap(1 if on else 0))
+
+
+def get_epilogue_overlap() -> bool:
+    return bool(load().rm_get_epilogue_overlap())
 
 
 def profile_enable(on: bool = True) -> None:

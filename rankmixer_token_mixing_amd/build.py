@@ -20,7 +20,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librankmixer.so")
-SOURCES = ["abi.cpp", "kernels_rows.hip", "kernels_moe.hip", "kernels_gemm.hip", "kernels_tokproj.hip", "kernels_bwd.hip", "kernels_variants.hip", "kernels_moe_train.hip", "kernels_probe.hip"]
+SOURCES = ["abi.cpp", "kernels_rows.hip", "kernels_moe.hip", "kernels_gemm.hip", "kernels_tokproj.hip", "kernels_bwd.hip", "kernels_variants.hip", "kernels_moe_train.hip", "kernels_probe.hip",
+           "kernels_gemm_defer.hip"]
 ARCH = os.environ.get("RM_OFFLOAD_ARCH", "gfx950")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in the device code
@@ -34,7 +35,7 @@ def source_hash() -> str:
     """sha256 (first 16 hex digits) of every C/C++/HIP source and header the
     library is built from; the build bakes it into rm_version()."""
     root = os.path.dirname(PKG)
-    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp", ".hpp")))
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp", ".hpp", ".inc")))
     files.append(os.path.join(root, "include", "rankmixer.h"))
     h = hashlib.sha256()
     for f in files:
@@ -60,9 +61,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librankmixer.so)")
 
 
+# per-source flags: the deferred-epilogue GEMM keeps its accumulators in AGPRs
+# that only its inline asm names, so the compiler must never spill into AGPRs
+EXTRA_FLAGS = {"kernels_gemm_defer.hip": ["-mllvm", "-amdgpu-spill-vgpr-to-agpr=0"]}
+
+
 def _compile(src: str, src_hash: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, f'-DRM_SRC_HASH="{src_hash}"', "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), f'-DRM_SRC_HASH="{src_hash}"', "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

@@ -542,6 +542,14 @@ rm_status rm_probe_copy(const void* src, void* dst, size_t bytes, void* stream) 
   return ok();
 }
 
+rm_status rm_set_epilogue_overlap(int on) {
+  if (on != 0 && on != 1) return fail(RM_ERR_INVALID, "epilogue overlap mode must be 0 or 1 (%d)", on);
+  rm::set_epilogue_overlap(on);
+  return ok();
+}
+
+int rm_get_epilogue_overlap(void) { return rm::epilogue_overlap() ? 1 : 0; }
+
 int rm_audit_enable(int on) {
   std::lock_guard<std::mutex> lk(g_audit_mu);
   g_audit_recs.clear();

@@ -24,4 +24,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
 }
 
+// one LDS DMA op on its own: 64 lanes x 16 bytes from sb + voff (per lane)
+// into LDS at m0v (prologues)
+__device__ __forceinline__ void dma1(uint32_t m0v, const void* sb, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v], %[sb]\n\t"
+               :
+               : [m] "s"(m0v), [sb] "s"(sb), [v] "v"(voff)
+               : "m0");
+}
+
 }  // namespace rm

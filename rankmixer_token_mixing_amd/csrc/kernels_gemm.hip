@@ -613,14 +613,6 @@ __device__ __forceinline__ void read_frags(Frags& nx, uint32_t la, uint32_t lb) 
                : [la] "v"(la), [lb] "v"(lb));
 }
 
-// one DMA op on its own (prologue)
-__device__ __forceinline__ void dma1(uint32_t m0v, const void* sb, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v], %[sb]\n\t"
-               :
-               : [m] "s"(m0v), [sb] "s"(sb), [v] "v"(voff)
-               : "m0");
-}
-
 // Start value of the pipelined kernel's accumulators: the bias of each
 // accumulator's column (zero without bias), so the epilogue adds nothing.
 // Register 4q+e of block (i, j) holds column wn*FN*32 + j*32 + 8q + 4lh + e
@@ -1144,6 +1136,7 @@ bool gemm_pipe_eligible(const GemmArgs& a) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.w_kmajor) return gemm_wt_eligible(a) ? launch_cfg<2, 4, 4, 2>(a, s) : hipErrorInvalidValue;
+  if (epilogue_overlap() && gemm_defer_eligible(a)) return launch_gemm_defer(a, s);
   switch (choose_cfg(a)) {
     case 0: return launch_cfg<2, 4, 4, 2>(a, s);
     case 1: return launch_cfg<2, 2, 4, 2>(a, s);

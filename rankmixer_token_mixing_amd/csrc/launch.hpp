@@ -117,7 +117,17 @@ struct GemmArgs {
 int gemm_tile_m(const GemmArgs& a);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // whether launch_gemm would run `a` on the hand-scheduled pipelined kernel
+// (the ring kernel with the epilogue after each tile, or the deferred-epilogue
+// kernel)
 bool gemm_pipe_eligible(const GemmArgs& a);
+// the deferred-epilogue kernel (kernels_gemm_defer.hip): bf16, dense, bias /
+// bias + GELU / both, K a multiple of 64 and at least 1024, M and N at least
+// 256; launch_gemm takes it for those when the epilogue-overlap mode is on
+bool gemm_defer_eligible(const GemmArgs& a);
+// the epilogue-overlap mode (process-wide, off by default)
+void set_epilogue_overlap(int on);
+bool epilogue_overlap();
+hipError_t launch_gemm_defer(const GemmArgs& a, hipStream_t s);
 // whether launch_gemm takes `a` with a K-major W (w_kmajor)
 bool gemm_wt_eligible(const GemmArgs& a);
 

@@ -299,3 +299,26 @@ def test_moe_training_entry_points_check_their_arguments(lib):
     g.wr_infer = None
     assert bwd(A16 * 10, C.byref(g), ws) == bd.RM_ERR_INVALID
     assert "grads.wr_infer" in err(lib)
+
+
+def test_epilogue_overlap_mode(lib):
+    assert lib.rm_get_epilogue_overlap() == 0  # the default
+    assert lib.rm_set_epilogue_overlap(2) == bd.RM_ERR_INVALID
+    assert "0 or 1" in err(lib)
+    try:
+        assert lib.rm_set_epilogue_overlap(1) == 0
+        assert lib.rm_get_epilogue_overlap() == 1
+    finally:
+        lib.rm_set_epilogue_overlap(0)
+    assert lib.rm_get_epilogue_overlap() == 0
+
+
+def test_generated_kstep_bodies_are_current():
+    # the committed inline-asm k-steps are what their generator writes
+    import importlib.util
+    path = os.path.join(ROOT, "rankmixer_token_mixing_amd", "csrc", "gemm_defer_gen.py")
+    spec = importlib.util.spec_from_file_location("gemm_defer_gen", path)
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    with open(os.path.join(ROOT, "rankmixer_token_mixing_amd", "csrc", "gemm_defer_kstep.inc")) as f:
+        assert f.read() == gen.render()
