@@ -33,8 +33,10 @@
  *    Larger shapes are RM_ERR_UNSUPPORTED.
  *  - The caller owns every buffer, including the workspace `ws`, sized with
  *    the matching rm_*_workspace_bytes call.  The library never allocates,
- *    frees or synchronises; work is enqueued on `stream` (a hipStream_t, NULL
- *    for the default stream) and is complete when that stream is.
+ *    frees or synchronises (its one fixed device array, the scratch of
+ *    rm_moe_route_noalloc, is part of its code object); work is enqueued on
+ *    `stream` (a hipStream_t, NULL for the default stream) and is complete
+ *    when that stream is.
  *  - Outputs must not alias inputs.
  *  - Results are deterministic: two calls with the same inputs give the same
  *    bits (no floating-point atomics anywhere).
@@ -217,6 +219,26 @@ size_t rm_moe_workspace_bytes(int64_t B, int T, int D, int E, int He, int dtype)
 rm_status rm_moe_route(const void* s, const void* wr, const float* br, float* gates, int* offsets,
                        int* rows, int64_t B, int T, int D, int E, int dtype, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* rm_moe_route without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, outputs and errors as rm_moe_route,
+ * minus ws / ws_bytes: its scratch (per-list counts, the tile list, the
+ * compacted gates and the entry map) lives in one fixed device array of
+ * rm_moe_route_noalloc_max_scratch_bytes() = 16 MiB that the library holds
+ * on each device it runs on until the process ends.  A call needs
+ * rm_moe_route_noalloc_scratch_bytes(B, T, E) of it (about 8 bytes per
+ * (sample, token, expert) entry: B*T*E up to about 2 million); larger calls
+ * -> RM_ERR_UNSUPPORTED.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine); its first call on a device looks up that
+ * device's copy of the array.  Every call on a device shares the array:
+ * calls that overlap on one device (two streams, two threads) race and must
+ * be ordered by the caller.  Nothing in the array needs clearing between
+ * calls (each call writes every element it reads). */
+size_t rm_moe_route_noalloc_scratch_bytes(int64_t B, int T, int E);
+size_t rm_moe_route_noalloc_max_scratch_bytes(void);
+rm_status rm_moe_route_noalloc(const void* s, const void* wr, const float* br, float* gates, int* offsets,
+                               int* rows, int64_t B, int T, int D, int E, int dtype, void* stream);
 
 /* One block: x_out = LN2(F(S) + S), S = LN1(TokenMix(x) + x).
  *   x, x_out: [B][T][D] dtype device.  hidden = Hd (dense) or He (MoE);

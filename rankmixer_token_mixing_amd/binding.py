@@ -106,6 +106,9 @@ _SIGNATURES = {
     "rm_probe_mfma_flop": (C.c_double, [_int]),
     "rm_probe_mfma_bf16": (_int, [_vp, _vp, _int, _vp]),
     "rm_probe_copy": (_int, [_vp, _vp, _sz, _vp]),
+    "rm_moe_route_noalloc_scratch_bytes": (_sz, [_i64, _int, _int]),
+    "rm_moe_route_noalloc_max_scratch_bytes": (_sz, []),
+    "rm_moe_route_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _int, _int, _int, _int, _vp]),
     "rm_set_epilogue_overlap": (_int, [_int]),
     "rm_get_epilogue_overlap": (_int, []),
     "rm_audit_enable": (_int, [_int]),
@@ -340,6 +343,16 @@ def rm_moe_route(s: torch.Tensor, wr: torch.Tensor, br: torch.Tensor):
     _check(lib.rm_moe_route(_p(s), _p(wr), _p(br), _p(gates), _p(offsets), _p(rows), B, T, D, E, _dt(s), _p(ws),
                             ws.numel(), _stream(s.device)))
     return gates, offsets, rows
+
+
+def rm_moe_route_noalloc(s: torch.Tensor, wr: torch.Tensor, br: torch.Tensor, gates: torch.Tensor,
+                         offsets: torch.Tensor, rows: torch.Tensor) -> None:
+    """rm_moe_route into caller-allocated outputs (gates [B,T,E] fp32, offsets
+    [T*E+1] int32, rows [B*T*E] int32) with the library's fixed scratch."""
+    B, T, D = s.shape
+    E = wr.shape[1]
+    _check(load().rm_moe_route_noalloc(_p(s), _p(wr), _p(br), _p(gates), _p(offsets), _p(rows), B, T, D, E, _dt(s),
+                                       _stream(s.device)))
 
 
 def rm_block_fwd(x: torch.Tensor, p: dict, out: Optional[torch.Tensor] = None) -> torch.Tensor:

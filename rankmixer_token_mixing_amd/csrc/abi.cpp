@@ -775,6 +775,87 @@ rm_status rm_moe_route(const void* s, const void* wr, const float* br, float* ga
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// rm_moe_route_noalloc: the routing step with its scratch (per-list counts,
+// the tile list and its length, the compacted gates and the (b, t, j) ->
+// entry map) in a fixed device array instead of a caller workspace.  Every
+// scratch element the call reads is written earlier in the same call, so
+// nothing is cleared between calls.
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;  // device -> that device's copy of `scratch`
+
+// the current device's address of `scratch`, looked up once per device
+rm_status scratch_base(void** out) {
+  int dev = -1;
+  RM_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* p = nullptr;
+    RM_TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    it = g_scratch_ptr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return RM_OK;
+}
+
+size_t route_scratch(Carver& c, int64_t B, int T, int E, rm::MoeWork* w) {
+  const int64_t G = (int64_t)T * E;
+  const int64_t nmax = B * G;
+  rm::MoeWork x{};
+  x.counts = (int*)c.take(G * 4);
+  x.ntiles = (int*)c.take(4);
+  x.tiles = (int*)c.take((size_t)(G * ((B + kMoeTileM - 1) / kMoeTileM)) * 2 * 4);
+  x.gatec = (float*)c.take(nmax * 4);
+  x.pos = (int*)c.take(nmax * 4);
+  if (w) *w = x;
+  return c.off;
+}
+
+}  // namespace
+
+size_t rm_moe_route_noalloc_scratch_bytes(int64_t B, int T, int E) {
+  if (B < 0 || T <= 0 || E <= 0) return 0;
+  Carver c(nullptr);
+  return route_scratch(c, B, T, E, nullptr);
+}
+
+size_t rm_moe_route_noalloc_max_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+rm_status rm_moe_route_noalloc(const void* s, const void* wr, const float* br, float* gates, int* offsets, int* rows,
+                               int64_t B, int T, int D, int E, int dtype, void* stream) {
+  RM_TRY(check_ffn_shape(B, T, D, dtype));
+  RM_TRY(check_moe_shape(B, T, E));
+  if (B == 0) return ok();
+  RM_TRY(check_ptr(s, "s")); RM_TRY(check_ptr(wr, "wr")); RM_TRY(check_ptr(br, "br"));
+  RM_TRY(check_ptr(gates, "gates")); RM_TRY(check_ptr(offsets, "offsets")); RM_TRY(check_ptr(rows, "rows"));
+  const size_t need = rm_moe_route_noalloc_scratch_bytes(B, T, E);
+  if (need > kNoAllocScratchBytes)
+    return fail(RM_ERR_UNSUPPORTED, "B*T*E = %lld needs %zu bytes of scratch, more than the fixed %zu",
+                (long long)(B * T * E), need, kNoAllocScratchBytes);
+  void* base = nullptr;
+  if (!auditing()) RM_TRY(scratch_base(&base));
+  Carver c(base);
+  rm::MoeWork w;
+  route_scratch(c, B, T, E, &w);
+  w.gates = gates;
+  w.offsets = offsets;
+  w.rows = rows;
+  hipStream_t st = (hipStream_t)stream;
+  audit("moe_router.s", s, B * T * D * (int64_t)elem_bytes(dtype));
+  audit("moe_router.wr", wr, (int64_t)T * E * D * elem_bytes(dtype));
+  audit("moe_router.br", br, (int64_t)T * E * 4);
+  RM_HIP(rm::launch_moe_router(s, (int64_t)T * D, D, wr, br, gates, B, T, D, E, dtype, st), "moe router");
+  RM_HIP(rm::launch_moe_compact(w, B, T, E, kMoeTileM, st), "moe compaction");
+  return ok();
+}
+
 size_t rm_block_workspace_bytes(int kind, int64_t B, int T, int D, int hidden, int E, int dtype) {
   Carver c(nullptr);
   return block_ws(c, kind, B, T, D, hidden, E, dtype, nullptr);

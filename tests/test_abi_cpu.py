@@ -322,3 +322,18 @@ def test_generated_kstep_bodies_are_current():
     spec.loader.exec_module(gen)
     with open(os.path.join(ROOT, "rankmixer_token_mixing_amd", "csrc", "gemm_defer_kstep.inc")) as f:
         assert f.read() == gen.render()
+
+
+def test_noalloc_route_refuses_more_than_its_scratch(lib):
+    # the size check runs on the host before the device is touched
+    assert lib.rm_moe_route_noalloc_max_scratch_bytes() == 16 << 20
+    B, T, E = 40000, 16, 8  # 5.1 M (sample, token, expert) entries
+    assert lib.rm_moe_route_noalloc_scratch_bytes(B, T, E) > lib.rm_moe_route_noalloc_max_scratch_bytes()
+    assert lib.rm_moe_route_noalloc_scratch_bytes(2048, 16, 8) < 3 << 20
+    st = lib.rm_moe_route_noalloc(A16, A16, A16, A16, A16, A16, B, T, 64, E, bd.RM_BF16, None)
+    assert st == bd.RM_ERR_UNSUPPORTED
+    assert "scratch" in err(lib)
+    # and it checks its arguments like rm_moe_route
+    assert lib.rm_moe_route_noalloc(None, A16, A16, A16, A16, A16, 4, 2, 64, 4, bd.RM_BF16, None) == bd.RM_ERR_INVALID
+    assert lib.rm_moe_route_noalloc(A16, A16, A16, A16, A16, A16, 4, 2, 64, 33, bd.RM_BF16, None) == \
+        bd.RM_ERR_UNSUPPORTED
