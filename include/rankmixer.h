@@ -263,7 +263,8 @@ size_t rm_model_workspace_bytes(const rm_model_desc* m, int64_t B);
 
 /* Dense block training forward: the forward of rm_block_fwd, which also keeps
  * what rm_block_bwd needs in the caller's `saved` buffer (S, the W1 product +
- * b1 before GELU, the W2 product + b2; size rm_block_saved_bytes).  The output
+ * b1 before GELU, its GELU, the W2 product + b2; size rm_block_saved_bytes).
+ * The output
  * equals rm_block_fwd's up to the rounding of the GELU input to dtype.
  *   Workspace: rm_block_workspace_bytes(RM_BLOCK_DENSE, B, T, D, hidden, 0, dtype).
  * Errors: a block that is not DENSE or has flags, D > 4096 -> RM_ERR_UNSUPPORTED
@@ -284,9 +285,13 @@ rm_status rm_block_fwd_train(const void* x, const rm_block_params* p, void* x_ou
  * with LNbwd(g) = (g*gamma - mean(g*gamma) - xhat * mean(g*gamma*xhat)) / sigma.
  *   x: the block input [B][T][D] dtype; saved: from rm_block_fwd_train on the
  *   same x and params; d_out, dx: [B][T][D] dtype; g: gradients (fp32).
- * Products run in dtype with fp32 accumulation (bf16: dV, dH, dU rounded to
- * bf16); sums over the batch and over rows run in a fixed order, so results
- * are deterministic.  B = 0 writes zero gradients.
+ * Products run in dtype with fp32 accumulation (bf16: dV and dU rounded to
+ * bf16, and dH too where it is stored); sums over the batch and over rows run
+ * in a fixed order, so results are deterministic.  bf16 with B a multiple of
+ * 64 and D, hidden >= 256: the dH product applies GELU' in its epilogue (dH is
+ * never stored) and the batch-contracting products read their operands as
+ * stored; otherwise they read transposed copies.  B = 0 writes zero
+ * gradients.
  *   Workspace: rm_block_bwd_workspace_bytes(B, T, D, hidden, dtype).
  * Errors: as rm_block_fwd_train; dx aliasing x or d_out -> RM_ERR_INVALID. */
 size_t rm_block_bwd_workspace_bytes(int64_t B, int T, int D, int hidden, int dtype);

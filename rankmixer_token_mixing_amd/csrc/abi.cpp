@@ -187,7 +187,8 @@ rm_status gemm_go(const char* name, const rm::GemmArgs& a, hipStream_t st) {
     const int64_t e = elem_bytes(a.dt);
     const int64_t arows = a.row_off && !a.a_rowidx ? (int64_t)a.M * a.G : a.M;
     const std::string n(name);
-    audit(n + ".A", a.A, (((int64_t)(a.G - 1) / a.a_gdiv) * a.a_gs + (arows - 1) * a.a_rs + a.K) * e);
+    const int64_t a_ext = a.a_kmajor ? ((int64_t)a.K - 1) * a.a_rs + a.M : (arows - 1) * a.a_rs + a.K;
+    audit(n + ".A", a.A, (((int64_t)(a.G - 1) / a.a_gdiv) * a.a_gs + a_ext) * e);
     audit(n + ".W", a.W, (((int64_t)(a.G - 1) / a.b_gdiv) * a.b_gs + (int64_t)a.N * a.K) * e);
     if (a.bias) audit(n + ".bias", a.bias, ((int64_t)(a.G - 1) * a.bias_gs + a.N) * 4);
     return RM_OK;
@@ -888,14 +889,16 @@ namespace {
 // W1 product + b1 before GELU, token-major [T][B][Hd]) and Z (the W2 product +
 // b2, [B][T][D])
 struct Saved {
-  void* S;
-  void* U;
-  void* Z;
+  void* S;  // [T][B][D] token-major
+  void* U;  // [T][B][Hd] W1 product + b1
+  void* H;  // [T][B][Hd] GELU(U)
+  void* Z;  // [T][B][D] W2 product + b2
 };
 size_t saved_carve(Carver& c, int64_t B, int T, int D, int Hd, int dt, Saved* w) {
   Saved x;
   x.S = c.take((size_t)B * T * D * elem_bytes(dt));
   x.U = c.take((size_t)B * T * Hd * elem_bytes(dt));
+  x.H = c.take((size_t)B * T * Hd * elem_bytes(dt));
   x.Z = c.take((size_t)B * T * D * elem_bytes(dt));
   if (w) *w = x;
   return c.off;
@@ -905,16 +908,67 @@ int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
 
 // workspace of the backward; the K = batch products read the transposed
 // activations with rows padded to Bp = B rounded up to 64 (zero tail)
+// The products of the dense backward.  dH = dV W2 reads W2_t [D][Hd] as a
+// K-major W; with kmajor (below) its epilogue also applies GELU'(U) and
+// writes dU plus the b1 partial sums.  dW2 = dV^T H and dW1 = dU^T S
+// contract over the batch: with kmajor both operands are read as they are
+// (token-major [B][.] per token = K-major), else from transposes padded to
+// Bp rows.
+rm::GemmArgs bwd_dH_args(const void* dV, const void* w2, void* C, int64_t B, int T, int D, int Hd, int dt) {
+  rm::GemmArgs g;
+  g.dt = dt; g.epi = rm::kEpiBias;
+  g.M = (int)B; g.N = Hd; g.K = D; g.G = T;
+  g.A = dV; g.a_gs = B * D; g.a_rs = D;
+  g.W = w2; g.b_gs = (int64_t)Hd * D; g.w_kmajor = 1;
+  g.C = C; g.c_gs = B * Hd; g.c_rs = Hd;
+  return g;
+}
+rm::GemmArgs bwd_dW_args(const void* A, int M, const void* W, int N, void* C, int64_t B, int T, int dt) {
+  rm::GemmArgs g;
+  g.dt = dt; g.epi = rm::kEpiBiasF32;
+  g.M = M; g.N = N; g.K = (int)B; g.G = T;
+  g.A = A; g.a_gs = B * M; g.a_rs = M; g.a_kmajor = 1;
+  g.W = W; g.b_gs = B * N; g.w_kmajor = 1;
+  g.C = C; g.c_gs = (int64_t)M * N; g.c_rs = N;
+  return g;
+}
+// whether the backward runs without transposes (a shape property)
+bool bwd_kmajor(int64_t B, int T, int D, int Hd, int dt) {
+  rm::GemmArgs h = bwd_dH_args(nullptr, nullptr, nullptr, B, T, D, Hd, dt);
+  h.epi = rm::kEpiGeluBwd;
+  return rm::gemm_kmajor_eligible(h) && rm::gemm_kmajor_eligible(bwd_dW_args(nullptr, D, nullptr, Hd, nullptr, B, T, dt)) &&
+         rm::gemm_kmajor_eligible(bwd_dW_args(nullptr, Hd, nullptr, D, nullptr, B, T, dt));
+}
+
 struct BwdWs {
+  bool km;  // bwd_kmajor
   void *dV, *dVt, *W2t, *dH, *dU, *dUt, *Ht, *St, *W1t;
   float *dSf, *dY1, *ln2p, *ln1p, *b2p, *b1p;
+  int b2_parts, b1_parts;  // partial sums per token of b2, b1
 };
 size_t bwd_carve(Carver& c, int64_t B, int T, int D, int Hd, int dt, BwdWs* w) {
   const size_t e = elem_bytes(dt);
   const int64_t Bp = pad64(B);
   const int64_t rt = rm::transpose_row_tiles(B, Bp);
   const int lg = rm::ln_bwd_grid(B, T, D);
-  BwdWs x;
+  BwdWs x{};
+  x.km = bwd_kmajor(B, T, D, Hd, dt);
+  if (x.km) {
+    x.b2_parts = rm::colsum64_parts(B);
+    x.b1_parts = rm::gemm_colsum_parts((int)B);
+    x.dV = c.take((size_t)T * B * D * e);
+    x.dU = c.take((size_t)T * B * Hd * e);
+    x.W1t = c.take((size_t)T * D * Hd * e);
+    x.dSf = (float*)c.take((size_t)T * B * D * 4);
+    x.dY1 = (float*)c.take((size_t)B * T * D * 4);
+    x.ln2p = (float*)c.take((size_t)lg * 2 * D * 4);
+    x.ln1p = (float*)c.take((size_t)lg * 2 * D * 4);
+    x.b2p = (float*)c.take((size_t)T * x.b2_parts * D * 4);
+    x.b1p = (float*)c.take((size_t)T * x.b1_parts * Hd * 4);
+    if (w) *w = x;
+    return c.off;
+  }
+  x.b2_parts = x.b1_parts = (int)rt;
   x.dV = c.take((size_t)T * B * D * e);
   x.dVt = c.take((size_t)T * D * Bp * e);
   x.W2t = c.take((size_t)T * Hd * D * e);
@@ -984,15 +1038,15 @@ rm_status rm_block_fwd_train(const void* x, const rm_block_params* p, void* x_ou
   // epilogue on the pipelined kernel, else a separate GELU pass
   rm::GemmArgs a1 = ffn1_args(sv.S, sb, sT, &p->pffn, sv.U, B, T, D, hidden, dtype);
   a1.epi = rm::kEpiBiasGeluDual;
-  a1.C2 = w.pffn.H;
+  a1.C2 = sv.H;
   if (rm::gemm_pipe_eligible(a1)) {
     RM_TIMED("ffn1", st, RM_TRY(gemm_go("block W1 product + GELU", a1, st)));
   } else {
     a1.epi = rm::kEpiBias;
     RM_TIMED("ffn1", st, RM_TRY(gemm_go("block W1 product", a1, st)));
-    RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.pffn.H, B * T * (int64_t)hidden, dtype, st), "GELU"));
+    RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, sv.H, B * T * (int64_t)hidden, dtype, st), "GELU"));
   }
-  rm::GemmArgs a2 = ffn2_args(w.pffn.H, &p->pffn, B, T, D, hidden, dtype);
+  rm::GemmArgs a2 = ffn2_args(sv.H, &p->pffn, B, T, D, hidden, dtype);
   a2.epi = rm::kEpiBias;
   a2.C = sv.Z;
   RM_TIMED("ffn2", st, RM_TRY(gemm_go("block W2 product", a2, st)));
@@ -1042,7 +1096,6 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   bwd_carve(c, B, T, D, hidden, dtype, &w);
   const int dt = dtype;
   const int64_t Bp = pad64(B);
-  const int rt = rm::transpose_row_tiles(B, Bp);
   const int lg = rm::ln_bwd_grid(B, T, D);
   audit("ln_bwd.x", x, B * T * D * (int64_t)elem_bytes(dt));
   audit("ln_bwd.d_out", d_out, B * T * D * (int64_t)elem_bytes(dt));
@@ -1050,43 +1103,52 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   audit("ln_bwd.ln1_g", p->ln1_g, (int64_t)D * 4);
   // X' = LN2(Z + S): dV = dY2 (token-major), gamma2 / beta2 partials
   RM_TIMED("ln2_bwd", st, RM_HIP(rm::launch_ln_bwd(0, d_out, nullptr, nullptr, sv.Z, sv.S, p->ln2_g, w.dV, w.ln2p, B, T, D, dt, st), "LayerNorm 2 backward"));
-  // dV^T (rows padded to Bp) and the b2 partials
-  RM_TIMED("tr_dV", st, RM_HIP(rm::launch_transpose(0, w.dV, nullptr, w.dVt, nullptr, nullptr, w.b2p, T, B, D, Bp, dt, st), "transpose dV"));
-  // dH = dV W2: W2_t [D][Hd] is the product's W read K-major where the
-  // kernel allows, else W2^T [T][Hd][D] first
-  rm::GemmArgs g1;
-  g1.dt = dt; g1.epi = rm::kEpiBias;
-  g1.M = (int)B; g1.N = Hd; g1.K = D; g1.G = T;
-  g1.A = w.dV; g1.a_gs = B * D; g1.a_rs = D;
-  g1.W = p->pffn.w2; g1.b_gs = (int64_t)Hd * D; g1.w_kmajor = 1;
-  g1.C = w.dH; g1.c_gs = B * Hd; g1.c_rs = Hd;
-  if (!rm::gemm_wt_eligible(g1)) {
-    audit("tr_W2.W", p->pffn.w2, (int64_t)T * D * Hd * elem_bytes(dt));
-    RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->pffn.w2, nullptr, w.W2t, nullptr, nullptr, nullptr, T, D, Hd, D, dt, st), "transpose W2"));
-    g1.W = w.W2t;
-    g1.w_kmajor = 0;
+  if (w.km) {
+    // b2 partials: column sums of dV over 64-row blocks
+    RM_TIMED("sums_dV", st, RM_HIP(rm::launch_colsum64(w.dV, w.b2p, T, B, D, dt, st), "dV column sums"));
+    // dU = (dV W2) * GELU'(U) from the product's epilogue, with the b1 partials
+    rm::GemmArgs g1 = bwd_dH_args(w.dV, p->pffn.w2, w.dU, B, T, D, Hd, dt);
+    g1.epi = rm::kEpiGeluBwd;
+    g1.aux = sv.U;
+    g1.colsum = w.b1p;
+    RM_TIMED("bwd_dH", st, RM_TRY(gemm_go("dH product + GELU backward", g1, st)));
+    // dW2 = dV^T H and dW1 = dU^T S (fp32), both operands read as stored
+    RM_TIMED("bwd_dW2", st, RM_TRY(gemm_go("dW2 product", bwd_dW_args(w.dV, D, sv.H, Hd, g->w2, B, T, dt), st)));
+    RM_TIMED("bwd_dW1", st, RM_TRY(gemm_go("dW1 product", bwd_dW_args(w.dU, Hd, sv.S, D, g->w1, B, T, dt), st)));
+  } else {
+    // dV^T (rows padded to Bp) and the b2 partials
+    RM_TIMED("tr_dV", st, RM_HIP(rm::launch_transpose(0, w.dV, nullptr, w.dVt, nullptr, nullptr, w.b2p, T, B, D, Bp, dt, st), "transpose dV"));
+    // dH = dV W2: W2_t [D][Hd] is the product's W read K-major where the
+    // kernel allows, else W2^T [T][Hd][D] first
+    rm::GemmArgs g1 = bwd_dH_args(w.dV, p->pffn.w2, w.dH, B, T, D, Hd, dt);
+    if (!rm::gemm_wt_eligible(g1)) {
+      audit("tr_W2.W", p->pffn.w2, (int64_t)T * D * Hd * elem_bytes(dt));
+      RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->pffn.w2, nullptr, w.W2t, nullptr, nullptr, nullptr, T, D, Hd, D, dt, st), "transpose W2"));
+      g1.W = w.W2t;
+      g1.w_kmajor = 0;
+    }
+    RM_TIMED("bwd_dH", st, RM_TRY(gemm_go("dH product", g1, st)));
+    // dU = dH * GELU'(U), also transposed, with the b1 partials, and H^T
+    // from the saved GELU(U)
+    RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.Ht, w.b1p, T, B, Hd, Bp, dt, st), "GELU backward"));
+    // dW2 = dV^T H (fp32)
+    rm::GemmArgs g2;
+    g2.dt = dt; g2.epi = rm::kEpiBiasF32;
+    g2.M = D; g2.N = Hd; g2.K = (int)Bp; g2.G = T;
+    g2.A = w.dVt; g2.a_gs = (int64_t)D * Bp; g2.a_rs = Bp;
+    g2.W = w.Ht; g2.b_gs = (int64_t)Hd * Bp;
+    g2.C = g->w2; g2.c_gs = (int64_t)D * Hd; g2.c_rs = Hd;
+    RM_TIMED("bwd_dW2", st, RM_TRY(gemm_go("dW2 product", g2, st)));
+    // dW1 = dU^T S (fp32)
+    RM_TIMED("tr_S", st, RM_HIP(rm::launch_transpose(0, sv.S, nullptr, w.St, nullptr, nullptr, nullptr, T, B, D, Bp, dt, st), "transpose S"));
+    rm::GemmArgs g3;
+    g3.dt = dt; g3.epi = rm::kEpiBiasF32;
+    g3.M = Hd; g3.N = D; g3.K = (int)Bp; g3.G = T;
+    g3.A = w.dUt; g3.a_gs = (int64_t)Hd * Bp; g3.a_rs = Bp;
+    g3.W = w.St; g3.b_gs = (int64_t)D * Bp;
+    g3.C = g->w1; g3.c_gs = (int64_t)Hd * D; g3.c_rs = D;
+    RM_TIMED("bwd_dW1", st, RM_TRY(gemm_go("dW1 product", g3, st)));
   }
-  RM_TIMED("bwd_dH", st, RM_TRY(gemm_go("dH product", g1, st)));
-  // dU = dH * GELU'(U), also transposed, with the b1 partials, and H^T =
-  // GELU(U)^T from the same read of U
-  RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.Ht, w.b1p, T, B, Hd, Bp, dt, st), "GELU backward"));
-  // dW2 = dV^T H (fp32)
-  rm::GemmArgs g2;
-  g2.dt = dt; g2.epi = rm::kEpiBiasF32;
-  g2.M = D; g2.N = Hd; g2.K = (int)Bp; g2.G = T;
-  g2.A = w.dVt; g2.a_gs = (int64_t)D * Bp; g2.a_rs = Bp;
-  g2.W = w.Ht; g2.b_gs = (int64_t)Hd * Bp;
-  g2.C = g->w2; g2.c_gs = (int64_t)D * Hd; g2.c_rs = Hd;
-  RM_TIMED("bwd_dW2", st, RM_TRY(gemm_go("dW2 product", g2, st)));
-  // dW1 = dU^T S (fp32)
-  RM_TIMED("tr_S", st, RM_HIP(rm::launch_transpose(0, sv.S, nullptr, w.St, nullptr, nullptr, nullptr, T, B, D, Bp, dt, st), "transpose S"));
-  rm::GemmArgs g3;
-  g3.dt = dt; g3.epi = rm::kEpiBiasF32;
-  g3.M = Hd; g3.N = D; g3.K = (int)Bp; g3.G = T;
-  g3.A = w.dUt; g3.a_gs = (int64_t)Hd * Bp; g3.a_rs = Bp;
-  g3.W = w.St; g3.b_gs = (int64_t)D * Bp;
-  g3.C = g->w1; g3.c_gs = (int64_t)Hd * D; g3.c_rs = D;
-  RM_TIMED("bwd_dW1", st, RM_TRY(gemm_go("dW1 product", g3, st)));
   // dS (W1 branch) = dU W1 (fp32, token-major): W1_t [Hd][D] read K-major
   // where the kernel allows, else W1^T first
   rm::GemmArgs g4;
@@ -1108,8 +1170,8 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   // fixed-order sums of the partials
   RM_TIMED("sums_ln", st, RM_HIP(rm::launch_sum_parts(w.ln2p, g->ln2_g, g->ln2_b, 1, lg, 2 * (int64_t)D, D, st), "gamma2 / beta2"));
   RM_TIMED("sums_ln", st, RM_HIP(rm::launch_sum_parts(w.ln1p, g->ln1_g, g->ln1_b, 1, lg, 2 * (int64_t)D, D, st), "gamma1 / beta1"));
-  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b2p, g->b2, nullptr, T, rt, D, D, st), "b2"));
-  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b1p, g->b1, nullptr, T, rt, Hd, Hd, st), "b1"));
+  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b2p, g->b2, nullptr, T, w.b2_parts, D, D, st), "b2"));
+  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b1p, g->b1, nullptr, T, w.b1_parts, Hd, Hd, st), "b1"));
   return ok();
 }
 

@@ -612,6 +612,43 @@ hipError_t launch_sum_parts(const float* part, float* out0, float* out1, int G, 
   return hipGetLastError();
 }
 
+// part[g][b][c] = the sum of in[g][r][c] over rows r = 64 b .. 64 b + 63 (< R):
+// one thread per 16-byte chunk of columns, rows in order
+template <typename T>
+__global__ __launch_bounds__(256) void k_colsum64(const T* __restrict__ in, float* __restrict__ part, int64_t R,
+                                                  int64_t C, int P) {
+  const int64_t g = blockIdx.z, b = blockIdx.y;
+  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (c >= C) return;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int64_t r0 = b * 64, r1 = min(R, r0 + 64);
+  const T* src = in + g * R * C + c;
+#pragma unroll 8
+  for (int64_t r = r0; r < r1; ++r) {
+    float v[8];
+    load_f32<T, 8>(src + r * C, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += v[e];
+  }
+  float* dst = part + (g * P + b) * C + c;
+  *reinterpret_cast<float4*>(dst) = make_float4(s[0], s[1], s[2], s[3]);
+  *reinterpret_cast<float4*>(dst + 4) = make_float4(s[4], s[5], s[6], s[7]);
+}
+
+int colsum64_parts(int64_t R) { return (int)((R + 63) / 64); }
+
+hipError_t launch_colsum64(const void* in, float* part, int G, int64_t R, int64_t C, int dt, hipStream_t s) {
+  if (C % 8) return hipErrorInvalidValue;
+  if (G == 0 || R == 0 || C == 0) return hipSuccess;
+  const int P = colsum64_parts(R);
+  const dim3 grid((unsigned)((C / 8 + 255) / 256), (unsigned)P, (unsigned)G);
+  if (dt == kBF16)
+    hipLaunchKernelGGL((k_colsum64<bf16>), grid, dim3(256), 0, s, (const bf16*)in, part, R, C, P);
+  else
+    hipLaunchKernelGGL((k_colsum64<float>), grid, dim3(256), 0, s, (const float*)in, part, R, C, P);
+  return hipGetLastError();
+}
+
 hipError_t launch_gelu_ew(const void* u, void* h, int64_t n, int dt, hipStream_t s) {
   if (n % 8) return hipErrorInvalidValue;
   const int64_t n8 = n / 8;

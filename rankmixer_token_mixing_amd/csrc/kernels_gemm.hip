@@ -50,6 +50,8 @@ struct KParams {
   void* C;
   long long c_gs, c_rs;
   void* C2;  // kEpiBiasGeluDual: GELU(C), same layout as C
+  const void* aux;  // kEpiGeluBwd: the pre-activation, same layout as C
+  float* colsum;    // kEpiGeluBwd: partial column sums
   const float* bias;
   long long bias_gs;
   const float* rowscale;
@@ -88,7 +90,7 @@ template <> struct Mma<float> {
 template <int EPI, typename T>
 struct OutType {
   typedef typename std::conditional<EPI == kEpiBiasGelu || EPI == kEpiBias || EPI == kEpiBiasScale ||
-                                        EPI == kEpiBiasGeluDual,
+                                        EPI == kEpiBiasGeluDual || EPI == kEpiGeluBwd,
                                     T, float>::type type;
 };
 
@@ -337,6 +339,78 @@ __device__ __forceinline__ void ring_epilogue(const KParams& p, const TileId& t,
       if (m < t.Mg && t.n0 + c * 8 < p.N)
         *reinterpret_cast<uint4*>((TO*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + t.n0 + c * 8) = val;
     }
+  } else if constexpr (EPI == kEpiGeluBwd) {
+    static_assert(BM == 256 && BN == 256, "GELU backward epilogue: 256 x 256 tiles");
+    constexpr int OCH = BN / 8;    // 16-byte chunks per output row
+    constexpr int RPP = NT / OCH;  // rows per pass (16)
+    const bf16* U = (const bf16*)p.aux + (long long)t.g * p.c_gs;
+    __syncthreads();  // every wave is done reading operand slots
+    // the tile's pre-activations into the LDS rows (whole row segments),
+    // every load of a thread in flight at once: rows and columns past the
+    // end re-read the last ones (their results are neither stored nor summed)
+    {
+      const int c = tid % OCH;
+      const int n = min(t.n0 + c * 8, p.N - 8);
+      uint4 u[BM / RPP];
+#pragma unroll
+      for (int pass = 0; pass < BM / RPP; ++pass) {
+        const int m = min(t.m0 + pass * RPP + tid / OCH, t.Mg - 1);
+        u[pass] = *reinterpret_cast<const uint4*>(U + (t.row_base + m) * p.c_rs + n);
+      }
+#pragma unroll
+      for (int pass = 0; pass < BM / RPP; ++pass) {
+        const int ml = pass * RPP + tid / OCH;
+        *reinterpret_cast<uint4*>(orow(ml) + ((c ^ (ml & (OCH - 1))) * 16)) = u[pass];
+      }
+    }
+    __syncthreads();
+    // in place: C = acc * GELU'(U), rounded to bf16
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int ml = wm * FM * 32 + i * 32 + lr;
+          const int phys = (nl >> 3) ^ (ml & (OCH - 1));
+          bf16* cell = reinterpret_cast<bf16*>(orow(ml) + phys * 16 + (nl & 7) * 2);
+          float u[4], v[4];
+          load_f32<bf16, 4>(cell, u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float gu, dgu;
+            gelu_and_grad(u[e], gu, dgu);
+            v[e] = acc[i][j][4 * q + e] * dgu;
+          }
+          store_from_f32<bf16, 4>(cell, v);
+        }
+      }
+    }
+    __syncthreads();
+    // whole row segments out; each thread also sums its 8 columns over the
+    // rows it stores (rows tid / OCH + 16 r of the tile)
+    float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const int c = tid % OCH;
+    const int n = t.n0 + c * 8;
+#pragma unroll 4
+    for (int pass = 0; pass < BM / RPP; ++pass) {
+      const int ml = pass * RPP + tid / OCH;
+      const uint4 val = *reinterpret_cast<const uint4*>(orow(ml) + ((c ^ (ml & (OCH - 1))) * 16));
+      const int m = t.m0 + ml;
+      if (m < t.Mg && n < p.N) {
+        *reinterpret_cast<uint4*>((bf16*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + n) = val;
+        float f[8];
+        load_f32<bf16, 8>(reinterpret_cast<const bf16*>(&val), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[e] += f[e];
+      }
+    }
+    if (n < p.N) {
+      float* dst = p.colsum + ((long long)(t.g * p.tiles_m + t.m0 / BM) * RPP + tid / OCH) * p.N + n;
+      *reinterpret_cast<float4*>(dst) = make_float4(cs[0], cs[1], cs[2], cs[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(cs[4], cs[5], cs[6], cs[7]);
+    }
   } else {
     store_direct<bf16, FM, FN, EPI>(p, t, acc, wm, wn, lr, lh);
   }
@@ -376,10 +450,11 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-template <int NWM, int NWN, int FM, int FN, int EPI, bool RAGGED, bool AIDX, bool WT = false>
+template <int NWM, int NWN, int FM, int FN, int EPI, bool RAGGED, bool AIDX, bool WT = false, bool AT = false>
 __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
   typedef Ring<NWM, NWN, FM, FN> RG;
   static_assert(!WT || (RG::BN == 256 && !RAGGED), "K-major W: 256-column tiles, dense");
+  static_assert(!AT || (WT && RG::BM == 256 && !AIDX), "K-major A: with K-major W, 256-row tiles");
   constexpr int BM = RG::BM, BN = RG::BN, BK = RG::BK, NW = RG::NW;
   constexpr int A_DMA = RG::A_DMA, B_DMA = RG::B_DMA;
 
@@ -410,10 +485,19 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
   const bf16* bsrc[B_DMA];
 #pragma unroll
   for (int i = 0; i < A_DMA; ++i) {
-    const int row = 8 * (wave + i * NW) + (lane >> 3);
-    const int m = min(t.m0 + row, t.Mg - 1);  // rows past the end re-read the last row
-    const long long r = AIDX ? (long long)p.a_rowidx[t.row_base + m] : t.row_base + m;
-    asrc[i] = Ab + r * p.a_rs + ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+    if constexpr (AT) {
+      // as the K-major W below: k-row r of the [64][BM] panel, columns past
+      // M re-read the row's last chunk
+      const int q = (wave + i * NW) * 64 + lane;
+      const int r = q / (BM / 8), c = q % (BM / 8);
+      const int m = min(t.m0 + ((c ^ wt_swz(r)) * 8), p.M - 8);
+      asrc[i] = Ab + (long long)r * p.a_rs + m;
+    } else {
+      const int row = 8 * (wave + i * NW) + (lane >> 3);
+      const int m = min(t.m0 + row, t.Mg - 1);  // rows past the end re-read the last row
+      const long long r = AIDX ? (long long)p.a_rowidx[t.row_base + m] : t.row_base + m;
+      asrc[i] = Ab + r * p.a_rs + ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+    }
   }
 #pragma unroll
   for (int i = 0; i < B_DMA; ++i) {
@@ -435,7 +519,7 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
   // k-slices past the end re-read the last slice; they land in slots no
   // compute reads again
   auto issueA = [&](uint4* dst, int kt) {
-    const int koff = min(kt, nk_real - 1) * BK;
+    const long long koff = (long long)min(kt, nk_real - 1) * BK * (AT ? p.a_rs : 1);
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i)
       __builtin_amdgcn_global_load_lds((global_cvoid*)(asrc[i] + koff), (lds_void*)(dst + (wave + i * NW) * 64), 16,
@@ -462,26 +546,33 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
   // fragments of k-step kk (16 k) double-buffered in registers
   auto compute = [&](const uint4* As, const uint4* Bs) {
     uint4 af[2][FM], bfr[2][FN];
+    // a fragment from a K-major panel of `width` columns: lane group g4 =
+    // lane/16 takes k rows 8*(g4/2) .. +7 of this k-step, columns 16*(g4%2)
+    // .. +15 of the 32-column block at col0; lane i16 addresses row i16/4 of
+    // each 4-row block, columns 4*(i16%4) .. +3
+    auto frag_tr = [&](const uint4* S, int width, int col0, int kk) {
+      const int g4 = lane >> 4, i16 = lane & 15;
+      const int col = col0 + (g4 & 1) * 16 + 4 * (i16 & 3);
+      uint2 h[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r = kk * 16 + (g4 >> 1) * 8 + hh * 4 + (i16 >> 2);
+        h[hh] = lds_read_tr16(reinterpret_cast<const char*>(S) + r * (width * 2) + (((col >> 3) ^ wt_swz(r)) << 4) +
+                              (col & 7) * 2);
+      }
+      return make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
+    };
     auto ld = [&](int kk, int b) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[b][i] = As[swz(wm * FM * 32 + i * 32 + lr, kk * 2 + lh)];
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (AT)
+          af[b][i] = frag_tr(As, BM, wm * FM * 32 + i * 32, kk);
+        else
+          af[b][i] = As[swz(wm * FM * 32 + i * 32 + lr, kk * 2 + lh)];
+      }
       if constexpr (WT) {
-        // lane group g4 = lane/16: k rows 8*(g4/2) .. +7 of this k-step,
-        // columns 16*(g4%2) .. +15 of block j; lane i16 addresses row i16/4
-        // of each 4-row block, columns 4*(i16%4) .. +3
-        const int g4 = lane >> 4, i16 = lane & 15;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = wn * FN * 32 + j * 32 + (g4 & 1) * 16 + 4 * (i16 & 3);
-          uint2 h[2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int r = kk * 16 + (g4 >> 1) * 8 + hh * 4 + (i16 >> 2);
-            h[hh] = lds_read_tr16(reinterpret_cast<const char*>(Bs) + r * (BN * 2) +
-                                  (((col >> 3) ^ wt_swz(r)) << 4) + (col & 7) * 2);
-          }
-          bfr[b][j] = make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
-        }
+        for (int j = 0; j < FN; ++j) bfr[b][j] = frag_tr(Bs, BN, wn * FN * 32 + j * 32, kk);
       } else {
 #pragma unroll
         for (int j = 0; j < FN; ++j) bfr[b][j] = Bs[swz(wn * FN * 32 + j * 32 + lr, kk * 2 + lh)];
@@ -989,6 +1080,7 @@ KParams make_params(const GemmArgs& a, int bm, int bn) {
   p.A = a.A; p.a_gs = a.a_gs; p.a_rs = a.a_rs; p.a_gdiv = a.a_gdiv; p.a_rowidx = a.a_rowidx;
   p.W = a.W; p.b_gs = a.b_gs; p.b_gdiv = a.b_gdiv;
   p.C = a.C; p.c_gs = a.c_gs; p.c_rs = a.c_rs; p.C2 = a.C2;
+  p.aux = a.aux; p.colsum = a.colsum;
   p.bias = a.bias; p.bias_gs = a.bias_gs;
   p.rowscale = a.rowscale;
   p.row_off = a.row_off; p.tiles = a.tiles; p.ntiles = a.ntiles;
@@ -1030,6 +1122,13 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
     if constexpr (FM == 4 && FN == 2 && NWN == 4) {
       if (!ring || ragged) return hipErrorInvalidValue;
       const dim3 block(NWM * NWN * kWave);
+      if (a.a_kmajor) {
+        // both operands [K][.]: the weight-gradient products
+        if (a.epi != kEpiBiasF32) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_gemm_ring<NWM, NWN, FM, FN, kEpiBiasF32, false, false, true, true>), grid, block, 0, s,
+                           p);
+        return hipGetLastError();
+      }
       switch (a.epi) {
         case kEpiBiasGelu:
           hipLaunchKernelGGL((k_gemm_ring<NWM, NWN, FM, FN, kEpiBiasGelu, false, false, true>), grid, block, 0, s, p);
@@ -1039,6 +1138,10 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
           break;
         case kEpiBiasF32:
           hipLaunchKernelGGL((k_gemm_ring<NWM, NWN, FM, FN, kEpiBiasF32, false, false, true>), grid, block, 0, s, p);
+          break;
+        case kEpiGeluBwd:
+          if (!a.aux || !a.colsum) return hipErrorInvalidValue;
+          hipLaunchKernelGGL((k_gemm_ring<NWM, NWN, FM, FN, kEpiGeluBwd, false, false, true>), grid, block, 0, s, p);
           break;
         default: return hipErrorInvalidValue;
       }
@@ -1127,6 +1230,15 @@ bool gemm_wt_eligible(const GemmArgs& a) {
   return choose_cfg(b) == 0;
 }
 
+bool gemm_kmajor_eligible(const GemmArgs& a) {
+  if (a.dt != kBF16 || a.K % 64 || a.row_off || a.a_rowidx || !a.w_kmajor || a.pipe == 0) return false;
+  if (a.M < 256 || a.N < 256 || a.N % 8 || a.b_gs % 8) return false;
+  if (a.a_kmajor) return a.epi == kEpiBiasF32 && a.M % 8 == 0 && a.a_rs % 8 == 0 && a.a_rs >= a.M && a.a_gs % 8 == 0;
+  return a.epi == kEpiGeluBwd && a.c_rs % 8 == 0 && a.c_gs % 8 == 0;
+}
+
+int gemm_colsum_parts(int M) { return ceil_div(M, 256) * 16; }
+
 bool gemm_pipe_eligible(const GemmArgs& a) {
   const TileCfg& t = kCfgs[choose_cfg(a)];
   if (!(t.fm == 4 && t.fn == 2) || a.dt != kBF16 || a.K % 64 || a.pipe == 0) return false;
@@ -1135,6 +1247,7 @@ bool gemm_pipe_eligible(const GemmArgs& a) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+  if (a.a_kmajor || a.epi == kEpiGeluBwd) return gemm_kmajor_eligible(a) ? launch_cfg<2, 4, 4, 2>(a, s) : hipErrorInvalidValue;
   if (a.w_kmajor) return gemm_wt_eligible(a) ? launch_cfg<2, 4, 4, 2>(a, s) : hipErrorInvalidValue;
   if (epilogue_overlap() && gemm_defer_eligible(a)) return launch_gemm_defer(a, s);
   switch (choose_cfg(a)) {

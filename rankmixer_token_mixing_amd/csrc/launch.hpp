@@ -79,6 +79,12 @@ enum Epilogue {
   // C(dt) = acc + bias[n] and C2(dt) = GELU(C) (same layout; training keeps
   // the pre-activation).  Pipelined kernel only.
   kEpiBiasGeluDual = 5,
+  // backward through the GELU: C(dt) = acc * GELU'(aux), aux (dt) the
+  // pre-activation U at C's layout, and colsum[(g * tiles_m + tm) * 16 + r][n]
+  // = the sum of the rounded C over rows m0 + r, m0 + r + 16, ... of M tile
+  // tm (256 rows) -- 16 partial column sums per M tile (the bias gradient).
+  // No bias.  K-major ring only (gemm_kmajor_eligible).
+  kEpiGeluBwd = 6,
 };
 
 // C_g[m][n] = sum_k A_g[m][k] * W_g[n][k], g = 0..G-1, followed by an epilogue.
@@ -109,6 +115,12 @@ struct GemmArgs {
   // k * N + n): the compiler-scheduled ring with transposed LDS fragment
   // reads, where gemm_wt_eligible (bf16, K % 64 == 0, dense, 256 x 256 tiles)
   int w_kmajor = 0;
+  // A group stored K-major, [K][M] (element (k, m) at (g / a_gdiv) * a_gs +
+  // k * a_rs + m), with w_kmajor: both operands read along their rows with
+  // transposed LDS fragment reads (the weight-gradient products, K = batch)
+  int a_kmajor = 0;
+  const void* aux = nullptr;  // kEpiGeluBwd: the pre-activation
+  float* colsum = nullptr;    // kEpiGeluBwd: the partial column sums
   int tile_cfg = -1;  // -1: choose automatically
   int pipe = -1;      // 0: never use the hand-scheduled ring (for comparisons)
 };
@@ -130,6 +142,13 @@ bool epilogue_overlap();
 hipError_t launch_gemm_defer(const GemmArgs& a, hipStream_t s);
 // whether launch_gemm takes `a` with a K-major W (w_kmajor)
 bool gemm_wt_eligible(const GemmArgs& a);
+// whether launch_gemm takes `a` on the K-major ring with 256 x 256 tiles
+// whatever the tile count: both operands K-major (a_kmajor, w_kmajor,
+// kEpiBiasF32) or a K-major W with the kEpiGeluBwd epilogue.  bf16, dense,
+// K a multiple of 64, M and N at least 256 and multiples of 8
+bool gemm_kmajor_eligible(const GemmArgs& a);
+// number of partial column sums per group that kEpiGeluBwd writes
+int gemm_colsum_parts(int M);
 
 // ---- dense block backward (kernels_bwd.hip) -----------------------------------
 
@@ -159,6 +178,10 @@ hipError_t launch_tm_add(const float* dy, void* dx, int64_t B, int T, int D, int
 // out[g][c] = scale * sum_p part[g][p][c] (fixed order); c < split -> out0, else out1
 hipError_t launch_sum_parts(const float* part, float* out0, float* out1, int G, int P, int64_t C, int64_t split,
                             hipStream_t s, float scale = 1.0f);
+// part[g][b][c] = sum of in[g][r][c] over the rows of 64-row block b
+// (colsum64_parts(R) blocks; in [G][R][C], C a multiple of 8)
+int colsum64_parts(int64_t R);
+hipError_t launch_colsum64(const void* in, float* part, int G, int64_t R, int64_t C, int dt, hipStream_t s);
 // h = GELU(u), n elements (a multiple of 8)
 hipError_t launch_gelu_ew(const void* u, void* h, int64_t n, int dt, hipStream_t s);
 

@@ -71,9 +71,10 @@ def _run(dtype, B, T, D, Hd, seed):
 @pytest.mark.parametrize("dtype,B,T,D,Hd", [
     ("f32", 64, 4, 64, 128),      # the tiny fp32 block
     ("f32", 33, 1, 64, 96),       # T = 1, batch not a multiple of 64
-    ("bf16", 300, 4, 128, 256),   # ragged batch: transposed rows padded to 320
+    ("bf16", 300, 4, 128, 256),   # ragged batch: transposed rows padded to 320 (the transposing path)
     ("bf16", 1, 2, 16, 32),       # one sample
-    ("bf16", 1024, 8, 256, 1024), # pipelined products (K = batch = 1024)
+    ("bf16", 1024, 8, 256, 1024), # no transposes: dH with the GELU backward epilogue, dW1 / dW2 read K-major
+    ("bf16", 320, 3, 384, 768),   # no transposes, ragged 256-tiles in every product (M = 320, D = 384)
     ("f32", 17, 8, 40, 24),       # heads of width 5: odd gathers
     ("bf16", 1024, 16, 256, 2048),  # dH reads W2 K-major (transposed fragment reads, 256 x 256 tiles)
     ("bf16", 1000, 32, 1024, 1024),  # ragged batch, dH and dS both read W K-major
@@ -129,3 +130,24 @@ def test_empty_batch_gives_zero_gradients():
     assert dx.shape == (0, 4, 64)
     for k in GRADS:
         assert torch.count_nonzero(g[k]).item() == 0, k
+
+
+@pytest.mark.parametrize("B,T,D,Hd,transpose_free", [(1024, 8, 256, 1024, True), (320, 3, 384, 768, True),
+                                                     (1000, 32, 1024, 1024, False), (300, 4, 128, 256, False)])
+def test_backward_path_choice(B, T, D, Hd, transpose_free):
+    # a batch that is a multiple of 64 with every product at least 256 x 256
+    # runs without transposes: the dH product's epilogue applies GELU' and
+    # the weight-gradient products read both operands as stored
+    from rankmixer_token_mixing_amd import binding as bd
+    dev = bd.upload_blocks([_block(T, D, Hd, "bf16", 3)])[0]
+    xd = bd.to_device(_act((B, T, D), "bf16", 4))
+    y, saved = bd.rm_block_fwd_train(xd, dev)
+    torch.cuda.synchronize()
+    bd.profile_enable(True)
+    try:
+        bd.rm_block_bwd(xd, dev, saved, bd.to_device(_act((B, T, D), "bf16", 5)))
+        torch.cuda.synchronize()
+        names = set(bd.profile_read())
+    finally:
+        bd.profile_enable(False)
+    assert ("gelu_bwd" not in names and "tr_S" not in names and "sums_dV" in names) == transpose_free, names
