@@ -676,6 +676,49 @@ def bench_epilogue_overlap(args) -> int:
     return 0
 
 
+def bench_vendor_gemm(args) -> int:
+    """The vendor library on the per-token FFN products of the ~1B-class
+    workload's block (B=1024, T=32, D=1536, hidden 6144): torch.bmm (which
+    calls hipBLASLt) on random bf16 operands of the W1 and W2 product shapes,
+    both operands contiguous, no bias and no epilogue -- a reference point
+    for the library's own fused products, not part of the method."""
+    import torch
+    from rankmixer_token_mixing_amd import perfmodel as pm
+
+    B, T, D, Hd = 1024, 32, 1536, 6144
+    g = torch.Generator(device="cuda").manual_seed(3)
+    shapes = {"ffn1": (T, B, D, Hd), "ffn2": (T, B, Hd, D)}
+    res = {}
+    for name, (G, M, K, N) in shapes.items():
+        a = torch.randn(G, M, K, device="cuda", generator=g).to(torch.bfloat16)
+        w = torch.randn(G, K, N, device="cuda", generator=g).to(torch.bfloat16).contiguous()
+        c = torch.empty(G, M, N, device="cuda", dtype=torch.bfloat16)
+        for _ in range(args.warmup):
+            torch.bmm(a, w, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            torch.bmm(a, w, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        fl = G * pm.gemm_flops(M, N, K)
+        res[name] = {"avg_ms": round(ms, 5), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "frac": round(fl / (ms * 1e-3) / 1e12 / pm.PEAK_BF16_TFLOPS, 4)}
+        log(f"{name}: {ms:.4f} ms")
+        del a, w, c
+    rec = {"metric": "vendor bf16 batched GEMM TFLOP/s on the W1 product shape (torch.bmm)",
+           "value": res["ffn1"]["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": res["ffn1"]["avg_ms"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"torch.bmm [T,B,D]x[T,D,H] and [T,B,H]x[T,H,D], B={B}, T={T}, D={D}, "
+                                  f"H={Hd}, bf16, no epilogue", "B": B, "T": T, "D": D, "hidden": Hd},
+           "products": res, "cpu_baseline": None}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -684,7 +727,7 @@ def main() -> int:
     ap.add_argument("--config", default="c3", help="workload (c3 is the benchmarked one)")
     ap.add_argument("--op", default="model",
                     choices=["model", "tokenize_project", "block_bwd", "block_variants", "moe_train", "ceilings",
-                             "epilogue_overlap"],
+                             "epilogue_overlap", "vendor_gemm"],
                     help="model: the block stack (default); tokenize_project: the projection "
                          "tokenizer alone on the pad-split model's embedding; block_bwd: the dense "
                          "block backward on block 0 of the workload; block_variants: the SwiGLU "
@@ -693,7 +736,8 @@ def main() -> int:
                          "step of the MoE block with dense-training / sparse-inference routers; "
                          "ceilings: the MFMA-loop and HBM-copy probes alone; epilogue_overlap: the W1 "
                          "and W2 products of block 0 with the epilogue after each tile and inside the "
-                         "next tile's main loop")
+                         "next tile's main loop; vendor_gemm: torch.bmm (hipBLASLt) on the same two "
+                         "product shapes, no epilogue")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the probes after the timed steps")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="samples in the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -745,6 +789,8 @@ def main() -> int:
         return bench_ceilings(args)
     if args.op == "epilogue_overlap":
         return bench_epilogue_overlap(args)
+    if args.op == "vendor_gemm":
+        return bench_vendor_gemm(args)
 
     cfg = si.CONFIGS[args.config]
     t0 = time.perf_counter()
