@@ -47,7 +47,10 @@ struct LnBwdArgs {
 // Element k of mixed token t is element t*d + (k mod d) of token k / d.
 // The gamma / beta partials of each wave accumulate in its own LDS region
 // [2][D] (dynamic LDS, kLnWaves * 2 * D floats), so registers hold only the
-// row being processed.
+// row being processed.  Inside a region, element c * VEC + e (chunk c, lane
+// c mod 64) sits at e * nch + c, so the 64 lanes of one update touch 64
+// consecutive floats (with the row's element order, lane L's eight floats
+// would share a bank with lanes L + 4, L + 8, ...).
 template <typename T, int VEC, int MAXI, int MODE>
 __global__ __launch_bounds__(kLnWaves* kWave) void k_ln_bwd(LnBwdArgs a) {
   extern __shared__ float wpart[];
@@ -165,8 +168,8 @@ __global__ __launch_bounds__(kLnWaves* kWave) void k_ln_bwd(LnBwdArgs a) {
           const float g = up[i][e] * a.gamma[k + e];
           sg += g;
           sgx += g * y[i][e];
-          pg[k + e] += up[i][e] * y[i][e];
-          pb[k + e] += up[i][e];
+          pg[e * nch + c] += up[i][e] * y[i][e];
+          pb[e * nch + c] += up[i][e];
         }
       }
     }
@@ -186,13 +189,16 @@ __global__ __launch_bounds__(kLnWaves* kWave) void k_ln_bwd(LnBwdArgs a) {
       }
     }
   }
-  // workgroup partials: the waves' regions added in a fixed order
+  // workgroup partials: the waves' regions added in a fixed order, back in
+  // the row's element order
   __syncthreads();
   float* out = a.part + (int64_t)blockIdx.x * 2 * D;
   for (int k = threadIdx.x; k < 2 * D; k += kLnWaves * kWave) {
-    float v = wpart[k];
+    const int h = k >= D ? 1 : 0, kk = k - h * D;
+    const int src = h * D + (kk % VEC) * nch + kk / VEC;
+    float v = wpart[src];
 #pragma unroll
-    for (int w = 1; w < kLnWaves; ++w) v += wpart[w * 2 * D + k];
+    for (int w = 1; w < kLnWaves; ++w) v += wpart[w * 2 * D + src];
     out[k] = v;
   }
 }
