@@ -273,3 +273,24 @@ def test_moe_single_expert_always_on_equals_pffn():
              "b2": p["b2"][:, 0].copy()}
     v2 = bd.rm_pffn_fwd(s, _dev(dense))
     assert rel_l2_rows(host(v), host(v2)) <= 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_moe_groups_of_every_size(dtype):
+    # expert groups of every size class: router biases spread the densities
+    # from ~3 % to ~97 %, so group counts (B = 1100) land on both sides of
+    # every 256-row tile boundary, with short and long last tiles
+    from rankmixer_token_mixing_amd import binding as bd
+    B, T, D, E, He = 1100, 4, 128, 8, 256
+    p = _moe_params(T, D, E, He, dtype, seed=21)
+    p["br"] = np.linspace(-1.9, 1.9, T * E).reshape(T, E).astype(np.float32)
+    s_np = orc.layer_norm(np.random.default_rng(22).standard_normal((B, T, D)), np.ones(D), np.zeros(D))
+    s = torch.from_numpy(s_np.astype(np.float32)).to(DT[dtype])
+    v, gates = bd.rm_moe_relu_fwd(s.cuda(), _dev(p), return_gates=True)
+    torch.cuda.synchronize()
+    counts = (host(gates) > 0).reshape(B, T * E).sum(axis=0)
+    rem = counts % 256
+    assert ((rem > 0) & (rem <= 128)).sum() >= 4 and (rem > 128).sum() >= 4, counts
+    rows = si.random_rows(B, 64, seed=23)
+    V_ref, _ = orc.moe_relu_pffn(s.to(torch.float64).numpy()[rows], **{k: p[k] for k in ("w1", "b1", "w2", "b2", "wr", "br")})
+    assert rel_l2_rows(host(v)[rows], V_ref) <= TOL[dtype]
