@@ -932,6 +932,16 @@ rm::GemmArgs bwd_dW_args(const void* A, int M, const void* W, int N, void* C, in
   g.C = C; g.c_gs = (int64_t)M * N; g.c_rs = N;
   return g;
 }
+// dS (W1 branch) = dU W1 (fp32, token-major): W1_t [Hd][D] read K-major
+rm::GemmArgs bwd_dS_args(const void* dU, const void* w1, float* C, int64_t B, int T, int D, int Hd, int dt) {
+  rm::GemmArgs g;
+  g.dt = dt; g.epi = rm::kEpiBiasF32;
+  g.M = (int)B; g.N = D; g.K = Hd; g.G = T;
+  g.A = dU; g.a_gs = B * Hd; g.a_rs = Hd;
+  g.W = w1; g.b_gs = (int64_t)D * Hd; g.w_kmajor = 1;
+  g.C = C; g.c_gs = B * D; g.c_rs = D;
+  return g;
+}
 // whether the backward runs without transposes (a shape property)
 bool bwd_kmajor(int64_t B, int T, int D, int Hd, int dt) {
   rm::GemmArgs h = bwd_dH_args(nullptr, nullptr, nullptr, B, T, D, Hd, dt);
@@ -958,7 +968,9 @@ size_t bwd_carve(Carver& c, int64_t B, int T, int D, int Hd, int dt, BwdWs* w) {
     x.b1_parts = rm::gemm_colsum_parts((int)B);
     x.dV = c.take((size_t)T * B * D * e);
     x.dU = c.take((size_t)T * B * Hd * e);
-    x.W1t = c.take((size_t)T * D * Hd * e);
+    // W1^T only where the dS product cannot read W1 as stored
+    x.W1t = rm::gemm_wt_eligible(bwd_dS_args(nullptr, nullptr, nullptr, B, T, D, Hd, dt))
+                ? nullptr : c.take((size_t)T * D * Hd * e);
     x.dSf = (float*)c.take((size_t)T * B * D * 4);
     x.dY1 = (float*)c.take((size_t)B * T * D * 4);
     x.ln2p = (float*)c.take((size_t)lg * 2 * D * 4);
@@ -1151,12 +1163,7 @@ rm_status rm_block_bwd(const void* x, const rm_block_params* p, const void* save
   }
   // dS (W1 branch) = dU W1 (fp32, token-major): W1_t [Hd][D] read K-major
   // where the kernel allows, else W1^T first
-  rm::GemmArgs g4;
-  g4.dt = dt; g4.epi = rm::kEpiBiasF32;
-  g4.M = (int)B; g4.N = D; g4.K = Hd; g4.G = T;
-  g4.A = w.dU; g4.a_gs = B * Hd; g4.a_rs = Hd;
-  g4.W = p->pffn.w1; g4.b_gs = (int64_t)D * Hd; g4.w_kmajor = 1;
-  g4.C = w.dSf; g4.c_gs = B * D; g4.c_rs = D;
+  rm::GemmArgs g4 = bwd_dS_args(w.dU, p->pffn.w1, w.dSf, B, T, D, Hd, dt);
   if (!rm::gemm_wt_eligible(g4)) {
     audit("tr_W1.W", p->pffn.w1, (int64_t)T * Hd * D * elem_bytes(dt));
     RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->pffn.w1, nullptr, w.W1t, nullptr, nullptr, nullptr, T, Hd, D, Hd, dt, st), "transpose W1"));

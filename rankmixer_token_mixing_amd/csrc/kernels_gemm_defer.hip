@@ -97,7 +97,6 @@ constexpr int kSlot = 32768;  // bytes per ring slot: 256 rows x 128 bytes
 // element 0, so no bias needs no branch)
 __device__ __align__(16) float g_no_bias[4] = {0.f, 0.f, 0.f, 0.f};
 
-
 constexpr int kUnits = 64;    // epilogue units per wave and tile: 4 x 4 blocks x 4 column quads
 
 struct DTile {
@@ -255,7 +254,7 @@ __global__ __launch_bounds__(256) void k_gemm_defer(DParams p) {
 
   // the accumulators are AGPRs a0..a255, named only inside the asm
   Frag8 f0, f1;
-  uint32_t P[2 * kUnits];  // the previous tile, packed bf16 (bias not yet added)
+  uint32_t P[2 * kUnits];  // the previous tile, bias included, packed bf16
   DPrev prev;
   const float c6 = 3.4358014090685174e-05f;  // degree-6 coefficient of the GELU tail (common.hpp)
   const float s65 = 6.5f;
