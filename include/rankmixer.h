@@ -328,8 +328,8 @@ typedef struct rm_moe_grads {
  *   x: [B][T][D] dtype; p: an MoE block without flags; wr_train: [T][E][D]
  *   dtype device; br_train: [T][E] fp32 device; x_out: [B][T][D] dtype;
  *   l_reg: one fp32 on the device; saved: the caller's buffer of
- *   rm_moe_saved_bytes for rm_moe_block_bwd (S, the W1 products + b1, the
- *   expert outputs, both gate sets, v).
+ *   rm_moe_saved_bytes for rm_moe_block_bwd (S, the W1 products + b1 and
+ *   their GELU, the expert outputs, both gate sets, v).
  *   Workspace: rm_moe_train_workspace_bytes(B, T, D, He, E, dtype).
  * B = 0 writes *l_reg = 0.
  * Errors: a block that is not MOE or has flags, D > 4096, T*E not a multiple
@@ -356,9 +356,12 @@ rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const 
  *   dS += dV;  dY1 = LNbwd1(dS);  dX = dY1 + TM(dY1)
  * Arguments as rm_moe_block_fwd_train (saved from that call on the same x and
  * parameters); d_out, dx: [B][T][D] dtype; g: fp32 gradients.  Products in
- * dtype with fp32 accumulation (bf16: the expert outputs y, dV, dy, dH and dU
- * are stored in bf16 between kernels); every sum over the batch in a fixed
- * order.
+ * dtype with fp32 accumulation (bf16: the expert outputs y, dV, dy and dU are
+ * stored in bf16 between kernels, and dH where it is stored); every sum over
+ * the batch in a fixed order.  bf16 with B a multiple of 64 and D, He >= 256:
+ * the dH products apply GELU' in their epilogue and the batch-contracting
+ * expert products read their operands as stored (no transposes of dy, H, dU
+ * or W2); otherwise they read transposed copies.
  * B = 0 writes zero gradients.
  *   Workspace: rm_moe_train_workspace_bytes(B, T, D, He, E, dtype) (the same
  *   size as the forward's; the two calls may share one buffer).

@@ -1190,6 +1190,7 @@ namespace {
 struct MoeSaved {
   void* S;   // [T][B][D] token-major
   void* U;   // [T*E][B][He]: W1 product + b1 of every (token, expert), group-major
+  void* H;   // [T*E][B][He]: GELU(U)
   void* Y;   // [B][T*E][D]: expert outputs
   float* Gt; // [B][T][E] training gates
   float* Gi; // [B][T][E] inference gates
@@ -1201,6 +1202,7 @@ size_t moe_saved_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt
   MoeSaved x;
   x.S = c.take((size_t)B * T * D * e);
   x.U = c.take((size_t)B * TE * He * e);
+  x.H = c.take((size_t)B * TE * He * e);
   x.Y = c.take((size_t)B * TE * D * e);
   x.Gt = (float*)c.take((size_t)B * TE * 4);
   x.Gi = (float*)c.take((size_t)B * TE * 4);
@@ -1209,31 +1211,69 @@ size_t moe_saved_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt
   return c.off;
 }
 
-// group-major [T*E][B][*]: H, dy, dH (so each (token, expert) slice is
+// The MoE backward's expert products over the T*E groups (dy, U, H
+// group-major [T*E][B][.]; dU [B][T][E*He]): dH = dy W2 reads W2 K-major and,
+// on the transpose-free path, applies GELU'(U) in its epilogue (writing dU
+// and the b1 partials); dW2 = dy^T H and dW1 = dU^T S then read both operands
+// as stored.
+rm::GemmArgs moe_dH_args(const void* dy, const void* w2, void* C, int64_t B, int64_t TE, int D, int He, int dt) {
+  rm::GemmArgs g;
+  g.dt = dt; g.epi = rm::kEpiGeluBwd;
+  g.M = (int)B; g.N = He; g.K = D; g.G = (int)TE;
+  g.A = dy; g.a_gs = B * D; g.a_rs = D;
+  g.W = w2; g.b_gs = (int64_t)He * D; g.w_kmajor = 1;
+  g.C = C; g.c_gs = He; g.c_rs = TE * He;   // dU [B][T][E*He]
+  g.aux_gs = B * He; g.aux_rs = He;          // U [T*E][B][He]
+  return g;
+}
+rm::GemmArgs moe_dW2_args(const void* dy, const void* H, float* C, int64_t B, int64_t TE, int D, int He, int dt) {
+  rm::GemmArgs g = bwd_dW_args(dy, D, H, He, C, B, (int)TE, dt);
+  return g;
+}
+rm::GemmArgs moe_dW1_args(const void* dU, const void* S, float* C, int64_t B, int T, int E, int D, int He, int dt) {
+  const int64_t TE = (int64_t)T * E;
+  rm::GemmArgs g = bwd_dW_args(dU, He, S, D, C, B, (int)TE, dt);
+  g.a_gs = He; g.a_rs = TE * He;  // dU [B][T][E*He]: group g's column block
+  g.b_gdiv = E;                    // S per token
+  return g;
+}
+bool moe_bwd_kmajor(int64_t B, int T, int D, int E, int He, int dt) {
+  const int64_t TE = (int64_t)T * E;
+  return rm::gemm_kmajor_eligible(moe_dH_args(nullptr, nullptr, nullptr, B, TE, D, He, dt)) &&
+         rm::gemm_kmajor_eligible(moe_dW2_args(nullptr, nullptr, nullptr, B, TE, D, He, dt)) &&
+         rm::gemm_kmajor_eligible(moe_dW1_args(nullptr, nullptr, nullptr, B, T, E, D, He, dt));
+}
+
+// group-major [T*E][B][*]: dy, dH (so each (token, expert) slice is
 // contiguous for its product and its transpose); dU [B][T][E*He] (one K axis
 // over a token's experts for the dS product)
 struct MoeTrainWs {
-  void* H;  // forward: GELU(U), same layout
+  bool km;  // moe_bwd_kmajor
   void *dV, *dy, *dz, *mask, *W2t, *dH, *dU, *dUt, *Ht, *dyt, *St, *W1tc, *dzt, *maskt;
   float *dSr, *dSf, *dY1, *ln2p, *ln1p, *b2p, *b1p, *brtp, *brip, *lpart;
+  int b2_parts, b1_parts;  // partial sums per group of b2, b1
 };
 size_t moe_train_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt, MoeTrainWs* w) {
   const size_t e = elem_bytes(dt);
   const int64_t TE = (int64_t)T * E, Bp = pad64(B);
   const int64_t rt = rm::transpose_row_tiles(B, Bp);
   const int lg = rm::ln_bwd_grid(B, T, D);
-  MoeTrainWs x;
-  x.H = c.take((size_t)B * TE * He * e);
+  MoeTrainWs x{};
+  x.km = moe_bwd_kmajor(B, T, D, E, He, dt);
+  x.b2_parts = x.km ? rm::colsum64_parts(B) : (int)rt;
+  x.b1_parts = x.km ? rm::gemm_colsum_parts((int)B) : (int)rt;
   x.dV = c.take((size_t)T * B * D * e);
   x.dy = c.take((size_t)B * TE * D * e);
   x.dz = c.take((size_t)B * TE * e);
   x.mask = c.take((size_t)B * TE * e);
-  x.W2t = c.take((size_t)TE * He * D * e);
-  x.dH = c.take((size_t)B * TE * He * e);
   x.dU = c.take((size_t)B * TE * He * e);
-  x.dUt = c.take((size_t)TE * He * Bp * e);
-  x.Ht = c.take((size_t)TE * He * Bp * e);
-  x.dyt = c.take((size_t)TE * D * Bp * e);
+  if (!x.km) {
+    x.W2t = c.take((size_t)TE * He * D * e);
+    x.dH = c.take((size_t)B * TE * He * e);
+    x.dUt = c.take((size_t)TE * He * Bp * e);
+    x.Ht = c.take((size_t)TE * He * Bp * e);
+    x.dyt = c.take((size_t)TE * D * Bp * e);
+  }
   x.St = c.take((size_t)T * D * Bp * e);
   x.W1tc = c.take((size_t)T * D * E * He * e);
   x.dzt = c.take((size_t)TE * Bp * e);
@@ -1243,8 +1283,8 @@ size_t moe_train_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt
   x.dY1 = (float*)c.take((size_t)B * T * D * 4);
   x.ln2p = (float*)c.take((size_t)lg * 2 * D * 4);
   x.ln1p = (float*)c.take((size_t)lg * 2 * D * 4);
-  x.b2p = (float*)c.take((size_t)TE * rt * D * 4);
-  x.b1p = (float*)c.take((size_t)TE * rt * He * 4);
+  x.b2p = (float*)c.take((size_t)TE * x.b2_parts * D * 4);
+  x.b1p = (float*)c.take((size_t)TE * x.b1_parts * He * 4);
   x.brtp = (float*)c.take((size_t)rt * TE * 4);
   x.brip = (float*)c.take((size_t)rt * TE * 4);
   x.lpart = (float*)c.take((size_t)rm::kSumParts * 4);
@@ -1331,18 +1371,18 @@ rm_status rm_moe_block_fwd_train(const void* x, const rm_block_params* p, const 
   a1.C = sv.U; a1.c_gs = B * He; a1.c_rs = He;
   a1.bias = p->moe.b1; a1.bias_gs = He;
   a1.epi = rm::kEpiBiasGeluDual;  // U (saved) and H = GELU(U) from one epilogue where the kernel allows
-  a1.C2 = w.H;
+  a1.C2 = sv.H;
   if (rm::gemm_pipe_eligible(a1)) {
     RM_TIMED("moe_ffn1", st, RM_TRY(gemm_go("expert W1 products + GELU", a1, st)));
   } else {
     a1.epi = rm::kEpiBias;
     RM_TIMED("moe_ffn1", st, RM_TRY(gemm_go("expert W1 products", a1, st)));
-    RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, w.H, B * TE * He, dt, st), "GELU"));
+    RM_TIMED("gelu", st, RM_HIP(rm::launch_gelu_ew(sv.U, sv.H, B * TE * He, dt, st), "GELU"));
   }
   rm::GemmArgs a2;
   a2.dt = dt; a2.epi = rm::kEpiBias;
   a2.M = (int)B; a2.N = D; a2.K = He; a2.G = (int)TE;
-  a2.A = w.H; a2.a_gs = B * He; a2.a_rs = He;
+  a2.A = sv.H; a2.a_gs = B * He; a2.a_rs = He;
   a2.W = p->moe.w2; a2.b_gs = (int64_t)D * He;
   a2.C = sv.Y; a2.c_gs = D; a2.c_rs = TE * D;
   a2.bias = p->moe.b2; a2.bias_gs = D;
@@ -1402,32 +1442,46 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
   audit("tr_W1.W", p->moe.w1, TE * He * D * elem_bytes(dt));
   RM_TIMED("moe_rows", st, RM_HIP(rm::launch_moe_bwd_rows(w.dV, sv.Y, sv.Gt, sv.Gi, wr_train, w.dy, w.dz, w.mask, w.dSr, B, T, E, D, dt, st), "gate backward"));
   // experts, densely over the T*E groups
-  RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->moe.w2, nullptr, w.W2t, nullptr, nullptr, nullptr, (int)TE, D, He, D, dt, st), "transpose W2"));
-  rm::GemmArgs g1;
-  g1.dt = dt; g1.epi = rm::kEpiBias;
-  g1.M = (int)B; g1.N = He; g1.K = D; g1.G = (int)TE;
-  g1.A = w.dy; g1.a_gs = B * D; g1.a_rs = D;
-  g1.W = w.W2t; g1.b_gs = (int64_t)He * D;
-  g1.C = w.dH; g1.c_gs = B * He; g1.c_rs = He;
-  RM_TIMED("bwd_dH", st, RM_TRY(gemm_go("expert dH products", g1, st)));
-  // dH and U are group-major; dU also goes out [B][T][E*He] for the dS product
-  RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.Ht, w.b1p, (int)TE, B, He, Bp, dt, st, -1, -1, He, TE * He), "GELU backward"));
-  RM_TIMED("tr_dy", st, RM_HIP(rm::launch_transpose(0, w.dy, nullptr, w.dyt, nullptr, nullptr, w.b2p, (int)TE, B, D, Bp, dt, st), "transpose dy"));
-  rm::GemmArgs g2;
-  g2.dt = dt; g2.epi = rm::kEpiBiasF32;
-  g2.M = D; g2.N = He; g2.K = (int)Bp; g2.G = (int)TE;
-  g2.A = w.dyt; g2.a_gs = (int64_t)D * Bp; g2.a_rs = Bp;
-  g2.W = w.Ht; g2.b_gs = (int64_t)He * Bp;
-  g2.C = g->w2; g2.c_gs = (int64_t)D * He; g2.c_rs = He;
-  RM_TIMED("bwd_dW2", st, RM_TRY(gemm_go("expert dW2 products", g2, st)));
-  RM_TIMED("tr_S", st, RM_HIP(rm::launch_transpose(0, sv.S, nullptr, w.St, nullptr, nullptr, nullptr, T, B, D, Bp, dt, st), "transpose S"));
-  rm::GemmArgs g3;
-  g3.dt = dt; g3.epi = rm::kEpiBiasF32;
-  g3.M = He; g3.N = D; g3.K = (int)Bp; g3.G = (int)TE;
-  g3.A = w.dUt; g3.a_gs = (int64_t)He * Bp; g3.a_rs = Bp;
-  g3.W = w.St; g3.b_gs = (int64_t)D * Bp; g3.b_gdiv = E;
-  g3.C = g->w1; g3.c_gs = (int64_t)He * D; g3.c_rs = D;
-  RM_TIMED("bwd_dW1", st, RM_TRY(gemm_go("expert dW1 products", g3, st)));
+  if (w.km) {
+    // b2 partials from dy; dU = (dy W2) * GELU'(U) from the dH product's
+    // epilogue with the b1 partials; dW2 = dy^T H and dW1 = dU^T S read their
+    // operands as stored
+    RM_TIMED("sums_dy", st, RM_HIP(rm::launch_colsum64(w.dy, w.b2p, (int)TE, B, D, dt, st), "dy column sums"));
+    rm::GemmArgs g1 = moe_dH_args(w.dy, p->moe.w2, w.dU, B, TE, D, He, dt);
+    g1.aux = sv.U;
+    g1.colsum = w.b1p;
+    RM_TIMED("bwd_dH", st, RM_TRY(gemm_go("expert dH products + GELU backward", g1, st)));
+    RM_TIMED("bwd_dW2", st, RM_TRY(gemm_go("expert dW2 products", moe_dW2_args(w.dy, sv.H, g->w2, B, TE, D, He, dt), st)));
+    RM_TIMED("tr_S", st, RM_HIP(rm::launch_transpose(0, sv.S, nullptr, w.St, nullptr, nullptr, nullptr, T, B, D, Bp, dt, st), "transpose S"));
+    RM_TIMED("bwd_dW1", st, RM_TRY(gemm_go("expert dW1 products", moe_dW1_args(w.dU, sv.S, g->w1, B, T, E, D, He, dt), st)));
+  } else {
+    RM_TIMED("tr_W2", st, RM_HIP(rm::launch_transpose(0, p->moe.w2, nullptr, w.W2t, nullptr, nullptr, nullptr, (int)TE, D, He, D, dt, st), "transpose W2"));
+    rm::GemmArgs g1;
+    g1.dt = dt; g1.epi = rm::kEpiBias;
+    g1.M = (int)B; g1.N = He; g1.K = D; g1.G = (int)TE;
+    g1.A = w.dy; g1.a_gs = B * D; g1.a_rs = D;
+    g1.W = w.W2t; g1.b_gs = (int64_t)He * D;
+    g1.C = w.dH; g1.c_gs = B * He; g1.c_rs = He;
+    RM_TIMED("bwd_dH", st, RM_TRY(gemm_go("expert dH products", g1, st)));
+    // dH and U are group-major; dU also goes out [B][T][E*He] for the dS product
+    RM_TIMED("gelu_bwd", st, RM_HIP(rm::launch_transpose(2, w.dH, sv.U, w.dUt, w.dU, w.Ht, w.b1p, (int)TE, B, He, Bp, dt, st, -1, -1, He, TE * He), "GELU backward"));
+    RM_TIMED("tr_dy", st, RM_HIP(rm::launch_transpose(0, w.dy, nullptr, w.dyt, nullptr, nullptr, w.b2p, (int)TE, B, D, Bp, dt, st), "transpose dy"));
+    rm::GemmArgs g2;
+    g2.dt = dt; g2.epi = rm::kEpiBiasF32;
+    g2.M = D; g2.N = He; g2.K = (int)Bp; g2.G = (int)TE;
+    g2.A = w.dyt; g2.a_gs = (int64_t)D * Bp; g2.a_rs = Bp;
+    g2.W = w.Ht; g2.b_gs = (int64_t)He * Bp;
+    g2.C = g->w2; g2.c_gs = (int64_t)D * He; g2.c_rs = He;
+    RM_TIMED("bwd_dW2", st, RM_TRY(gemm_go("expert dW2 products", g2, st)));
+    RM_TIMED("tr_S", st, RM_HIP(rm::launch_transpose(0, sv.S, nullptr, w.St, nullptr, nullptr, nullptr, T, B, D, Bp, dt, st), "transpose S"));
+    rm::GemmArgs g3;
+    g3.dt = dt; g3.epi = rm::kEpiBiasF32;
+    g3.M = He; g3.N = D; g3.K = (int)Bp; g3.G = (int)TE;
+    g3.A = w.dUt; g3.a_gs = (int64_t)He * Bp; g3.a_rs = Bp;
+    g3.W = w.St; g3.b_gs = (int64_t)D * Bp; g3.b_gdiv = E;
+    g3.C = g->w1; g3.c_gs = (int64_t)He * D; g3.c_rs = D;
+    RM_TIMED("bwd_dW1", st, RM_TRY(gemm_go("expert dW1 products", g3, st)));
+  }
   // dS from the experts: per token one product over the E experts' hidden units
   // concatenated along K (dU is [B][T][E*He], W1 per token viewed as [E*He][D])
   RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->moe.w1, nullptr, w.W1tc, nullptr, nullptr, nullptr, T, (int64_t)E * He, D, (int64_t)E * He, dt, st), "transpose W1"));
@@ -1458,8 +1512,8 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
   RM_TIMED("tm_add", st, RM_HIP(rm::launch_tm_add(w.dY1, dx, B, T, D, dt, st), "token mix backward"));
   RM_TIMED("sums_ln", st, RM_HIP(rm::launch_sum_parts(w.ln2p, g->ln2_g, g->ln2_b, 1, lg, 2 * (int64_t)D, D, st), "gamma2 / beta2"));
   RM_TIMED("sums_ln", st, RM_HIP(rm::launch_sum_parts(w.ln1p, g->ln1_g, g->ln1_b, 1, lg, 2 * (int64_t)D, D, st), "gamma1 / beta1"));
-  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b2p, g->b2, nullptr, (int)TE, rt, D, D, st), "b2"));
-  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b1p, g->b1, nullptr, (int)TE, rt, He, He, st), "b1"));
+  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b2p, g->b2, nullptr, (int)TE, w.b2_parts, D, D, st), "b2"));
+  RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.b1p, g->b1, nullptr, (int)TE, w.b1_parts, He, He, st), "b1"));
   RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.brtp, g->br_train, nullptr, 1, rt, TE, TE, st), "training router bias"));
   RM_TIMED("sums_bias", st, RM_HIP(rm::launch_sum_parts(w.brip, g->br_infer, nullptr, 1, rt, TE, TE, st, lambda), "inference router bias"));
   return ok();

@@ -50,7 +50,8 @@ struct KParams {
   void* C;
   long long c_gs, c_rs;
   void* C2;  // kEpiBiasGeluDual: GELU(C), same layout as C
-  const void* aux;  // kEpiGeluBwd: the pre-activation, same layout as C
+  const void* aux;  // kEpiGeluBwd: the pre-activation, group g row m at g * aux_gs + m * aux_rs
+  long long aux_gs, aux_rs;
   float* colsum;    // kEpiGeluBwd: partial column sums
   const float* bias;
   long long bias_gs;
@@ -343,7 +344,7 @@ __device__ __forceinline__ void ring_epilogue(const KParams& p, const TileId& t,
     static_assert(BM == 256 && BN == 256, "GELU backward epilogue: 256 x 256 tiles");
     constexpr int OCH = BN / 8;    // 16-byte chunks per output row
     constexpr int RPP = NT / OCH;  // rows per pass (16)
-    const bf16* U = (const bf16*)p.aux + (long long)t.g * p.c_gs;
+    const bf16* U = (const bf16*)p.aux + (long long)t.g * p.aux_gs;
     __syncthreads();  // every wave is done reading operand slots
     // the tile's pre-activations into the LDS rows (whole row segments),
     // every load of a thread in flight at once: rows and columns past the
@@ -355,7 +356,7 @@ __device__ __forceinline__ void ring_epilogue(const KParams& p, const TileId& t,
 #pragma unroll
       for (int pass = 0; pass < BM / RPP; ++pass) {
         const int m = min(t.m0 + pass * RPP + tid / OCH, t.Mg - 1);
-        u[pass] = *reinterpret_cast<const uint4*>(U + (t.row_base + m) * p.c_rs + n);
+        u[pass] = *reinterpret_cast<const uint4*>(U + (t.row_base + m) * p.aux_rs + n);
       }
 #pragma unroll
       for (int pass = 0; pass < BM / RPP; ++pass) {
@@ -1081,6 +1082,8 @@ KParams make_params(const GemmArgs& a, int bm, int bn) {
   p.W = a.W; p.b_gs = a.b_gs; p.b_gdiv = a.b_gdiv;
   p.C = a.C; p.c_gs = a.c_gs; p.c_rs = a.c_rs; p.C2 = a.C2;
   p.aux = a.aux; p.colsum = a.colsum;
+  p.aux_gs = a.aux_gs >= 0 ? a.aux_gs : a.c_gs;
+  p.aux_rs = a.aux_rs >= 0 ? a.aux_rs : a.c_rs;
   p.bias = a.bias; p.bias_gs = a.bias_gs;
   p.rowscale = a.rowscale;
   p.row_off = a.row_off; p.tiles = a.tiles; p.ntiles = a.ntiles;
@@ -1234,7 +1237,8 @@ bool gemm_kmajor_eligible(const GemmArgs& a) {
   if (a.dt != kBF16 || a.K % 64 || a.row_off || a.a_rowidx || !a.w_kmajor || a.pipe == 0) return false;
   if (a.M < 256 || a.N < 256 || a.N % 8 || a.b_gs % 8) return false;
   if (a.a_kmajor) return a.epi == kEpiBiasF32 && a.M % 8 == 0 && a.a_rs % 8 == 0 && a.a_rs >= a.M && a.a_gs % 8 == 0;
-  return a.epi == kEpiGeluBwd && a.c_rs % 8 == 0 && a.c_gs % 8 == 0;
+  const int64_t ags = a.aux_gs >= 0 ? a.aux_gs : a.c_gs, ars = a.aux_rs >= 0 ? a.aux_rs : a.c_rs;
+  return a.epi == kEpiGeluBwd && a.c_rs % 8 == 0 && a.c_gs % 8 == 0 && ags % 8 == 0 && ars % 8 == 0;
 }
 
 int gemm_colsum_parts(int M) { return ceil_div(M, 256) * 16; }

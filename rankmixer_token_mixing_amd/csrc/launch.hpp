@@ -120,6 +120,7 @@ struct GemmArgs {
   // transposed LDS fragment reads (the weight-gradient products, K = batch)
   int a_kmajor = 0;
   const void* aux = nullptr;  // kEpiGeluBwd: the pre-activation
+  int64_t aux_gs = -1, aux_rs = -1;  // its group and row strides (elements; -1: C's)
   float* colsum = nullptr;    // kEpiGeluBwd: the partial column sums
   int tile_cfg = -1;  // -1: choose automatically
   int pipe = -1;      // 0: never use the hand-scheduled ring (for comparisons)

@@ -91,7 +91,8 @@ def _run(dtype, B, T, D, E, He, seed, separated):
     ("f32", 33, 2, 40, 4, 24, False),      # batch not a multiple of 64, heads of width 20
     ("bf16", 300, 4, 128, 4, 128, True),   # ragged batch: transposed rows padded to 320
     ("bf16", 1, 2, 16, 4, 32, True),       # one sample
-    ("bf16", 1024, 8, 256, 4, 256, True),  # pipelined products (K = batch = 1024)
+    ("bf16", 1024, 8, 256, 4, 256, True),  # no transposes: GELU' in the dH epilogue, K-major dW1 / dW2
+    ("bf16", 320, 2, 384, 4, 384, True),   # no transposes, ragged 256-tiles (B = 320, D = He = 384)
     ("f32", 96, 1, 64, 8, 32, False),      # T = 1: the token mix is the identity
 ])
 def test_moe_training_matches_oracle(dtype, B, T, D, E, He, separated):
@@ -175,3 +176,23 @@ def test_moe_empty_batch():
     assert float(l_reg.item()) == 0.0
     for k in MOE_GRADS:
         assert torch.count_nonzero(g[k]).item() == 0, k
+
+
+@pytest.mark.parametrize("B,T,D,E,He,transpose_free", [(1024, 8, 256, 4, 256, True), (320, 2, 384, 4, 384, True),
+                                                       (300, 4, 128, 4, 128, False)])
+def test_moe_backward_path_choice(B, T, D, E, He, transpose_free):
+    # bf16, a batch that is a multiple of 64 and experts at least 256 wide
+    # run without transposes of dy, H, dU or W2
+    from rankmixer_token_mixing_amd import binding as bd
+    blk = bd.upload_blocks([_block(T, D, E, He, "bf16", 3, True)])[0]
+    xd = bd.to_device(_act((B, T, D), "bf16", 4))
+    y, l_reg, saved = bd.rm_moe_block_fwd_train(xd, blk)
+    torch.cuda.synchronize()
+    bd.profile_enable(True)
+    try:
+        bd.rm_moe_block_bwd(xd, blk, saved, bd.to_device(_act((B, T, D), "bf16", 5)), LAM)
+        torch.cuda.synchronize()
+        names = set(bd.profile_read())
+    finally:
+        bd.profile_enable(False)
+    assert ("gelu_bwd" not in names and "tr_dy" not in names and "sums_dy" in names) == transpose_free, names
