@@ -593,6 +593,27 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
     ld(3, 1);
     mm(0);
     mm(1);
+    if constexpr (AT) {
+      // keep the double buffering: left alone, the scheduler moves each
+      // fragment read next to its first MFMA and waits for it there; pinned
+      // as k-step 0's reads, then each k-step's MFMAs with the next k-step's
+      // reads spread between them, the reads' latency hides under MFMAs.
+      // (With both operands transposed the fragments take few registers; on
+      // the other forms the extra live fragments spill.)
+      constexpr int NR = 2 * FM + 2 * FN;  // transposed LDS reads per k-step
+      constexpr int NM = FM * FN;          // MFMAs per k-step
+      static_assert(NM > 1, "the K-major A form has 4 x 2 blocks per wave");
+      constexpr int PER = (NR + NM - 2) / (NM - 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (kk < 3 && i < NM - 1) __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+        }
+      }
+    }
   };
 
   // prologue: A_0 -> slot 0, W_0 -> slot 1, A_1 -> slot 2
