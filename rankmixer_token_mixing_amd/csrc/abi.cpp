@@ -1237,6 +1237,17 @@ rm::GemmArgs moe_dW1_args(const void* dU, const void* S, float* C, int64_t B, in
   g.b_gdiv = E;                    // S per token
   return g;
 }
+// dS per token over the E experts' hidden units (dU [B][T][E*He]; W1 of
+// token t, [E*He][D] as stored, is the K-major W)
+rm::GemmArgs moe_dS_args(const void* dU, const void* w1, float* C, int64_t B, int T, int D, int E, int He, int dt) {
+  rm::GemmArgs g;
+  g.dt = dt; g.epi = rm::kEpiBiasF32;
+  g.M = (int)B; g.N = D; g.K = E * He; g.G = T;
+  g.A = dU; g.a_gs = (int64_t)E * He; g.a_rs = (int64_t)T * E * He;
+  g.W = w1; g.b_gs = (int64_t)D * E * He; g.w_kmajor = 1;
+  g.C = C; g.c_gs = B * D; g.c_rs = D;
+  return g;
+}
 bool moe_bwd_kmajor(int64_t B, int T, int D, int E, int He, int dt) {
   const int64_t TE = (int64_t)T * E;
   return rm::gemm_kmajor_eligible(moe_dH_args(nullptr, nullptr, nullptr, B, TE, D, He, dt)) &&
@@ -1275,7 +1286,8 @@ size_t moe_train_carve(Carver& c, int64_t B, int T, int D, int E, int He, int dt
     x.dyt = c.take((size_t)TE * D * Bp * e);
   }
   x.St = c.take((size_t)T * D * Bp * e);
-  x.W1tc = c.take((size_t)T * D * E * He * e);
+  if (!rm::gemm_wt_eligible(moe_dS_args(nullptr, nullptr, nullptr, B, T, D, E, He, dt)))
+    x.W1tc = c.take((size_t)T * D * E * He * e);
   x.dzt = c.take((size_t)TE * Bp * e);
   x.maskt = c.take((size_t)TE * Bp * e);
   x.dSr = (float*)c.take((size_t)T * B * D * 4);
@@ -1484,13 +1496,12 @@ rm_status rm_moe_block_bwd(const void* x, const rm_block_params* p, const void* 
   }
   // dS from the experts: per token one product over the E experts' hidden units
   // concatenated along K (dU is [B][T][E*He], W1 per token viewed as [E*He][D])
-  RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->moe.w1, nullptr, w.W1tc, nullptr, nullptr, nullptr, T, (int64_t)E * He, D, (int64_t)E * He, dt, st), "transpose W1"));
-  rm::GemmArgs g4;
-  g4.dt = dt; g4.epi = rm::kEpiBiasF32;
-  g4.M = (int)B; g4.N = D; g4.K = E * He; g4.G = T;
-  g4.A = w.dU; g4.a_gs = (int64_t)E * He; g4.a_rs = TE * He;
-  g4.W = w.W1tc; g4.b_gs = (int64_t)D * E * He;
-  g4.C = w.dSf; g4.c_gs = B * D; g4.c_rs = D;
+  rm::GemmArgs g4 = moe_dS_args(w.dU, p->moe.w1, w.dSf, B, T, D, E, He, dt);
+  if (!rm::gemm_wt_eligible(g4)) {
+    RM_TIMED("tr_W1", st, RM_HIP(rm::launch_transpose(0, p->moe.w1, nullptr, w.W1tc, nullptr, nullptr, nullptr, T, (int64_t)E * He, D, (int64_t)E * He, dt, st), "transpose W1"));
+    g4.W = w.W1tc;
+    g4.w_kmajor = 0;
+  }
   RM_TIMED("bwd_dS", st, RM_TRY(gemm_go("expert dS products", g4, st)));
   // routers: dWr = dz^T S (training), lambda * mask^T S (inference); biases from the column sums
   RM_TIMED("tr_router", st, RM_HIP(rm::launch_transpose(0, w.dz, nullptr, w.dzt, nullptr, nullptr, w.brtp, 1, B, TE, Bp, dt, st), "transpose dz"));

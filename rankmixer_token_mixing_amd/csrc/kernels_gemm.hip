@@ -29,6 +29,7 @@
 //    fetched from a 16-byte zero block.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "frag.hpp"
@@ -726,6 +727,132 @@ __device__ __forceinline__ void read_frags(Frags& nx, uint32_t la, uint32_t lb) 
                : [la] "v"(la), [lb] "v"(lb));
 }
 
+// ---- K-major operands (the backward products) ----------------------------
+// A K-major operand's stage slice is [64 k][256] in LDS (512-byte rows,
+// chunks swizzled by wt_swz), and each of its fragments is two transposed
+// 64-bit reads (rows +0..3 and +4..7 of the lane group's 8 k-rows, 2048
+// bytes apart), whose halves the compiler places side by side as the MFMA
+// operand.  WT: W K-major, A as above (four A reads of 16 bytes, four W
+// reads of 8 per k-step); KK: both K-major (twelve reads of 8 per k-step,
+// two behind each of the first six MFMAs).  Addresses: la (or la0..la3, one
+// per A block) and lb0, lb1 (one per W block) for the next k-step.
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+struct FragsWT {
+  u32x4 a0, a1, a2, a3;
+  u32x2 b0l, b0h, b1l, b1h;
+};
+struct FragsKK {
+  u32x2 a0l, a0h, a1l, a1h, a2l, a2h, a3l, a3h, b0l, b0h, b1l, b1h;
+};
+__device__ __forceinline__ u32x4 cat2(u32x2 lo, u32x2 hi) { return u32x4{lo.x, lo.y, hi.x, hi.y}; }
+
+// fragment addresses of one k-step: a[0] (N-major A) or a[0..3] (K-major A,
+// one per row block), b[0] (N-major W) or b[0..1] (K-major W)
+struct PAddr {
+  uint32_t a[4];
+  uint32_t b[2];
+};
+
+// the two halves of a transposed fragment: rows +0..3 at offset o0 (k-step
+// KI's 16 rows further down the slice), rows +4..7 at o1 = o0 + 2048
+#define RM_TR(dst, addr, h) "ds_read_b64_tr_b16 %[" #dst "], %[" #addr "] offset:%[o" #h "]\n\t"
+
+#define RM_KSTEP_WT_BODY(D0, D1, D2, D3)                                                                     \
+  RM_MF(c00, b0, a0) RM_RD(na0, la, 0) RM_TR(nb0l, lb0, 0) D0 RM_MF(c01, b1, a0) RM_TR(nb0h, lb0, 1)        \
+      RM_TR(nb1l, lb1, 0) RM_MF(c10, b0, a1) RM_TR(nb1h, lb1, 1) D1 RM_MF(c11, b1, a1) RM_RD(na1, la, 4096) \
+          RM_MF(c20, b0, a2) RM_RD(na2, la, 8192) D2 RM_MF(c21, b1, a2) RM_RD(na3, la, 12288)               \
+              RM_MF(c30, b0, a3) D3 RM_MF(c31, b1, a3) "s_waitcnt lgkmcnt(0)\n\t"
+#define RM_KSTEP_KK_BODY(D0, D1, D2, D3)                                                                      \
+  RM_MF(c00, b0, a0) RM_TR(na0l, la0, 0) RM_TR(na0h, la0, 1) D0 RM_MF(c01, b1, a0) RM_TR(nb0l, lb0, 0)        \
+      RM_TR(nb0h, lb0, 1) RM_MF(c10, b0, a1) RM_TR(nb1l, lb1, 0) RM_TR(nb1h, lb1, 1) D1 RM_MF(c11, b1, a1)    \
+          RM_TR(na1l, la1, 0) RM_TR(na1h, la1, 1) RM_MF(c20, b0, a2) RM_TR(na2l, la2, 0) RM_TR(na2h, la2, 1) \
+              D2 RM_MF(c21, b1, a2) RM_TR(na3l, la3, 0) RM_TR(na3h, la3, 1) RM_MF(c30, b0, a3) D3            \
+                  RM_MF(c31, b1, a3) "s_waitcnt lgkmcnt(0)\n\t"
+#define RM_D(v) RM_DMA(v) RM_M0NEXT
+
+#define RM_ACC8                                                                                \
+  [c00] "+v"(acc[0][0]), [c01] "+v"(acc[0][1]), [c10] "+v"(acc[1][0]), [c11] "+v"(acc[1][1]), \
+      [c20] "+v"(acc[2][0]), [c21] "+v"(acc[2][1]), [c30] "+v"(acc[3][0]), [c31] "+v"(acc[3][1])
+#define RM_OUT_WT                                                                                      \
+  RM_ACC8, [na0] "=&v"(nx.a0), [na1] "=&v"(nx.a1), [na2] "=&v"(nx.a2), [na3] "=&v"(nx.a3),             \
+      [nb0l] "=&v"(nx.b0l), [nb0h] "=&v"(nx.b0h), [nb1l] "=&v"(nx.b1l), [nb1h] "=&v"(nx.b1h)
+#define RM_OUT_KK                                                                                         \
+  RM_ACC8, [na0l] "=&v"(nx.a0l), [na0h] "=&v"(nx.a0h), [na1l] "=&v"(nx.a1l), [na1h] "=&v"(nx.a1h),         \
+      [na2l] "=&v"(nx.a2l), [na2h] "=&v"(nx.a2h), [na3l] "=&v"(nx.a3l), [na3h] "=&v"(nx.a3h),             \
+      [nb0l] "=&v"(nx.b0l), [nb0h] "=&v"(nx.b0h), [nb1l] "=&v"(nx.b1l), [nb1h] "=&v"(nx.b1h)
+#define RM_IN_FR [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3), [b0] "v"(b0), [b1] "v"(b1)
+#define RM_IN_DMA \
+  [mb] "s"(mb), [sb] "s"(sb), [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [ms] "n"(MS)
+#define RM_IN_OFF [o0] "n"(KI * 8192), [o1] "n"(KI * 8192 + 2048)
+#define RM_IN_WT_ADDR [la] "v"(ad.a[0]), [lb0] "v"(ad.b[0]), [lb1] "v"(ad.b[1])
+#define RM_IN_KK_ADDR \
+  [la0] "v"(ad.a[0]), [la1] "v"(ad.a[1]), [la2] "v"(ad.a[2]), [la3] "v"(ad.a[3]), [lb0] "v"(ad.b[0]), [lb1] "v"(ad.b[1])
+
+// k-step KI (0..3) of a stage; K-major addresses are the stage's, N-major
+// ones already the k-step's
+template <int KI>
+__device__ __forceinline__ void kstep(floatx16 (&acc)[4][2], const FragsWT& cu, FragsWT& nx, const PAddr& ad) {
+  const u32x4 a0 = cu.a0, a1 = cu.a1, a2 = cu.a2, a3 = cu.a3, b0 = cat2(cu.b0l, cu.b0h), b1 = cat2(cu.b1l, cu.b1h);
+  asm volatile(RM_KSTEP_WT_BODY("", "", "", "") : RM_OUT_WT : RM_IN_FR, RM_IN_WT_ADDR, RM_IN_OFF);
+}
+template <int MS, int KI>
+__device__ __forceinline__ void kstep_dma(floatx16 (&acc)[4][2], const FragsWT& cu, FragsWT& nx, const PAddr& ad,
+                                          uint32_t mb, const void* sb, const uint32_t* v) {
+  const u32x4 a0 = cu.a0, a1 = cu.a1, a2 = cu.a2, a3 = cu.a3, b0 = cat2(cu.b0l, cu.b0h), b1 = cat2(cu.b1l, cu.b1h);
+  asm volatile("s_mov_b32 m0, %[mb]\n\t" RM_KSTEP_WT_BODY(RM_D(v0), RM_D(v1), RM_D(v2), RM_DMA(v3))
+               : RM_OUT_WT
+               : RM_IN_FR, RM_IN_WT_ADDR, RM_IN_OFF, RM_IN_DMA
+               : "m0", "scc");
+}
+__device__ __forceinline__ void read_frags(FragsWT& nx, const PAddr& ad) {
+  constexpr int KI = 0;
+  asm volatile(RM_RD(na0, la, 0) RM_TR(nb0l, lb0, 0) RM_TR(nb0h, lb0, 1) RM_TR(nb1l, lb1, 0) RM_TR(nb1h, lb1, 1)
+                   RM_RD(na1, la, 4096) RM_RD(na2, la, 8192) RM_RD(na3, la, 12288) "s_waitcnt lgkmcnt(0)\n\t"
+               : [na0] "=&v"(nx.a0), [na1] "=&v"(nx.a1), [na2] "=&v"(nx.a2), [na3] "=&v"(nx.a3),
+                 [nb0l] "=&v"(nx.b0l), [nb0h] "=&v"(nx.b0h), [nb1l] "=&v"(nx.b1l), [nb1h] "=&v"(nx.b1h)
+               : RM_IN_WT_ADDR, RM_IN_OFF);
+}
+
+template <int KI>
+__device__ __forceinline__ void kstep(floatx16 (&acc)[4][2], const FragsKK& cu, FragsKK& nx, const PAddr& ad) {
+  const u32x4 a0 = cat2(cu.a0l, cu.a0h), a1 = cat2(cu.a1l, cu.a1h), a2 = cat2(cu.a2l, cu.a2h),
+              a3 = cat2(cu.a3l, cu.a3h), b0 = cat2(cu.b0l, cu.b0h), b1 = cat2(cu.b1l, cu.b1h);
+  asm volatile(RM_KSTEP_KK_BODY("", "", "", "") : RM_OUT_KK : RM_IN_FR, RM_IN_KK_ADDR, RM_IN_OFF);
+}
+template <int MS, int KI>
+__device__ __forceinline__ void kstep_dma(floatx16 (&acc)[4][2], const FragsKK& cu, FragsKK& nx, const PAddr& ad,
+                                          uint32_t mb, const void* sb, const uint32_t* v) {
+  const u32x4 a0 = cat2(cu.a0l, cu.a0h), a1 = cat2(cu.a1l, cu.a1h), a2 = cat2(cu.a2l, cu.a2h),
+              a3 = cat2(cu.a3l, cu.a3h), b0 = cat2(cu.b0l, cu.b0h), b1 = cat2(cu.b1l, cu.b1h);
+  asm volatile("s_mov_b32 m0, %[mb]\n\t" RM_KSTEP_KK_BODY(RM_D(v0), RM_D(v1), RM_D(v2), RM_DMA(v3))
+               : RM_OUT_KK
+               : RM_IN_FR, RM_IN_KK_ADDR, RM_IN_OFF, RM_IN_DMA
+               : "m0", "scc");
+}
+__device__ __forceinline__ void read_frags(FragsKK& nx, const PAddr& ad) {
+  constexpr int KI = 0;
+  asm volatile(RM_TR(na0l, la0, 0) RM_TR(na0h, la0, 1) RM_TR(nb0l, lb0, 0) RM_TR(nb0h, lb0, 1) RM_TR(nb1l, lb1, 0)
+                   RM_TR(nb1h, lb1, 1) RM_TR(na1l, la1, 0) RM_TR(na1h, la1, 1) RM_TR(na2l, la2, 0)
+                       RM_TR(na2h, la2, 1) RM_TR(na3l, la3, 0) RM_TR(na3h, la3, 1) "s_waitcnt lgkmcnt(0)\n\t"
+               : [na0l] "=&v"(nx.a0l), [na0h] "=&v"(nx.a0h), [na1l] "=&v"(nx.a1l), [na1h] "=&v"(nx.a1h),
+                 [na2l] "=&v"(nx.a2l), [na2h] "=&v"(nx.a2h), [na3l] "=&v"(nx.a3l), [na3h] "=&v"(nx.a3h),
+                 [nb0l] "=&v"(nx.b0l), [nb0h] "=&v"(nx.b0h), [nb1l] "=&v"(nx.b1l), [nb1h] "=&v"(nx.b1h)
+               : RM_IN_KK_ADDR, RM_IN_OFF);
+}
+
+// the N-major form through the same interface
+template <int KI>
+__device__ __forceinline__ void kstep(floatx16 (&acc)[4][2], const Frags& cu, Frags& nx, const PAddr& ad) {
+  kstep(acc, cu, nx, ad.a[0], ad.b[0]);
+}
+template <int MS, int KI>
+__device__ __forceinline__ void kstep_dma(floatx16 (&acc)[4][2], const Frags& cu, Frags& nx, const PAddr& ad,
+                                          uint32_t mb, const void* sb, const uint32_t* v) {
+  kstep_dma<MS>(acc, cu, nx, ad.a[0], ad.b[0], mb, sb, v);
+}
+__device__ __forceinline__ void read_frags(Frags& nx, const PAddr& ad) { read_frags(nx, ad.a[0], ad.b[0]); }
+
 // Start value of the pipelined kernel's accumulators: the bias of each
 // accumulator's column (zero without bias), so the epilogue adds nothing.
 // Register 4q+e of block (i, j) holds column wn*FN*32 + j*32 + 8q + 4lh + e
@@ -846,6 +973,95 @@ __device__ __forceinline__ void pipe_epilogue_bf16(const KParams& p, const TileI
   }
 }
 
+// GELU-backward epilogue of the persistent pipelined ring (256 x 256 tiles):
+// C = acc * GELU'(U), rounded to bf16, in the halves of the bf16 epilogue.
+// Per half: the half's 128 rows of U into the staging slots (whole row
+// segments, every load of a thread in flight at once; rows and columns past
+// the end re-read the last ones, their results neither stored nor summed),
+// C computed in place, then stored.  Each thread also sums its 8 columns over
+// the rows it stores -- the tile rows congruent to tid / 32 mod 16 -- into
+// colsum[(g * tiles_m + m0 / 256) * 16 + tid / 32][N].
+template <int NWM, int NWN, int FN, typename Init>
+__device__ __forceinline__ void pipe_epilogue_gelubwd(const KParams& p, const TileId& t,
+                                                      const floatx16 (&acc)[4][FN], int wave, int lane, char* stage,
+                                                      Init& init_next) {
+  constexpr int BN = NWN * FN * 32, NT = NWM * NWN * kWave;
+  constexpr int OCH = BN / 8;      // 16-byte chunks per output row
+  constexpr int RPP = NT / OCH;    // staging rows per store pass (16)
+  constexpr int SROWS = NWM * 64;  // staging rows per half
+  static_assert(NWM * 128 == 256 && BN == 256 && RPP == 16, "GELU backward epilogue: 256 x 256 tiles");
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int tid = threadIdx.x;
+  const bf16* U = (const bf16*)p.aux + (long long)t.g * p.aux_gs;
+  const int c = tid % OCH;
+  const int n = t.n0 + c * 8;
+  float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // staging row sr of half h holds tile row (sr / 64) * 128 + 64 h + sr % 64
+  auto tile_row = [&](int sr, int h) { return (sr / 64) * 128 + h * 64 + (sr % 64); };
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    {
+      const int nu = min(n, p.N - 8);
+      uint4 u[SROWS / RPP];
+#pragma unroll
+      for (int pass = 0; pass < SROWS / RPP; ++pass) {
+        const int m = min(t.m0 + tile_row(pass * RPP + tid / OCH, h), t.Mg - 1);
+        u[pass] = *reinterpret_cast<const uint4*>(U + (t.row_base + m) * p.aux_rs + nu);
+      }
+#pragma unroll
+      for (int pass = 0; pass < SROWS / RPP; ++pass) {
+        const int sr = pass * RPP + tid / OCH;
+        *reinterpret_cast<uint4*>(stage + sr * (BN * 2) + ((c ^ (sr & (OCH - 1))) * 16)) = u[pass];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * h + ii;
+      const int sr = wm * 64 + ii * 32 + lr;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wn * FN * 32 + j * 32 + 8 * q + 4 * lh;
+          const int phys = (nl >> 3) ^ (sr & (OCH - 1));
+          bf16* cell = reinterpret_cast<bf16*>(stage + sr * (BN * 2) + phys * 16 + (nl & 7) * 2);
+          float u[4], v[4];
+          load_f32<bf16, 4>(cell, u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float gu, dgu;
+            gelu_and_grad(u[e], gu, dgu);
+            v[e] = acc[i][j][4 * q + e] * dgu;
+          }
+          store_from_f32<bf16, 4>(cell, v);
+        }
+    }
+    if (h == 1) init_next();  // the accumulators are read for the last time above
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < SROWS / RPP; ++pass) {
+      const int sr = pass * RPP + tid / OCH;
+      const int m = t.m0 + tile_row(sr, h);
+      const uint4 val = *reinterpret_cast<const uint4*>(stage + sr * (BN * 2) + ((c ^ (sr & (OCH - 1))) * 16));
+      if (m < t.Mg && n < p.N) {
+        *reinterpret_cast<uint4*>((bf16*)p.C + (t.row_base + m) * p.c_rs + (long long)t.g * p.c_gs + n) = val;
+        float f[8];
+        load_f32<bf16, 8>(reinterpret_cast<const bf16*>(&val), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[e] += f[e];
+      }
+    }
+    __syncthreads();  // staging is free again
+  }
+  if (n < p.N) {
+    float* dst = p.colsum + ((long long)(t.g * p.tiles_m + t.m0 / 256) * RPP + tid / OCH) * p.N + n;
+    *reinterpret_cast<float4*>(dst) = make_float4(cs[0], cs[1], cs[2], cs[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(cs[4], cs[5], cs[6], cs[7]);
+  }
+}
+
 // fp32 epilogue of the persistent pipelined ring, in four quarters through
 // slots 3 and 4: quarter i holds accumulator row block i of every wave, tile
 // rows wm*128 + 32i + lr at staging row wm*32 + lr, BN*4 bytes per row in
@@ -897,7 +1113,7 @@ __device__ __forceinline__ void pipe_epilogue_f32(const KParams& p, const TileId
 // RAGGED: the tiles are the device-side (group, m0) list times the N tiles,
 // group g's rows start at row_off[g]; AIDX: A row m of group g is row
 // a_rowidx[row_off[g] + m] of that group's A.
-template <int NWM, int NWN, int EPI, bool RAGGED, bool AIDX>
+template <int NWM, int NWN, int EPI, bool RAGGED, bool AIDX, bool WT = false, bool AT = false>
 __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
   constexpr int FM = 4, FN = 2;
   typedef Ring<NWM, NWN, FM, FN> RG;
@@ -905,6 +1121,9 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
   constexpr int A_DMA = RG::A_DMA, B_DMA = RG::B_DMA;
   constexpr uint32_t SLOTB = RG::SLOT * 16;  // bytes per slot
   static_assert(B_DMA == 4 && (A_DMA == 4 || A_DMA == 8), "DMA ops come in blocks of four");
+  static_assert(!WT || (BM == 256 && BN == 256 && !RAGGED && !AIDX), "K-major operands: 256 x 256 tiles, dense");
+  static_assert(!AT || WT, "a K-major A comes with a K-major W");
+  typedef typename std::conditional<AT, FragsKK, typename std::conditional<WT, FragsWT, Frags>::type>::type FR;
   static_assert(BM / 2 * BN * 2 <= 2 * (int)SLOTB && BM / 4 * BN * 4 <= 2 * (int)SLOTB,
                 "a staged part of the output tile must fit in two slots");
 
@@ -957,15 +1176,36 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
   auto setup = [&](const TileId& t) {
     Ab = (const char*)p.A + (long long)(t.g / p.a_gdiv) * p.a_gs * 2;
     Bb = (const char*)p.W + (long long)(t.g / p.b_gdiv) * p.b_gs * 2;
+    if constexpr (AT) {
+      // 1 KB block (wave + i*NW) of the [64][BM] slice: k-row r, LDS chunk c
+      // holds the row's chunk c ^ wt_swz(r); columns past M re-read the
+      // row's last chunk
 #pragma unroll
-    for (int i = 0; i < A_DMA; ++i) {
+      for (int i = 0; i < A_DMA; ++i) {
+        const int q = (wave + i * NW) * 64 + lane;
+        const int r = q / (BM / 8), c = q % (BM / 8);
+        const int m = min(t.m0 + ((c ^ wt_swz(r)) * 8), p.M - 8);
+        va[i] = (uint32_t)(((long long)r * p.a_rs + m) * 2);
+      }
+    }
+    if constexpr (WT) {
+#pragma unroll
+      for (int i = 0; i < B_DMA; ++i) {
+        const int q = (wave + i * NW) * 64 + lane;
+        const int r = q / (BN / 8), c = q % (BN / 8);
+        const int n = min(t.n0 + ((c ^ wt_swz(r)) * 8), p.N - 8);
+        vw[i] = (uint32_t)(((long long)r * p.N + n) * 2);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (AT ? 0 : A_DMA); ++i) {
       const int row = 8 * (wave + i * NW) + (lane >> 3);
       const int m = min(t.m0 + row, t.Mg - 1);  // rows past the end re-read the last row
       const long long r = AIDX ? (long long)p.a_rowidx[t.row_base + m] : t.row_base + m;
       va[i] = (uint32_t)((r * p.a_rs + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
     }
 #pragma unroll
-    for (int i = 0; i < B_DMA; ++i) {
+    for (int i = 0; i < (WT ? 0 : B_DMA); ++i) {
       const int row = 8 * (wave + i * NW) + (lane >> 3);
       int n;
       if constexpr (EPI == kEpiSwiglu) {
@@ -980,17 +1220,27 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
       vw[i] = (uint32_t)(((long long)n * K + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
     }
   };
-  auto kbase = [&](const char* base, int kt) -> const void* { return base + (long long)min(kt, nk - 1) * 128; };
+  // stage kt's slice: 128 bytes further along each row (N-major) or 64 rows
+  // further down (K-major); slices past the end re-read the last one
+  const long long a_kst = AT ? 128LL * p.a_rs : 128, w_kst = WT ? 128LL * p.N : 128;
+  auto kbase = [&](const char* base, long long kst, int kt) -> const void* {
+    return base + (long long)min(kt, nk - 1) * kst;
+  };
   auto issue_a = [&](int s, int kt) {
 #pragma unroll
-    for (int i = 0; i < A_DMA; ++i) dma1(slot(s) + wof + i * NW * 1024, kbase(Ab, kt), va[i]);
+    for (int i = 0; i < A_DMA; ++i) dma1(slot(s) + wof + i * NW * 1024, kbase(Ab, a_kst, kt), va[i]);
   };
   auto issue_w = [&](int s, int kt) {
 #pragma unroll
-    for (int i = 0; i < B_DMA; ++i) dma1(slot(s) + wof + i * NW * 1024, kbase(Bb, kt), vw[i]);
+    for (int i = 0; i < B_DMA; ++i) dma1(slot(s) + wof + i * NW * 1024, kbase(Bb, w_kst, kt), vw[i]);
   };
 
-  // fragment address of lane for k-step kk: row * 128 + swizzled chunk
+  // fragment address of lane for k-step kk.  N-major: row * 128 + swizzled
+  // chunk, per kk.  K-major: lane group g4 = lane / 16 takes k-rows
+  // 8 * (g4 / 2) .. +7 of the k-step and columns 16 * (g4 % 2) .. +15 of the
+  // 32-column block, lane i16 row i16 / 4 of each 4-row half and columns
+  // 4 * (i16 % 4) .. +3; the swizzle depends on k-row bits the k-step and
+  // half do not change, so they are the offsets kk * 16 rows (+ 4 rows)
   const int wm = wave / NWN, wn = wave % NWN;
   const int lr = lane & 31, lh = lane >> 5;
   uint32_t oa[4], ob[4];
@@ -1000,6 +1250,32 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
     oa[kk] = (uint32_t)(wm * FM * 32 + lr) * 128 + ch;
     ob[kk] = (uint32_t)(wn * FN * 32 + lr) * 128 + ch;
   }
+  uint32_t ota[4], otb[2];
+  {
+    const int g4 = lane >> 4, i16 = lane & 15;
+    const int r0 = (g4 >> 1) * 8 + (i16 >> 2), sw = wt_swz(r0);
+    const int cl = (g4 & 1) * 16 + 4 * (i16 & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = wm * FM * 32 + i * 32 + cl;
+      ota[i] = (uint32_t)(r0 * (BM * 2) + (((col >> 3) ^ sw) << 4) + (col & 7) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = wn * FN * 32 + j * 32 + cl;
+      otb[j] = (uint32_t)(r0 * (BN * 2) + (((col >> 3) ^ sw) << 4) + (col & 7) * 2);
+    }
+  }
+  // a K-major operand's addresses are the stage's (the k-step is an
+  // immediate offset of the read), an N-major one's the k-step's
+  auto paddr = [&](uint32_t sA, uint32_t sW, int kk) {
+    PAddr ad;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ad.a[i] = AT ? sA + ota[i] : sA + oa[kk];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) ad.b[j] = WT ? sW + otb[j] : sW + ob[kk];
+    return ad;
+  };
 
   TileId t;
   tile_of(v, t);
@@ -1016,25 +1292,25 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
     issue_w(3, 1);
     wait_vmcnt<B_DMA>();
     __builtin_amdgcn_s_barrier();
-    Frags f0, f1;
-    read_frags(f0, slot(0) + oa[0], slot(1) + ob[0]);
+    FR f0, f1;
+    read_frags(f0, paddr(slot(0), slot(1), 0));
 
     for (int k = 0; k < nk; ++k) {
       const uint32_t sA = slot(2 * k), sW = slot(2 * k + 1);
       // A_{k+2} into the slot of W_{k-1}
       const uint32_t dA = slot(2 * k + 4) + wof;
-      kstep_dma<NW * 1024>(acc, f0, f1, sA + oa[1], sW + ob[1], dA, kbase(Ab, k + 2), va);
+      kstep_dma<NW * 1024, 1>(acc, f0, f1, paddr(sA, sW, 1), dA, kbase(Ab, a_kst, k + 2), va);
       if constexpr (A_DMA == 8)
-        kstep_dma<NW * 1024>(acc, f1, f0, sA + oa[2], sW + ob[2], dA + 4 * NW * 1024, kbase(Ab, k + 2), va + 4);
+        kstep_dma<NW * 1024, 2>(acc, f1, f0, paddr(sA, sW, 2), dA + 4 * NW * 1024, kbase(Ab, a_kst, k + 2), va + 4);
       else
-        kstep(acc, f1, f0, sA + oa[2], sW + ob[2]);
-      kstep(acc, f0, f1, sA + oa[3], sW + ob[3]);
+        kstep<2>(acc, f1, f0, paddr(sA, sW, 2));
+      kstep<3>(acc, f0, f1, paddr(sA, sW, 3));
       // everything but A_{k+2} has landed: A_{k+1} and W_{k+1}
       wait_vmcnt<A_DMA>();
       __builtin_amdgcn_s_barrier();
       // stage k's slots are free: W_{k+2} into A_k's; read stage k+1's first fragments
-      kstep_dma<NW * 1024>(acc, f1, f0, slot(2 * k + 2) + oa[0], slot(2 * k + 3) + ob[0], sA + wof,
-                           kbase(Bb, k + 2), vw);
+      kstep_dma<NW * 1024, 0>(acc, f1, f0, paddr(slot(2 * k + 2), slot(2 * k + 3), 0), sA + wof,
+                           kbase(Bb, w_kst, k + 2), vw);
     }
     wait_vmcnt<0>();  // no DMA may land in LDS after this point
     // the last MFMAs' results are read by ordinary code from here on
@@ -1058,6 +1334,8 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
     if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias || EPI == kEpiSwiglu || EPI == kEpiBiasScale ||
                   EPI == kEpiBiasGeluDual)
       pipe_epilogue_bf16<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB, init_next);
+    else if constexpr (EPI == kEpiGeluBwd)
+      pipe_epilogue_gelubwd<NWM, NWN, FN>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB, init_next);
     else
       pipe_epilogue_f32<NWM, NWN, FN, EPI>(p, cur, acc, wave, lane, (char*)lds + 3 * SLOTB, init_next);
     if (!more) break;
@@ -1082,6 +1360,15 @@ constexpr int kNumCfgs = 4;
 constexpr int kMoeCfg = 0;  // ragged expert products: 256 x 256 tiles
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// K-major operands on the pipelined kernel: every DMA offset is 32-bit (the
+// N-major A's rows, as for the forward products; a K-major slice spans 64
+// rows of its operand)
+bool gemm_kmajor_pipe_fits(const GemmArgs& a) {
+  const long long lim = 1LL << 32;
+  const bool a_fits = a.a_kmajor ? (63LL * a.a_rs + a.M) * 2 < lim : ((long long)(a.M - 1) * a.a_rs + a.K) * 2 < lim;
+  return a_fits && (63LL * a.N + a.N) * 2 < lim;
+}
 
 
 int choose_cfg(const GemmArgs& a) {
@@ -1146,6 +1433,24 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
     if constexpr (FM == 4 && FN == 2 && NWN == 4) {
       if (!ring || ragged) return hipErrorInvalidValue;
       const dim3 block(NWM * NWN * kWave);
+      // the backward products (fp32 result, or GELU backward) on the
+      // hand-scheduled persistent form, one workgroup per CU; the forward
+      // epilogues on a K-major W stay on the ring
+      if (a.pipe != 0 && gemm_kmajor_pipe_fits(a) && (a.epi == kEpiBiasF32 || a.epi == kEpiGeluBwd)) {
+        const int cus = device_cus();
+        const dim3 grid2(grid.x <= (unsigned)cus ? grid.x : (unsigned)(cus / 8 * 8 > 0 ? cus / 8 * 8 : cus));
+        if (a.a_kmajor && a.epi == kEpiBiasF32)
+          hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasF32, false, false, true, true>), grid2, block, 0, s, p);
+        else if (a.a_kmajor)
+          return hipErrorInvalidValue;
+        else if (a.epi == kEpiBiasF32)
+          hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiBiasF32, false, false, true>), grid2, block, 0, s, p);
+        else if (a.aux && a.colsum)
+          hipLaunchKernelGGL((k_gemm_pipe<NWM, NWN, kEpiGeluBwd, false, false, true>), grid2, block, 0, s, p);
+        else
+          return hipErrorInvalidValue;
+        return hipGetLastError();
+      }
       if (a.a_kmajor) {
         // both operands [K][.]: the weight-gradient products
         if (a.epi != kEpiBiasF32) return hipErrorInvalidValue;
@@ -1249,6 +1554,9 @@ int gemm_tile_m(const GemmArgs& a) { return kCfgs[choose_cfg(a)].bm(); }
 
 bool gemm_wt_eligible(const GemmArgs& a) {
   if (a.dt != kBF16 || a.K % 64 || a.row_off || a.N % 8 || a.N < 256) return false;
+  // the backward's fp32 products (dS) take 256 x 256 tiles whatever their
+  // count: the alternative is a transposed copy of the weight
+  if (a.epi == kEpiBiasF32 && a.M >= 256) return true;
   GemmArgs b = a;
   b.w_kmajor = 0;
   return choose_cfg(b) == 0;

@@ -112,8 +112,10 @@ struct GemmArgs {
   const int* ntiles = nullptr;
   int max_mtiles = 0;
   // W group stored K-major, [K][N] (element (k, n) at (g / b_gdiv) * b_gs +
-  // k * N + n): the compiler-scheduled ring with transposed LDS fragment
-  // reads, where gemm_wt_eligible (bf16, K % 64 == 0, dense, 256 x 256 tiles)
+  // k * N + n), read along its rows with transposed LDS fragment reads, where
+  // gemm_wt_eligible (bf16, K % 64 == 0, dense, 256 x 256 tiles): the
+  // backward epilogues (fp32 result, GELU backward) on the hand-scheduled
+  // pipelined kernel, the forward ones on the compiler-scheduled ring
   int w_kmajor = 0;
   // A group stored K-major, [K][M] (element (k, m) at (g / a_gdiv) * a_gs +
   // k * a_rs + m), with w_kmajor: both operands read along their rows with
@@ -143,10 +145,12 @@ bool epilogue_overlap();
 hipError_t launch_gemm_defer(const GemmArgs& a, hipStream_t s);
 // whether launch_gemm takes `a` with a K-major W (w_kmajor)
 bool gemm_wt_eligible(const GemmArgs& a);
-// whether launch_gemm takes `a` on the K-major ring with 256 x 256 tiles
+// whether launch_gemm takes `a` with K-major operands and 256 x 256 tiles
 // whatever the tile count: both operands K-major (a_kmajor, w_kmajor,
 // kEpiBiasF32) or a K-major W with the kEpiGeluBwd epilogue.  bf16, dense,
-// K a multiple of 64, M and N at least 256 and multiples of 8
+// K a multiple of 64, M and N at least 256 and multiples of 8.  They run on
+// the hand-scheduled pipelined kernel (the ring where a 32-bit DMA offset
+// would not fit)
 bool gemm_kmajor_eligible(const GemmArgs& a);
 // number of partial column sums per group that kEpiGeluBwd writes
 int gemm_colsum_parts(int M);

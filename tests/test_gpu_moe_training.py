@@ -196,3 +196,5 @@ def test_moe_backward_path_choice(B, T, D, E, He, transpose_free):
     finally:
         bd.profile_enable(False)
     assert ("gelu_bwd" not in names and "tr_dy" not in names and "sums_dy" in names) == transpose_free, names
+    # dS reads each token's W1 as stored where the product is at least 256 x 256
+    assert ("tr_W1" not in names) == (B >= 256 and D >= 256), names
