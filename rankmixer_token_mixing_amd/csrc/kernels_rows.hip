@@ -101,12 +101,17 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_token_mix(const void*
 // ---------------------------------------------------------------------------
 // S[b,t,:] = LN(TokenMix(X)[b,t,:] + X[b,t,:]) * g + beta.  One wave per row.
 // Element k of mixed token t is element t*d + (k mod d) of token k / d.
+// Rows move in 16-byte chunks (OV elements); the gather takes each chunk in
+// pieces of VEC elements (VEC divides the head width d, so a piece never
+// crosses a head).
 
 template <typename T, int VEC, int MAXI>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __restrict__ x, T* __restrict__ s,
                                                                   const float* __restrict__ g,
                                                                   const float* __restrict__ beta,
                                                                   int64_t B, int T_, int D, int token_major) {
+  constexpr int OV = 16 / (int)sizeof(T), PV = OV / VEC;
+  static_assert(OV % VEC == 0, "pieces of a chunk");
   // the T rows of one sample gather from the same [T][D] block: keep them on
   // one XCD so the second read of each element hits its L2
   const int64_t row = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * kRowsPerBlock + (threadIdx.x / kWave);
@@ -116,20 +121,27 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __res
   const int t = (int)(row - b * T_);
   const int d = D / T_;
   const T* xb = x + b * (int64_t)T_ * D;
-  const int nch = D / VEC;
-  float v[MAXI][VEC];
+  const int nch = D / OV;
+  float v[MAXI][OV];
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     const int c = lane + i * kWave;
     if (c < nch) {
-      const int k = c * VEC;
-      const int tp = k / d, j = k - tp * d;
-      float m[VEC], r[VEC];
-      load_f32<T, VEC>(xb + (int64_t)tp * D + t * d + j, m);
-      load_f32<T, VEC>(xb + (int64_t)t * D + k, r);
+      const int k = c * OV;
+      float m[OV], r[OV];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
+      for (int pc = 0; pc < PV; ++pc) {
+        const int kp = k + pc * VEC;
+        const int tp = kp / d, j = kp - tp * d;
+        float piece[VEC];
+        load_f32<T, VEC>(xb + (int64_t)tp * D + t * d + j, piece);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) m[pc * VEC + e] = piece[e];
+      }
+      load_f32<T, OV>(xb + (int64_t)t * D + k, r);
+#pragma unroll
+      for (int e = 0; e < OV; ++e) {
         v[i][e] = m[e] + r[e];
         sum += v[i][e];
       }
@@ -142,7 +154,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __res
     const int c = lane + i * kWave;
     if (c < nch) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
+      for (int e = 0; e < OV; ++e) {
         const float q = v[i][e] - mean;
         sq += q * q;
       }
@@ -155,11 +167,11 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __res
   for (int i = 0; i < MAXI; ++i) {
     const int c = lane + i * kWave;
     if (c < nch) {
-      const int k = c * VEC;
-      float o[VEC];
+      const int k = c * OV;
+      float o[OV];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) o[e] = (v[i][e] - mean) * rstd * g[k + e] + beta[k + e];
-      store_from_f32<T, VEC>(sr + k, o);
+      for (int e = 0; e < OV; ++e) o[e] = (v[i][e] - mean) * rstd * g[k + e] + beta[k + e];
+      store_from_f32<T, OV>(sr + k, o);
     }
   }
 }
@@ -247,18 +259,20 @@ __global__ __launch_bounds__(kBndThreads) void k_ln_mix_ln(const T* __restrict__
                                                            const float* __restrict__ g1,
                                                            const float* __restrict__ be1, int64_t B, int T_,
                                                            int D, int pitch) {
+  constexpr int OV = 16 / (int)sizeof(T), PV = OV / VEC;  // 16-byte chunks, gathered in pieces of VEC
+  static_assert(OV % VEC == 0, "pieces of a chunk");
   extern __shared__ uint4 bnd_lds[];
   T* xl = reinterpret_cast<T*>(bnd_lds);
   const int NW = blockDim.x / kWave;  // T/2 waves (at most 16): two rows each
   const int64_t b = blockIdx.x;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int d = D / T_, nch = D / VEC;
+  const int d = D / T_, nch = D / OV;
   // phase 1, two rows per wave at a time: every load of both rows is issued
   // before any is used (chunk indices past the row re-read its last chunk and
   // are left out of the sums and stores)
   for (int t0 = wave; t0 < T_; t0 += 2 * NW) {
     const int tr[2] = {t0, t0 + NW < T_ ? t0 + NW : t0};
-    float v[2][MAXI][VEC], q[2][MAXI][VEC];
+    float v[2][MAXI][OV], q[2][MAXI][OV];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const T* zr = z + (b * T_ + tr[r]) * (int64_t)D;
@@ -266,8 +280,8 @@ __global__ __launch_bounds__(kBndThreads) void k_ln_mix_ln(const T* __restrict__
 #pragma unroll
       for (int i = 0; i < MAXI; ++i) {
         const int c = min(lane + i * kWave, nch - 1);
-        load_f32<T, VEC>(zr + c * VEC, v[r][i]);
-        load_f32<T, VEC>(sr + c * VEC, q[r][i]);
+        load_f32<T, OV>(zr + c * OV, v[r][i]);
+        load_f32<T, OV>(sr + c * OV, q[r][i]);
       }
     }
 #pragma unroll
@@ -278,7 +292,7 @@ __global__ __launch_bounds__(kBndThreads) void k_ln_mix_ln(const T* __restrict__
       for (int i = 0; i < MAXI; ++i) {
         const bool in = lane + i * kWave < nch;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
+        for (int e = 0; e < OV; ++e) {
           v[r][i][e] += q[r][i][e];
           sum += in ? v[r][i][e] : 0.f;
         }
@@ -289,7 +303,7 @@ __global__ __launch_bounds__(kBndThreads) void k_ln_mix_ln(const T* __restrict__
       for (int i = 0; i < MAXI; ++i) {
         const bool in = lane + i * kWave < nch;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
+        for (int e = 0; e < OV; ++e) {
           const float dv = v[r][i][e] - mean;
           sq += in ? dv * dv : 0.f;
         }
@@ -299,30 +313,37 @@ __global__ __launch_bounds__(kBndThreads) void k_ln_mix_ln(const T* __restrict__
       for (int i = 0; i < MAXI; ++i) {
         const int c = lane + i * kWave;
         if (c < nch) {
-          const int k = c * VEC;
-          float o[VEC];
+          const int k = c * OV;
+          float o[OV];
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) o[e] = (v[r][i][e] - mean) * rstd * g2[k + e] + be2[k + e];
-          store_from_f32<T, VEC>(xl + tr[r] * pitch + k, o);
+          for (int e = 0; e < OV; ++e) o[e] = (v[r][i][e] - mean) * rstd * g2[k + e] + be2[k + e];
+          store_from_f32<T, OV>(xl + tr[r] * pitch + k, o);
         }
       }
     }
   }
   __syncthreads();
   for (int h = wave; h < T_; h += NW) {
-    float v[MAXI][VEC];
+    float v[MAXI][OV];
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
       const int c = lane + i * kWave;
       if (c < nch) {
-        const int k = c * VEC;
-        const int tp = k / d, j = k - tp * d;
-        float m[VEC], r[VEC];
-        load_f32<T, VEC>(xl + tp * pitch + h * d + j, m);
-        load_f32<T, VEC>(xl + h * pitch + k, r);
+        const int k = c * OV;
+        float m[OV], r[OV];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
+        for (int pc = 0; pc < PV; ++pc) {
+          const int kp = k + pc * VEC;
+          const int tp = kp / d, j = kp - tp * d;
+          float piece[VEC];
+          load_f32<T, VEC>(xl + tp * pitch + h * d + j, piece);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) m[pc * VEC + e] = piece[e];
+        }
+        load_f32<T, OV>(xl + h * pitch + k, r);
+#pragma unroll
+        for (int e = 0; e < OV; ++e) {
           v[i][e] = m[e] + r[e];
           sum += v[i][e];
         }
@@ -335,7 +356,7 @@ __global__ __launch_bounds__(kBndThreads) void k_ln_mix_ln(const T* __restrict__
       const int c = lane + i * kWave;
       if (c < nch) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
+        for (int e = 0; e < OV; ++e) {
           const float q = v[i][e] - mean;
           sq += q * q;
         }
@@ -347,11 +368,11 @@ __global__ __launch_bounds__(kBndThreads) void k_ln_mix_ln(const T* __restrict__
     for (int i = 0; i < MAXI; ++i) {
       const int c = lane + i * kWave;
       if (c < nch) {
-        const int k = c * VEC;
-        float o[VEC];
+        const int k = c * OV;
+        float o[OV];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) o[e] = (v[i][e] - mean) * rstd * g1[k + e] + be1[k + e];
-        store_from_f32<T, VEC>(orow + k, o);
+        for (int e = 0; e < OV; ++e) o[e] = (v[i][e] - mean) * rstd * g1[k + e] + be1[k + e];
+        store_from_f32<T, OV>(orow + k, o);
       }
     }
   }
@@ -441,7 +462,7 @@ hipError_t mix_ln_vec(const void* x, void* so, const float* g, const float* b, i
   const dim3 grid((unsigned)((B * T_ + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
   const T* xx = (const T*)x;
   T* ss = (T*)so;
-  switch (pick_maxi(D / VEC)) {
+  switch (pick_maxi(D / (16 / (int)sizeof(T)))) {
     case 0: return hipErrorInvalidValue;
     case 1: hipLaunchKernelGGL((k_mix_ln<T, VEC, 1>), grid, block, 0, s, xx, ss, g, b, B, T_, D, tm); break;
     case 2: hipLaunchKernelGGL((k_mix_ln<T, VEC, 2>), grid, block, 0, s, xx, ss, g, b, B, T_, D, tm); break;
@@ -517,7 +538,7 @@ hipError_t ln_mix_ln_vec(const void* z, void* s, const float* g2, const float* b
   const dim3 grid((unsigned)B), block(nw * kWave);
   const T* zz = (const T*)z;
   T* ss = (T*)s;
-  switch (pick_maxi3(D / VEC)) {
+  switch (pick_maxi3(D / (16 / (int)sizeof(T)))) {
     case 0: return hipErrorInvalidValue;
     case 3: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 3>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
     case 1: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 1>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
