@@ -657,8 +657,9 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
 //  * a stage is four k-steps of 16.  Each k-step is one asm block: its eight
 //    MFMAs, the six fragment reads of the next k-step in the order the next
 //    block consumes them (A_0, W_0, W_1, A_1, A_2, A_3) behind the first six
-//    MFMAs, and up to four DMA ops; the block waits for its own reads at its
-//    end, so no LDS load result outlives the statement that issued it.
+//    MFMAs, and up to four DMA ops behind its last MFMA; the block waits for
+//    its own reads at its end, so no LDS load result outlives the statement
+//    that issued it.
 //  * the stage barrier sits before the last k-step.  By then every wave has
 //    read all of stage k's fragments (the last k-step's were read by the
 //    third block), so after it stage k's slots take W_{k+2} (first block
@@ -668,9 +669,9 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
 //  * DMA and fragment reads are plain asm, invisible to the compiler's wait
 //    tracking; the waits are explicit: before barrier k, everything but the
 //    A_{k+2} ops (the newest A_DMA) has landed, i.e. A_{k+1} and W_{k+1}.
-// Spread this way, the eight waves' DMA ops no longer arrive in one burst
-// that stalls each wave's MFMA issue behind the vector-memory queue, and no
-// fragment read latency is exposed at a stage boundary.
+// Spread over the stage this way, the eight waves' DMA ops no longer arrive
+// in one burst that stalls each wave's MFMA issue behind the vector-memory
+// queue, and no fragment read latency is exposed at a stage boundary.
 
 struct Frags {
   u32x4 a0, a1, a2, a3, b0, b1;
@@ -681,15 +682,20 @@ struct Frags {
 #define RM_DMA(v) "global_load_lds_dwordx4 %[" #v "], %[sb]\n\t"
 #define RM_M0NEXT "s_add_u32 m0, m0, %[ms]\n\t"
 
-// one k-step with four DMA ops: voff v0..v3 against the 64-bit base sb, LDS
-// destinations mb, mb + ms, mb + 2ms, mb + 3ms (M0 is set at least one
-// instruction before each DMA that reads it)
-#define RM_KSTEP_DMA                                                                                     \
-  "s_mov_b32 m0, %[mb]\n\t" RM_MF(c00, b0, a0) RM_RD(na0, la, 0) RM_DMA(v0) RM_M0NEXT RM_MF(c01, b1, a0) \
-      RM_RD(nb0, lb, 0) RM_MF(c10, b0, a1) RM_RD(nb1, lb, 4096) RM_DMA(v1) RM_M0NEXT RM_MF(c11, b1, a1)  \
-          RM_RD(na1, la, 4096) RM_MF(c20, b0, a2) RM_RD(na2, la, 8192) RM_DMA(v2) RM_M0NEXT               \
-              RM_MF(c21, b1, a2) RM_RD(na3, la, 12288) RM_MF(c30, b0, a3) RM_DMA(v3) RM_MF(c31, b1, a3)  \
-                  "s_waitcnt lgkmcnt(0)\n\t"
+// the four DMA ops of a k-step: voff v0..v3 against the 64-bit base sb, LDS
+// destinations mb, mb + ms, mb + 2ms, mb + 3ms (M0 is written one
+// instruction before each DMA that reads it: the s_nop is that wait state)
+#define RM_DMA4 \
+  RM_DMA(v0) RM_M0NEXT "s_nop 0\n\t" RM_DMA(v1) RM_M0NEXT "s_nop 0\n\t" RM_DMA(v2) RM_M0NEXT "s_nop 0\n\t" RM_DMA(v3)
+
+// one k-step with four DMA ops, issued behind its eight MFMAs: a DMA op
+// whose issue waits for room in the vector-memory queue then holds up no
+// MFMA of the block (between the MFMAs it cost 1-2.5 % of a product)
+#define RM_KSTEP_DMA                                                                                          \
+  "s_mov_b32 m0, %[mb]\n\t" RM_MF(c00, b0, a0) RM_RD(na0, la, 0) RM_MF(c01, b1, a0) RM_RD(nb0, lb, 0)         \
+      RM_MF(c10, b0, a1) RM_RD(nb1, lb, 4096) RM_MF(c11, b1, a1) RM_RD(na1, la, 4096) RM_MF(c20, b0, a2)        \
+          RM_RD(na2, la, 8192) RM_MF(c21, b1, a2) RM_RD(na3, la, 12288) RM_MF(c30, b0, a3) RM_MF(c31, b1, a3)    \
+              RM_DMA4 "s_waitcnt lgkmcnt(0)\n\t"
 #define RM_KSTEP                                                                                               \
   RM_MF(c00, b0, a0) RM_RD(na0, la, 0) RM_MF(c01, b1, a0) RM_RD(nb0, lb, 0) RM_MF(c10, b0, a1) RM_RD(nb1, lb, 4096) \
       RM_MF(c11, b1, a1) RM_RD(na1, la, 4096) RM_MF(c20, b0, a2) RM_RD(na2, la, 8192) RM_MF(c21, b1, a2)           \
@@ -758,17 +764,19 @@ struct PAddr {
 // KI's 16 rows further down the slice), rows +4..7 at o1 = o0 + 2048
 #define RM_TR(dst, addr, h) "ds_read_b64_tr_b16 %[" #dst "], %[" #addr "] offset:%[o" #h "]\n\t"
 
-#define RM_KSTEP_WT_BODY(D0, D1, D2, D3)                                                                     \
-  RM_MF(c00, b0, a0) RM_RD(na0, la, 0) RM_TR(nb0l, lb0, 0) D0 RM_MF(c01, b1, a0) RM_TR(nb0h, lb0, 1)        \
-      RM_TR(nb1l, lb1, 0) RM_MF(c10, b0, a1) RM_TR(nb1h, lb1, 1) D1 RM_MF(c11, b1, a1) RM_RD(na1, la, 4096) \
-          RM_MF(c20, b0, a2) RM_RD(na2, la, 8192) D2 RM_MF(c21, b1, a2) RM_RD(na3, la, 12288)               \
-              RM_MF(c30, b0, a3) D3 RM_MF(c31, b1, a3) "s_waitcnt lgkmcnt(0)\n\t"
-#define RM_KSTEP_KK_BODY(D0, D1, D2, D3)                                                                      \
-  RM_MF(c00, b0, a0) RM_TR(na0l, la0, 0) RM_TR(na0h, la0, 1) D0 RM_MF(c01, b1, a0) RM_TR(nb0l, lb0, 0)        \
-      RM_TR(nb0h, lb0, 1) RM_MF(c10, b0, a1) RM_TR(nb1l, lb1, 0) RM_TR(nb1h, lb1, 1) D1 RM_MF(c11, b1, a1)    \
-          RM_TR(na1l, la1, 0) RM_TR(na1h, la1, 1) RM_MF(c20, b0, a2) RM_TR(na2l, la2, 0) RM_TR(na2h, la2, 1) \
-              D2 RM_MF(c21, b1, a2) RM_TR(na3l, la3, 0) RM_TR(na3h, la3, 1) RM_MF(c30, b0, a3) D3            \
+#define RM_KSTEP_WT_BODY(TAIL)                                                                              \
+  RM_MF(c00, b0, a0) RM_RD(na0, la, 0) RM_TR(nb0l, lb0, 0) RM_MF(c01, b1, a0) RM_TR(nb0h, lb0, 1) RM_TR(nb1l, lb1, 0) \
+      RM_MF(c10, b0, a1) RM_TR(nb1h, lb1, 1) RM_MF(c11, b1, a1) RM_RD(na1, la, 4096) RM_MF(c20, b0, a2)              \
+          RM_RD(na2, la, 8192) RM_MF(c21, b1, a2) RM_RD(na3, la, 12288) RM_MF(c30, b0, a3) RM_MF(c31, b1, a3) TAIL   \
+              "s_waitcnt lgkmcnt(0)\n\t"
+#define RM_KSTEP_KK_BODY(D0, D1, D2, D3)                                                                       \
+  RM_MF(c00, b0, a0) RM_TR(na0l, la0, 0) RM_TR(na0h, la0, 1) D0 RM_MF(c01, b1, a0) RM_TR(nb0l, lb0, 0)         \
+      RM_TR(nb0h, lb0, 1) RM_MF(c10, b0, a1) RM_TR(nb1l, lb1, 0) RM_TR(nb1h, lb1, 1) D1 RM_MF(c11, b1, a1)     \
+          RM_TR(na1l, la1, 0) RM_TR(na1h, la1, 1) RM_MF(c20, b0, a2) RM_TR(na2l, la2, 0) RM_TR(na2h, la2, 1)  \
+              D2 RM_MF(c21, b1, a2) RM_TR(na3l, la3, 0) RM_TR(na3h, la3, 1) RM_MF(c30, b0, a3) D3             \
                   RM_MF(c31, b1, a3) "s_waitcnt lgkmcnt(0)\n\t"
+// the KK form keeps its DMA ops between its MFMAs (behind them it measured
+// 1-2 % slower, unlike the other forms)
 #define RM_D(v) RM_DMA(v) RM_M0NEXT
 
 #define RM_ACC8                                                                                \
@@ -794,13 +802,13 @@ struct PAddr {
 template <int KI>
 __device__ __forceinline__ void kstep(floatx16 (&acc)[4][2], const FragsWT& cu, FragsWT& nx, const PAddr& ad) {
   const u32x4 a0 = cu.a0, a1 = cu.a1, a2 = cu.a2, a3 = cu.a3, b0 = cat2(cu.b0l, cu.b0h), b1 = cat2(cu.b1l, cu.b1h);
-  asm volatile(RM_KSTEP_WT_BODY("", "", "", "") : RM_OUT_WT : RM_IN_FR, RM_IN_WT_ADDR, RM_IN_OFF);
+  asm volatile(RM_KSTEP_WT_BODY("") : RM_OUT_WT : RM_IN_FR, RM_IN_WT_ADDR, RM_IN_OFF);
 }
 template <int MS, int KI>
 __device__ __forceinline__ void kstep_dma(floatx16 (&acc)[4][2], const FragsWT& cu, FragsWT& nx, const PAddr& ad,
                                           uint32_t mb, const void* sb, const uint32_t* v) {
   const u32x4 a0 = cu.a0, a1 = cu.a1, a2 = cu.a2, a3 = cu.a3, b0 = cat2(cu.b0l, cu.b0h), b1 = cat2(cu.b1l, cu.b1h);
-  asm volatile("s_mov_b32 m0, %[mb]\n\t" RM_KSTEP_WT_BODY(RM_D(v0), RM_D(v1), RM_D(v2), RM_DMA(v3))
+  asm volatile("s_mov_b32 m0, %[mb]\n\t" RM_KSTEP_WT_BODY(RM_DMA4)
                : RM_OUT_WT
                : RM_IN_FR, RM_IN_WT_ADDR, RM_IN_OFF, RM_IN_DMA
                : "m0", "scc");
