@@ -136,6 +136,32 @@ def measure_ceilings(bd, copy_mib: int = 100, pairs: int = 6) -> dict:
         e1.synchronize()
         ms.append(e0.elapsed_time(e1))
     mfma = lib.rm_probe_mfma_flop(iters) / (statistics.median(ms) * 1e-3) / 1e12
+
+    def timed_median(fn, reps=10, warm=3):
+        for _ in range(warm):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    # the same MFMA loop on constant operands (every fragment 1.0): the
+    # multipliers' inputs never change, so this is the loop without the
+    # data-dependent switching energy of random operands
+    ones = torch.ones_like(frags)
+    mfma_const = lib.rm_probe_mfma_flop(iters) / (timed_median(lambda: bd.probe_mfma_bf16(ones, out, iters)) * 1e-3) / 1e12
+    del ones
+    # the products' k-step (MFMAs fed by its LDS fragment reads) on random bf16
+    slab = torch.randn(lib.rm_probe_kstep_slab_bytes() // 2, device="cuda").to(torch.bfloat16)
+    kout = torch.empty(lib.rm_probe_kstep_out_floats(), dtype=torch.float32, device="cuda")
+    kiters = 2000
+    kstep = lib.rm_probe_kstep_flop(kiters) / (timed_median(lambda: bd.probe_kstep_bf16(slab, kout, kiters)) * 1e-3) / 1e12
+    del slab, kout
     n = copy_mib << 20
     bufs = [(torch.empty(n, dtype=torch.uint8, device="cuda"), torch.empty(n, dtype=torch.uint8, device="cuda"))
             for _ in range(pairs)]
@@ -155,11 +181,15 @@ def measure_ceilings(bd, copy_mib: int = 100, pairs: int = 6) -> dict:
     warm = [timed_copy(*bufs[0]) for _ in range(10)][2:]
     del bufs
     return {"mfma_bf16_random_tflops": round(mfma, 1),
+            "mfma_bf16_constant_tflops": round(mfma_const, 1),
+            "kstep_bf16_random_tflops": round(kstep, 1),
             "copy_cold_gbs": round(2 * n / (statistics.median(cold) * 1e-3) / 1e9, 1),
             "copy_warm_gbs": round(2 * n / (statistics.median(warm) * 1e-3) / 1e9, 1),
             "copy_bytes": 2 * n,
             "how": "librankmixer probes: rm_probe_mfma_bf16 (8 waves per CU of v_mfma_f32_32x32x16_bf16 on "
-                   "random bf16 fragments, median of 10 launches) and rm_probe_copy (median per copy, cold: "
+                   "random bf16 fragments, and on constant ones; median of 10 launches), rm_probe_kstep_bf16 (the "
+                   "products' k-step: 8 MFMAs + 6 LDS fragment reads per wave, 8 waves per CU, random bf16 in LDS, "
+                   "no DMA or barriers) and rm_probe_copy (median per copy, cold: "
                    f"round-robin over {pairs} buffer pairs)"}
 
 
@@ -183,6 +213,8 @@ def bench_ceilings(args) -> int:
            "unit": "TFLOP/s", "n_gpus": 1, "higher_is_better": True, "data": "synthetic (random bf16)",
            "dtype": "bf16", "config": {"workload": "MFMA loop and HBM copy probes"},
            "mfma_frac_of_spec": round(c["mfma_bf16_random_tflops"] / pm.PEAK_BF16_TFLOPS, 4),
+           "mfma_constant_frac_of_spec": round(c["mfma_bf16_constant_tflops"] / pm.PEAK_BF16_TFLOPS, 4),
+           "kstep_frac_of_spec": round(c["kstep_bf16_random_tflops"] / pm.PEAK_BF16_TFLOPS, 4),
            "copy_cold_frac_of_spec": round(c["copy_cold_gbs"] / pm.PEAK_HBM_GBS, 4),
            "copy_warm_frac_of_spec": round(c["copy_warm_gbs"] / pm.PEAK_HBM_GBS, 4), **c}
     print(json.dumps(rec), flush=True)

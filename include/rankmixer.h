@@ -399,6 +399,14 @@ int rm_profile_read(int idx, char* name, size_t name_len, double* total_ms, int*
  * different pair of fragments; out (device, rm_probe_mfma_out_floats() fp32)
  * receives one sum per lane so nothing is optimised away.
  * rm_probe_mfma_flop(iters) is the launch's flop count (32768 per MFMA).
+ * rm_probe_kstep_bf16: the grouped products' k-step on its own -- per wave
+ * and k-step eight v_mfma_f32_32x32x16_bf16 on a 128 x 64 tile and the six
+ * 16-byte LDS fragment reads of the next k-step, from the products' own LDS
+ * layout -- with eight waves per compute unit and no DMA or barriers, for
+ * iters rounds of four k-steps; `slab` (device, rm_probe_kstep_slab_bytes()
+ * bytes of bf16, the caller's random values) is copied into LDS as the A and
+ * W slices; out (device, rm_probe_kstep_out_floats() fp32) receives one sum
+ * per lane.  rm_probe_kstep_flop(iters) is the launch's flop count.
  * rm_probe_copy: dst[0..bytes) = src[0..bytes) with 16-byte loads and stores
  * (bytes a multiple of 16; src, dst 16-byte aligned, not overlapping).
  * Errors: NULL or misaligned pointers, iters < 1 -> RM_ERR_INVALID. */
@@ -406,6 +414,10 @@ size_t rm_probe_mfma_frag_bytes(void);
 int64_t rm_probe_mfma_out_floats(void);
 double rm_probe_mfma_flop(int iters);
 rm_status rm_probe_mfma_bf16(const void* frags, float* out, int iters, void* stream);
+size_t rm_probe_kstep_slab_bytes(void);
+int64_t rm_probe_kstep_out_floats(void);
+double rm_probe_kstep_flop(int iters);
+rm_status rm_probe_kstep_bf16(const void* slab, float* out, int iters, void* stream);
 rm_status rm_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 /* How the bf16 grouped products finish a tile (bias, GELU, packing to bf16,

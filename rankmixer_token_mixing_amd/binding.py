@@ -105,6 +105,10 @@ _SIGNATURES = {
     "rm_probe_mfma_out_floats": (_i64, []),
     "rm_probe_mfma_flop": (C.c_double, [_int]),
     "rm_probe_mfma_bf16": (_int, [_vp, _vp, _int, _vp]),
+    "rm_probe_kstep_slab_bytes": (_sz, []),
+    "rm_probe_kstep_out_floats": (_i64, []),
+    "rm_probe_kstep_flop": (C.c_double, [_int]),
+    "rm_probe_kstep_bf16": (_int, [_vp, _vp, _int, _vp]),
     "rm_probe_copy": (_int, [_vp, _vp, _sz, _vp]),
     "rm_moe_route_noalloc_scratch_bytes": (_sz, [_i64, _int, _int]),
     "rm_moe_route_noalloc_max_scratch_bytes": (_sz, []),
@@ -497,6 +501,12 @@ def probe_mfma_bf16(frags: torch.Tensor, out: torch.Tensor, iters: int) -> None:
     """The MFMA ceiling probe (see rm_probe_mfma_bf16); frags: random bytes of
     rm_probe_mfma_frag_bytes(), out: rm_probe_mfma_out_floats() fp32."""
     _check(load().rm_probe_mfma_bf16(_p(frags), _p(out), iters, _stream(frags.device)))
+
+
+def probe_kstep_bf16(slab: torch.Tensor, out: torch.Tensor, iters: int) -> None:
+    """The k-step probe (see rm_probe_kstep_bf16); slab: rm_probe_kstep_slab_bytes()
+    bytes of bf16, out: rm_probe_kstep_out_floats() fp32."""
+    _check(load().rm_probe_kstep_bf16(_p(slab), _p(out), iters, _stream(slab.device)))
 
 
 def probe_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int) -> None:

@@ -533,6 +533,20 @@ rm_status rm_probe_mfma_bf16(const void* frags, float* out, int iters, void* str
   return ok();
 }
 
+size_t rm_probe_kstep_slab_bytes(void) { return (size_t)rm::kProbeSlabBytes; }
+
+int64_t rm_probe_kstep_out_floats(void) { return (int64_t)rm::probe_kstep_blocks() * 512; }
+
+double rm_probe_kstep_flop(int iters) { return (double)rm::probe_kstep_blocks() * 8 * iters * 32 * 32768.0; }
+
+rm_status rm_probe_kstep_bf16(const void* slab, float* out, int iters, void* stream) {
+  RM_TRY(check_ptr(slab, "slab"));
+  RM_TRY(check_ptr(out, "out"));
+  if (iters < 1) return fail(RM_ERR_INVALID, "iters=%d must be positive", iters);
+  RM_HIP(rm::launch_probe_kstep(slab, out, iters, (hipStream_t)stream), "k-step probe");
+  return ok();
+}
+
 rm_status rm_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
   RM_TRY(check_ptr(src, "src"));
   RM_TRY(check_ptr(dst, "dst"));

@@ -673,12 +673,6 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
 // in one burst that stalls each wave's MFMA issue behind the vector-memory
 // queue, and no fragment read latency is exposed at a stage boundary.
 
-struct Frags {
-  u32x4 a0, a1, a2, a3, b0, b1;
-};
-
-#define RM_MF(c, b, a) "v_mfma_f32_32x32x16_bf16 %[" #c "], %[" #b "], %[" #a "], %[" #c "]\n\t"
-#define RM_RD(dst, addr, off) "ds_read_b128 %[" #dst "], %[" #addr "] offset:" #off "\n\t"
 #define RM_DMA(v) "global_load_lds_dwordx4 %[" #v "], %[sb]\n\t"
 #define RM_M0NEXT "s_add_u32 m0, m0, %[ms]\n\t"
 
@@ -696,24 +690,6 @@ struct Frags {
       RM_MF(c10, b0, a1) RM_RD(nb1, lb, 4096) RM_MF(c11, b1, a1) RM_RD(na1, la, 4096) RM_MF(c20, b0, a2)        \
           RM_RD(na2, la, 8192) RM_MF(c21, b1, a2) RM_RD(na3, la, 12288) RM_MF(c30, b0, a3) RM_MF(c31, b1, a3)    \
               RM_DMA4 "s_waitcnt lgkmcnt(0)\n\t"
-#define RM_KSTEP                                                                                               \
-  RM_MF(c00, b0, a0) RM_RD(na0, la, 0) RM_MF(c01, b1, a0) RM_RD(nb0, lb, 0) RM_MF(c10, b0, a1) RM_RD(nb1, lb, 4096) \
-      RM_MF(c11, b1, a1) RM_RD(na1, la, 4096) RM_MF(c20, b0, a2) RM_RD(na2, la, 8192) RM_MF(c21, b1, a2)           \
-          RM_RD(na3, la, 12288) RM_MF(c30, b0, a3) RM_MF(c31, b1, a3) "s_waitcnt lgkmcnt(0)\n\t"
-
-#define RM_KSTEP_ACC                                                                                   \
-  [c00] "+v"(acc[0][0]), [c01] "+v"(acc[0][1]), [c10] "+v"(acc[1][0]), [c11] "+v"(acc[1][1]),         \
-      [c20] "+v"(acc[2][0]), [c21] "+v"(acc[2][1]), [c30] "+v"(acc[3][0]), [c31] "+v"(acc[3][1]),     \
-      [na0] "=&v"(nx.a0), [na1] "=&v"(nx.a1), [na2] "=&v"(nx.a2), [na3] "=&v"(nx.a3), [nb0] "=&v"(nx.b0), \
-      [nb1] "=&v"(nx.b1)
-#define RM_KSTEP_IN \
-  [a0] "v"(cu.a0), [a1] "v"(cu.a1), [a2] "v"(cu.a2), [a3] "v"(cu.a3), [b0] "v"(cu.b0), [b1] "v"(cu.b1), \
-      [la] "v"(la), [lb] "v"(lb)
-
-__device__ __forceinline__ void kstep(floatx16 (&acc)[4][2], const Frags& cu, Frags& nx, uint32_t la, uint32_t lb) {
-  asm volatile(RM_KSTEP : RM_KSTEP_ACC : RM_KSTEP_IN);
-}
-
 template <int MS>
 __device__ __forceinline__ void kstep_dma(floatx16 (&acc)[4][2], const Frags& cu, Frags& nx, uint32_t la,
                                           uint32_t lb, uint32_t mb, const void* sb, const uint32_t* v) {
@@ -722,15 +698,6 @@ __device__ __forceinline__ void kstep_dma(floatx16 (&acc)[4][2], const Frags& cu
                : RM_KSTEP_IN, [mb] "s"(mb), [sb] "s"(sb), [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]),
                  [v3] "v"(v[3]), [ms] "n"(MS)
                : "m0", "scc");
-}
-
-// the six fragment reads of one k-step on their own (first k-step of a tile)
-__device__ __forceinline__ void read_frags(Frags& nx, uint32_t la, uint32_t lb) {
-  asm volatile(RM_RD(na0, la, 0) RM_RD(nb0, lb, 0) RM_RD(nb1, lb, 4096) RM_RD(na1, la, 4096) RM_RD(na2, la, 8192)
-                   RM_RD(na3, la, 12288) "s_waitcnt lgkmcnt(0)\n\t"
-               : [na0] "=&v"(nx.a0), [na1] "=&v"(nx.a1), [na2] "=&v"(nx.a2), [na3] "=&v"(nx.a3), [nb0] "=&v"(nx.b0),
-                 [nb1] "=&v"(nx.b1)
-               : [la] "v"(la), [lb] "v"(lb));
 }
 
 // ---- K-major operands (the backward products) ----------------------------

@@ -9,10 +9,17 @@
 //    inputs change from one MFMA to the next as they do when fragments stream
 //    from LDS.  Two workgroups of four waves per compute unit: two waves per
 //    SIMD, as in the products.
+//  * k_kstep_loop: the pipelined products' k-step alone (frag.hpp's kstep):
+//    per wave and k-step eight MFMAs on a 128 x 64 tile and the six 16-byte
+//    fragment reads of the next k-step from the products' swizzled LDS layout
+//    (a 32 KB A slice and a 32 KB W slice of random bf16), eight waves per
+//    compute unit as in the products, no DMA and no barriers: the rate the
+//    main loop could reach with its operands fed from LDS.
 //  * k_copy: a streaming copy of 16-byte chunks, four loads in flight per
 //    lane; HBM bandwidth as a kernel sees it (with a cold or warm last-level
 //    cache, depending on what the caller ran before).
 #include "common.hpp"
+#include "frag.hpp"
 #include "launch.hpp"
 
 namespace rm {
@@ -56,6 +63,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   out[wave * 64 + lane] = sum;
 }
 
+// eight waves of the products' 2 x 4 wave grid; the slab is the A slice
+// (bytes 0..32K) and the W slice (32K..64K) in the products' LDS layout
+__global__ __launch_bounds__(512) void k_kstep_loop(const uint4* __restrict__ slab, float* __restrict__ out,
+                                                    int iters) {
+  __shared__ uint4 lds[kProbeSlabBytes / 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kProbeSlabBytes / 16; i += 512) lds[i] = slab[i];
+  __syncthreads();
+  const int wm = wave / 4, wn = wave % 4, lr = lane & 31, lh = lane >> 5;
+  uint32_t oa[4], ob[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const uint32_t ch = (uint32_t)(((kk * 2 + lh) ^ ((lr >> 1) & 7)) * 16);
+    oa[kk] = (uint32_t)(wm * 128 + lr) * 128 + ch;
+    ob[kk] = (uint32_t)(wn * 64 + lr) * 128 + ch;
+  }
+  const uint32_t sA = (uint32_t)(uintptr_t)lds, sW = sA + kProbeSlabBytes / 2;
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  Frags f0, f1;
+  read_frags(f0, sA + oa[0], sW + ob[0]);
+  for (int it = 0; it < iters; ++it) {
+    kstep(acc, f0, f1, sA + oa[1], sW + ob[1]);
+    kstep(acc, f1, f0, sA + oa[2], sW + ob[2]);
+    kstep(acc, f0, f1, sA + oa[3], sW + ob[3]);
+    kstep(acc, f1, f0, sA + oa[0], sW + ob[0]);
+  }
+  // the last MFMAs' results are read by ordinary code from here on
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t" ::);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum += acc[i][j][e];
+  out[(long long)blockIdx.x * 512 + tid] = sum;
+}
+
 __global__ __launch_bounds__(256) void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, long long n) {
   const long long stride = (long long)gridDim.x * blockDim.x;
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -76,6 +127,13 @@ int probe_mfma_waves() { return device_cus() * 8; }
 hipError_t launch_probe_mfma(const void* frags, float* out, int iters, hipStream_t s) {
   const int blocks = device_cus() * 2;
   hipLaunchKernelGGL(k_mfma_loop, dim3(blocks), dim3(256), 0, s, (const uint4*)frags, out, iters);
+  return hipGetLastError();
+}
+
+int probe_kstep_blocks() { return device_cus(); }
+
+hipError_t launch_probe_kstep(const void* slab, float* out, int iters, hipStream_t s) {
+  hipLaunchKernelGGL(k_kstep_loop, dim3(probe_kstep_blocks()), dim3(512), 0, s, (const uint4*)slab, out, iters);
   return hipGetLastError();
 }
 

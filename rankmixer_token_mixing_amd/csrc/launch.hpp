@@ -232,5 +232,10 @@ int probe_mfma_waves();
 constexpr long long kProbeFragBytes = 64LL * 16 * 64 * 16;
 hipError_t launch_probe_mfma(const void* frags, float* out, int iters, hipStream_t s);
 hipError_t launch_probe_copy(const void* src, void* dst, long long n16, hipStream_t s);
+// the k-step probe: one workgroup of 8 waves per compute unit; slab: the A and
+// W slices (kProbeSlabBytes of bf16), out: probe_kstep_blocks() * 512 floats
+constexpr int kProbeSlabBytes = 65536;
+int probe_kstep_blocks();
+hipError_t launch_probe_kstep(const void* slab, float* out, int iters, hipStream_t s);
 
 }  // namespace rm
