@@ -337,3 +337,23 @@ def test_noalloc_route_refuses_more_than_its_scratch(lib):
     assert lib.rm_moe_route_noalloc(None, A16, A16, A16, A16, A16, 4, 2, 64, 4, bd.RM_BF16, None) == bd.RM_ERR_INVALID
     assert lib.rm_moe_route_noalloc(A16, A16, A16, A16, A16, A16, 4, 2, 64, 33, bd.RM_BF16, None) == \
         bd.RM_ERR_UNSUPPORTED
+
+
+def test_probe_entry_points_check_their_arguments(lib):
+    RM_ERR_INVALID = 1
+    assert lib.rm_probe_mfma_frag_bytes() == 64 * 16 * 64 * 16
+    assert lib.rm_probe_kstep_slab_bytes() == 65536
+    # flop counts follow the launch shapes: 32768 flop per MFMA, 64 MFMAs per
+    # round and wave (MFMA loop), 32 per round and wave (k-step, 8 waves per block)
+    waves = lib.rm_probe_mfma_out_floats() // 64
+    assert lib.rm_probe_mfma_flop(10) == waves * 10 * 64 * 32768.0
+    blocks = lib.rm_probe_kstep_out_floats() // 512
+    assert lib.rm_probe_kstep_flop(10) == blocks * 8 * 10 * 32 * 32768.0
+    assert lib.rm_probe_mfma_bf16(None, C.c_void_p(A16), 1, None) == RM_ERR_INVALID
+    assert lib.rm_probe_kstep_bf16(None, C.c_void_p(A16), 1, None) == RM_ERR_INVALID
+    assert "slab" in err(lib)
+    assert lib.rm_probe_kstep_bf16(C.c_void_p(A16), C.c_void_p(A16), 0, None) == RM_ERR_INVALID
+    assert "iters" in err(lib)
+    assert lib.rm_probe_copy(C.c_void_p(A16), C.c_void_p(2 * A16), 24, None) == RM_ERR_INVALID
+    assert lib.rm_probe_copy(C.c_void_p(A16), C.c_void_p(A16 + 16), 64, None) == RM_ERR_INVALID
+    assert "overlap" in err(lib)
