@@ -681,6 +681,8 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
 // instruction before each DMA that reads it: the s_nop is that wait state)
 #define RM_DMA4 \
   RM_DMA(v0) RM_M0NEXT "s_nop 0\n\t" RM_DMA(v1) RM_M0NEXT "s_nop 0\n\t" RM_DMA(v2) RM_M0NEXT "s_nop 0\n\t" RM_DMA(v3)
+#define RM_IN_DMA4 \
+  [mb] "s"(mb), [sb] "s"(sb), [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [ms] "n"(MS)
 
 // one k-step with four DMA ops, issued behind its eight MFMAs: a DMA op
 // whose issue waits for room in the vector-memory queue then holds up no
@@ -690,6 +692,16 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_ring(KParams p) {
       RM_MF(c10, b0, a1) RM_RD(nb1, lb, 4096) RM_MF(c11, b1, a1) RM_RD(na1, la, 4096) RM_MF(c20, b0, a2)        \
           RM_RD(na2, la, 8192) RM_MF(c21, b1, a2) RM_RD(na3, la, 12288) RM_MF(c30, b0, a3) RM_MF(c31, b1, a3)    \
               RM_DMA4 "s_waitcnt lgkmcnt(0)\n\t"
+// a k-step's four DMA ops alone: the share of the slice loads of a wave
+// whose rows of the tile are all past the end (it issues no MFMAs)
+template <int MS>
+__device__ __forceinline__ void dma4(uint32_t mb, const void* sb, const uint32_t* v) {
+  asm volatile("s_mov_b32 m0, %[mb]\n\ts_nop 0\n\t" RM_DMA4 "\n\t"
+               :
+               : RM_IN_DMA4
+               : "m0", "scc");
+}
+
 template <int MS>
 __device__ __forceinline__ void kstep_dma(floatx16 (&acc)[4][2], const Frags& cu, Frags& nx, uint32_t la,
                                           uint32_t lb, uint32_t mb, const void* sb, const uint32_t* v) {
@@ -1268,6 +1280,22 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
     wait_vmcnt<B_DMA>();
     __builtin_amdgcn_s_barrier();
     FR f0, f1;
+    // a wave whose 128 rows of the tile all lie past the end of the group
+    // (the short last tile of a ragged group) issues its share of the slice
+    // loads and takes part in every barrier, but no fragment read or MFMA:
+    // its SIMD's matrix core then serves only the other wave
+    const bool idle = !WT && t.m0 + (wave / NWN) * (FM * 32) >= t.Mg;
+    if (idle) {
+      for (int k = 0; k < nk; ++k) {
+        const uint32_t sA = slot(2 * k);
+        const uint32_t dA = slot(2 * k + 4) + wof;
+        dma4<NW * 1024>(dA, kbase(Ab, a_kst, k + 2), va);
+        if constexpr (A_DMA == 8) dma4<NW * 1024>(dA + 4 * NW * 1024, kbase(Ab, a_kst, k + 2), va + 4);
+        wait_vmcnt<A_DMA>();
+        __builtin_amdgcn_s_barrier();
+        dma4<NW * 1024>(sA + wof, kbase(Bb, w_kst, k + 2), vw);
+      }
+    } else {
     read_frags(f0, paddr(slot(0), slot(1), 0));
 
     for (int k = 0; k < nk; ++k) {
@@ -1286,6 +1314,7 @@ __global__ __launch_bounds__(NWM* NWN* kWave) void k_gemm_pipe(KParams p) {
       // stage k's slots are free: W_{k+2} into A_k's; read stage k+1's first fragments
       kstep_dma<NW * 1024, 0>(acc, f1, f0, paddr(slot(2 * k + 2), slot(2 * k + 3), 0), sA + wof,
                            kbase(Bb, w_kst, k + 2), vw);
+    }
     }
     wait_vmcnt<0>();  // no DMA may land in LDS after this point
     // the last MFMAs' results are read by ordinary code from here on
