@@ -707,8 +707,7 @@ __device__ __forceinline__ void kstep_dma(floatx16 (&acc)[4][2], const Frags& cu
                                           uint32_t lb, uint32_t mb, const void* sb, const uint32_t* v) {
   asm volatile(RM_KSTEP_DMA
                : RM_KSTEP_ACC
-               : RM_KSTEP_IN, [mb] "s"(mb), [sb] "s"(sb), [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]),
-                 [v3] "v"(v[3]), [ms] "n"(MS)
+               : RM_KSTEP_IN, RM_IN_DMA4
                : "m0", "scc");
 }
 
@@ -769,8 +768,6 @@ struct PAddr {
       [na2l] "=&v"(nx.a2l), [na2h] "=&v"(nx.a2h), [na3l] "=&v"(nx.a3l), [na3h] "=&v"(nx.a3h),             \
       [nb0l] "=&v"(nx.b0l), [nb0h] "=&v"(nx.b0h), [nb1l] "=&v"(nx.b1l), [nb1h] "=&v"(nx.b1h)
 #define RM_IN_FR [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3), [b0] "v"(b0), [b1] "v"(b1)
-#define RM_IN_DMA \
-  [mb] "s"(mb), [sb] "s"(sb), [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [ms] "n"(MS)
 #define RM_IN_OFF [o0] "n"(KI * 8192), [o1] "n"(KI * 8192 + 2048)
 #define RM_IN_WT_ADDR [la] "v"(ad.a[0]), [lb0] "v"(ad.b[0]), [lb1] "v"(ad.b[1])
 #define RM_IN_KK_ADDR \
@@ -789,7 +786,7 @@ __device__ __forceinline__ void kstep_dma(floatx16 (&acc)[4][2], const FragsWT& 
   const u32x4 a0 = cu.a0, a1 = cu.a1, a2 = cu.a2, a3 = cu.a3, b0 = cat2(cu.b0l, cu.b0h), b1 = cat2(cu.b1l, cu.b1h);
   asm volatile("s_mov_b32 m0, %[mb]\n\t" RM_KSTEP_WT_BODY(RM_DMA4)
                : RM_OUT_WT
-               : RM_IN_FR, RM_IN_WT_ADDR, RM_IN_OFF, RM_IN_DMA
+               : RM_IN_FR, RM_IN_WT_ADDR, RM_IN_OFF, RM_IN_DMA4
                : "m0", "scc");
 }
 __device__ __forceinline__ void read_frags(FragsWT& nx, const PAddr& ad) {
@@ -814,7 +811,7 @@ __device__ __forceinline__ void kstep_dma(floatx16 (&acc)[4][2], const FragsKK& 
               a3 = cat2(cu.a3l, cu.a3h), b0 = cat2(cu.b0l, cu.b0h), b1 = cat2(cu.b1l, cu.b1h);
   asm volatile("s_mov_b32 m0, %[mb]\n\t" RM_KSTEP_KK_BODY(RM_D(v0), RM_D(v1), RM_D(v2), RM_DMA(v3))
                : RM_OUT_KK
-               : RM_IN_FR, RM_IN_KK_ADDR, RM_IN_OFF, RM_IN_DMA
+               : RM_IN_FR, RM_IN_KK_ADDR, RM_IN_OFF, RM_IN_DMA4
                : "m0", "scc");
 }
 __device__ __forceinline__ void read_frags(FragsKK& nx, const PAddr& ad) {
