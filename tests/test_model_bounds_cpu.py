@@ -232,3 +232,29 @@ def test_audit_mode_enqueues_nothing_and_is_off_by_default(lib):
     name = C.create_string_buffer(16)
     a, b = C.c_uint64(), C.c_uint64()
     assert lib.rm_audit_read(0, name, 16, C.byref(a), C.byref(b)) == bd.RM_ERR_INVALID
+
+
+@pytest.mark.parametrize("seed", __import__("tests.sweep_cases", fromlist=["SEEDS"]).SEEDS)
+def test_sweep_cases_read_inside_their_buffers(lib, seed):
+    # every stack of the GPU shape sweep, audited on host tensors first: each
+    # launch it would make reads inside a caller buffer or the workspace
+    from tests import sweep_cases as sc
+    case = sc.draw(seed)
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    blocks = bd.upload_blocks(case.blocks, device="cpu")
+    head = None
+    if case.head:
+        head = {"w": torch.from_numpy(case.head_params["w"]), "c": case.head_params["c"]}
+    model = bd.Model(blocks, case.T, case.D, dt, F=case.F, head=head)
+    inp = bd.to_device(case.inp, device="cpu")
+    x = torch.empty((case.B, case.T, case.D), dtype=dt)
+    pooled = torch.empty((case.B, case.D), dtype=torch.float32) if case.head else None
+    logit = torch.empty(case.B, dtype=torch.float32) if case.head else None
+    ws = model.workspace_bytes(case.B)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    recs = _audited(lib, lambda: lib.rm_model_fwd(C.byref(model.desc), inp.data_ptr(), x.data_ptr(), ptr(pooled),
+                                                  ptr(logit), case.B, WS_BASE, ws, None))
+    params = _tensors(*blocks)
+    outs = [t for t in (x, pooled, logit) if t is not None]
+    _check_inside(recs, params + [inp] + outs + ([head["w"]] if head else []), ws,
+                  must_read=[inp] + [t for t in params if t.dim() > 1])
