@@ -101,3 +101,97 @@ def draw(seed: int) -> Case:
 
 
 SEEDS = tuple(range(1000, 1048))
+
+
+# ---------------------------------------------------------------------------
+# training: one dense (GELU FFN) or MoE block with the Add & Norm after the
+# mix, its training forward and backward.  MoE routers keep every
+# pre-activation far from the ReLU kink (biases +-3, |w . s| near 0.5), so
+# the fp64 oracle and the kernels take the same gate decisions.
+
+TRAIN_WORK_CAP = 1.5e8  # B * T * D * hidden * (E or 1)
+# at least 16 samples: a per-token gradient is a sum over the batch, and over
+# a handful of samples that sum can nearly cancel; in bf16 each summand
+# carries the rounding of D-long dot products of rounded activations, so the
+# error of a nearly cancelled token group, measured against the group's own
+# norm, says nothing about the kernels (the same case in fp32 agrees to
+# 1e-6).  The fixed tests cover B = 1 on short rows.
+TRAIN_MIN_B = 16
+
+
+@dataclass
+class TrainCase:
+    seed: int
+    kind: str
+    dtype: str
+    B: int
+    T: int
+    D: int
+    H: int
+    E: int
+    blk: dict = field(default_factory=dict)
+    x: Optional[np.ndarray] = None
+    d_out: Optional[np.ndarray] = None
+
+    def describe(self) -> str:
+        moe = f" E={self.E}" if self.kind == "moe" else ""
+        return f"seed {self.seed}: {self.kind} {self.dtype} B={self.B} T={self.T} D={self.D} hidden={self.H}{moe}"
+
+
+def _act(rng, shape, dtype):
+    a = rng.standard_normal(shape).astype(np.float32)
+    return si.to_bf16_bits(a) if dtype == "bf16" else a
+
+
+def draw_train(seed: int) -> TrainCase:
+    rng = np.random.default_rng(seed)
+    kind = "moe" if rng.random() < 0.45 else "dense"
+    dtype = "bf16" if rng.random() < 0.6 else "f32"
+    T = int(rng.choice(TS))
+    while True:
+        D = T * int(rng.integers(1, 97))
+        if D % 8 == 0 and 16 <= D <= 768:
+            break
+    E = 0
+    if kind == "moe":
+        # the training path keeps T * E a multiple of 8
+        E = int(rng.choice([e for e in range(1, 9) if (T * e) % 8 == 0]))
+        H = 8 * int(rng.integers(1, 49))
+    else:
+        H = 8 * int(rng.integers(1, 65))
+    B = int(rng.integers(TRAIN_MIN_B, 1100 if T <= 4 else 400))
+    B = max(TRAIN_MIN_B, min(B, int(TRAIN_WORK_CAP // (T * D * H * max(E, 1)))))
+    if rng.random() < 0.25:
+        # the backward's transpose-free path: bf16, whole 64-row blocks of at
+        # least 256 rows, widths of at least 256
+        dtype, T = "bf16", int(rng.choice([1, 2]))
+        D, H = int(rng.choice([256, 320, 384])), int(rng.choice([256, 320]))
+        B = int(rng.choice([256, 320, 384]))
+        if kind == "moe":
+            E = 8 // T
+    case = TrainCase(seed, kind, dtype, B, T, D, H, E)
+    if kind == "moe":
+        sign = np.where(rng.random((2, T, E)) < 0.6, 1.0, -1.0)
+        p = {"w1": rng.standard_normal((T, E, H, D)) / math.sqrt(D), "b1": 0.1 * rng.standard_normal((T, E, H)),
+             "w2": rng.standard_normal((T, E, D, H)) / math.sqrt(H), "b2": 0.1 * rng.standard_normal((T, E, D)),
+             "wr": 0.5 * rng.standard_normal((T, E, D)) / math.sqrt(D), "br": 3.0 * sign[0],
+             "wr_train": 0.5 * rng.standard_normal((T, E, D)) / math.sqrt(D), "br_train": 3.0 * sign[1]}
+        mats = ("w1", "w2", "wr", "wr_train")
+    else:
+        p = {"w1": rng.standard_normal((T, H, D)) / math.sqrt(D), "b1": 0.1 * rng.standard_normal((T, H)),
+             "w2": rng.standard_normal((T, D, H)) / math.sqrt(H), "b2": 0.1 * rng.standard_normal((T, D))}
+        mats = ("w1", "w2")
+    for k in ("ln1", "ln2"):
+        p[k + "_g"] = 1 + 0.1 * rng.standard_normal(D)
+        p[k + "_b"] = 0.1 * rng.standard_normal(D)
+    p = {k: v.astype(np.float32) for k, v in p.items()}
+    if dtype == "bf16":
+        for k in mats:
+            p[k] = si.to_bf16_bits(p[k])
+    case.blk = p
+    case.x = _act(rng, (B, T, D), dtype)
+    case.d_out = _act(rng, (B, T, D), dtype)
+    return case
+
+
+TRAIN_SEEDS = tuple(range(2000, 2032))

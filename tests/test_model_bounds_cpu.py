@@ -258,3 +258,53 @@ def test_sweep_cases_read_inside_their_buffers(lib, seed):
     outs = [t for t in (x, pooled, logit) if t is not None]
     _check_inside(recs, params + [inp] + outs + ([head["w"]] if head else []), ws,
                   must_read=[inp] + [t for t in params if t.dim() > 1])
+
+
+@pytest.mark.parametrize("seed", __import__("tests.sweep_cases", fromlist=["TRAIN_SEEDS"]).TRAIN_SEEDS)
+def test_training_sweep_cases_read_inside_their_buffers(lib, seed):
+    # every block of the GPU training sweep, its training forward and
+    # backward audited on host tensors (the saved tensors and the workspace
+    # are stand-ins at WS_BASE)
+    from tests import sweep_cases as sc
+    case = sc.draw_train(seed)
+    bf = bd.RM_BF16 if case.dtype == "bf16" else bd.RM_F32
+    blk = bd.upload_blocks([case.blk], device="cpu")[0]
+    x = bd.to_device(case.x, device="cpu")
+    d_out = bd.to_device(case.d_out, device="cpu")
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    B, T, D, H, E = case.B, case.T, case.D, case.H, case.E
+    bp = bd._block_struct(blk)
+    if case.kind == "dense":
+        saved_n = lib.rm_block_saved_bytes(B, T, D, H, bf)
+        ws = max(lib.rm_block_workspace_bytes(bd.RM_BLOCK_DENSE, B, T, D, H, 0, bf),
+                 lib.rm_block_bwd_workspace_bytes(B, T, D, H, bf))
+        shapes = [(T, H, D), (T, H), (T, D, H), (T, D), (D,), (D,), (D,), (D,)]
+        grads = [torch.empty(s, dtype=torch.float32) for s in shapes]
+        gs = bd.BlockGrads(*[t.data_ptr() for t in grads])
+        fwd = lambda: lib.rm_block_fwd_train(x.data_ptr(), C.byref(bp), y.data_ptr(), WS_BASE, saved_n, B, T, D, H,  # noqa: E731
+                                             bf, WS_BASE, ws, None)
+        bwd = lambda: lib.rm_block_bwd(x.data_ptr(), C.byref(bp), WS_BASE, saved_n, d_out.data_ptr(), dx.data_ptr(),  # noqa: E731
+                                       C.byref(gs), B, T, D, H, bf, WS_BASE, ws, None)
+        extra = []
+    else:
+        saved_n = max(lib.rm_moe_saved_bytes(B, T, D, H, E, bf), 16)
+        ws = lib.rm_moe_train_workspace_bytes(B, T, D, H, E, bf)
+        l_reg = torch.empty(1, dtype=torch.float32)
+        shapes = {"w1": (T, E, H, D), "b1": (T, E, H), "w2": (T, E, D, H), "b2": (T, E, D), "wr_train": (T, E, D),
+                  "br_train": (T, E), "wr": (T, E, D), "br": (T, E), "ln1_g": (D,), "ln1_b": (D,), "ln2_g": (D,),
+                  "ln2_b": (D,)}
+        grads = [torch.empty(shapes[k], dtype=torch.float32) for k in bd.MOE_GRADS]
+        gs = bd.MoeGrads(*[t.data_ptr() for t in grads])
+        wrt, brt = blk["wr_train"], blk["br_train"]
+        fwd = lambda: lib.rm_moe_block_fwd_train(x.data_ptr(), C.byref(bp), wrt.data_ptr(), brt.data_ptr(),  # noqa: E731
+                                                 y.data_ptr(), l_reg.data_ptr(), WS_BASE, saved_n, B, T, D, H, E, bf,
+                                                 WS_BASE, ws, None)
+        bwd = lambda: lib.rm_moe_block_bwd(x.data_ptr(), C.byref(bp), wrt.data_ptr(), brt.data_ptr(), 0.37,  # noqa: E731
+                                           WS_BASE, saved_n, d_out.data_ptr(), dx.data_ptr(), C.byref(gs), B, T, D, H,
+                                           E, bf, WS_BASE, ws, None)
+        extra = [l_reg]
+    params = _tensors(blk)
+    for call in (fwd, bwd):
+        recs = _audited(lib, call)
+        _check_inside(recs, params + [x, d_out, y, dx] + grads + extra, max(ws, saved_n))
