@@ -162,18 +162,28 @@ __global__ __launch_bounds__(256) void k_router_lds(const T* __restrict__ s, int
   }
 }
 
+// threads per workgroup of the count and the scatter: one workgroup per
+// (token, expert) group walks the batch in strides of this many samples
+constexpr int kCompactThreads = 1024;
+
 // counts[g] = #{b : gates[b, g] > 0}, g = t*E + j; one workgroup per group
-__global__ __launch_bounds__(256) void k_moe_count(const float* __restrict__ gates, int* __restrict__ counts,
-                                                   int64_t B, int G) {
+__global__ __launch_bounds__(kCompactThreads) void k_moe_count(const float* __restrict__ gates,
+                                                               int* __restrict__ counts, int64_t B, int G) {
+  constexpr int NW = kCompactThreads / kWave;
   const int g = blockIdx.x;
   int c = 0;
   for (int64_t b = threadIdx.x; b < B; b += blockDim.x) c += gates[b * G + g] > 0.f ? 1 : 0;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, kWave);
-  __shared__ int part[4];
+  __shared__ int part[NW];
   if (lane_id() == 0) part[threadIdx.x / kWave] = c;
   __syncthreads();
-  if (threadIdx.x == 0) counts[g] = part[0] + part[1] + part[2] + part[3];
+  if (threadIdx.x == 0) {
+    int n = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) n += part[w];
+    counts[g] = n;
+  }
 }
 
 // offsets = exclusive scan of counts; tile list of (g, m0) pairs with bm rows
@@ -222,13 +232,14 @@ __global__ __launch_bounds__(256) void k_moe_scan(const int* __restrict__ counts
 }
 
 // stable scatter: entry offsets[g] + rank of each active b (in increasing b)
-__global__ __launch_bounds__(256) void k_moe_scatter(const float* __restrict__ gates,
-                                                     const int* __restrict__ offsets, int* __restrict__ rows,
-                                                     float* __restrict__ gatec, int* __restrict__ pos,
-                                                     int64_t B, int G) {
+__global__ __launch_bounds__(kCompactThreads) void k_moe_scatter(const float* __restrict__ gates,
+                                                                 const int* __restrict__ offsets,
+                                                                 int* __restrict__ rows, float* __restrict__ gatec,
+                                                                 int* __restrict__ pos, int64_t B, int G) {
+  constexpr int NW = kCompactThreads / kWave;
   const int g = blockIdx.x;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
-  __shared__ int wtot[4];
+  __shared__ int wtot[NW];
   int running = offsets[g];
   for (int64_t base = 0; base < B; base += blockDim.x) {
     const int64_t b = base + threadIdx.x;
@@ -238,9 +249,12 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const float* __restrict__ g
     const int before = __popcll(mask & ((1ull << lane) - 1ull));
     if (lane == 0) wtot[wave] = __popcll(mask);
     __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wave; ++w) wbase += wtot[w];
-    const int total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    int wbase = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      wbase += w < wave ? wtot[w] : 0;
+      total += wtot[w];
+    }
     if (b < B) {
       if (on) {
         const int idx = running + wbase + before;
@@ -440,9 +454,10 @@ hipError_t launch_moe_router(const void* s, int64_t sb, int64_t sT, const void* 
 hipError_t launch_moe_compact(const MoeWork& w, int64_t B, int T, int E, int bm, hipStream_t st) {
   const int G = T * E;
   if (G > kMaxGroups) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_moe_count, dim3(G), dim3(256), 0, st, w.gates, w.counts, B, G);
+  hipLaunchKernelGGL(k_moe_count, dim3(G), dim3(kCompactThreads), 0, st, w.gates, w.counts, B, G);
   hipLaunchKernelGGL(k_moe_scan, dim3(1), dim3(256), 0, st, w.counts, w.offsets, w.tiles, w.ntiles, G, bm);
-  hipLaunchKernelGGL(k_moe_scatter, dim3(G), dim3(256), 0, st, w.gates, w.offsets, w.rows, w.gatec, w.pos, B, G);
+  hipLaunchKernelGGL(k_moe_scatter, dim3(G), dim3(kCompactThreads), 0, st, w.gates, w.offsets, w.rows, w.gatec,
+                     w.pos, B, G);
   return hipGetLastError();
 }
 
