@@ -888,6 +888,8 @@ def main() -> int:
         "mix_ln1": 2 * cfg.B * cfg.T * cfg.D * eb,
         "ln2": cfg.B * cfg.T * cfg.D * 3 * eb,  # Z and the residual S in, X' out
         "ln2_mix_ln1": cfg.B * cfg.T * cfg.D * 3 * eb,  # Z and S in, the next block's S out
+        # the fp32 embedding in (each element once), the first block's S out
+        "tokenize_mix_ln1": cfg.B * (4 * cfg.F + cfg.T * cfg.D * eb),
     }
     def table(prof):
         kern = {}

@@ -1589,15 +1589,30 @@ rm_status rm_model_fwd(const rm_model_desc* m, const void* in, void* x_out, floa
   const int T = m->T, D = m->D, dt = m->dtype;
   const void* cur = in;
   int next = 0;
-  if (m->F > 0) {
+  // every block kind carves S first, so S sits at the same address for all
+  // blocks and a boundary pass can leave the next block's S there
+  bool s_given = false;
+  if (m->F > 0 && m->L > 0 && !(m->blocks[0].flags & RM_BLOCK_NO_MIX_NORM) &&
+      rm::mix_ln_emb_supported(T, D, m->F, dt)) {
+    // block 0's token mix + LayerNorm 1 read the embedding in place: the
+    // tokenized X0 never reaches HBM
+    const rm_block_params& p0 = m->blocks[0];
+    Carver bc(blk_region);
+    BlockWs w0;
+    block_ws(bc, p0.kind, B, T, D, p0.hidden, p0.E, dt, &w0);
+    audit("mix_ln1_emb.emb", in, B * m->F * 4);
+    audit("mix_ln1_emb.ln1_g", p0.ln1_g, (int64_t)D * 4);
+    audit("mix_ln1_emb.ln1_b", p0.ln1_b, (int64_t)D * 4);
+    RM_TIMED("tokenize_mix_ln1", st,
+             RM_HIP(rm::launch_mix_ln_emb((const float*)in, m->F, w0.S, p0.ln1_g, p0.ln1_b, B, T, D, dt, st),
+                    "pad-split tokenizer + token mix + LayerNorm"));
+    s_given = true;
+  } else if (m->F > 0) {
     audit("tokenize.emb", in, B * m->F * 4);
     RM_TIMED("tokenize", st, RM_HIP(rm::launch_tokenize_padsplit((const float*)in, B, m->F, T, D, dt, buf[0], st), "tokenize"));
     cur = buf[0];
     next = 1;
   }
-  // every block kind carves S first, so S sits at the same address for all
-  // blocks and a boundary pass can leave the next block's S there
-  bool s_given = false;
   for (int l = 0; l < m->L; ++l) {
     void* dst = (l == m->L - 1 && x_out) ? x_out : buf[next];
     // this block's own layout in the shared region

@@ -177,6 +177,94 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln(const T* __res
 }
 
 // ---------------------------------------------------------------------------
+// The same S computed straight from the pad-split tokenizer's input: element
+// (t, k) of sample b's X0 is emb[b][t*D + k] cast to T (0 past F), read where
+// it lies, so X0 is never written.  F % 4 == 0 keeps every sample's row
+// 16-byte aligned; a piece that straddles F is read element by element.
+
+template <typename T, int N>
+__device__ __forceinline__ void load_emb(const float* __restrict__ er, int idx, int F, float (&out)[N]) {
+  if (idx + N <= F) {
+    float f[N];
+    load_f32<float, N>(er + idx, f);
+#pragma unroll
+    for (int e = 0; e < N; ++e) out[e] = to_f32(from_f32<T>(f[e]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e) out[e] = idx + e < F ? to_f32(from_f32<T>(er[idx + e])) : 0.f;
+  }
+}
+
+template <typename T, int VEC, int MAXI>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_mix_ln_emb(const float* __restrict__ emb, int F,
+                                                                      T* __restrict__ s, const float* __restrict__ g,
+                                                                      const float* __restrict__ beta, int64_t B,
+                                                                      int T_, int D) {
+  constexpr int OV = 16 / (int)sizeof(T), PV = OV / VEC;
+  static_assert(OV % VEC == 0, "pieces of a chunk");
+  const int64_t row = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * kRowsPerBlock + (threadIdx.x / kWave);
+  if (row >= B * T_) return;
+  const int lane = lane_id();
+  const int64_t b = row / T_;
+  const int t = (int)(row - b * T_);
+  const int d = D / T_;
+  const float* er = emb + b * (int64_t)F;
+  const int nch = D / OV;
+  float v[MAXI][OV];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+      const int k = c * OV;
+      float m[OV], r[OV];
+#pragma unroll
+      for (int pc = 0; pc < PV; ++pc) {
+        const int kp = k + pc * VEC;
+        const int tp = kp / d, j = kp - tp * d;
+        float piece[VEC];
+        load_emb<T, VEC>(er, tp * D + t * d + j, F, piece);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) m[pc * VEC + e] = piece[e];
+      }
+      load_emb<T, OV>(er, t * D + k, F, r);
+#pragma unroll
+      for (int e = 0; e < OV; ++e) {
+        v[i][e] = m[e] + r[e];
+        sum += v[i][e];
+      }
+    }
+  }
+  const float mean = wave_sum(sum) / (float)D;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < OV; ++e) {
+        const float q = v[i][e] - mean;
+        sq += q * q;
+      }
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D + ln_eps());
+  // token-major S row (b, t) at [t][b]
+  T* sr = s + ((int64_t)t * B + b) * (int64_t)D;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nch) {
+      const int k = c * OV;
+      float o[OV];
+#pragma unroll
+      for (int e = 0; e < OV; ++e) o[e] = (v[i][e] - mean) * rstd * g[k + e] + beta[k + e];
+      store_from_f32<T, OV>(sr + k, o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // out[r,:] = LN(z[r,:] + res[r,:]) * g + beta over rows of D (D % 8 == 0), 8
 // elements per lane-chunk, fp32 arithmetic.  Row r = b * Tn + t; the residual
 // (optional) of row r starts at res + b * res_bs + t * res_ts, so a
@@ -521,6 +609,45 @@ hipError_t launch_mix_ln(const void* x, void* so, const float* g, const float* b
     case 4: return mix_ln_vec<float, 4>(x, so, g, b, B, T, D, tm, s);
     case 2: return mix_ln_vec<float, 2>(x, so, g, b, B, T, D, tm, s);
     default: return mix_ln_vec<float, 1>(x, so, g, b, B, T, D, tm, s);
+  }
+}
+
+template <typename T, int VEC>
+hipError_t mix_ln_emb_vec(const float* emb, int F, void* so, const float* g, const float* b, int64_t B, int T_,
+                          int D, hipStream_t s) {
+  const dim3 grid((unsigned)((B * T_ + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * kWave);
+  T* ss = (T*)so;
+  switch (pick_maxi(D / (16 / (int)sizeof(T)))) {
+    case 0: return hipErrorInvalidValue;
+    case 1: hipLaunchKernelGGL((k_mix_ln_emb<T, VEC, 1>), grid, block, 0, s, emb, F, ss, g, b, B, T_, D); break;
+    case 2: hipLaunchKernelGGL((k_mix_ln_emb<T, VEC, 2>), grid, block, 0, s, emb, F, ss, g, b, B, T_, D); break;
+    case 4: hipLaunchKernelGGL((k_mix_ln_emb<T, VEC, 4>), grid, block, 0, s, emb, F, ss, g, b, B, T_, D); break;
+    case 8: hipLaunchKernelGGL((k_mix_ln_emb<T, VEC, 8>), grid, block, 0, s, emb, F, ss, g, b, B, T_, D); break;
+    default: hipLaunchKernelGGL((k_mix_ln_emb<T, VEC, 16>), grid, block, 0, s, emb, F, ss, g, b, B, T_, D); break;
+  }
+  return hipGetLastError();
+}
+
+bool mix_ln_emb_supported(int T, int D, int64_t F, int dt) {
+  return F > 0 && F % 4 == 0 && F <= (int64_t)T * D && row_width_supported(T, D, dt);
+}
+
+hipError_t launch_mix_ln_emb(const float* emb, int64_t F, void* so, const float* g, const float* b, int64_t B, int T,
+                             int D, int dt, hipStream_t s) {
+  if (!mix_ln_emb_supported(T, D, F, dt)) return hipErrorInvalidValue;
+  const int d = D / T;
+  if (dt == kBF16) {
+    switch (chunk_elems(d, 2)) {
+      case 8: return mix_ln_emb_vec<bf16, 8>(emb, (int)F, so, g, b, B, T, D, s);
+      case 4: return mix_ln_emb_vec<bf16, 4>(emb, (int)F, so, g, b, B, T, D, s);
+      case 2: return mix_ln_emb_vec<bf16, 2>(emb, (int)F, so, g, b, B, T, D, s);
+      default: return mix_ln_emb_vec<bf16, 1>(emb, (int)F, so, g, b, B, T, D, s);
+    }
+  }
+  switch (chunk_elems(d, 4)) {
+    case 4: return mix_ln_emb_vec<float, 4>(emb, (int)F, so, g, b, B, T, D, s);
+    case 2: return mix_ln_emb_vec<float, 2>(emb, (int)F, so, g, b, B, T, D, s);
+    default: return mix_ln_emb_vec<float, 1>(emb, (int)F, so, g, b, B, T, D, s);
   }
 }
 

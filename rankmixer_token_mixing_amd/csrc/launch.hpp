@@ -24,6 +24,12 @@ hipError_t launch_token_mix(const void* x, void* y, int64_t B, int T, int D, int
 // token_major, at [t][b] (so the rows of one token are contiguous)
 hipError_t launch_mix_ln(const void* x, void* s_out, const float* g, const float* b, int64_t B,
                          int T, int D, int dt, bool token_major, hipStream_t s);
+// the same S, token-major, from the pad-split tokenizer's fp32 input emb
+// [B][F] (X0[b][t][k] = emb[b][t*D + k] cast to dt, 0 past F) without
+// writing X0; F % 4 == 0 and F <= T*D
+bool mix_ln_emb_supported(int T, int D, int64_t F, int dt);
+hipError_t launch_mix_ln_emb(const float* emb, int64_t F, void* s_out, const float* g, const float* b, int64_t B,
+                             int T, int D, int dt, hipStream_t s);
 // out = LN(z) for fp32 rows z [rows][D]
 // out[r] = LN(z[r] + res[r]) * g + b over rows r = b*Tn + t (fp32 math); z,
 // res (optional) and out in dtype dt, res row r at res + b * res_bs + t * res_ts

@@ -183,3 +183,37 @@ def test_ragged_tiles_of_the_pipelined_products():
     rows = np.unique(np.concatenate([si.random_rows(cfg.B, 24, seed=3), np.arange(1024, 1100, 7), [1099]]))
     ref = orc.block_fwd(inputs["x"][rows], blk)
     assert rel_l2_rows(y[rows], ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,B,T,D,F,kinds", [
+    ("bf16", 4096, 16, 320, 5000, ("dense", "dense")),   # the pad-split model's shape (pieces of 4)
+    ("bf16", 100, 4, 64, 100, ("dense",)),               # pieces of 8, one straddling F = 100
+    ("bf16", 70, 4, 64, 4, ("moe", "dense")),            # four floats, the rest padding
+    ("bf16", 33, 8, 128, 1024, ("swiglu", "dense")),     # F = T * D: no padding
+    ("f32", 65, 5, 40, 196, ("dense", "moe")),           # fp32, heads of 8, pieces of 4 straddling F
+])
+def test_tokenizer_fused_into_the_first_mix_is_exact(dtype, B, T, D, F, kinds):
+    # rm_model_fwd reads the embedding in place where F % 4 == 0 and block 0
+    # starts with the token mix + LayerNorm 1; the result equals tokenizing
+    # first and running the same blocks on X0, bit for bit
+    from rankmixer_token_mixing_amd import binding as bd
+    from tests.test_gpu_boundary import _block
+    rng = np.random.default_rng(B + F)
+    emb = (0.3 * rng.standard_normal((B, F))).astype(np.float32)
+    np_blocks = [_block(k, T, D, 64, dtype, 60 + i) for i, k in enumerate(kinds)]
+    blocks = bd.upload_blocks(np_blocks)
+    head_w = (rng.standard_normal(D) / D).astype(np.float32)
+    head = {"w": bd.to_device(head_w), "c": 0.25}
+    fused = bd.Model(blocks, T, D, DT[dtype], F=F, head=head)
+    plain = bd.Model(blocks, T, D, DT[dtype], F=0, head=head)
+    embd = bd.to_device(emb)
+    note(f"[gpu] fused tokenizer {dtype} B={B} T={T} D={D} F={F} {kinds}")
+    a = bd.rm_model_fwd(fused, embd, want_x=True, want_pooled=True)
+    x0 = bd.rm_tokenize_padsplit(embd, T, D, DT[dtype])
+    b = bd.rm_model_fwd(plain, x0, want_x=True, want_pooled=True)
+    torch.cuda.synchronize()
+    for k in ("x", "pooled", "logit"):
+        assert torch.equal(a[k], b[k]), k
+    if B <= 100:
+        ref = orc.model_fwd(emb, np_blocks, T, D, dtype, F, {"w": head_w, "c": head["c"]})
+        assert rel_l2_rows(host(a["x"]), ref["x"]) <= TOL[dtype]
