@@ -340,8 +340,8 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void k_ln_rows(const T* __re
 constexpr int kBndThreads = 1024;
 constexpr int kBndLdsMax = 128 * 1024;
 
-template <typename T, int VEC, int MAXI>
-__global__ __launch_bounds__(kBndThreads) void k_ln_mix_ln(const T* __restrict__ z, T* s,
+template <typename T, int VEC, int MAXI, int R>
+__global__ __launch_bounds__(R == 2 ? kBndThreads : kBndThreads / 2) void k_ln_mix_ln(const T* __restrict__ z, T* s,
                                                            const float* __restrict__ g2,
                                                            const float* __restrict__ be2,
                                                            const float* __restrict__ g1,
@@ -351,18 +351,21 @@ __global__ __launch_bounds__(kBndThreads) void k_ln_mix_ln(const T* __restrict__
   static_assert(OV % VEC == 0, "pieces of a chunk");
   extern __shared__ uint4 bnd_lds[];
   T* xl = reinterpret_cast<T*>(bnd_lds);
-  const int NW = blockDim.x / kWave;  // T/2 waves (at most 16): two rows each
+  const int NW = blockDim.x / kWave;  // T/R waves (at most 16): R rows each
   const int64_t b = blockIdx.x;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int d = D / T_, nch = D / OV;
-  // phase 1, two rows per wave at a time: every load of both rows is issued
-  // before any is used (chunk indices past the row re-read its last chunk and
+  // phase 1, R rows per wave at a time (rows t0, t0 + NW, ...): every load of
+  // those rows is issued before any is used (a row index past T re-reads row
+  // t0 and is skipped; chunk indices past the row re-read its last chunk and
   // are left out of the sums and stores)
-  for (int t0 = wave; t0 < T_; t0 += 2 * NW) {
-    const int tr[2] = {t0, t0 + NW < T_ ? t0 + NW : t0};
-    float v[2][MAXI][OV], q[2][MAXI][OV];
+  for (int t0 = wave; t0 < T_; t0 += R * NW) {
+    int tr[R];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < R; ++r) tr[r] = t0 + r * NW < T_ ? t0 + r * NW : t0;
+    float v[R][MAXI][OV], q[R][MAXI][OV];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
       const T* zr = z + (b * T_ + tr[r]) * (int64_t)D;
       const T* sr = s + ((int64_t)tr[r] * B + b) * D;
 #pragma unroll
@@ -373,8 +376,8 @@ __global__ __launch_bounds__(kBndThreads) void k_ln_mix_ln(const T* __restrict__
       }
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      if (r == 1 && t0 + NW >= T_) break;
+    for (int r = 0; r < R; ++r) {
+      if (r > 0 && t0 + r * NW >= T_) break;
       float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < MAXI; ++i) {
@@ -656,24 +659,42 @@ namespace {
 // up to 16 bytes
 int bnd_pitch(int T, int D, int eb) { return D + ((D / T * eb + 15) / 16 * 16) / eb; }
 
-template <typename T, int VEC>
-hipError_t ln_mix_ln_vec(const void* z, void* s, const float* g2, const float* b2, const float* g1,
-                         const float* b1, int64_t B, int T_, int D, hipStream_t st) {
+template <typename T, int VEC, int R>
+hipError_t ln_mix_ln_rows(const void* z, void* s, const float* g2, const float* b2, const float* g1,
+                          const float* b1, int64_t B, int T_, int D, hipStream_t st) {
   const int pitch = bnd_pitch(T_, D, (int)sizeof(T));
   const size_t lds = (size_t)T_ * pitch * sizeof(T);
-  const int nw = std::min(kBndThreads / kWave, std::max(1, (T_ + 1) / 2));
+  const int nw = std::min(kBndThreads / kWave, std::max(1, (T_ + R - 1) / R));
   const dim3 grid((unsigned)B), block(nw * kWave);
   const T* zz = (const T*)z;
   T* ss = (T*)s;
-  switch (pick_maxi3(D / (16 / (int)sizeof(T)))) {
+  const int maxi = pick_maxi3(D / (16 / (int)sizeof(T)));
+  if constexpr (R == 4) {  // rows of two chunks per lane only
+    if (maxi != 2) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 2, R>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch);
+    return hipGetLastError();
+  }
+  switch (maxi) {
     case 0: return hipErrorInvalidValue;
-    case 3: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 3>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
-    case 1: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 1>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
-    case 2: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 2>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
-    case 4: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 4>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
+    case 3: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 3, R>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
+    case 1: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 1, R>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
+    case 2: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 2, R>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
+    case 4: hipLaunchKernelGGL((k_ln_mix_ln<T, VEC, 4, R>), grid, block, lds, st, zz, ss, g2, b2, g1, b1, B, T_, D, pitch); break;
     default: return hipErrorInvalidValue;  // wider rows: see ln_mix_ln_supported
   }
   return hipGetLastError();
+}
+
+template <typename T, int VEC>
+hipError_t ln_mix_ln_vec(const void* z, void* s, const float* g2, const float* b2, const float* g1,
+                         const float* b1, int64_t B, int T_, int D, hipStream_t st) {
+  // rows of two chunks per lane (D of 1024 bf16 or 512 fp32 at most): four rows per wave,
+  // so twice the samples fit on a compute unit (rows of D = 768 with T = 16:
+  // 53.2-53.8 against 56.5-56.7 us per pass); one-chunk rows (D = 320, T = 16)
+  // measured slower that way (49-50 against 45 us) and keep two
+  const int maxi = pick_maxi3(D / (16 / (int)sizeof(T)));
+  if (maxi == 2 && T_ <= 32) return ln_mix_ln_rows<T, VEC, 4>(z, s, g2, b2, g1, b1, B, T_, D, st);
+  return ln_mix_ln_rows<T, VEC, 2>(z, s, g2, b2, g1, b1, B, T_, D, st);
 }
 }  // namespace
 

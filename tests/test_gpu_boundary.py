@@ -101,6 +101,11 @@ def test_mixed_kinds():
     ("bf16", 600, 32, 1536, 32),  # the ~1B-class shape: three chunks per lane, the LDS nearly full
     ("bf16", 70, 64, 128, 32),    # T > 32: each wave normalises several pairs of rows
     ("bf16", 40, 16, 2048, 32),   # four chunks per lane
+    # two chunks per lane: four rows per wave in the first phase
+    ("bf16", 131, 16, 768, 64),   # the ~100M-class width
+    ("bf16", 77, 5, 640, 32),     # T = 5: waves of three and of two rows
+    ("f32", 45, 12, 480, 32),     # fp32 rows of 120 chunks, heads of 40
+    ("bf16", 50, 32, 1024, 32),   # T = 32 at the widest such row
 ])
 def test_dense_stacks(dtype, B, T, D, H):
     blocks = [_block("dense", T, D, H, dtype, 20 + i) for i in range(3)]
