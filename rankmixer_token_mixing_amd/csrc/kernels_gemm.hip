@@ -1388,6 +1388,15 @@ bool gemm_kmajor_pipe_fits(const GemmArgs& a) {
 int choose_cfg(const GemmArgs& a) {
   if (a.tile_cfg >= 0 && a.tile_cfg < kNumCfgs) return a.tile_cfg;
   if (a.row_off) return kMoeCfg;
+  {
+    // eight waves on 256 x 256 tiles wherever they fill at least one round of
+    // the persistent grid with little padding: a part-filled last round costs
+    // less than running every tile on four waves (one per SIMD) of 256 x 128
+    // (B = 2048, T = 16, N = 768, K = 3072: 155-158 against 168-169 us)
+    const long long tm = ceil_div(a.M, 256), tn = ceil_div(a.N, 256);
+    const double eff = (double)a.M * a.N / ((double)tm * 256 * tn * 256);
+    if ((long long)a.G * tm * tn >= device_cus() && eff >= 0.8) return 0;
+  }
   for (int c = 0; c < kNumCfgs; ++c) {
     const TileCfg& t = kCfgs[c];
     const long long tm = ceil_div(a.M, t.bm()), tn = ceil_div(a.N, t.bn());
